@@ -1,0 +1,241 @@
+"""Dense float64 definitions of the layer-end selection path.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources (the pages' titles; section / equation / algorithm of each):
+
+* TideKV -- "Delayed KV Eviction via Layer-Wise Chunked Prefill for
+  Memory-Efficient Long-Context LLM Inference": §4.2 Eqs. (4)-(8),
+  Algorithm 2 (LayerEndCompress), §4.3 memory model, §6.1 setup.
+* QEvict -- "Recoverable Quantized KV Eviction for Attention-Drift-Robust
+  Long-Context Decoding": §4.2 cumulative window scoring, §4.3 recoverable
+  hierarchy, Appendix A routing.
+
+Readings where the pages are silent (each also listed in the design doc):
+pooling weights w_q = 1; GQA aggregation is a sum over the group with query
+head h mapped to KV head floor(h / G); the 1-D max-pool over key positions runs
+over the candidate range only, stride 1, window clipped at its edges; ties in
+the pooled score are broken by lowest position; the retained set is emitted in
+ascending position order; ``budget`` counts non-mandatory picks.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(D), the logit scale of TideKV Eq. (4)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def logits(q: np.ndarray, k: np.ndarray, *, causal: bool, scale: float) -> np.ndarray:
+    """Observation logits l[q, i] = (Q_q . K_i) * scale   (TideKV Eq. (4)).
+
+    q: [W, D] float64 observation queries, k: [S, D] float64 keys.  With
+    ``causal`` the W queries sit at absolute positions S-W .. S-1 and a key past
+    the query's own position gets -inf ("logits for keys beyond its causal
+    position are set to -inf", §4.2).  Without it (decode queries that follow
+    the cache) every key is visible.
+    """
+    W = q.shape[0]
+    S = k.shape[0]
+    l = (q @ k.T) * scale
+    if causal:
+        qpos = (S - W) + np.arange(W)
+        future = np.arange(S)[None, :] > qpos[:, None]
+        l = np.where(future, -np.inf, l)
+    return l
+
+
+def softmax_rows(l: np.ndarray) -> np.ndarray:
+    """a[q, i] = exp(l[q, i] - M_q) / Z_q with M_q = max_i l, Z_q = sum_i exp(l - M_q).
+
+    This is the fixed point of TideKV's two-pass recurrence (Eqs. (5)-(6) give
+    M_q and Z_q after the last key block; Eq. (7), left, forms a): computed
+    here densely, whole rows at once.
+    """
+    M = l.max(axis=1, keepdims=True)
+    e = np.exp(l - M)
+    Z = e.sum(axis=1, keepdims=True)
+    return e / Z
+
+
+def head_scores(q_obs: np.ndarray, k: np.ndarray, *, causal: bool = True,
+                scale: float | None = None) -> np.ndarray:
+    """Per-KV-head key importance s[b, h_kv, i]   (TideKV Eq. (7), right; §4.2 GQA).
+
+    s = sum over the G query heads of the KV group and over the W window
+    queries of a[q, i] (pooling weights w_q = 1).  Query head h belongs to KV
+    head floor(h / G).  q_obs: [Bt, Hq, W, D], k: [Bt, Hkv, S, D] (float64).
+    Returns float64 [Bt, Hkv, S].  Loops per query head so that only one
+    [W, S] logit matrix is alive at a time.
+    """
+    Bt, Hq, W, D = q_obs.shape
+    _, Hkv, S, _ = k.shape
+    assert Hq % Hkv == 0 and k.shape[3] == D
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(D)
+    s = np.zeros((Bt, Hkv, S), dtype=np.float64)
+    for b in range(Bt):
+        for h in range(Hq):
+            hk = h // G
+            a = softmax_rows(logits(q_obs[b, h], k[b, hk], causal=causal, scale=scale))
+            s[b, hk] += a.sum(axis=0)
+    return s
+
+
+def max_pool(s: np.ndarray, kernel: int, lo: int, hi: int) -> np.ndarray:
+    """1-D max-pool of the key scores along positions over the candidate range.
+
+    p[i] = max{ s[j] : j in [i-h, i+h] and lo <= j < hi },  h = (kernel-1)/2,
+    for lo <= i < hi; entries outside [lo, hi) are 0.  This is the smoothing
+    step "pool to p_i" of TideKV Algorithm 2 read as a stride-1, same-length
+    max filter that does not reach into the mandatory ranges (the pages give
+    no kernel; its size comes from the workload).
+    """
+    assert kernel >= 1 and kernel % 2 == 1
+    h = (kernel - 1) // 2
+    S = s.shape[-1]
+    p = np.zeros_like(s)
+    if hi <= lo:
+        return p
+    ext = np.full(s.shape[:-1] + (S + 2 * h,), -np.inf)
+    ext[..., lo + h:hi + h] = s[..., lo:hi]
+    best = np.full(s.shape[:-1] + (hi - lo,), -np.inf)
+    for off in range(-h, h + 1):
+        best = np.maximum(best, ext[..., lo + h + off:hi + h + off])
+    p[..., lo:hi] = best
+    return p
+
+
+def select(p: np.ndarray, budget: int, n_sink: int, window: int) -> np.ndarray:
+    """Retained positions per (b, h_kv)   (TideKV Eq. (8); Algorithm 2 selection).
+
+    R = Top_budget{ p_i : n_sink <= i < S-W }  U  [0, n_sink)  U  [S-W, S),
+    where the mandatory set (sinks and the observation window) is always kept
+    and ``budget`` counts the non-mandatory picks, so |R| = budget + n_sink + W.
+    Candidates are ordered by (p descending, position ascending); R is returned
+    in ascending position order as int32 [Bt, Hkv, budget + n_sink + W].
+    """
+    S = p.shape[-1]
+    lo, hi = n_sink, S - window
+    if not (0 <= n_sink and 1 <= window <= S and lo <= hi and 0 <= budget <= hi - lo):
+        raise ValueError("infeasible budget / window")
+    lead = p.shape[:-1]
+    flat = p.reshape(-1, S)
+    out = np.empty((flat.shape[0], budget + n_sink + window), dtype=np.int32)
+    cand = np.arange(lo, hi)
+    for r in range(flat.shape[0]):
+        order = np.lexsort((cand, -flat[r, lo:hi]))   # last key is primary
+        top = cand[order[:budget]]
+        keep = np.concatenate([np.arange(0, lo), top, np.arange(hi, S)])
+        keep.sort()
+        assert keep.size == budget + n_sink + window
+        out[r] = keep
+    return out.reshape(lead + (out.shape[1],))
+
+
+def compact_rows(x: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Gather retained rows x[b, h, idx[b, h, r], :]   (TideKV Algorithm 2, GATHER).
+
+    x: [Bt, Hkv, S, D] of any dtype (bit patterns are copied unchanged),
+    idx: [Bt, Hkv, n]. Returns [Bt, Hkv, n, D].
+    """
+    return np.take_along_axis(x, idx.astype(np.int64)[..., None], axis=2)
+
+
+def layer_end_compress(q_obs, k, v, *, budget, window, pool_kernel, n_sink=0,
+                       causal=True, scale=None, k_store=None, v_store=None):
+    """LayerEndCompress end to end: scores -> pool -> select -> gather.
+
+    q_obs/k are float64 values; k_store/v_store are the stored tensors (bits)
+    to gather from (default: k and v themselves).  Returns a dict with s, p,
+    idx, k_hat, v_hat.
+    """
+    S = k.shape[2]
+    s = head_scores(q_obs, k, causal=causal, scale=scale)
+    p = max_pool(s, pool_kernel, n_sink, S - window)
+    idx = select(p, budget, n_sink, window)
+    ks = k if k_store is None else k_store
+    vs = v if v_store is None else v_store
+    return {"s": s, "p": p, "idx": idx,
+            "k_hat": compact_rows(ks, idx), "v_hat": compact_rows(vs, idx)}
+
+
+# ---------------------------------------------------------------------------
+# QEvict-style window tiers
+# ---------------------------------------------------------------------------
+
+def window_sums(s: np.ndarray, win: int) -> np.ndarray:
+    """Cumulative window score w_j = sum_{i in window j} s_i over contiguous
+    windows of ``win`` tokens (QEvict §4.2: windows are ranked by accumulated
+    attention).  s: [..., S] with S a multiple of win -> [..., S/win]."""
+    S = s.shape[-1]
+    assert S % win == 0
+    return s.reshape(s.shape[:-1] + (S // win, win)).sum(axis=-1)
+
+
+def route_tiers(w: np.ndarray, n_full: int, n_quant: int):
+    """Rank windows by (w descending, index ascending); the first n_full go to
+    the full-precision tier (0), the next n_quant to the low-bit tier (1) and
+    the rest are evicted (2)   (QEvict §4.3 and Appendix A: routing by rank
+    under the tier capacities).
+
+    Returns (tier int8 [..., nW], rank int32 [..., nW]) where rank[j] is the
+    0-based position of window j in that order.
+    """
+    nW = w.shape[-1]
+    flat = w.reshape(-1, nW)
+    tier = np.empty(flat.shape, dtype=np.int8)
+    rank = np.empty(flat.shape, dtype=np.int32)
+    j = np.arange(nW)
+    for r in range(flat.shape[0]):
+        order = np.lexsort((j, -flat[r]))
+        rank[r, order] = j
+    tier[:] = np.where(rank < n_full, 0, np.where(rank < n_full + n_quant, 1, 2))
+    return tier.reshape(w.shape), rank.reshape(w.shape)
+
+
+def quant_int4(x: np.ndarray):
+    """Asymmetric 4-bit codes of one group of values along axis 0.
+
+    QEvict quantises the recoverable tier with an asymmetric low-bit code
+    (§4.3; the summary names no formula).  Reading used: per group, lo = min,
+    hi = max, scale = (hi - lo) / 15, code = clip(rint((x - lo) / scale), 0, 15)
+    with round-half-to-even, codes 0 when scale == 0.  Evaluated in float32
+    with exactly this operation order so the codes are decided in the same
+    precision as on the device.
+
+    x: float32 [n, ...] -> (codes uint8 [n, ...], lo float32 [...], scale float32 [...]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    lo = x.min(axis=0)
+    hi = x.max(axis=0)
+    scale = np.float32(hi - lo) / np.float32(15.0)
+    scale = np.asarray(scale, dtype=np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    q = np.rint((x - lo).astype(np.float32) / safe).astype(np.float32)
+    q = np.clip(q, 0, 15)
+    q = np.where(scale == 0, np.float32(0.0), q)
+    return q.astype(np.uint8), lo.astype(np.float32), scale
+
+
+def dequant_int4(codes: np.ndarray, lo: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """x_hat = lo + code * scale in float32 with two roundings (multiply, then
+    add; no fused multiply-add).  Returns float32; the caller rounds to bf16."""
+    prod = (codes.astype(np.float32) * scale.astype(np.float32)).astype(np.float32)
+    return (lo.astype(np.float32) + prod).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Memory model
+# ---------------------------------------------------------------------------
+
+def cache_bytes(n_layers: int, batch: int, n_kv_heads: int, tokens: int,
+                head_dim: int, elem_bytes: int) -> int:
+    """Bytes of a K+V cache: 2 * N * B * H_kv * tokens * D * b
+    (TideKV §3, prompt KV size; §4.3 active-layer KV with N = 1)."""
+    return 2 * n_layers * batch * n_kv_heads * tokens * head_dim * elem_bytes

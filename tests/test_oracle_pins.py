@@ -1,0 +1,316 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle:
+brute force in plain Python, closed forms, invariants the pages state, and
+the memory figures the pages print (tests/golden/memory_pins.json)."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- scores ----
+
+def _brute_scores(q, k, causal, scale):
+    """Triple loops with math.exp: every logit, row max, normaliser and sum
+    written out element by element (independent of numpy matmul/broadcast)."""
+    Bt, Hq, W, D = q.shape
+    _, Hkv, S, _ = k.shape
+    G = Hq // Hkv
+    s = [[[0.0] * S for _ in range(Hkv)] for _ in range(Bt)]
+    for b in range(Bt):
+        for h in range(Hq):
+            hk = h // G
+            for qi in range(W):
+                pos = S - W + qi
+                row = []
+                for i in range(S):
+                    if causal and i > pos:
+                        row.append(None)
+                        continue
+                    acc = 0.0
+                    for d in range(D):
+                        acc += float(q[b, h, qi, d]) * float(k[b, hk, i, d])
+                    row.append(acc * scale)
+                m = max(x for x in row if x is not None)
+                z = sum(math.exp(x - m) for x in row if x is not None)
+                for i, x in enumerate(row):
+                    if x is not None:
+                        s[b][hk][i] += math.exp(x - m) / z
+    return np.array(s)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_scores_match_brute_force(causal):
+    q = _rand((2, 4, 3, 5), 1)
+    k = _rand((2, 2, 11, 5), 2, 1.5)
+    sc = 0.37
+    got = oracle.head_scores(q, k, causal=causal, scale=sc)
+    ref = _brute_scores(q, k, causal, sc)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    q = _rand((1, 2, 2, 16), 3)
+    k = _rand((1, 1, 9, 16), 4)
+    np.testing.assert_allclose(oracle.head_scores(q, k),
+                               _brute_scores(q, k, True, 0.25), rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_row_sums_give_w_times_group(causal):
+    spec = synth.config(1)
+    x = synth.make_layer(spec, 1)
+    q = synth.to_f64(x["q"], spec.dtype)
+    k = synth.to_f64(x["k"], spec.dtype)
+    s = oracle.head_scores(q, k, causal=causal)
+    np.testing.assert_allclose(s.sum(-1), spec.obs_window * spec.group, rtol=1e-12)
+
+
+def _harmonic(n):
+    return sum(Fraction(1, j) for j in range(1, n + 1))
+
+
+@pytest.mark.parametrize("how", ["equal_keys", "zero_queries"])
+def test_closed_form_uniform_attention(how):
+    """All logits of a row equal -> a[q,i] = 1/(S-W+q+1) on visible keys, so a
+    prefix key gets G*(H_S - H_{S-W}) and window key S-W+r gets
+    G*(H_S - H_{S-W+r})."""
+    Bt, Hq, Hkv, D, S, W = 1, 4, 2, 64, 512, 16
+    G = Hq // Hkv
+    q = _rand((Bt, Hq, W, D), 5)
+    k = _rand((Bt, Hkv, S, D), 6)
+    if how == "equal_keys":
+        k[:] = k[:, :, :1, :]
+    else:
+        q[:] = 0.0
+    s = oracle.head_scores(q, k)
+    HS = _harmonic(S)
+    prefix = float(G * (HS - _harmonic(S - W)))
+    assert abs(prefix - 0.0634344342767) < 1e-12
+    np.testing.assert_allclose(s[..., :S - W], prefix, rtol=1e-12)
+    for r in range(W):
+        np.testing.assert_allclose(s[..., S - W + r], float(G * (HS - _harmonic(S - W + r))),
+                                   rtol=1e-12)
+    # every candidate ties: the selection is the lowest positions
+    p = oracle.max_pool(s, 5, 0, S - W)
+    idx = oracle.select(p, 64, 0, W)
+    want = np.concatenate([np.arange(64), np.arange(S - W, S)])
+    assert (idx == want).all()
+    idx = oracle.select(p, 10, 3, W)
+    want = np.concatenate([np.arange(3), np.arange(3, 13), np.arange(S - W, S)])
+    assert (idx == want).all()
+
+
+def test_spike_key_takes_almost_all_mass():
+    """One prefix key aligned with every query at logit +60 takes all of the
+    normalised weight: s[i*] ~= W*G and the max-pool plateau is
+    [i*-h, i*+h] clipped to the candidates."""
+    Bt, Hq, Hkv, D, S, W = 1, 2, 1, 8, 64, 4
+    q = np.zeros((Bt, Hq, W, D)); q[..., 0] = 1.0
+    k = _rand((Bt, Hkv, S, D), 7, 0.01)
+    k[..., 0] = 0.0
+    i_star = 20
+    k[0, 0, i_star, 0] = 60.0 * math.sqrt(D)
+    s = oracle.head_scores(q, k)
+    assert abs(s[0, 0, i_star] - W * Hq) < W * Hq * S * math.exp(-59)
+    p = oracle.max_pool(s, 7, 0, S - W)
+    plateau = np.flatnonzero(p[0, 0] == s[0, 0, i_star])
+    assert plateau.tolist() == list(range(i_star - 3, i_star + 4))
+    # a spike at the candidate edge is clipped
+    p2 = oracle.max_pool(s, 7, 18, S - W)
+    assert np.flatnonzero(p2[0, 0] == s[0, 0, i_star]).tolist() == list(range(18, 24))
+
+
+def test_causal_mask_hides_future_window_key():
+    """A window key S-W+r with a huge logit for every query is seen only by
+    the W-r queries at or after its position: its score is G*(W-r) up to
+    exp(-huge) terms, and a non-causal run gives it G*W."""
+    Bt, Hq, Hkv, D, S, W, r = 1, 3, 1, 4, 40, 8, 5
+    q = np.zeros((Bt, Hq, W, D)); q[..., 1] = 1.0
+    k = _rand((Bt, Hkv, S, D), 8, 0.01); k[..., 1] = 0.0
+    j = S - W + r
+    k[0, 0, j, 1] = 80.0 * 2.0          # logit 80 at scale 1/2
+    s = oracle.head_scores(q, k)
+    assert abs(s[0, 0, j] - Hq * (W - r)) < Hq * W * S * math.exp(-70)
+    s_nc = oracle.head_scores(q, k, causal=False)
+    assert abs(s_nc[0, 0, j] - Hq * W) < Hq * W * S * math.exp(-70)
+
+
+def test_gqa_group_is_contiguous():
+    """Query heads [h_kv*G, (h_kv+1)*G) read KV head h_kv."""
+    Bt, Hq, Hkv, D, S, W = 1, 4, 2, 4, 24, 2
+    q = np.zeros((Bt, Hq, W, D)); q[0, 0:2, :, 2] = 1.0     # heads 0,1 -> KV head 0
+    k = _rand((Bt, Hkv, S, D), 9, 0.01); k[..., 2] = 0.0
+    k[0, 0, 5, 2] = 100.0 * 2.0
+    s = oracle.head_scores(q, k)
+    assert abs(s[0, 0, 5] - 2 * W) < 1e-12          # both heads of group 0
+    assert s[0, 1].max() < 0.2                        # group 1 stays near uniform
+
+
+# ------------------------------------------------------------------ pool ----
+
+@pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9])
+@pytest.mark.parametrize("lo,hi", [(0, 50), (3, 41), (10, 12), (7, 7)])
+def test_max_pool_matches_sliding_window(kernel, lo, hi):
+    S = 50
+    s = _rand((2, 3, S), kernel * 100 + lo)
+    got = oracle.max_pool(s, kernel, lo, hi)
+    h = (kernel - 1) // 2
+    pad = np.full((2, 3, S + 2 * h), -np.inf)
+    pad[..., h + lo:h + hi] = s[..., lo:hi]
+    win = np.lib.stride_tricks.sliding_window_view(pad, kernel, axis=-1)
+    want = np.zeros_like(s)
+    if hi > lo:
+        want[..., lo:hi] = win.max(-1)[..., lo:hi]
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- select ----
+
+def test_select_matches_brute_force_sort():
+    spec = synth.config(1)
+    x = synth.make_layer(spec, 1)
+    s = oracle.head_scores(synth.to_f64(x["q"], "f32"), synth.to_f64(x["k"], "f32"))
+    S, W = spec.seq_len, spec.obs_window
+    for n_sink, B, kern in [(0, 64, 5), (4, 64, 5), (0, 0, 3), (2, S - W - 2, 1), (0, 200, 9)]:
+        p = oracle.max_pool(s, kern, n_sink, S - W)
+        idx = oracle.select(p, B, n_sink, W)
+        assert idx.shape == (1, 2, B + n_sink + W)
+        for h in range(2):
+            cand = sorted(range(n_sink, S - W), key=lambda i: (-p[0, h, i], i))
+            want = sorted(list(range(n_sink)) + cand[:B] + list(range(S - W, S)))
+            assert idx[0, h].tolist() == want
+            assert (np.diff(idx[0, h]) > 0).all()
+
+
+def test_select_ties_take_lowest_positions():
+    p = np.array([[0.0, 3.0, 1.0, 3.0, 3.0, 2.0, 3.0, 0.5, 9.0, 9.0]])
+    # candidates [1, 8), window W = 2 -> positions 8, 9 mandatory; sinks 1
+    idx = oracle.select(p, 3, 1, 2)
+    assert idx.tolist() == [[0, 1, 3, 4, 8, 9]]
+
+
+@pytest.mark.parametrize("B,n_sink,W", [(5, 0, 8), (-1, 0, 2), (0, 0, 0), (0, 0, 11), (2, 9, 1)])
+def test_select_rejects_infeasible(B, n_sink, W):
+    with pytest.raises(ValueError):
+        oracle.select(np.zeros((1, 10)), B, n_sink, W)
+
+
+# ---------------------------------------------------------------- gather ----
+
+def test_compact_rows_are_byte_identical():
+    rng = np.random.default_rng(11)
+    kb = rng.integers(0, 65536, size=(2, 3, 40, 8), dtype=np.uint16)
+    idx = np.sort(rng.choice(40, size=(2, 3, 12)), axis=-1).astype(np.int32)
+    out = oracle.compact_rows(kb, idx)
+    for b in range(2):
+        for h in range(3):
+            for r in range(12):
+                assert out[b, h, r].tobytes() == kb[b, h, idx[b, h, r]].tobytes()
+
+
+def test_layer_end_compress_keeps_budget_plus_window():
+    spec = synth.config(1)
+    x = synth.make_layer(spec, 1)
+    q, k = synth.to_f64(x["q"], "f32"), synth.to_f64(x["k"], "f32")
+    out = oracle.layer_end_compress(q, k, x["v"], budget=spec.budget,
+                                    window=spec.obs_window, pool_kernel=spec.pool_kernel,
+                                    k_store=x["k"], v_store=x["v"])
+    n = spec.budget + spec.obs_window
+    assert out["idx"].shape == (1, 2, n)
+    S, W = spec.seq_len, spec.obs_window
+    for h in range(2):
+        assert out["idx"][0, h, -W:].tolist() == list(range(S - W, S))
+        assert (np.diff(out["idx"][0, h]) > 0).all()
+    assert out["k_hat"].tobytes() == np.stack(
+        [x["k"][0, h, out["idx"][0, h]] for h in range(2)])[None].tobytes()
+    # sinks are boosted x4 in the generator and win on score
+    assert set(range(4)) <= set(out["idx"][0, 0].tolist())
+
+
+# ----------------------------------------------------------------- tiers ----
+
+def test_window_sums_and_ranks():
+    s = np.arange(24, dtype=np.float64).reshape(1, 24)
+    w = oracle.window_sums(s, 4)
+    assert w.tolist() == [[6, 22, 38, 54, 70, 86]]
+    tier, rank = oracle.route_tiers(w, 1, 3)
+    assert rank.tolist() == [[5, 4, 3, 2, 1, 0]]
+    assert tier.tolist() == [[2, 2, 1, 1, 1, 0]]
+    # equal sums rank by index
+    tier, rank = oracle.route_tiers(np.ones((2, 5)), 2, 2)
+    assert rank.tolist() == [[0, 1, 2, 3, 4]] * 2
+    assert tier.tolist() == [[0, 0, 1, 1, 2]] * 2
+
+
+def test_route_tiers_brute_force():
+    w = np.random.default_rng(12).integers(0, 5, size=(3, 16)).astype(np.float64)
+    tier, rank = oracle.route_tiers(w, 4, 8)
+    for r in range(3):
+        order = sorted(range(16), key=lambda j: (-w[r, j], j))
+        for pos, j in enumerate(order):
+            assert rank[r, j] == pos
+            assert tier[r, j] == (0 if pos < 4 else 1 if pos < 12 else 2)
+
+
+# ------------------------------------------------------------------ int4 ----
+
+def test_int4_range_and_extremes():
+    x = np.random.default_rng(13).standard_normal((64, 128)).astype(np.float32)
+    codes, lo, scale = oracle.quant_int4(x)
+    assert codes.dtype == np.uint8 and codes.max() <= 15
+    assert (codes[x.argmin(0), np.arange(128)] == 0).all()
+    assert (codes[x.argmax(0), np.arange(128)] == 15).all()
+    xh = oracle.dequant_int4(codes, lo, scale)
+    assert (np.abs(x - xh) <= scale / 2 * (1 + 1e-5) + 4 * np.spacing(np.abs(x) + np.abs(lo))).all()
+
+
+def test_int4_constant_group_is_exact():
+    x = np.full((64, 3), 1.375, dtype=np.float32)
+    codes, lo, scale = oracle.quant_int4(x)
+    assert (codes == 0).all() and (scale == 0).all()
+    assert (oracle.dequant_int4(codes, lo, scale) == x).all()
+
+
+def test_int4_identity_codes_and_half_even():
+    lo_v, sc = np.float32(-2.0), np.float32(0.25)       # hi = -2 + 15*0.25 = 1.75
+    c = np.array([0, 15] + list(range(16)) + [3, 7], dtype=np.float32)
+    x = (lo_v + c * sc).astype(np.float32)[:, None]
+    codes, lo, scale = oracle.quant_int4(x)
+    assert lo[0] == lo_v and scale[0] == sc
+    assert codes[:, 0].tolist() == c.astype(int).tolist()
+    # half-way points lo + (c + 0.5) * scale round to the even code
+    half = (lo_v + (np.arange(15) + 0.5) * sc).astype(np.float32)
+    xx = np.concatenate([[lo_v, lo_v + 15 * sc], half]).astype(np.float32)[:, None]
+    codes, _, _ = oracle.quant_int4(xx)
+    want = [0, 15] + [int(2 * round((c + 0.5) / 2)) for c in range(15)]
+    assert codes[:, 0].tolist() == want
+
+
+# ---------------------------------------------------------------- memory ----
+
+def test_memory_figures_printed_by_the_pages():
+    with open(os.path.join(GOLDEN, "memory_pins.json")) as f:
+        pins = json.load(f)["pins"]
+    for p in pins:
+        got = oracle.cache_bytes(p["layers"], p["batch"], p["kv_heads"], p["tokens"],
+                                 p["head_dim"], p["elem_bytes"])
+        assert got == int(p["value_gib"] * 2**30), p["what"]
+
+
+def test_linear_budget_schedule():
+    b = [synth.sweep_budget(l) for l in range(32)]
+    assert b[0] == 4096 and b[31] == 512
+    assert all(x >= y for x, y in zip(b, b[1:]))
+    assert sum(b) == 73743
