@@ -1,0 +1,261 @@
+"""Python binding of libkvsel (attention-score KV selection and compaction).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libkvsel.so``; PyTorch supplies device memory and the current stream.  The
+function names follow the C ABI in ``include/kvsel.h``:
+
+    score(q_obs, k, ...)         -> (pooled, raw)     kvsel_score
+    select(pooled, budget, ...)  -> idx               kvsel_select
+    compact(k, v, idx, ...)      -> (k_hat, v_hat)    kvsel_compact
+    route_tiers(scores, k, v, ...) -> dict            kvsel_route_tiers
+
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+
+OK, ERR_ARG, ERR_BUDGET, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_DEVICE = range(6)
+BF16, F32 = 0, 1
+
+
+class KvselError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class Desc(ctypes.Structure):
+    """kvsel_desc."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32), ("obs_window", ctypes.c_int32),
+        ("n_sink", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
+class TierDesc(ctypes.Structure):
+    """kvsel_tier_desc."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+        ("win", ctypes.c_int32), ("n_full", ctypes.c_int32),
+        ("n_quant", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvsel.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m attention_score_eviction_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    DP, TP = ctypes.POINTER(Desc), ctypes.POINTER(TierDesc)
+    L.kvsel_status_str.argtypes = [ctypes.c_int]
+    L.kvsel_status_str.restype = ctypes.c_char_p
+    L.kvsel_score_workspace.argtypes = [DP]
+    L.kvsel_score_workspace.restype = SZ
+    L.kvsel_score.argtypes = [DP, P, P, P, P, I32, P, SZ, P]
+    L.kvsel_score.restype = ctypes.c_int
+    L.kvsel_select_workspace.argtypes = [DP, I32]
+    L.kvsel_select_workspace.restype = SZ
+    L.kvsel_select.argtypes = [DP, P, I32, P, P, SZ, P]
+    L.kvsel_select.restype = ctypes.c_int
+    L.kvsel_compact.argtypes = [DP, P, P, P, I32, P, P, P]
+    L.kvsel_compact.restype = ctypes.c_int
+    L.kvsel_route_tiers_workspace.argtypes = [TP]
+    L.kvsel_route_tiers_workspace.restype = SZ
+    L.kvsel_route_tiers.argtypes = [TP, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P]
+    L.kvsel_route_tiers.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().kvsel_status_str(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise KvselError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("kvsel operates on device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("kvsel needs contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def make_desc(q_obs: torch.Tensor, k: torch.Tensor, *, n_sink: int = 0, causal: bool = True,
+              scale: float = 0.0) -> Desc:
+    """kvsel_desc from Q_obs [Bt,Hq,W,D] and K [Bt,Hkv,S,D]."""
+    Bt, Hq, W, D = q_obs.shape
+    Bk, Hkv, S, Dk = k.shape
+    if Bk != Bt or Dk != D or q_obs.dtype != k.dtype:
+        raise ValueError("q_obs / k shape or dtype mismatch")
+    return Desc(Bt, Hq, Hkv, D, S, W, n_sink, int(bool(causal)), _dtype_code(k), float(scale))
+
+
+def desc_of(batch, n_q_heads, n_kv_heads, head_dim, seq_len, obs_window, *, n_sink=0,
+            causal=True, dtype=torch.bfloat16, scale=0.0) -> Desc:
+    return Desc(batch, n_q_heads, n_kv_heads, head_dim, seq_len, obs_window, n_sink,
+                int(bool(causal)), BF16 if dtype == torch.bfloat16 else F32, float(scale))
+
+
+def score_workspace_bytes(desc: Desc) -> int:
+    return int(lib().kvsel_score_workspace(ctypes.byref(desc)))
+
+
+def score(q_obs: torch.Tensor, k: torch.Tensor, *, pool_kernel: int, n_sink: int = 0,
+          causal: bool = True, scale: float = 0.0, pooled: Optional[torch.Tensor] = None,
+          raw: Optional[torch.Tensor] = None, want_raw: bool = True,
+          workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_score: returns (pooled [Bt,Hkv,S] fp32, raw [Bt,Hkv,S] fp32 or None)."""
+    d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
+    shape = (d.batch, d.n_kv_heads, d.seq_len)
+    if pooled is None:
+        pooled = torch.empty(shape, dtype=torch.float32, device=k.device)
+    if raw is None and want_raw:
+        raw = torch.empty(shape, dtype=torch.float32, device=k.device)
+    nbytes = score_workspace_bytes(d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    st = lib().kvsel_score(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(raw), _ptr(pooled),
+                           int(pool_kernel), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kvsel_score")
+    return pooled, raw
+
+
+def select(pooled: torch.Tensor, budget: int, *, obs_window: int, n_q_heads: int,
+           head_dim: int, n_sink: int = 0, causal: bool = True,
+           idx: Optional[torch.Tensor] = None, dtype=torch.bfloat16, stream=None):
+    """kvsel_select: returns idx [Bt,Hkv,budget+n_sink+W] int32 (ascending)."""
+    Bt, Hkv, S = pooled.shape
+    d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
+                dtype=dtype)
+    n_keep = budget + n_sink + obs_window
+    if idx is None:
+        idx = torch.empty((Bt, Hkv, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
+    st = lib().kvsel_select(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx), None, 0,
+                            _stream(stream))
+    _check(st, "kvsel_select")
+    return idx
+
+
+def compact(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, *,
+            k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+            stream=None):
+    """kvsel_compact: returns (k_hat, v_hat) [Bt,Hkv,n_keep,D]."""
+    Bt, Hkv, S, D = k.shape
+    n_keep = idx.shape[-1]
+    d = Desc(Bt, Hkv, Hkv, D, S, 1, 0, 1, _dtype_code(k), 0.0)
+    if k_out is None:
+        k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
+    if v is not None and v_out is None:
+        v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
+    st = lib().kvsel_compact(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(idx), int(n_keep),
+                             _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check(st, "kvsel_compact")
+    return k_out, v_out
+
+
+def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
+                       pool_kernel: int, n_sink: int = 0, causal: bool = True,
+                       scale: float = 0.0, stream=None) -> dict:
+    """score -> select -> compact on one stream (TideKV's layer-end step)."""
+    W = q_obs.shape[2]
+    pooled, raw = score(q_obs, k, pool_kernel=pool_kernel, n_sink=n_sink, causal=causal,
+                        scale=scale, stream=stream)
+    idx = select(pooled, budget, obs_window=W, n_q_heads=q_obs.shape[1], head_dim=k.shape[3],
+                 n_sink=n_sink, causal=causal, dtype=k.dtype, stream=stream)
+    k_hat, v_hat = compact(k, v, idx, stream=stream)
+    return {"s": raw, "p": pooled, "idx": idx, "k_hat": k_hat, "v_hat": v_hat}
+
+
+@dataclass
+class TierOutputs:
+    tier: torch.Tensor
+    rank: torch.Tensor
+    k_full: torch.Tensor
+    v_full: torch.Tensor
+    k_codes: torch.Tensor
+    v_codes: torch.Tensor
+    k_meta: torch.Tensor
+    v_meta: torch.Tensor
+    k_prom: torch.Tensor
+    v_prom: torch.Tensor
+
+
+def route_tiers_workspace_bytes(td: TierDesc) -> int:
+    return int(lib().kvsel_route_tiers_workspace(ctypes.byref(td)))
+
+
+def route_tiers(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, n_full: int,
+                n_quant: int, win: int = 64, promote: Optional[torch.Tensor] = None,
+                out: Optional[TierOutputs] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> TierOutputs:
+    """kvsel_route_tiers (QEvict window tiers with int4 and promotion)."""
+    Bt, Hkv, S, D = k.shape
+    td = TierDesc(Bt, Hkv, D, S, win, n_full, n_quant, _dtype_code(k))
+    nW = S // win
+    n_prom = 0 if promote is None else promote.shape[-1]
+    dev = k.device
+    if out is None:
+        e = lambda *s, dt: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        out = TierOutputs(
+            e(Bt, Hkv, nW, dt=torch.int8), e(Bt, Hkv, nW, dt=torch.int32),
+            e(Bt, Hkv, n_full * win, D, dt=k.dtype), e(Bt, Hkv, n_full * win, D, dt=k.dtype),
+            e(Bt, Hkv, n_quant, win, D // 2, dt=torch.uint8),
+            e(Bt, Hkv, n_quant, win, D // 2, dt=torch.uint8),
+            e(Bt, Hkv, n_quant, D, 2, dt=torch.float32), e(Bt, Hkv, n_quant, D, 2, dt=torch.float32),
+            e(Bt, Hkv, n_prom * win, D, dt=k.dtype), e(Bt, Hkv, n_prom * win, D, dt=k.dtype))
+    nbytes = route_tiers_workspace_bytes(td)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    nz = lambda t: _ptr(t) if t is not None and t.numel() > 0 else None  # noqa: E731
+    st = lib().kvsel_route_tiers(
+        ctypes.byref(td), _ptr(scores), _ptr(k), _ptr(v), _ptr(out.tier), _ptr(out.rank),
+        nz(out.k_full), nz(out.v_full), nz(out.k_codes), nz(out.v_codes), nz(out.k_meta),
+        nz(out.v_meta), nz(promote), int(n_prom), nz(out.k_prom), nz(out.v_prom),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kvsel_route_tiers")
+    return out
+
+
+EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_select_workspace",
+           "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers")

@@ -1,0 +1,154 @@
+// C ABI of libkvsel: argument validation and launch sequencing.
+//
+// Every precondition is checked on the host before anything is enqueued, and
+// no check calls the HIP runtime, so invalid calls fail the same way on a
+// machine without a GPU.  The library holds no global mutable state.
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+
+using namespace kvsel;
+
+namespace {
+
+constexpr int64_t kMaxSeq = (int64_t)1 << 28;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+kvsel_status check_desc(const kvsel_desc* d) {
+  if (!d) return KVSEL_ERR_ARG;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return KVSEL_ERR_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return KVSEL_ERR_ARG;
+  if (d->head_dim < 1 || d->seq_len < 1 || d->seq_len > kMaxSeq) return KVSEL_ERR_ARG;
+  if (d->obs_window < 1 || d->obs_window > d->seq_len) return KVSEL_ERR_ARG;
+  if (d->n_sink < 0 || d->n_sink > d->seq_len - d->obs_window) return KVSEL_ERR_ARG;
+  if (d->causal != 0 && d->causal != 1) return KVSEL_ERR_ARG;
+  if (d->dtype != KVSEL_BF16 && d->dtype != KVSEL_F32) return KVSEL_ERR_ARG;
+  if (!(d->scale >= 0.f) || isinf(d->scale)) return KVSEL_ERR_ARG;
+  if ((int64_t)d->batch * d->n_kv_heads > 65535) return KVSEL_ERR_ARG;
+  if ((int64_t)(d->n_q_heads / d->n_kv_heads) * d->obs_window > (1 << 20)) return KVSEL_ERR_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
+  return KVSEL_OK;
+}
+
+kvsel_status check_tier_desc(const kvsel_tier_desc* d) {
+  if (!d) return KVSEL_ERR_ARG;
+  if (d->batch < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->seq_len < 1) return KVSEL_ERR_ARG;
+  if ((int64_t)d->batch * d->n_kv_heads > 65535 || d->seq_len > kMaxSeq) return KVSEL_ERR_ARG;
+  if (d->win < 1 || d->seq_len % d->win != 0) return KVSEL_ERR_ARG;
+  const int nwin = d->seq_len / d->win;
+  if (d->n_full < 0 || d->n_quant < 0 || d->n_full + d->n_quant > nwin) return KVSEL_ERR_ARG;
+  if (d->dtype != KVSEL_BF16 && d->dtype != KVSEL_F32) return KVSEL_ERR_ARG;
+  if (d->dtype != KVSEL_BF16) return KVSEL_ERR_UNSUPPORTED;
+  if (d->win != 64 || nwin > 4096) return KVSEL_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
+  return KVSEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvsel_status_str(kvsel_status s) {
+  switch (s) {
+    case KVSEL_OK: return "ok";
+    case KVSEL_ERR_ARG: return "invalid argument";
+    case KVSEL_ERR_BUDGET: return "infeasible budget";
+    case KVSEL_ERR_WORKSPACE: return "workspace too small";
+    case KVSEL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVSEL_ERR_DEVICE: return "device launch error";
+  }
+  return "unknown status";
+}
+
+size_t kvsel_score_workspace(const kvsel_desc* desc) {
+  if (check_desc(desc) != KVSEL_OK) return 0;
+  ScorePlan p;
+  plan_score(*desc, &p);
+  return p.total;
+}
+
+kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* k,
+                         float* raw_scores, float* pooled, int32_t pool_kernel, void* ws,
+                         size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (!q_obs || !k || !pooled) return KVSEL_ERR_ARG;
+  if (!aligned16(q_obs) || !aligned16(k) || !aligned16(pooled) || !aligned16(raw_scores))
+    return KVSEL_ERR_ARG;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 1 + 2 * (1 << 20))
+    return KVSEL_ERR_ARG;
+  ScorePlan p;
+  plan_score(*desc, &p);
+  if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVSEL_ERR_ARG;
+  return launch_score(*desc, p, q_obs, k, raw_scores, pooled, pool_kernel, (char*)ws,
+                      (hipStream_t)stream);
+}
+
+size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget) {
+  (void)desc;
+  (void)budget;
+  return 0;
+}
+
+kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t budget,
+                          int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink)
+    return KVSEL_ERR_BUDGET;
+  if (!pooled || !idx || !aligned16(pooled) || !aligned16(idx)) return KVSEL_ERR_ARG;
+  return launch_select(*desc, pooled, budget, idx, (hipStream_t)stream);
+}
+
+kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
+                           const int32_t* idx, int32_t n_keep, void* k_out, void* v_out,
+                           void* stream) {
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (n_keep < 0) return KVSEL_ERR_ARG;
+  if (!k || !k_out || (n_keep > 0 && !idx)) return KVSEL_ERR_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVSEL_ERR_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(k_out) ||
+      !aligned16(v_out))
+    return KVSEL_ERR_ARG;
+  return launch_compact(*desc, k, v, idx, n_keep, k_out, v_out, (hipStream_t)stream);
+}
+
+size_t kvsel_route_tiers_workspace(const kvsel_tier_desc* desc) {
+  if (check_tier_desc(desc) != KVSEL_OK) return 0;
+  TierPlan p;
+  plan_tiers(*desc, &p);
+  return p.total;
+}
+
+kvsel_status kvsel_route_tiers(const kvsel_tier_desc* desc, const float* token_scores,
+                               const void* k, const void* v, int8_t* tier, int32_t* win_rank,
+                               void* k_full, void* v_full, uint8_t* k_codes, uint8_t* v_codes,
+                               float* k_meta, float* v_meta, const int32_t* promote,
+                               int32_t n_promote, void* k_prom, void* v_prom, void* ws,
+                               size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_tier_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (n_promote < 0) return KVSEL_ERR_ARG;
+  if (!token_scores || !k || !v || !tier || !win_rank) return KVSEL_ERR_ARG;
+  if (desc->n_full > 0 && (!k_full || !v_full)) return KVSEL_ERR_ARG;
+  if (desc->n_quant > 0 && (!k_codes || !v_codes || !k_meta || !v_meta)) return KVSEL_ERR_ARG;
+  if (n_promote > 0 && (!promote || !k_prom || !v_prom || desc->n_quant == 0)) return KVSEL_ERR_ARG;
+  const void* ptrs[] = {token_scores, k, v, tier, win_rank, k_full, v_full, k_codes,
+                        v_codes, k_meta, v_meta, promote, k_prom, v_prom, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return KVSEL_ERR_ARG;
+  TierPlan p;
+  plan_tiers(*desc, &p);
+  if (ws_bytes < p.total || !ws) return KVSEL_ERR_WORKSPACE;
+  return launch_tiers(*desc, p, token_scores, k, v, tier, win_rank, k_full, v_full, k_codes,
+                      v_codes, k_meta, v_meta, promote, n_promote, k_prom, v_prom, (char*)ws,
+                      (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal declarations shared by the kvsel HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvsel.h"
+
+namespace kvsel {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Score launch plan.  Keys of one (batch, KV head) are split into chunks of
+// `chunk` keys (a multiple of the per-step key count); query rows of the head
+// group (G*W of them) are split into groups of at most `qcap` rows.  One
+// workgroup handles one (chunk, head, row group).  The result does not depend
+// on this split beyond fp32 rounding of the per-chunk statistics.
+// ---------------------------------------------------------------------------
+struct ScorePlan {
+  int nheads;     // Bt * Hkv
+  int G;          // query heads per KV head
+  int GW;         // query rows per KV head (G * W)
+  int GWr;        // GW rounded up to 16
+  int maxqt;      // 16-row query tiles per workgroup (template choice)
+  int nwaves;     // waves per workgroup
+  int qcap;       // rows per group = 16 * maxqt
+  int ngroups;    // ceil(GW / qcap)
+  int chunk;      // keys per workgroup
+  int nchunk;     // ceil(S / chunk)
+  size_t off_part, off_lse, off_raw, off_grp, total;   // workspace layout (bytes)
+};
+
+bool plan_score(const kvsel_desc& d, ScorePlan* p);
+
+struct ScoreArgs {
+  const void* q;       // [Bt,Hq,W,D]
+  const void* k;       // [Bt,Hkv,S,D]
+  float2* part;        // [nheads][nchunk][GWr] (max, sum) in log2 units
+  float* lse;          // [nheads][GWr] row log2-sum-exp
+  float* s_out;        // [ngroups][nheads][S] (ngroups == 1: the raw scores)
+  int Hq, Hkv, G, W, S, GW, GWr, qcap, chunk, nchunk, causal;
+  float c;             // scale * log2(e)
+};
+
+kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
+                          float* raw, float* pooled, int pool_kernel, char* ws,
+                          hipStream_t stream);
+kvsel_status launch_select(const kvsel_desc& d, const float* pooled, int budget, int32_t* idx,
+                           hipStream_t stream);
+kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
+                            const int32_t* idx, int n_keep, void* k_out, void* v_out,
+                            hipStream_t stream);
+
+struct TierPlan {
+  int nheads, nwin;
+  size_t off_slot, total;
+};
+bool plan_tiers(const kvsel_tier_desc& d, TierPlan* p);
+kvsel_status launch_tiers(const kvsel_tier_desc& d, const TierPlan& p, const float* scores,
+                          const void* k, const void* v, int8_t* tier, int32_t* rank,
+                          void* k_full, void* v_full, uint8_t* k_codes, uint8_t* v_codes,
+                          float* k_meta, float* v_meta, const int32_t* promote, int n_promote,
+                          void* k_prom, void* v_prom, char* ws, hipStream_t stream);
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace kvsel

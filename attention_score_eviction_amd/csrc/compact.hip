@@ -1,0 +1,55 @@
+// Retained-row gather (kvsel_compact) for gfx950.
+//
+// TideKV ("Delayed KV Eviction via Layer-Wise Chunked Prefill ..."),
+// Algorithm 2, GATHER(K, V, R): the kept K and V rows are copied, bit for
+// bit, into a compact per-KV-head cache.  Each row (D elements, 128-512 B)
+// is moved as 16-byte vectors by consecutive lanes, so every wave issues
+// fully coalesced 16 B/lane loads and stores.
+#include "common.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kRowsPerBlock = 64;
+
+__global__ void __launch_bounds__(256) compact_kernel(const u32x4_t* __restrict__ k,
+                                                      const u32x4_t* __restrict__ v,
+                                                      const int32_t* __restrict__ idx,
+                                                      u32x4_t* __restrict__ ko,
+                                                      u32x4_t* __restrict__ vo, int S,
+                                                      int n_keep, int vpr) {
+  const int head = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int32_t* ih = idx + (size_t)head * n_keep;
+  const size_t src_base = (size_t)head * S;
+  const size_t dst_base = (size_t)head * n_keep;
+  for (int t = threadIdx.x; t < kRowsPerBlock * vpr; t += 256) {
+    const int r = r0 + t / vpr;
+    const int c = t - (t / vpr) * vpr;
+    if (r >= n_keep) break;
+    const int src = ih[r];
+    const bool ok = src >= 0 && src < S;
+    const size_t so = (src_base + (ok ? src : 0)) * vpr + c;
+    const size_t dsto = (dst_base + r) * vpr + c;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    ko[dsto] = ok ? k[so] : zero;
+    if (v) vo[dsto] = ok ? v[so] : zero;
+  }
+}
+
+}  // namespace
+
+kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
+                            const int32_t* idx, int n_keep, void* k_out, void* v_out,
+                            hipStream_t stream) {
+  if (n_keep == 0) return KVSEL_OK;
+  const int e = d.dtype == KVSEL_F32 ? 4 : 2;
+  const int vpr = d.head_dim * e / 16;
+  const int nheads = d.batch * d.n_kv_heads;
+  hipLaunchKernelGGL(compact_kernel, dim3((n_keep + kRowsPerBlock - 1) / kRowsPerBlock, nheads),
+                     dim3(256), 0, stream, (const u32x4_t*)k, (const u32x4_t*)v, idx,
+                     (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, n_keep, vpr);
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+}  // namespace kvsel

@@ -1,0 +1,435 @@
+// Observation-window key scoring (kvsel_score) for gfx950.
+//
+// TideKV ("Delayed KV Eviction via Layer-Wise Chunked Prefill ..."),
+// Section 4.2: the logits of Eq. (4) are streamed over key blocks twice.
+// Pass 1 finds each query row's running maximum and normaliser (Eqs. 5-6);
+// pass 2 recomputes the logits, normalises them (Eq. 7, left) and sums them
+// over the window queries and the GQA group (Eq. 7, right, unit weights).
+// A 1-D max filter over the candidate positions then smooths the per-key
+// scores (Algorithm 2, "pool to p_i").
+//
+// Kernel design (CDNA4, wave64):
+//  * One workgroup = one chunk of keys x one KV head x one group of up to
+//    qcap query rows.  The group's query rows are staged once in LDS in MFMA
+//    fragment order (each 16-row tile is 64 lanes x D*e/64 16-byte vectors,
+//    so every ds_read_b128 is a contiguous, conflict-free 1 KiB).
+//  * Every wave streams its own 64-key blocks straight from HBM into
+//    registers (4 tiles of 16 keys; each lane reads D*e/4 contiguous bytes of
+//    one key row, which is exactly its MFMA operand fragment), then loops over
+//    the query tiles in LDS.  Waves never synchronise inside the key loop.
+//  * The contraction uses v_mfma_f32_16x16x32_bf16 (bf16 inputs) or
+//    v_mfma_f32_16x16x4_f32 (fp32 inputs), fp32 accumulation.  The operand
+//    roles are swapped between the passes so that the dimension each pass
+//    reduces over stays inside a lane: pass 1 puts keys on the MFMA rows
+//    (each lane keeps running max/sum for one query row), pass 2 puts query
+//    rows on the MFMA rows (each lane keeps the running column sum for one key).
+//  * Exponentials are exp2 with scale*log2(e) folded into one FMA per logit.
+#include <math.h>
+
+#include "common.h"
+
+namespace kvsel {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int NV>
+struct Frag {
+  u32x4_t v[NV];
+};
+
+// 16-byte vectors per lane for one 16-row x D tile.
+template <typename T, int D>
+constexpr int nvec() { return D * (int)sizeof(T) / 64; }
+
+// Lane (row r = lane%16, group g = lane/16) holds vectors v = 0..NV-1 covering
+// elements [(4v+g)*16/e, +16/e) of its row.  A and B operands use the same
+// element-to-k assignment, so the contraction covers every d exactly once.
+template <int NV>
+__device__ __forceinline__ void load_frag_global(Frag<NV>& f, const char* row_bytes, int g) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) f.v[i] = *(const u32x4_t*)(row_bytes + (4 * i + g) * 16);
+}
+
+template <typename T, int NV>
+__device__ __forceinline__ f32x4_t mma(const Frag<NV>& a, const Frag<NV>& b, f32x4_t c) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v[i]),
+                                                  __builtin_bit_cast(bf16x8_t, b.v[i]), c, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v[i][e]),
+                                                 __uint_as_float(b.v[i][e]), c, 0, 0, 0);
+  }
+  return c;
+}
+
+// Stage query rows [0, nrows) of a group (row-major, D elements each) into LDS
+// in fragment order: vector (tile t, v, lane) at index (t*NV + v)*64 + lane.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void stage_queries(u32x4_t* qs, const T* qg, int nrows, int nqt) {
+  constexpr int NV = nvec<T, D>();
+  const int total = nqt * NV * 64;
+  for (int id = threadIdx.x; id < total; id += NT) {
+    const int lane = id & 63;
+    const int v = (id >> 6) % NV;
+    const int t = (id >> 6) / NV;
+    const int row = t * 16 + (lane & 15);
+    const int g = lane >> 4;
+    u32x4_t val = {0u, 0u, 0u, 0u};
+    if (row < nrows) val = *(const u32x4_t*)((const char*)(qg + (size_t)row * D) + (4 * v + g) * 16);
+    qs[id] = val;
+  }
+}
+
+__device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
+  const float mn = fmaxf(m, mo);
+  const float mu = (mn == -INFINITY) ? 0.f : mn;
+  z = z * __builtin_amdgcn_exp2f(m - mu) + zo * __builtin_amdgcn_exp2f(mo - mu);
+  m = mn;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: per (chunk, head, row group) partial (max, sum of exp2) per query row.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MAXQT, int NW>
+__global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
+  constexpr int NV = nvec<T, D>();
+  constexpr int NT = NW * 64;
+  __shared__ u32x4_t qs[MAXQT * NV * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int chunk = blockIdx.x, head = blockIdx.y, grp = blockIdx.z;
+  const int b = head / a.Hkv, hk = head - b * a.Hkv;
+  const int row0 = grp * a.qcap;
+  const int nrows = min(a.qcap, a.GW - row0);
+  const int nqt = (nrows + 15) >> 4;
+  const T* qg = (const T*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
+  stage_queries<T, D, NT>(qs, qg, nrows, nqt);
+  __syncthreads();
+
+  const char* kh = (const char*)((const T*)a.k + (size_t)head * a.S * D);
+  const int S = a.S;
+  const float c = a.c;
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+  float m[MAXQT], z[MAXQT];
+#pragma unroll
+  for (int t = 0; t < MAXQT; ++t) { m[t] = -INFINITY; z[t] = 0.f; }
+
+  const int k0 = chunk * a.chunk;
+  const int kend = min(S, k0 + a.chunk);
+  for (int kb = k0 + wave * 64; kb < kend; kb += NW * 64) {
+    Frag<NV> kf[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int row = min(kb + kt * 16 + l16, S - 1);
+      load_frag_global<NV>(kf[kt], kh + (size_t)row * D * sizeof(T), g);
+    }
+    const bool msk = (kb + 64 > mask_from);
+#pragma unroll
+    for (int t = 0; t < MAXQT; ++t) {
+      if (t < nqt) {
+        Frag<NV> qf;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) qf.v[i] = qs[(t * NV + i) * 64 + lane];
+        f32x4_t acc[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          // rows = keys (kb + kt*16 + 4g + i), column = query row (t*16 + l16)
+          acc[kt] = mma<T, NV>(kf[kt], qf, acc[kt]);
+        }
+        if (msk) {
+          const int qrow = row0 + t * 16 + l16;
+          const int lim = a.causal ? min(S - a.W + (qrow % a.W), S - 1) : (S - 1);
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (kb + kt * 16 + 4 * g + i > lim) acc[kt][i] = -INFINITY;
+        }
+        float mx = acc[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[kt][i]);
+        const float mnew = fmaxf(m[t], mx * c);
+        const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[kt][i], c, -mu));
+        z[t] = z[t] * __builtin_amdgcn_exp2f(m[t] - mu) + sum;
+        m[t] = mnew;
+      }
+    }
+  }
+
+  // Lanes l16, l16+16, l16+32, l16+48 hold partials of the same query row.
+#pragma unroll
+  for (int t = 0; t < MAXQT; ++t) {
+    if (t < nqt) {
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float mo = __shfl_xor(m[t], off);
+        const float zo = __shfl_xor(z[t], off);
+        lse_merge(m[t], z[t], mo, zo);
+      }
+    }
+  }
+  __syncthreads();  // the query tiles are no longer read
+  float2* red = (float2*)qs;  // [NW][MAXQT*16]
+  if (g == 0) {
+#pragma unroll
+    for (int t = 0; t < MAXQT; ++t)
+      if (t < nqt) red[wave * MAXQT * 16 + t * 16 + l16] = make_float2(m[t], z[t]);
+  }
+  __syncthreads();
+  for (int r = tid; r < nrows; r += NT) {
+    float mm = -INFINITY, zz = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      const float2 pz = red[w * MAXQT * 16 + r];
+      lse_merge(mm, zz, pz.x, pz.y);
+    }
+    a.part[((size_t)head * a.nchunk + chunk) * a.GWr + row0 + r] = make_float2(mm, zz);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine the per-chunk partials of each query row: lse = max + log2(sum).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) score_combine(const float2* __restrict__ part,
+                                                     float* __restrict__ lse, int nheads,
+                                                     int nchunk, int GW, int GWr) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= nheads * GW) return;
+  const int head = t / GW, r = t - head * GW;
+  float m = -INFINITY, z = 0.f;
+  const float2* p = part + (size_t)head * nchunk * GWr + r;
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const float2 pz = p[(size_t)ch * GWr];
+    lse_merge(m, z, pz.x, pz.y);
+  }
+  lse[(size_t)head * GWr + r] = m + log2f(z);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: s[key] = sum over the group's query rows of exp2(l*c - lse[row]).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int MAXQT, int NW>
+__global__ void __launch_bounds__(NW * 64) score_pass2(ScoreArgs a) {
+  constexpr int NV = nvec<T, D>();
+  constexpr int NT = NW * 64;
+  __shared__ u32x4_t qs[MAXQT * NV * 64];
+  __shared__ float ls[MAXQT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int chunk = blockIdx.x, head = blockIdx.y, grp = blockIdx.z;
+  const int b = head / a.Hkv, hk = head - b * a.Hkv;
+  const int row0 = grp * a.qcap;
+  const int nrows = min(a.qcap, a.GW - row0);
+  const int nqt = (nrows + 15) >> 4;
+  const T* qg = (const T*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
+  stage_queries<T, D, NT>(qs, qg, nrows, nqt);
+  for (int r = tid; r < nqt * 16; r += NT)
+    ls[r] = (r < nrows) ? a.lse[(size_t)head * a.GWr + row0 + r] : INFINITY;
+  __syncthreads();
+
+  const char* kh = (const char*)((const T*)a.k + (size_t)head * a.S * D);
+  const int S = a.S;
+  const float c = a.c;
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+  float* out = a.s_out + ((size_t)grp * gridDim.y + head) * S;
+  const int k0 = chunk * a.chunk;
+  const int kend = min(S, k0 + a.chunk);
+  for (int kb = k0 + wave * 64; kb < kend; kb += NW * 64) {
+    Frag<NV> kf[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int row = min(kb + kt * 16 + l16, S - 1);
+      load_frag_global<NV>(kf[kt], kh + (size_t)row * D * sizeof(T), g);
+    }
+    const bool msk = (kb + 64 > mask_from);
+    float as[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < MAXQT; ++t) {
+      if (t < nqt) {
+        Frag<NV> qf;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) qf.v[i] = qs[(t * NV + i) * 64 + lane];
+        const f32x4_t lq = *(const f32x4_t*)&ls[t * 16 + 4 * g];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          // rows = query rows (t*16 + 4g + i), column = key (kb + kt*16 + l16)
+          acc = mma<T, NV>(qf, kf[kt], acc);
+          if (msk) {
+            const int key = kb + kt * 16 + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int qrow = row0 + t * 16 + 4 * g + i;
+              const int lim = a.causal ? min(S - a.W + (qrow % a.W), S - 1) : (S - 1);
+              if (key > lim) acc[i] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) as[kt] += __builtin_amdgcn_exp2f(fmaf(acc[i], c, -lq[i]));
+        }
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      as[kt] += __shfl_xor(as[kt], 16);
+      as[kt] += __shfl_xor(as[kt], 32);
+    }
+    const float mine = g == 0 ? as[0] : (g == 1 ? as[1] : (g == 2 ? as[2] : as[3]));
+    const int key = kb + g * 16 + l16;
+    if (key < kend) out[key] = mine;
+  }
+}
+
+// Sum the per-group partial scores in group order (only when ngroups > 1).
+__global__ void __launch_bounds__(256) score_group_sum(const float* __restrict__ sg,
+                                                       float* __restrict__ s, size_t n,
+                                                       int ngroups) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = sg[i];
+  for (int gi = 1; gi < ngroups; ++gi) v += sg[(size_t)gi * n + i];
+  s[i] = v;
+}
+
+// p[i] = max of s[j], j in [i-h, i+h] within the candidates [lo, hi); 0 outside.
+__global__ void __launch_bounds__(256) maxpool_kernel(const float* __restrict__ s,
+                                                   float* __restrict__ p, int S, int lo, int hi,
+                                                   int h) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= S) return;
+  const size_t base = (size_t)blockIdx.y * S;
+  float v = 0.f;
+  if (i >= lo && i < hi) {
+    const int j0 = max(lo, i - h), j1 = min(hi - 1, i + h);
+    v = s[base + j0];
+    for (int j = j0 + 1; j <= j1; ++j) v = fmaxf(v, s[base + j]);
+  }
+  p[base + i] = v;
+}
+
+template <typename T, int D, int MAXQT, int NW>
+void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
+  hipLaunchKernelGGL((score_pass1<T, D, MAXQT, NW>), grid, dim3(NW * 64), 0, stream, args);
+  const int n = p.nheads * p.GW;
+  hipLaunchKernelGGL(score_combine, dim3((n + 255) / 256), dim3(256), 0, stream, args.part,
+                     args.lse, p.nheads, p.nchunk, p.GW, p.GWr);
+  hipLaunchKernelGGL((score_pass2<T, D, MAXQT, NW>), grid, dim3(NW * 64), 0, stream, args);
+}
+
+template <typename T, int D>
+bool dispatch_qt(int maxqt, const ScoreArgs& args, dim3 grid, hipStream_t stream,
+                 const ScorePlan& p) {
+  switch (maxqt) {
+    case 8: launch_passes<T, D, 8, 4>(args, grid, stream, p); return true;
+    case 16: launch_passes<T, D, 16, 4>(args, grid, stream, p); return true;
+    case 20:
+      if constexpr (nvec<T, D>() <= 4) {
+        launch_passes<T, D, 20, 8>(args, grid, stream, p);
+        return true;
+      }
+      return false;
+    default: return false;
+  }
+}
+
+}  // namespace
+
+bool plan_score(const kvsel_desc& d, ScorePlan* p) {
+  const int e = d.dtype == KVSEL_F32 ? 4 : 2;
+  const int tile_bytes = 16 * d.head_dim * e;
+  p->nheads = d.batch * d.n_kv_heads;
+  p->G = d.n_q_heads / d.n_kv_heads;
+  p->GW = p->G * d.obs_window;
+  p->GWr = (p->GW + 15) / 16 * 16;
+  const int nqt = p->GWr / 16;
+  // Query tiles per workgroup: the whole group when it fits in about 80 KiB
+  // of LDS (20 tiles of 4 KiB need 8 waves to keep one workgroup per CU
+  // busy), else groups of 16 tiles (64 KiB), each re-reading its key chunk.
+  int maxqt;
+  if (nqt <= 8) maxqt = 8;
+  else if (nqt <= 16) maxqt = 16;
+  else if (nqt <= 20 && tile_bytes <= 4096) maxqt = 20;
+  else maxqt = 16;
+  if (tile_bytes > 4096) maxqt = 8;
+  p->maxqt = maxqt;
+  p->nwaves = (maxqt == 20) ? 8 : 4;
+  p->qcap = 16 * maxqt;
+  p->ngroups = (p->GW + p->qcap - 1) / p->qcap;
+  // Key chunk: a multiple of one workgroup step; aim for >= ~1024 workgroups.
+  const int step = p->nwaves * 64;
+  const long wg_per_chunk = (long)p->nheads * p->ngroups;
+  long want_chunks = (1024 + wg_per_chunk - 1) / wg_per_chunk;
+  long steps = (long)d.seq_len / (step * want_chunks);
+  if (steps < 1) steps = 1;
+  p->chunk = (int)(steps * step);
+  p->nchunk = (d.seq_len + p->chunk - 1) / p->chunk;
+  size_t off = 0;
+  p->off_part = off;
+  off = align256(off + (size_t)p->nheads * p->nchunk * p->GWr * sizeof(float2));
+  p->off_lse = off;
+  off = align256(off + (size_t)p->nheads * p->GWr * sizeof(float));
+  p->off_raw = off;
+  off = align256(off + (size_t)p->nheads * d.seq_len * sizeof(float));
+  p->off_grp = off;
+  if (p->ngroups > 1) off = align256(off + (size_t)p->ngroups * p->nheads * d.seq_len * sizeof(float));
+  p->total = off;
+  return true;
+}
+
+kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
+                          float* raw, float* pooled, int pool_kernel, char* ws,
+                          hipStream_t stream) {
+  ScoreArgs a;
+  a.q = q;
+  a.k = k;
+  a.part = (float2*)(ws + p.off_part);
+  a.lse = (float*)(ws + p.off_lse);
+  float* s = raw ? raw : (float*)(ws + p.off_raw);
+  a.s_out = p.ngroups > 1 ? (float*)(ws + p.off_grp) : s;
+  a.Hq = d.n_q_heads;
+  a.Hkv = d.n_kv_heads;
+  a.G = p.G;
+  a.W = d.obs_window;
+  a.S = d.seq_len;
+  a.GW = p.GW;
+  a.GWr = p.GWr;
+  a.qcap = p.qcap;
+  a.chunk = p.chunk;
+  a.nchunk = p.nchunk;
+  a.causal = d.causal;
+  const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
+  a.c = scale * kLog2e;
+  const dim3 grid(p.nchunk, p.nheads, p.ngroups);
+  bool ok = false;
+  if (d.dtype == KVSEL_BF16) {
+    ok = d.head_dim == 128 ? dispatch_qt<uint16_t, 128>(p.maxqt, a, grid, stream, p)
+                           : dispatch_qt<uint16_t, 64>(p.maxqt, a, grid, stream, p);
+  } else {
+    ok = d.head_dim == 128 ? dispatch_qt<float, 128>(p.maxqt, a, grid, stream, p)
+                           : dispatch_qt<float, 64>(p.maxqt, a, grid, stream, p);
+  }
+  if (!ok) return KVSEL_ERR_UNSUPPORTED;
+  if (p.ngroups > 1) {
+    const size_t n = (size_t)p.nheads * d.seq_len;
+    hipLaunchKernelGGL(score_group_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       a.s_out, s, n, p.ngroups);
+  }
+  const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
+  hipLaunchKernelGGL(maxpool_kernel, dim3((d.seq_len + 255) / 256, p.nheads), dim3(256), 0, stream,
+                     s, pooled, d.seq_len, lo, hi, (pool_kernel - 1) / 2);
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+}  // namespace kvsel

@@ -1,0 +1,275 @@
+// Window tiering (kvsel_route_tiers) for gfx950.
+//
+// QEvict ("Recoverable Quantized KV Eviction for Attention-Drift-Robust
+// Long-Context Decoding"), Sections 4.1-4.3: the cache is cut into
+// contiguous windows, each window is scored by its accumulated attention,
+// and windows are routed by rank into a full-precision tier, a recoverable
+// low-bit tier and an evicted tier; low-bit windows are promoted back by
+// dequantisation.  The low-bit code here is asymmetric int4 with one
+// (lo, scale) pair per channel of a window; its exact rule is in kvsel.h.
+//
+// Kernels:
+//   tier_rank_kernel     one workgroup per (batch, KV head): window sums in a
+//                        fixed reduction order, exact rank by counting, tier
+//                        id, and each window's slot inside its tier
+//   tier_move_kernel     one workgroup per window: full tier -> 16 B/lane row
+//                        copy; int4 tier -> LDS-staged per-channel min/max,
+//                        codes, nibble packing
+//   tier_promote_kernel  one workgroup per promoted window: dequantise to bf16
+#include <math.h>
+
+#include "common.h"
+
+namespace kvsel {
+namespace {
+
+constexpr int kWin = 64;
+constexpr int kRankThreads = 1024;
+
+__device__ __forceinline__ uint32_t block_excl_scan_1024(uint32_t v, uint32_t* total,
+                                                         uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < 16 ? wsum[lane] : 0u;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint32_t t = __shfl_up(w, off);
+      if (lane >= off) w += t;
+    }
+    if (lane < 16) wsum[lane] = w;
+  }
+  __syncthreads();
+  const uint32_t before = wave > 0 ? wsum[wave - 1] : 0u;
+  *total = wsum[15];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// nwin <= 4096 windows per head.
+__global__ void __launch_bounds__(kRankThreads) tier_rank_kernel(
+    const float* __restrict__ scores, int8_t* __restrict__ tier, int32_t* __restrict__ rank,
+    int32_t* __restrict__ slot, int S, int nwin, int n_full, int n_quant) {
+  __shared__ float w[4096];
+  __shared__ uint32_t wsum[16];
+  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* s = scores + (size_t)head * S;
+  // Window sums: one wave per window, lane l adds tokens l; tree in fixed order.
+  for (int j = wave; j < nwin; j += kRankThreads / 64) {
+    float x = s[(size_t)j * kWin + lane];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if (lane == 0) w[j] = x;
+  }
+  __syncthreads();
+  uint32_t cf = 0u, cq = 0u;
+  for (int base = 0; base < nwin; base += kRankThreads) {
+    const int j = base + tid;
+    int t = 2;
+    if (j < nwin) {
+      const float wj = w[j];
+      int rk = 0;
+      for (int i = 0; i < nwin; ++i) {
+        const float wi = w[i];
+        rk += (wi > wj) || (wi == wj && i < j);
+      }
+      t = rk < n_full ? 0 : (rk < n_full + n_quant ? 1 : 2);
+      rank[(size_t)head * nwin + j] = rk;
+      tier[(size_t)head * nwin + j] = (int8_t)t;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan_1024(((uint32_t)(t == 0) << 16) | (uint32_t)(t == 1), &tot,
+                                             wsum);
+    if (j < nwin)
+      slot[(size_t)head * nwin + j] = t == 0 ? (int)(cf + (ex >> 16))
+                                             : (t == 1 ? (int)(cq + (ex & 0xffffu)) : -1);
+    cf += tot >> 16;
+    cq += tot & 0xffffu;
+  }
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) tier_move_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int8_t* __restrict__ tier, const int32_t* __restrict__ slot,
+    uint16_t* __restrict__ k_full, uint16_t* __restrict__ v_full, uint8_t* __restrict__ k_codes,
+    uint8_t* __restrict__ v_codes, float* __restrict__ k_meta, float* __restrict__ v_meta, int S,
+    int nwin, int n_full, int n_quant) {
+  constexpr int VPW = kWin * D * 2 / 16;  // 16-byte vectors per window per tensor
+  __shared__ uint16_t xs[2][kWin * D];
+  __shared__ float lo_s[2][D], sc_s[2][D];
+  const int j = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
+  const int t = tier[(size_t)head * nwin + j];
+  if (t == 2) return;
+  const int sl = slot[(size_t)head * nwin + j];
+  // Ranks form a permutation for finite scores, so slots stay below the tier
+  // capacity; the guard keeps malformed scores from writing out of bounds.
+  if (sl < 0 || sl >= (t == 0 ? n_full : n_quant)) return;
+  const size_t src = ((size_t)head * S + (size_t)j * kWin) * D;
+  if (t == 0) {
+    const size_t dst = ((size_t)head * n_full * kWin + (size_t)sl * kWin) * D;
+    const u32x4_t* ks = (const u32x4_t*)(k + src);
+    const u32x4_t* vs = (const u32x4_t*)(v + src);
+    u32x4_t* kd = (u32x4_t*)(k_full + dst);
+    u32x4_t* vd = (u32x4_t*)(v_full + dst);
+    for (int i = tid; i < VPW; i += 256) {
+      kd[i] = ks[i];
+      vd[i] = vs[i];
+    }
+    return;
+  }
+  // int4 tier: stage the window of K and V in LDS.
+  for (int i = tid; i < VPW; i += 256) {
+    ((u32x4_t*)xs[0])[i] = ((const u32x4_t*)(k + src))[i];
+    ((u32x4_t*)xs[1])[i] = ((const u32x4_t*)(v + src))[i];
+  }
+  __syncthreads();
+  // Per-channel range: thread -> (tensor, channel).
+  for (int id = tid; id < 2 * D; id += 256) {
+    const int tn = id / D, ch = id - tn * D;
+    float lo = bf16_to_f32(xs[tn][ch]), hi = lo;
+    for (int r = 1; r < kWin; ++r) {
+      const float x = bf16_to_f32(xs[tn][r * D + ch]);
+      lo = fminf(lo, x);
+      hi = fmaxf(hi, x);
+    }
+    const float sc = __fdiv_rn(__fsub_rn(hi, lo), 15.0f);
+    lo_s[tn][ch] = lo;
+    sc_s[tn][ch] = sc;
+    float* meta = tn == 0 ? k_meta : v_meta;
+    const size_t mo = (((size_t)head * n_quant + sl) * D + ch) * 2;
+    meta[mo] = lo;
+    meta[mo + 1] = sc;
+  }
+  __syncthreads();
+  // Codes: each thread packs 16 bytes = 32 channels of one token.
+  constexpr int BPT = D / 2;              // packed bytes per token
+  constexpr int VPT = BPT / 16;           // 16-byte vectors per token
+  for (int id = tid; id < 2 * kWin * VPT; id += 256) {
+    const int tn = id / (kWin * VPT);
+    const int rem = id - tn * (kWin * VPT);
+    const int r = rem / VPT, vc = rem - r * VPT;
+    uint32_t word[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t wv = 0u;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const int ch0 = vc * 32 + q * 8 + bi * 2;
+        uint32_t cpair = 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ch = ch0 + h;
+          const float sc = sc_s[tn][ch];
+          uint32_t code = 0u;
+          if (sc != 0.f) {
+            const float x = bf16_to_f32(xs[tn][r * D + ch]);
+            float qf = rintf(__fdiv_rn(__fsub_rn(x, lo_s[tn][ch]), sc));
+            qf = fminf(fmaxf(qf, 0.f), 15.f);
+            code = (uint32_t)qf;
+          }
+          cpair |= code << (4 * h);
+        }
+        wv |= cpair << (8 * bi);
+      }
+      word[q] = wv;
+    }
+    uint8_t* codes = tn == 0 ? k_codes : v_codes;
+    const size_t co = (((size_t)head * n_quant + sl) * kWin + r) * BPT + vc * 16;
+    *(u32x4_t*)(codes + co) = u32x4_t{word[0], word[1], word[2], word[3]};
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) tier_promote_kernel(
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
+    const float* __restrict__ k_meta, const float* __restrict__ v_meta,
+    const int32_t* __restrict__ promote, uint16_t* __restrict__ k_prom,
+    uint16_t* __restrict__ v_prom, int n_quant, int n_promote) {
+  constexpr int BPT = D / 2;
+  const int pi = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
+  const int sl = promote[(size_t)head * n_promote + pi];
+  const bool ok = sl >= 0 && sl < n_quant;
+  // Each thread writes 8 bf16 (16 bytes) = 8 channels of one token.
+  for (int id = tid; id < 2 * kWin * (D / 8); id += 256) {
+    const int tn = id / (kWin * (D / 8));
+    const int rem = id - tn * (kWin * (D / 8));
+    const int r = rem / (D / 8), c8 = (rem - r * (D / 8)) * 8;
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    if (ok) {
+      const uint8_t* codes = (tn == 0 ? k_codes : v_codes) +
+                             (((size_t)head * n_quant + sl) * kWin + r) * BPT + c8 / 2;
+      const float* meta = (tn == 0 ? k_meta : v_meta) + (((size_t)head * n_quant + sl) * D) * 2;
+      const uint32_t packed = *(const uint32_t*)codes;  // 8 codes
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = c8 + e;
+        const uint32_t code = (packed >> (4 * e)) & 0xfu;
+        const float lo = meta[2 * ch], sc = meta[2 * ch + 1];
+        const float x = __fadd_rn(lo, __fmul_rn((float)code, sc));
+        out[e >> 1] |= (uint32_t)f32_to_bf16_rne(x) << (16 * (e & 1));
+      }
+    }
+    uint16_t* dst = (tn == 0 ? k_prom : v_prom) +
+                    (((size_t)head * n_promote + pi) * kWin + r) * D + c8;
+    *(u32x4_t*)dst = u32x4_t{out[0], out[1], out[2], out[3]};
+  }
+}
+
+}  // namespace
+
+bool plan_tiers(const kvsel_tier_desc& d, TierPlan* p) {
+  p->nheads = d.batch * d.n_kv_heads;
+  p->nwin = d.seq_len / d.win;
+  p->off_slot = 0;
+  p->total = align256((size_t)p->nheads * p->nwin * sizeof(int32_t));
+  return true;
+}
+
+kvsel_status launch_tiers(const kvsel_tier_desc& d, const TierPlan& p, const float* scores,
+                          const void* k, const void* v, int8_t* tier, int32_t* rank,
+                          void* k_full, void* v_full, uint8_t* k_codes, uint8_t* v_codes,
+                          float* k_meta, float* v_meta, const int32_t* promote, int n_promote,
+                          void* k_prom, void* v_prom, char* ws, hipStream_t stream) {
+  int32_t* slot = (int32_t*)(ws + p.off_slot);
+  hipLaunchKernelGGL(tier_rank_kernel, dim3(p.nheads), dim3(kRankThreads), 0, stream, scores,
+                     tier, rank, slot, d.seq_len, p.nwin, d.n_full, d.n_quant);
+  const dim3 g(p.nwin, p.nheads);
+  if (d.head_dim == 128) {
+    hipLaunchKernelGGL(tier_move_kernel<128>, g, dim3(256), 0, stream, (const uint16_t*)k,
+                       (const uint16_t*)v, tier, slot, (uint16_t*)k_full, (uint16_t*)v_full,
+                       k_codes, v_codes, k_meta, v_meta, d.seq_len, p.nwin, d.n_full, d.n_quant);
+    if (n_promote > 0)
+      hipLaunchKernelGGL(tier_promote_kernel<128>, dim3(n_promote, p.nheads), dim3(256), 0,
+                         stream, k_codes, v_codes, k_meta, v_meta, promote, (uint16_t*)k_prom,
+                         (uint16_t*)v_prom, d.n_quant, n_promote);
+  } else {
+    hipLaunchKernelGGL(tier_move_kernel<64>, g, dim3(256), 0, stream, (const uint16_t*)k,
+                       (const uint16_t*)v, tier, slot, (uint16_t*)k_full, (uint16_t*)v_full,
+                       k_codes, v_codes, k_meta, v_meta, d.seq_len, p.nwin, d.n_full, d.n_quant);
+    if (n_promote > 0)
+      hipLaunchKernelGGL(tier_promote_kernel<64>, dim3(n_promote, p.nheads), dim3(256), 0,
+                         stream, k_codes, v_codes, k_meta, v_meta, promote, (uint16_t*)k_prom,
+                         (uint16_t*)v_prom, d.n_quant, n_promote);
+  }
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+}  // namespace kvsel

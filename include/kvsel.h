@@ -1,0 +1,224 @@
+/*
+ * kvsel.h -- C ABI of the attention-score KV selection and compaction library
+ * (libkvsel.so, HIP kernels for gfx950 / MI355X).
+ *
+ * One layer-end step of an observation-window KV eviction method, split into
+ * the three calls of the path and an optional tier router:
+ *
+ *   kvsel_score    observation-window attention scores, reduced over the
+ *                  window queries and the GQA group, then max-pooled
+ *   kvsel_select   top-`budget` candidate positions per KV head, plus the
+ *                  always-kept sinks and observation window
+ *   kvsel_compact  gather of the kept K/V rows into a compact cache
+ *   kvsel_route_tiers  contiguous-window routing into full / int4 / evicted
+ *                  tiers with int4 quantisation and promotion by dequantisation
+ *
+ * Sources (web pages this library implements; title, then section/equation):
+ *   [TideKV] "TideKV: Delayed KV Eviction via Layer-Wise Chunked Prefill for
+ *            Memory-Efficient Long-Context LLM Inference", Section 4.2
+ *            (Eqs. 4-8), Algorithm 2 (LayerEndCompress), Algorithm 1.
+ *   [QEvict] "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-
+ *            Robust Long-Context Decoding", Sections 4.1-4.3.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Shapes use: Bt batch, Hq query heads, Hkv KV heads (G = Hq/Hkv), D head
+ *    dimension, S prompt length, W observation window, n_sink leading
+ *    mandatory positions.  All tensors are dense, row-major, contiguous.
+ *      q_obs   [Bt, Hq,  W, D]   element type `dtype`
+ *      k, v    [Bt, Hkv, S, D]   element type `dtype`
+ *      scores  [Bt, Hkv, S]      float32
+ *      idx     [Bt, Hkv, n_keep] int32, n_keep = budget + n_sink + W
+ *      k_out   [Bt, Hkv, n_keep, D]
+ *    Query head h reads KV head floor(h / G).
+ *  - Every pointer argument is a DEVICE pointer (hipMalloc'd or equivalent)
+ *    unless stated otherwise and must be 16-byte aligned.  The caller owns all
+ *    buffers; the library never allocates, frees or keeps device memory.
+ *    Scratch memory is passed in as `ws` with a size from the matching
+ *    *_workspace() query.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; no call synchronises the host or reads device memory back.
+ *  - Every precondition is checked before anything is enqueued.  A failed check
+ *    returns a status and enqueues nothing; checks never touch the GPU, so the
+ *    argument validation also runs on a machine without a GPU.  A failed
+ *    kernel launch returns KVSEL_ERR_DEVICE.  No C++ exception crosses the ABI.
+ *  - Output buffers must not overlap inputs or each other.
+ *  - Calls on one stream are ordered; concurrent calls on different streams
+ *    must use different workspaces and outputs.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVSEL_OK = 0,
+  KVSEL_ERR_ARG = 1,          /* bad shape, null or misaligned pointer, bad enum */
+  KVSEL_ERR_BUDGET = 2,       /* budget outside [0, S - W - n_sink] */
+  KVSEL_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the workspace query */
+  KVSEL_ERR_UNSUPPORTED = 4,  /* valid but not built (head_dim other than 64/128) */
+  KVSEL_ERR_DEVICE = 5        /* a HIP launch reported an error */
+} kvsel_status;
+
+typedef enum { KVSEL_BF16 = 0, KVSEL_F32 = 1 } kvsel_dtype;
+
+/* Shape of one layer-end selection problem. */
+typedef struct {
+  int32_t batch;       /* Bt >= 1 */
+  int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t seq_len;     /* S >= 1: keys in the layer's full prompt KV */
+  int32_t obs_window;  /* W, 1 <= W <= S: observation queries; with causal=1
+                          also the last W key positions, always kept */
+  int32_t n_sink;      /* leading positions always kept, 0 <= n_sink <= S - W */
+  int32_t causal;      /* 1: query q (0-based) sits at position S-W+q and sees
+                          keys <= S-W+q (TideKV Eq. 4 causal mask);
+                          0: queries follow the cache and see every key */
+  int32_t dtype;       /* kvsel_dtype of q_obs, k and v */
+  float scale;         /* logit scale; 0 selects 1/sqrt(head_dim) (Eq. 4) */
+} kvsel_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kvsel_status_str(kvsel_status s);
+
+/* Bytes of scratch kvsel_score needs for `desc` (0 on an invalid desc). */
+size_t kvsel_score_workspace(const kvsel_desc* desc);
+
+/*
+ * kvsel_score -- per-KV-head key importance, TideKV Section 4.2.
+ *
+ * For each (b, query head h, window query q) the logits are
+ *   l[i] = scale * <q_obs[b,h,q,:], k[b,floor(h/G),i,:]>          (Eq. 4)
+ * (-inf past the query's causal position when causal=1), normalised with the
+ * row's log-sum-exp found in a first streaming pass over the keys
+ * (Eqs. 5-6) and recomputed in a second pass (Eq. 7, left):
+ *   a[i] = exp(l[i] - M) / Z.
+ * raw_scores[b,hk,i] = sum over the G query heads of KV head hk and the W
+ * queries of a[i]  (Eq. 7, right, with unit pooling weights; a sum, so each
+ * head's row sums to G*W).
+ * pooled[b,hk,i] = max of raw_scores over positions j with |j - i| <= h,
+ * h = (pool_kernel-1)/2, and j in the candidate range C = [n_sink, S-W),
+ * for i in C; 0 outside C (the "pool to p_i" step of Algorithm 2, read as a
+ * stride-1 1-D max filter that does not reach into the mandatory ranges).
+ *
+ *   q_obs       [Bt,Hq,W,D] dtype, device
+ *   k           [Bt,Hkv,S,D] dtype, device
+ *   raw_scores  [Bt,Hkv,S] float32, device, may be NULL (then kept in ws)
+ *   pooled      [Bt,Hkv,S] float32, device, required
+ *   pool_kernel odd, >= 1
+ *   ws          device scratch of >= kvsel_score_workspace(desc) bytes
+ *               (may be NULL when that size is 0)
+ * Errors: KVSEL_ERR_ARG (shape, pointer, pool_kernel even or < 1),
+ *         KVSEL_ERR_UNSUPPORTED (head_dim), KVSEL_ERR_WORKSPACE,
+ *         KVSEL_ERR_DEVICE.
+ * Numerics: bf16 or fp32 inputs, fp32 products and sums; the result does
+ * not depend on how the keys are blocked; repeated calls are bitwise equal.
+ */
+kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* k,
+                         float* raw_scores, float* pooled, int32_t pool_kernel,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of scratch kvsel_select needs (currently always 0). */
+size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget);
+
+/*
+ * kvsel_select -- retained set R per (b, KV head), TideKV Eq. (8).
+ *
+ * R = Top_budget{ pooled[i] : i in [n_sink, S-W) }  U  [0, n_sink)  U  [S-W, S),
+ * candidates ordered by (score descending, position ascending), so equal
+ * scores keep the lowest positions.  The mandatory set is always kept and
+ * `budget` counts only the non-mandatory picks: |R| = budget + n_sink + W,
+ * which is TideKV's K_l with the window counted inside the budget.
+ * idx[b,hk,:] receives R in ascending position order (int32).
+ *
+ *   pooled  [Bt,Hkv,S] float32, device; every candidate value must be a
+ *           finite number >= 0 (as kvsel_score produces)
+ *   budget  0 <= budget <= S - W - n_sink, else KVSEL_ERR_BUDGET
+ *   idx     [Bt,Hkv,budget+n_sink+W] int32, device
+ * Selection is exact: the budget-th largest value is found bit for bit by a
+ * radix select over the fp32 bit patterns.
+ */
+kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t budget,
+                          int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_compact -- GATHER of Algorithm 2: k_out[b,hk,r,:] = k[b,hk,idx[b,hk,r],:]
+ * and the same for v, byte for byte.  The position metadata of the compact
+ * cache is idx itself (absolute positions, TideKV Section 5 cache manager).
+ *
+ *   k, v         [Bt,Hkv,S,D] dtype, device
+ *   idx          [Bt,Hkv,n_keep] int32, device
+ *   n_keep       >= 0
+ *   k_out, v_out [Bt,Hkv,n_keep,D] dtype, device
+ * An index outside [0, S) yields an all-zero row (never an out-of-bounds
+ * read).  v may be NULL together with v_out to gather K only.
+ */
+kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
+                           const int32_t* idx, int32_t n_keep, void* k_out, void* v_out,
+                           void* stream);
+
+/* Shape of a window-tier routing problem (QEvict Sections 4.1-4.3). */
+typedef struct {
+  int32_t batch;       /* Bt >= 1 */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t seq_len;     /* S, a multiple of win */
+  int32_t win;         /* tokens per window and per int4 group: 64 */
+  int32_t n_full;      /* windows kept in the full-precision tier */
+  int32_t n_quant;     /* windows kept in the int4 tier; n_full + n_quant <= S/win */
+  int32_t dtype;       /* kvsel_dtype of k, v: KVSEL_BF16 only */
+} kvsel_tier_desc;
+
+/* Bytes of scratch kvsel_route_tiers needs. */
+size_t kvsel_route_tiers_workspace(const kvsel_tier_desc* desc);
+
+/*
+ * kvsel_route_tiers -- QEvict cumulative window scoring and three-tier routing.
+ *
+ * Window j of (b, hk) covers tokens [j*win, (j+1)*win); its score is the sum
+ * of token_scores over the window (Section 4.2, cumulative attention).
+ * Windows are ranked by (score descending, index ascending); ranks
+ * [0, n_full) go to the full tier (0), the next n_quant to the int4 tier (1),
+ * the rest are evicted (2) (Section 4.3, routing by rank under tier
+ * capacities).  Within each tier windows keep ascending index order.
+ *
+ * int4 rule for one group = one channel c of one window, K and V separately
+ * (asymmetric codes, Section 4.3; formula is this library's reading):
+ *   lo = min x, hi = max x, scale = (hi - lo) / 15  (fp32, IEEE division)
+ *   code = 0 if scale == 0 else clamp(rint((x - lo) / scale), 0, 15),
+ *   rint rounding half to even; packed two per byte, even channel in the
+ *   low nibble.  Dequantisation: x' = bf16_rne(lo + code * scale), with the
+ *   product and the sum each rounded to fp32 (no fused multiply-add).
+ *
+ *   token_scores [Bt,Hkv,S] float32 (e.g. kvsel_score raw scores)
+ *   k, v         [Bt,Hkv,S,D] bf16
+ *   tier         [Bt,Hkv,S/win] int8 out
+ *   win_rank     [Bt,Hkv,S/win] int32 out (0 = highest score)
+ *   k_full,v_full [Bt,Hkv,n_full*win,D] bf16 out: full-tier windows copied
+ *   k_codes,v_codes [Bt,Hkv,n_quant,win,D/2] uint8 out: packed codes
+ *   k_meta,v_meta   [Bt,Hkv,n_quant,D,2] float32 out: (lo, scale)
+ *   promote      [Bt,Hkv,n_promote] int32: slots in [0, n_quant) of the int4
+ *                tier (its ascending window order) to promote; may be NULL
+ *                when n_promote == 0
+ *   k_prom,v_prom [Bt,Hkv,n_promote*win,D] bf16 out: dequantised windows
+ * A promote slot outside [0, n_quant) yields all-zero rows.
+ * Scores closer than fp32 rounding may rank differently from an exact sum.
+ */
+kvsel_status kvsel_route_tiers(const kvsel_tier_desc* desc, const float* token_scores,
+                               const void* k, const void* v, int8_t* tier, int32_t* win_rank,
+                               void* k_full, void* v_full, uint8_t* k_codes, uint8_t* v_codes,
+                               float* k_meta, float* v_meta, const int32_t* promote,
+                               int32_t n_promote, void* k_prom, void* v_prom,
+                               void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

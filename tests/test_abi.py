@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvsel.h declares, rejects invalid arguments before launching anything,
+and sizes its workspace with the prompt length (never with W x S)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import attention_score_eviction_amd as kvsel
+    if not os.path.exists(kvsel.LIB_PATH):
+        from attention_score_eviction_amd import build
+        build.build()
+    kvsel.lib()
+    return kvsel
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(kv):
+    names = _declared()
+    assert "kvsel_score" in names and "kvsel_route_tiers" in names
+    lib = ctypes.CDLL(kv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kvsel.h but not exported"
+    assert set(kv.EXPORTS) == set(names)
+
+
+def test_status_strings(kv):
+    assert kv.status_str(kv.OK) == "ok"
+    assert "budget" in kv.status_str(kv.ERR_BUDGET)
+    assert kv.status_str(99) == "unknown status"
+
+
+FAKE = 0x10000          # aligned, never dereferenced: validation fails first
+
+
+def _desc(kv, **kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=8192, obs_window=32,
+                n_sink=0, causal=1, dtype=kv.BF16, scale=0.0)
+    base.update(kw)
+    return kv.Desc(**base)
+
+
+def _score(kv, d, pool=7, ws_bytes=None, q=FAKE, k=FAKE, pooled=FAKE, raw=None, ws=FAKE):
+    L = kv.lib()
+    if ws_bytes is None:
+        ws_bytes = L.kvsel_score_workspace(ctypes.byref(d))
+    return L.kvsel_score(ctypes.byref(d), q, k, raw, pooled, pool, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=30), "ERR_ARG"),            # Hq % Hkv != 0
+    (dict(obs_window=0), "ERR_ARG"),
+    (dict(obs_window=8193), "ERR_ARG"),          # W > S
+    (dict(n_sink=-1), "ERR_ARG"),
+    (dict(n_sink=8190), "ERR_ARG"),              # n_sink > S - W
+    (dict(causal=2), "ERR_ARG"),
+    (dict(dtype=7), "ERR_ARG"),
+    (dict(scale=-1.0), "ERR_ARG"),
+    (dict(scale=float("inf")), "ERR_ARG"),
+    (dict(batch=0), "ERR_ARG"),
+    (dict(head_dim=96), "ERR_UNSUPPORTED"),
+])
+def test_score_rejects_bad_desc(kv, kw, status):
+    d = _desc(kv, **kw)
+    assert _score(kv, d, ws_bytes=1 << 30) == getattr(kv, status)
+    assert kv.lib().kvsel_score(None, FAKE, FAKE, None, FAKE, 7, FAKE, 1 << 30, None) == kv.ERR_ARG
+
+
+def test_score_rejects_bad_arguments(kv):
+    d = _desc(kv)
+    assert _score(kv, d, pool=4) == kv.ERR_ARG           # even pool kernel
+    assert _score(kv, d, pool=0) == kv.ERR_ARG
+    assert _score(kv, d, q=None) == kv.ERR_ARG
+    assert _score(kv, d, pooled=None) == kv.ERR_ARG
+    assert _score(kv, d, k=FAKE + 4) == kv.ERR_ARG       # misaligned
+    need = kv.lib().kvsel_score_workspace(ctypes.byref(d))
+    assert need > 0
+    assert _score(kv, d, ws_bytes=need - 1) == kv.ERR_WORKSPACE
+    assert _score(kv, d, ws=None) == kv.ERR_WORKSPACE
+
+
+def test_select_budget_checks(kv):
+    L = kv.lib()
+    d = _desc(kv, seq_len=1000, obs_window=40, n_sink=4)
+    sel = lambda b, p=FAKE, i=FAKE: L.kvsel_select(ctypes.byref(d), p, b, i, None, 0, None)  # noqa
+    assert sel(-1) == kv.ERR_BUDGET
+    assert sel(1000 - 40 - 4 + 1) == kv.ERR_BUDGET
+    assert sel(10, p=None) == kv.ERR_ARG
+    assert sel(10, i=FAKE + 2) == kv.ERR_ARG
+    assert L.kvsel_select_workspace(ctypes.byref(d), 10) == 0
+
+
+def test_compact_checks(kv):
+    L = kv.lib()
+    d = _desc(kv)
+    c = lambda n, k=FAKE, v=FAKE, i=FAKE, ko=FAKE, vo=FAKE: L.kvsel_compact(  # noqa
+        ctypes.byref(d), k, v, i, n, ko, vo, None)
+    assert c(-1) == kv.ERR_ARG
+    assert c(10, k=None) == kv.ERR_ARG
+    assert c(10, vo=None) == kv.ERR_ARG           # v without v_out
+    assert c(10, i=None) == kv.ERR_ARG
+    assert c(10, ko=FAKE + 8) == kv.ERR_ARG
+
+
+def test_tier_checks(kv):
+    L = kv.lib()
+    td = kv.TierDesc(16, 8, 128, 32768, 64, 128, 256, kv.BF16)
+    need = L.kvsel_route_tiers_workspace(ctypes.byref(td))
+    assert need >= 16 * 8 * 512 * 4
+    args = [FAKE] * 12
+    call = lambda td, n_prom=0, ws_bytes=need, a=args: L.kvsel_route_tiers(  # noqa
+        ctypes.byref(td), *a[:11], None, n_prom, FAKE, FAKE, FAKE, ws_bytes, None)
+    bad = [kv.TierDesc(16, 8, 128, 32768 + 1, 64, 128, 256, kv.BF16),     # S % win
+           kv.TierDesc(16, 8, 128, 32768, 64, 400, 200, kv.BF16),         # capacities > windows
+           kv.TierDesc(0, 8, 128, 32768, 64, 128, 256, kv.BF16)]
+    for t in bad:
+        assert call(t) == kv.ERR_ARG
+    assert call(kv.TierDesc(16, 8, 128, 32768, 32, 128, 256, kv.BF16)) == kv.ERR_UNSUPPORTED
+    assert call(kv.TierDesc(16, 8, 128, 32768, 64, 128, 256, kv.F32)) == kv.ERR_UNSUPPORTED
+    assert call(td, n_prom=3) == kv.ERR_ARG        # promote list missing
+    assert call(td, ws_bytes=need - 1) == kv.ERR_WORKSPACE
+
+
+def test_workspace_is_linear_in_prompt_not_window_times_prompt(kv):
+    """The dense [Hq, W, S] score tensor is never formed (TideKV Section 4.2
+    temporary-memory bound): scratch is the per-key score vector plus small
+    per-row statistics."""
+    L = kv.lib()
+    for S, W, Hq in [(8192, 32, 32), (65536, 64, 32), (131072, 64, 40)]:
+        d = _desc(kv, seq_len=S, obs_window=W, n_q_heads=Hq)
+        ws = L.kvsel_score_workspace(ctypes.byref(d))
+        dense = Hq * W * S * 4
+        assert ws <= 8 * S * 4 + 4 * 1024 * 1024, (S, ws)
+        assert ws * 20 < dense
