@@ -94,193 +94,275 @@ __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo
   m = mn;
 }
 
+// Causal limit of a query row: the last key it may see.
+__device__ __forceinline__ int key_limit(const ScoreArgs& a, int qrow) {
+  return a.causal ? min(a.S - a.W + (qrow % a.W), a.S - 1) : (a.S - 1);
+}
+
+template <int NV>
+__device__ __forceinline__ void load_key_block(Frag<NV> (&kf)[4], const char* kh, int kb, int S,
+                                               int row_bytes, int l16, int g) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int row = min(kb + kt * 16 + l16, S - 1);
+    load_frag_global<NV>(kf[kt], kh + (size_t)row * row_bytes, g);
+  }
+}
+
+// One 64-key block of pass 1 against all NQT query tiles.  MFMAs of tile
+// t+1 are issued before the exp work of tile t.  MASK applies the causal /
+// tail mask (only the blocks that reach the window or the end of the keys).
+template <typename T, int NV, int NQT, bool MASK>
+__device__ __forceinline__ void pass1_block(const int* lims, const Frag<NV> (&kf)[4],
+                                            const u32x4_t* qs, float (&m)[NQT],
+                                            float (&z)[NQT], int kb, int row0, int lane, int g,
+                                            int l16, float c) {
+  f32x4_t acc[2][4];
+  {
+    Frag<NV> qf;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qf.v[i] = qs[i * 64 + lane];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      acc[0][kt] = mma<T, NV>(kf[kt], qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+  }
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    f32x4_t(&cur)[4] = acc[t & 1];
+    if (t + 1 < NQT) {
+      Frag<NV> qf;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) qf.v[i] = qs[((t + 1) * NV + i) * 64 + lane];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        acc[(t + 1) & 1][kt] = mma<T, NV>(kf[kt], qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+    }
+    // cur[kt][i]: key kb + kt*16 + 4g + i, query row t*16 + l16
+    if constexpr (MASK) {
+      const int lim = lims[t * 16 + l16];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb + kt * 16 + 4 * g + i > lim) cur[kt][i] = -INFINITY;
+    }
+    float mx = fmaxf(cur[0][0], cur[0][1]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = (kt == 0 ? 2 : 0); i < 4; ++i) mx = fmaxf(mx, cur[kt][i]);
+    const float mnew = fmaxf(m[t], mx * c);
+    const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mu));
+    z[t] = z[t] * __builtin_amdgcn_exp2f(m[t] - mu) + sum;
+    m[t] = mnew;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One 64-key block of pass 2: as[kt] collects, for key kb + kt*16 + l16, the
+// normalised weights of the query rows 4g..4g+3 of every tile.
+template <typename T, int NV, int NQT, bool MASK>
+__device__ __forceinline__ void pass2_block(const int* lims, const Frag<NV> (&kf)[4],
+                                            const u32x4_t* qs, const float* ls,
+                                            float (&as)[4], int kb, int row0, int lane, int g,
+                                            int l16, float c) {
+  f32x4_t acc[2][4];
+  {
+    Frag<NV> qf;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qf.v[i] = qs[i * 64 + lane];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      acc[0][kt] = mma<T, NV>(qf, kf[kt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+  }
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    f32x4_t(&cur)[4] = acc[t & 1];
+    if (t + 1 < NQT) {
+      Frag<NV> qf;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) qf.v[i] = qs[((t + 1) * NV + i) * 64 + lane];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        acc[(t + 1) & 1][kt] = mma<T, NV>(qf, kf[kt], f32x4_t{0.f, 0.f, 0.f, 0.f});
+    }
+    // cur[kt][i]: query row t*16 + 4g + i, key kb + kt*16 + l16
+    const f32x4_t lq = *(const f32x4_t*)&ls[t * 16 + 4 * g];
+    if constexpr (MASK) {
+      const int4 lim = *(const int4*)&lims[t * 16 + 4 * g];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int key = kb + kt * 16 + l16;
+        if (key > lim.x) cur[kt][0] = -INFINITY;
+        if (key > lim.y) cur[kt][1] = -INFINITY;
+        if (key > lim.z) cur[kt][2] = -INFINITY;
+        if (key > lim.w) cur[kt][3] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) as[kt] += __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -lq[i]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1: per (chunk, head, row group) partial (max, sum of exp2) per query row.
+// NQT = query tiles of 16 rows handled by every wave (rows past the group's
+// end are zero and their statistics are dropped).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int MAXQT, int NW>
+template <typename T, int D, int NQT, int NW>
 __global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
   constexpr int NV = nvec<T, D>();
   constexpr int NT = NW * 64;
-  __shared__ u32x4_t qs[MAXQT * NV * 64];
+  constexpr int RB = D * (int)sizeof(T);
+  __shared__ u32x4_t qs[NQT * NV * 64];
+  __shared__ int lims[NQT * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int chunk = blockIdx.x, head = blockIdx.y, grp = blockIdx.z;
   const int b = head / a.Hkv, hk = head - b * a.Hkv;
   const int row0 = grp * a.qcap;
   const int nrows = min(a.qcap, a.GW - row0);
-  const int nqt = (nrows + 15) >> 4;
-  const T* qg = (const T*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
-  stage_queries<T, D, NT>(qs, qg, nrows, nqt);
-  __syncthreads();
-
-  const char* kh = (const char*)((const T*)a.k + (size_t)head * a.S * D);
   const int S = a.S;
   const float c = a.c;
-  const int mask_from = a.causal ? (S - a.W + 1) : S;
-  float m[MAXQT], z[MAXQT];
-#pragma unroll
-  for (int t = 0; t < MAXQT; ++t) { m[t] = -INFINITY; z[t] = 0.f; }
-
+  const char* kh = (const char*)((const T*)a.k + (size_t)head * S * D);
   const int k0 = chunk * a.chunk;
   const int kend = min(S, k0 + a.chunk);
-  for (int kb = k0 + wave * 64; kb < kend; kb += NW * 64) {
-    Frag<NV> kf[4];
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+
+  // Issue this wave's first key block before staging the queries.
+  int kb = k0 + wave * 64;
+  Frag<NV> kf[4];
+  if (kb < kend) load_key_block<NV>(kf, kh, kb, S, RB, l16, g);
+  const T* qg = (const T*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
+  stage_queries<T, D, NT>(qs, qg, nrows, NQT);
+  for (int r = tid; r < NQT * 16; r += NT) lims[r] = key_limit(a, row0 + r);
+  __syncthreads();
+
+  float m[NQT], z[NQT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int row = min(kb + kt * 16 + l16, S - 1);
-      load_frag_global<NV>(kf[kt], kh + (size_t)row * D * sizeof(T), g);
-    }
-    const bool msk = (kb + 64 > mask_from);
-#pragma unroll
-    for (int t = 0; t < MAXQT; ++t) {
-      if (t < nqt) {
-        Frag<NV> qf;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) qf.v[i] = qs[(t * NV + i) * 64 + lane];
-        f32x4_t acc[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          // rows = keys (kb + kt*16 + 4g + i), column = query row (t*16 + l16)
-          acc[kt] = mma<T, NV>(kf[kt], qf, acc[kt]);
-        }
-        if (msk) {
-          const int qrow = row0 + t * 16 + l16;
-          const int lim = a.causal ? min(S - a.W + (qrow % a.W), S - 1) : (S - 1);
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (kb + kt * 16 + 4 * g + i > lim) acc[kt][i] = -INFINITY;
-        }
-        float mx = acc[0][0];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[kt][i]);
-        const float mnew = fmaxf(m[t], mx * c);
-        const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-        float sum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[kt][i], c, -mu));
-        z[t] = z[t] * __builtin_amdgcn_exp2f(m[t] - mu) + sum;
-        m[t] = mnew;
-      }
-    }
+  for (int t = 0; t < NQT; ++t) { m[t] = -INFINITY; z[t] = 0.f; }
+
+  for (; kb < kend; kb += NW * 64) {
+    if (kb != k0 + wave * 64) load_key_block<NV>(kf, kh, kb, S, RB, l16, g);
+    // An opaque zero offset makes the query-fragment reads loop-variant, so
+    // they are re-read from LDS every block instead of all being kept live
+    // in registers (16 VGPRs per tile).
+    int lds_off = 0;
+    asm volatile("" : "+v"(lds_off));
+    const u32x4_t* qsv = qs + lds_off;
+    if (kb + 64 > mask_from)
+      pass1_block<T, NV, NQT, true>(lims, kf, qsv, m, z, kb, row0, lane, g, l16, c);
+    else
+      pass1_block<T, NV, NQT, false>(lims, kf, qsv, m, z, kb, row0, lane, g, l16, c);
   }
 
   // Lanes l16, l16+16, l16+32, l16+48 hold partials of the same query row.
 #pragma unroll
-  for (int t = 0; t < MAXQT; ++t) {
-    if (t < nqt) {
+  for (int t = 0; t < NQT; ++t) {
 #pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float mo = __shfl_xor(m[t], off);
-        const float zo = __shfl_xor(z[t], off);
-        lse_merge(m[t], z[t], mo, zo);
-      }
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float mo = __shfl_xor(m[t], off);
+      const float zo = __shfl_xor(z[t], off);
+      lse_merge(m[t], z[t], mo, zo);
     }
   }
   __syncthreads();  // the query tiles are no longer read
-  float2* red = (float2*)qs;  // [NW][MAXQT*16]
+  float2* red = (float2*)qs;  // [NW][NQT*16]
   if (g == 0) {
 #pragma unroll
-    for (int t = 0; t < MAXQT; ++t)
-      if (t < nqt) red[wave * MAXQT * 16 + t * 16 + l16] = make_float2(m[t], z[t]);
+    for (int t = 0; t < NQT; ++t) red[wave * NQT * 16 + t * 16 + l16] = make_float2(m[t], z[t]);
   }
   __syncthreads();
   for (int r = tid; r < nrows; r += NT) {
     float mm = -INFINITY, zz = 0.f;
     for (int w = 0; w < NW; ++w) {
-      const float2 pz = red[w * MAXQT * 16 + r];
+      const float2 pz = red[w * NQT * 16 + r];
       lse_merge(mm, zz, pz.x, pz.y);
     }
-    a.part[((size_t)head * a.nchunk + chunk) * a.GWr + row0 + r] = make_float2(mm, zz);
+    // partials laid out [head][row][chunk] so the combine reads them contiguously
+    a.part[((size_t)head * a.GWr + row0 + r) * a.nchunk + chunk] = make_float2(mm, zz);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine the per-chunk partials of each query row: lse = max + log2(sum).
+// Combine the per-chunk partials of each query row (one wave per row, fixed
+// merge tree): lse = max + log2(sum).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) score_combine(const float2* __restrict__ part,
                                                      float* __restrict__ lse, int nheads,
                                                      int nchunk, int GW, int GWr) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= nheads * GW) return;
-  const int head = t / GW, r = t - head * GW;
+  const int row_id = (blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (row_id >= nheads * GW) return;
+  const int head = row_id / GW, r = row_id - head * GW;
+  const float2* p = part + ((size_t)head * GWr + r) * nchunk;
   float m = -INFINITY, z = 0.f;
-  const float2* p = part + (size_t)head * nchunk * GWr + r;
-  for (int ch = 0; ch < nchunk; ++ch) {
-    const float2 pz = p[(size_t)ch * GWr];
+  for (int ch = lane; ch < nchunk; ch += 64) {
+    const float2 pz = p[ch];
     lse_merge(m, z, pz.x, pz.y);
   }
-  lse[(size_t)head * GWr + r] = m + log2f(z);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float zo = __shfl_xor(z, off);
+    lse_merge(m, z, mo, zo);
+  }
+  if (lane == 0) lse[(size_t)head * GWr + r] = m + log2f(z);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: s[key] = sum over the group's query rows of exp2(l*c - lse[row]).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int MAXQT, int NW>
+template <typename T, int D, int NQT, int NW>
 __global__ void __launch_bounds__(NW * 64) score_pass2(ScoreArgs a) {
   constexpr int NV = nvec<T, D>();
   constexpr int NT = NW * 64;
-  __shared__ u32x4_t qs[MAXQT * NV * 64];
-  __shared__ float ls[MAXQT * 16];
+  constexpr int RB = D * (int)sizeof(T);
+  __shared__ u32x4_t qs[NQT * NV * 64];
+  __shared__ float ls[NQT * 16];
+  __shared__ int lims[NQT * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int chunk = blockIdx.x, head = blockIdx.y, grp = blockIdx.z;
   const int b = head / a.Hkv, hk = head - b * a.Hkv;
   const int row0 = grp * a.qcap;
   const int nrows = min(a.qcap, a.GW - row0);
-  const int nqt = (nrows + 15) >> 4;
-  const T* qg = (const T*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
-  stage_queries<T, D, NT>(qs, qg, nrows, nqt);
-  for (int r = tid; r < nqt * 16; r += NT)
-    ls[r] = (r < nrows) ? a.lse[(size_t)head * a.GWr + row0 + r] : INFINITY;
-  __syncthreads();
-
-  const char* kh = (const char*)((const T*)a.k + (size_t)head * a.S * D);
   const int S = a.S;
   const float c = a.c;
-  const int mask_from = a.causal ? (S - a.W + 1) : S;
-  float* out = a.s_out + ((size_t)grp * gridDim.y + head) * S;
+  const char* kh = (const char*)((const T*)a.k + (size_t)head * S * D);
   const int k0 = chunk * a.chunk;
   const int kend = min(S, k0 + a.chunk);
-  for (int kb = k0 + wave * 64; kb < kend; kb += NW * 64) {
-    Frag<NV> kf[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int row = min(kb + kt * 16 + l16, S - 1);
-      load_frag_global<NV>(kf[kt], kh + (size_t)row * D * sizeof(T), g);
-    }
-    const bool msk = (kb + 64 > mask_from);
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+
+  int kb = k0 + wave * 64;
+  Frag<NV> kf[4];
+  if (kb < kend) load_key_block<NV>(kf, kh, kb, S, RB, l16, g);
+  const T* qg = (const T*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
+  stage_queries<T, D, NT>(qs, qg, nrows, NQT);
+  for (int r = tid; r < NQT * 16; r += NT) {
+    ls[r] = (r < nrows) ? a.lse[(size_t)head * a.GWr + row0 + r] : INFINITY;
+    lims[r] = key_limit(a, row0 + r);
+  }
+  __syncthreads();
+
+  float* out = a.s_out + ((size_t)grp * gridDim.y + head) * S;
+  for (; kb < kend; kb += NW * 64) {
+    if (kb != k0 + wave * 64) load_key_block<NV>(kf, kh, kb, S, RB, l16, g);
+    int lds_off = 0;
+    asm volatile("" : "+v"(lds_off));
+    const u32x4_t* qsv = qs + lds_off;
+    const float* lsv = ls + lds_off;
     float as[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < MAXQT; ++t) {
-      if (t < nqt) {
-        Frag<NV> qf;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) qf.v[i] = qs[(t * NV + i) * 64 + lane];
-        const f32x4_t lq = *(const f32x4_t*)&ls[t * 16 + 4 * g];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-          // rows = query rows (t*16 + 4g + i), column = key (kb + kt*16 + l16)
-          acc = mma<T, NV>(qf, kf[kt], acc);
-          if (msk) {
-            const int key = kb + kt * 16 + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int qrow = row0 + t * 16 + 4 * g + i;
-              const int lim = a.causal ? min(S - a.W + (qrow % a.W), S - 1) : (S - 1);
-              if (key > lim) acc[i] = -INFINITY;
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) as[kt] += __builtin_amdgcn_exp2f(fmaf(acc[i], c, -lq[i]));
-        }
-      }
-    }
+    if (kb + 64 > mask_from)
+      pass2_block<T, NV, NQT, true>(lims, kf, qsv, lsv, as, kb, row0, lane, g, l16, c);
+    else
+      pass2_block<T, NV, NQT, false>(lims, kf, qsv, lsv, as, kb, row0, lane, g, l16, c);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       as[kt] += __shfl_xor(as[kt], 16);
@@ -319,19 +401,22 @@ __global__ void __launch_bounds__(256) maxpool_kernel(const float* __restrict__ 
   p[base + i] = v;
 }
 
-template <typename T, int D, int MAXQT, int NW>
+template <typename T, int D, int NQT, int NW>
 void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
-  hipLaunchKernelGGL((score_pass1<T, D, MAXQT, NW>), grid, dim3(NW * 64), 0, stream, args);
-  const int n = p.nheads * p.GW;
-  hipLaunchKernelGGL(score_combine, dim3((n + 255) / 256), dim3(256), 0, stream, args.part,
+  hipLaunchKernelGGL((score_pass1<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
+  const int n = p.nheads * p.GW;   // rows, one wave each
+  hipLaunchKernelGGL(score_combine, dim3((n + 3) / 4), dim3(256), 0, stream, args.part,
                      args.lse, p.nheads, p.nchunk, p.GW, p.GWr);
-  hipLaunchKernelGGL((score_pass2<T, D, MAXQT, NW>), grid, dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((score_pass2<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 
 template <typename T, int D>
-bool dispatch_qt(int maxqt, const ScoreArgs& args, dim3 grid, hipStream_t stream,
+bool dispatch_qt(int nqt, const ScoreArgs& args, dim3 grid, hipStream_t stream,
                  const ScorePlan& p) {
-  switch (maxqt) {
+  switch (nqt) {
+    case 1: launch_passes<T, D, 1, 4>(args, grid, stream, p); return true;
+    case 2: launch_passes<T, D, 2, 4>(args, grid, stream, p); return true;
+    case 4: launch_passes<T, D, 4, 4>(args, grid, stream, p); return true;
     case 8: launch_passes<T, D, 8, 4>(args, grid, stream, p); return true;
     case 16: launch_passes<T, D, 16, 4>(args, grid, stream, p); return true;
     case 20:
@@ -354,15 +439,19 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   p->GW = p->G * d.obs_window;
   p->GWr = (p->GW + 15) / 16 * 16;
   const int nqt = p->GWr / 16;
-  // Query tiles per workgroup: the whole group when it fits in about 80 KiB
-  // of LDS (20 tiles of 4 KiB need 8 waves to keep one workgroup per CU
-  // busy), else groups of 16 tiles (64 KiB), each re-reading its key chunk.
+  // Query tiles per workgroup: the whole group, rounded up to a built tile
+  // count, when it fits in about 80 KiB of LDS (20 tiles of 4 KiB run 8 waves
+  // per workgroup, one workgroup per CU); otherwise groups of 16 tiles, each
+  // re-reading its key chunk.
   int maxqt;
-  if (nqt <= 8) maxqt = 8;
+  if (nqt <= 1) maxqt = 1;
+  else if (nqt <= 2) maxqt = 2;
+  else if (nqt <= 4) maxqt = 4;
+  else if (nqt <= 8) maxqt = 8;
   else if (nqt <= 16) maxqt = 16;
   else if (nqt <= 20 && tile_bytes <= 4096) maxqt = 20;
   else maxqt = 16;
-  if (tile_bytes > 4096) maxqt = 8;
+  if (tile_bytes > 4096 && maxqt > 8) maxqt = 8;
   p->maxqt = maxqt;
   p->nwaves = (maxqt == 20) ? 8 : 4;
   p->qcap = 16 * maxqt;

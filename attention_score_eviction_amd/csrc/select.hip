@@ -17,7 +17,7 @@ namespace kvsel {
 namespace {
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelPerThread = 4;
+constexpr int kSelPerThread = 16;
 
 // Exclusive prefix sum over the workgroup; *total receives the sum of all.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total,
@@ -47,6 +47,25 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   return before + incl - v;
 }
 
+// Histogram update with wave-level aggregation: scores cluster in a few
+// bins, so lanes sharing a bin are counted by one leader lane (up to two
+// distinct bins per wave per call) before the remaining lanes add one each.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const unsigned long long act = __ballot(active);
+    if (act == 0ull) return;
+    const int leader = __ffsll((long long)act) - 1;
+    const uint32_t lb = __shfl(bin, leader);
+    const bool same = active && bin == lb;
+    const unsigned long long mk = __ballot(same);
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(mk));
+    active = active && !same;
+  }
+  if (active) atomicAdd(&hist[bin], 1u);
+}
+
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __restrict__ pooled,
                                                              int32_t* __restrict__ idx, int S,
                                                              int lo, int hi, int budget,
@@ -68,9 +87,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     const int nb = r == 2 ? 1024 : 2048;
     for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0u;
     __syncthreads();
-    for (int i = lo + tid; i < hi; i += kSelThreads) {
-      const uint32_t x = u[i];
-      if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & (uint32_t)(nb - 1)], 1u);
+    for (int base = lo; base < hi; base += kSelThreads) {
+      const int i = base + tid;
+      const uint32_t x = i < hi ? u[i] : 0u;
+      hist_add(hist, (x >> shift) & (uint32_t)(nb - 1), i < hi && (x & pmask) == prefix);
     }
     __syncthreads();
     // Thread t owns bins nb-1-2t and nb-2-2t (descending value order).

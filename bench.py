@@ -1,0 +1,207 @@
+"""Throughput of the layer-end KV selection path on one MI355X.
+
+A step is one pass of the whole path over one layer of synthetic input that
+is already resident in HBM: kvsel_score (two streaming passes over K, row
+statistics, max-pool) -> kvsel_select (exact top-B + window) -> kvsel_compact
+(K/V gather).  The metric is prompt-KV tokens scored + selected + compacted
+per second per layer.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8k|llama64k|qwen128k]
+                  [--no-cpu]
+
+Prints one JSON line.  Default workload: one Llama-3-8B-shaped layer at an
+8192-token prompt (32 query / 8 KV heads, D = 128, bf16, W = 32, pool 7,
+B = 1024).
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses  # noqa: F401
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "prompt-KV tokens scored+selected+compacted/sec per layer; % of HBM BW peak"
+WORKLOADS = {
+    "llama8k": (2, "llama3-8b-layer-8k"),
+    "llama64k": (3, "llama3-8b-layer0-64k"),
+    "qwen128k": (4, "qwen3-14b-layer-128k"),
+}
+
+
+def algorithmic_bytes(spec: synth.LayerSpec) -> dict:
+    """Bytes the path must move per layer (two K sweeps, score vectors, gather)."""
+    e = 2 if spec.dtype == "bf16" else 4
+    H = spec.batch * spec.n_kv_heads
+    S, W, D, n_keep = spec.seq_len, spec.obs_window, spec.head_dim, spec.n_keep
+    k_sweep = H * S * D * e
+    d = {
+        "score_pass1": k_sweep,
+        "score_pass2": k_sweep + H * S * 4,            # K sweep + raw score write
+        "maxpool": H * S * 4 + H * (S - W) * 4,        # raw read + pooled write
+        "select": H * (S - W) * 4 + H * n_keep * 4,    # pooled read + idx write
+        "compact": 2 * 2 * H * n_keep * D * e + H * n_keep * 4,
+    }
+    d["path"] = sum(d.values())
+    return d
+
+
+def cpu_baseline(spec: synth.LayerSpec, x: dict, budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, timed on this host on the same layer."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q64 = synth.to_f64(x["q"], spec.dtype)
+    k64 = synth.to_f64(x["k"], spec.dtype)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layer_end_compress(q64, k64, x["v"], budget=spec.budget,
+                                  window=spec.obs_window, pool_kernel=spec.pool_kernel,
+                                  n_sink=spec.n_sink, causal=bool(spec.causal),
+                                  k_store=x["k"], v_store=x["v"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": spec.batch * spec.seq_len * reps / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} full layer(s) of the same workload through the fp64 oracle "
+                      f"({el:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards by KV head with no exchange); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import attention_score_eviction_amd as kvsel
+
+    cid, wname = WORKLOADS[args.workload]
+    spec = synth.config(cid)          # the 64K workload is the sweep's layer 0 (B = 4096)
+    x = synth.make_layer(spec, cid)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if spec.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    Bt, Hkv, S, D = k.shape
+    W, B, n_keep = spec.obs_window, spec.budget, spec.n_keep
+    pooled = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev)
+    raw = torch.empty_like(pooled)
+    desc = kvsel.make_desc(q, k, n_sink=spec.n_sink, causal=bool(spec.causal))
+    ws = torch.empty(max(kvsel.score_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
+    k_hat = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=dev)
+    v_hat = torch.empty_like(k_hat)
+    stream = torch.cuda.current_stream()
+
+    def score():
+        kvsel.score(q, k, pool_kernel=spec.pool_kernel, n_sink=spec.n_sink,
+                    causal=bool(spec.causal), pooled=pooled, raw=raw, workspace=ws, stream=stream)
+
+    def select():
+        kvsel.select(pooled, B, obs_window=W, n_q_heads=spec.n_q_heads, head_dim=D,
+                     n_sink=spec.n_sink, causal=bool(spec.causal), idx=idx, dtype=k.dtype,
+                     stream=stream)
+
+    def compact():
+        kvsel.compact(k, v, idx, k_out=k_hat, v_out=v_hat, stream=stream)
+
+    def step():
+        score()
+        select()
+        compact()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-call breakdown on the same stream (events bracket each ABI call).
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3   # us per call
+
+    reps = max(args.steps, 50)
+    us = {"kvsel_score": timed(score, reps), "kvsel_select": timed(select, reps),
+          "kvsel_compact": timed(compact, reps)}
+
+    ab = algorithmic_bytes(spec)
+    tokens = Bt * S
+    value = tokens / (ms_step * 1e-3)
+    path_gbs = ab["path"] / (ms_step * 1e-3) / 1e9
+    # Dominant call: kvsel_score (both K sweeps).  Its algorithmic bytes are
+    # the two K sweeps, the raw score write and the max-pool read/write.
+    score_bytes = ab["score_pass1"] + ab["score_pass2"] + ab["maxpool"]
+    score_gbs = score_bytes / (us["kvsel_score"] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wname, "batch": Bt, "seq_len": S, "n_q_heads": spec.n_q_heads,
+                   "n_kv_heads": Hkv, "head_dim": D, "obs_window": W,
+                   "pool_kernel": spec.pool_kernel, "budget": B, "parallelism": "none"},
+        "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+        "path_algorithmic_bytes": ab["path"],
+        "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
+        "wall_s": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "kvsel_score", "bytes_per_launch": score_bytes},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(spec, x)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
