@@ -17,7 +17,6 @@ namespace kvsel {
 namespace {
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelPerThread = 16;
 
 // Exclusive prefix sum over the workgroup; *total receives the sum of all.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total,
@@ -66,19 +65,54 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
+// Each thread takes 16 consecutive scores per batch as four 16-byte loads
+// (scalar loads only at the unaligned ends), so a sweep keeps many bytes in
+// flight per CU.  Elements outside [lo, hi) come back invalid.
+constexpr int kPerThread = 16;
+constexpr int kBatch = kSelThreads * kPerThread;
+
+__device__ __forceinline__ uint32_t load16(const uint32_t* row, int p0, int lo, int hi,
+                                           uint32_t (&x)[kPerThread]) {
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int p = p0 + 4 * v;
+    if (p >= lo && p + 3 < hi) {
+      const u32x4_t w = *(const u32x4_t*)(row + p);
+      x[4 * v] = w[0];
+      x[4 * v + 1] = w[1];
+      x[4 * v + 2] = w[2];
+      x[4 * v + 3] = w[3];
+      valid |= 0xfu << (4 * v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = p + e;
+        const bool ok = i >= lo && i < hi;
+        x[4 * v + e] = ok ? row[i] : 0u;
+        valid |= (uint32_t)ok << (4 * v + e);
+      }
+    }
+  }
+  return valid;
+}
+
 __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __restrict__ pooled,
                                                              int32_t* __restrict__ idx, int S,
                                                              int lo, int hi, int budget,
                                                              int n_sink, int W, int n_keep) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t wsum[kSelThreads / 64];
-  __shared__ uint32_t pick[2];
+  __shared__ uint32_t pick[3];
   const int head = blockIdx.x, tid = threadIdx.x;
   const uint32_t* u = (const uint32_t*)pooled + (size_t)head * S;
   int32_t* out = idx + (size_t)head * n_keep;
   for (int i = tid; i < n_sink; i += kSelThreads) out[i] = i;
   for (int j = tid; j < W; j += kSelThreads) out[n_sink + budget + j] = S - W + j;
   if (budget == 0) return;
+  // First batch start: at or below lo, on a 16-byte boundary of the buffer.
+  const int ofs = (int)(((size_t)head * S) & 3u);
+  const int base0 = lo - ((lo + ofs) & 3);
 
   // Radix select: digit r covers bits [shift, shift+nbits).
   uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)budget;
@@ -87,10 +121,13 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     const int nb = r == 2 ? 1024 : 2048;
     for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0u;
     __syncthreads();
-    for (int base = lo; base < hi; base += kSelThreads) {
-      const int i = base + tid;
-      const uint32_t x = i < hi ? u[i] : 0u;
-      hist_add(hist, (x >> shift) & (uint32_t)(nb - 1), i < hi && (x & pmask) == prefix);
+    for (int base = base0; base < hi; base += kBatch) {
+      uint32_t x[kPerThread];
+      const uint32_t valid = load16(u, base + tid * kPerThread, lo, hi, x);
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        hist_add(hist, (x[e] >> shift) & (uint32_t)(nb - 1),
+                 ((valid >> e) & 1u) && (x[e] & pmask) == prefix);
     }
     __syncthreads();
     // Thread t owns bins nb-1-2t and nb-2-2t (descending value order).
@@ -106,9 +143,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
       if (above < rem && rem <= above + cA) {
         pick[0] = (uint32_t)bA;
         pick[1] = above;
+        pick[2] = cA;
       } else if (above + cA < rem && rem <= above + cA + cB) {
         pick[0] = (uint32_t)bB;
         pick[1] = above + cA;
+        pick[2] = cB;
       }
     }
     __syncthreads();
@@ -116,38 +155,41 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     rem -= pick[1];
     prefix |= digit << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
+    const bool whole_bin = rem == pick[2];
     __syncthreads();
+    // The whole boundary bin is kept: no need to resolve the lower bits.
+    if (whole_bin) break;
   }
-  // prefix is now the exact bit pattern of the budget-th largest candidate;
-  // all larger values are kept and the first `rem` equal ones (by position).
-  const uint32_t thr = prefix, need_eq = rem;
+  // Kept: (x & pmask) > prefix, and the first `rem` elements (by position)
+  // with (x & pmask) == prefix.  After three rounds pmask covers every bit
+  // and prefix is the exact bit pattern of the budget-th largest score.
+  const uint32_t need_eq = rem;
   uint32_t cgt = 0u, ceq = 0u;
-  for (int base = lo; base < hi; base += kSelThreads * kSelPerThread) {
-    const int i0 = base + tid * kSelPerThread;
-    bool gt[kSelPerThread], eq[kSelPerThread];
-    uint32_t ngt = 0u, neq = 0u;
+  for (int base = base0; base < hi; base += kBatch) {
+    const int i0 = base + tid * kPerThread;
+    uint32_t x[kPerThread];
+    const uint32_t valid = load16(u, i0, lo, hi, x);
+    uint32_t gt = 0u, eq = 0u;
 #pragma unroll
-    for (int e = 0; e < kSelPerThread; ++e) {
-      const int i = i0 + e;
-      const bool valid = i < hi;
-      const uint32_t x = valid ? u[i] : 0u;
-      gt[e] = valid && x > thr;
-      eq[e] = valid && x == thr;
-      ngt += gt[e];
-      neq += eq[e];
+    for (int e = 0; e < kPerThread; ++e) {
+      const uint32_t km = x[e] & pmask;
+      const bool ok = (valid >> e) & 1u;
+      gt |= (uint32_t)(ok && km > prefix) << e;
+      eq |= (uint32_t)(ok && km == prefix) << e;
     }
+    const uint32_t ngt = __popc(gt), neq = __popc(eq);
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan((ngt << 16) | neq, &tot, wsum);
     uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
 #pragma unroll
-    for (int e = 0; e < kSelPerThread; ++e) {
+    for (int e = 0; e < kPerThread; ++e) {
       // slot < budget always holds for finite non-negative scores; the
       // guard keeps malformed input from writing outside this row.
-      if (gt[e]) {
+      if ((gt >> e) & 1u) {
         const uint32_t slot = gtb + min(eqb, need_eq);
         if (slot < (uint32_t)budget) out[n_sink + slot] = i0 + e;
         ++gtb;
-      } else if (eq[e]) {
+      } else if ((eq >> e) & 1u) {
         const uint32_t slot = gtb + eqb;
         if (eqb < need_eq && slot < (uint32_t)budget) out[n_sink + slot] = i0 + e;
         ++eqb;
