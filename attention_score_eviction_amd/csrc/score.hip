@@ -109,6 +109,18 @@ __device__ __forceinline__ void load_key_block(Frag<NV> (&kf)[4], const char* kh
   }
 }
 
+// Ask the scheduler to alternate the next tile's MFMAs with the current
+// tile's vector work (one MFMA, then a few VALU ops), so one wave keeps the
+// matrix pipe busy while it runs the exponentials.
+template <int NMFMA>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+  }
+}
+
 // One 64-key block of pass 1 against all NQT query tiles.  MFMAs of tile
 // t+1 are issued before the exp work of tile t.  MASK applies the causal /
 // tail mask (only the blocks that reach the window or the end of the keys).
@@ -160,6 +172,7 @@ __device__ __forceinline__ void pass1_block(const int* lims, const Frag<NV> (&kf
       for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mu));
     z[t] = z[t] * __builtin_amdgcn_exp2f(m[t] - mu) + sum;
     m[t] = mnew;
+    if (t + 1 < NQT) interleave_mfma_valu<4 * NV * (sizeof(T) == 2 ? 1 : 4)>();
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -208,6 +221,7 @@ __device__ __forceinline__ void pass2_block(const int* lims, const Frag<NV> (&kf
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) as[kt] += __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -lq[i]));
+    if (t + 1 < NQT) interleave_mfma_valu<4 * NV * (sizeof(T) == 2 ? 1 : 4)>();
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -250,7 +264,10 @@ __global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
   for (int t = 0; t < NQT; ++t) { m[t] = -INFINITY; z[t] = 0.f; }
 
   for (; kb < kend; kb += NW * 64) {
-    if (kb != k0 + wave * 64) load_key_block<NV>(kf, kh, kb, S, RB, l16, g);
+    // Prefetch the next block into registers while this one is consumed.
+    Frag<NV> kn[4];
+    const bool has_next = kb + NW * 64 < kend;
+    if (has_next) load_key_block<NV>(kn, kh, kb + NW * 64, S, RB, l16, g);
     // An opaque zero offset makes the query-fragment reads loop-variant, so
     // they are re-read from LDS every block instead of all being kept live
     // in registers (16 VGPRs per tile).
@@ -261,6 +278,10 @@ __global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
       pass1_block<T, NV, NQT, true>(lims, kf, qsv, m, z, kb, row0, lane, g, l16, c);
     else
       pass1_block<T, NV, NQT, false>(lims, kf, qsv, m, z, kb, row0, lane, g, l16, c);
+    if (has_next) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) kf[kt] = kn[kt];
+    }
   }
 
   // Lanes l16, l16+16, l16+32, l16+48 hold partials of the same query row.
@@ -353,7 +374,9 @@ __global__ void __launch_bounds__(NW * 64) score_pass2(ScoreArgs a) {
 
   float* out = a.s_out + ((size_t)grp * gridDim.y + head) * S;
   for (; kb < kend; kb += NW * 64) {
-    if (kb != k0 + wave * 64) load_key_block<NV>(kf, kh, kb, S, RB, l16, g);
+    Frag<NV> kn[4];
+    const bool has_next = kb + NW * 64 < kend;
+    if (has_next) load_key_block<NV>(kn, kh, kb + NW * 64, S, RB, l16, g);
     int lds_off = 0;
     asm volatile("" : "+v"(lds_off));
     const u32x4_t* qsv = qs + lds_off;
@@ -363,6 +386,10 @@ __global__ void __launch_bounds__(NW * 64) score_pass2(ScoreArgs a) {
       pass2_block<T, NV, NQT, true>(lims, kf, qsv, lsv, as, kb, row0, lane, g, l16, c);
     else
       pass2_block<T, NV, NQT, false>(lims, kf, qsv, lsv, as, kb, row0, lane, g, l16, c);
+    if (has_next) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) kf[kt] = kn[kt];
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       as[kt] += __shfl_xor(as[kt], 16);
@@ -456,11 +483,20 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   p->nwaves = (maxqt == 20) ? 8 : 4;
   p->qcap = 16 * maxqt;
   p->ngroups = (p->GW + p->qcap - 1) / p->qcap;
-  // Key chunk: a multiple of one workgroup step; aim for >= ~1024 workgroups.
+  // Key chunk: a multiple of one workgroup step, sized so the grid is about
+  // one full wave of resident workgroups (fewer, longer workgroups amortise
+  // the query staging and keep the key prefetch busy).
   const int step = p->nwaves * 64;
+  const int lds_bytes = maxqt * tile_bytes + maxqt * 16 * 8;
+  int wg_per_cu = (160 * 1024) / lds_bytes;
+  const int wave_cap = 8 / p->nwaves;     // about two waves per SIMD
+  if (wg_per_cu > wave_cap) wg_per_cu = wave_cap;
+  if (wg_per_cu < 1) wg_per_cu = 1;
+  const long target_wg = 256L * wg_per_cu;
   const long wg_per_chunk = (long)p->nheads * p->ngroups;
-  long want_chunks = (1024 + wg_per_chunk - 1) / wg_per_chunk;
-  long steps = (long)d.seq_len / (step * want_chunks);
+  long want_chunks = (target_wg + wg_per_chunk - 1) / wg_per_chunk;
+  if (want_chunks < 1) want_chunks = 1;
+  long steps = ((long)d.seq_len + (long)step * want_chunks - 1) / ((long)step * want_chunks);
   if (steps < 1) steps = 1;
   p->chunk = (int)(steps * step);
   p->nchunk = (d.seq_len + p->chunk - 1) / p->chunk;
