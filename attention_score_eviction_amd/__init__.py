@@ -141,6 +141,10 @@ def score_workspace_bytes(desc: Desc) -> int:
     return int(lib().kvsel_score_workspace(ctypes.byref(desc)))
 
 
+def select_workspace_bytes(desc: Desc, budget: int) -> int:
+    return int(lib().kvsel_select_workspace(ctypes.byref(desc), int(budget)))
+
+
 def score(q_obs: torch.Tensor, k: torch.Tensor, *, pool_kernel: int, n_sink: int = 0,
           causal: bool = True, scale: float = 0.0, pooled: Optional[torch.Tensor] = None,
           raw: Optional[torch.Tensor] = None, want_raw: bool = True,
@@ -163,7 +167,8 @@ def score(q_obs: torch.Tensor, k: torch.Tensor, *, pool_kernel: int, n_sink: int
 
 def select(pooled: torch.Tensor, budget: int, *, obs_window: int, n_q_heads: int,
            head_dim: int, n_sink: int = 0, causal: bool = True,
-           idx: Optional[torch.Tensor] = None, dtype=torch.bfloat16, stream=None):
+           idx: Optional[torch.Tensor] = None, dtype=torch.bfloat16,
+           workspace: Optional[torch.Tensor] = None, stream=None):
     """kvsel_select: returns idx [Bt,Hkv,budget+n_sink+W] int32 (ascending)."""
     Bt, Hkv, S = pooled.shape
     d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
@@ -171,7 +176,12 @@ def select(pooled: torch.Tensor, budget: int, *, obs_window: int, n_q_heads: int
     n_keep = budget + n_sink + obs_window
     if idx is None:
         idx = torch.empty((Bt, Hkv, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
-    st = lib().kvsel_select(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx), None, 0,
+    nbytes = select_workspace_bytes(d, budget)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=pooled.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    st = lib().kvsel_select(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx), ws_ptr, ws_n,
                             _stream(stream))
     _check(st, "kvsel_select")
     return idx

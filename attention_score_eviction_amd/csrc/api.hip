@@ -88,21 +88,25 @@ kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* 
 }
 
 size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget) {
-  (void)desc;
-  (void)budget;
-  return 0;
+  if (check_desc(desc) != KVSEL_OK) return 0;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink) return 0;
+  SelectPlan p;
+  plan_select(*desc, budget, &p);
+  return p.total;
 }
 
 kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t budget,
                           int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   const kvsel_status st = check_desc(desc);
   if (st != KVSEL_OK) return st;
   if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink)
     return KVSEL_ERR_BUDGET;
   if (!pooled || !idx || !aligned16(pooled) || !aligned16(idx)) return KVSEL_ERR_ARG;
-  return launch_select(*desc, pooled, budget, idx, (hipStream_t)stream);
+  SelectPlan p;
+  plan_select(*desc, budget, &p);
+  if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVSEL_ERR_ARG;
+  return launch_select(*desc, p, pooled, budget, idx, (char*)ws, (hipStream_t)stream);
 }
 
 kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,

@@ -51,8 +51,14 @@ struct ScoreArgs {
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
                           hipStream_t stream);
-kvsel_status launch_select(const kvsel_desc& d, const float* pooled, int budget, int32_t* idx,
-                           hipStream_t stream);
+struct SelectPlan {
+  bool multi;     // sliced multi-workgroup kernels (long rows)
+  int ns;         // slices per row
+  size_t off_hist, off_gtc, off_candc, off_offs, off_params, off_cval, off_cidx, total;
+};
+bool plan_select(const kvsel_desc& d, int budget, SelectPlan* p);
+kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
+                           int budget, int32_t* idx, char* ws, hipStream_t stream);
 kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
                             const int32_t* idx, int n_keep, void* k_out, void* v_out,
                             hipStream_t stream);

@@ -18,9 +18,12 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 
-// Exclusive prefix sum over the workgroup; *total receives the sum of all.
+// Exclusive prefix sum over a workgroup of NT threads; *total receives the
+// sum of all.  wsum must hold NT/64 entries.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total,
                                                          uint32_t* wsum) {
+  constexpr int NWV = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t incl = v;
 #pragma unroll
@@ -31,17 +34,17 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    uint32_t w = lane < kSelThreads / 64 ? wsum[lane] : 0u;
+    uint32_t w = lane < NWV ? wsum[lane] : 0u;
 #pragma unroll
-    for (int off = 1; off < kSelThreads / 64; off <<= 1) {
+    for (int off = 1; off < NWV; off <<= 1) {
       const uint32_t t = __shfl_up(w, off);
       if (lane >= off) w += t;
     }
-    if (lane < kSelThreads / 64) wsum[lane] = w;
+    if (lane < NWV) wsum[lane] = w;
   }
   __syncthreads();
   const uint32_t before = wave > 0 ? wsum[wave - 1] : 0u;
-  *total = wsum[kSelThreads / 64 - 1];
+  *total = wsum[NWV - 1];
   __syncthreads();
   return before + incl - v;
 }
@@ -63,6 +66,36 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
     active = active && !same;
   }
   if (active) atomicAdd(&hist[bin], 1u);
+}
+
+// Among `nb` histogram bins read in descending value order, find the bin
+// holding the rem-th largest counted element.  pick[0] = that bin, pick[1] =
+// count strictly above it, pick[2] = its own count.  Every thread must call.
+template <int NT>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t rem,
+                                           uint32_t* wsum, uint32_t* pick) {
+  constexpr int MAXPER = 2048 / NT;
+  const int per = nb / NT;
+  const int t = threadIdx.x;
+  uint32_t c[MAXPER];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j) {
+    c[j] = j < per ? hist[nb - 1 - t * per - j] : 0u;
+    local += c[j];
+  }
+  uint32_t tot;
+  uint32_t run = block_exclusive_scan<NT>(local, &tot, wsum);
+#pragma unroll
+  for (int j = 0; j < MAXPER; ++j) {
+    if (j < per && run < rem && rem <= run + c[j]) {
+      pick[0] = (uint32_t)(nb - 1 - t * per - j);
+      pick[1] = run;
+      pick[2] = c[j];
+    }
+    run += c[j];
+  }
+  __syncthreads();
 }
 
 // Each thread takes 16 consecutive scores per batch as four 16-byte loads
@@ -130,27 +163,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
                  ((valid >> e) & 1u) && (x[e] & pmask) == prefix);
     }
     __syncthreads();
-    // Thread t owns bins nb-1-2t and nb-2-2t (descending value order).
-    const int bA = nb - 1 - 2 * tid, bB = bA - 1;
-    uint32_t cA = 0u, cB = 0u;
-    if (bB >= 0) {
-      cA = hist[bA];
-      cB = hist[bB];
-    }
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(cA + cB, &tot, wsum);
-    if (bB >= 0) {
-      if (above < rem && rem <= above + cA) {
-        pick[0] = (uint32_t)bA;
-        pick[1] = above;
-        pick[2] = cA;
-      } else if (above + cA < rem && rem <= above + cA + cB) {
-        pick[0] = (uint32_t)bB;
-        pick[1] = above + cA;
-        pick[2] = cB;
-      }
-    }
-    __syncthreads();
+    find_digit<kSelThreads>(hist, nb, rem, wsum, pick);
     const uint32_t digit = pick[0];
     rem -= pick[1];
     prefix |= digit << shift;
@@ -179,7 +192,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     }
     const uint32_t ngt = __popc(gt), neq = __popc(eq);
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan((ngt << 16) | neq, &tot, wsum);
+    const uint32_t ex = block_exclusive_scan<kSelThreads>((ngt << 16) | neq, &tot, wsum);
     uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -201,15 +214,362 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-workgroup select for long rows.  A row's candidate range is cut into
+// slices of kSlice scores (256 threads x 16).  The kernels run in order:
+//   sel_init     zero the row's first-digit histogram, write the mandatory set
+//   sel_hist     per slice: 11-bit first-digit histogram -> global (atomics)
+//   sel_cand     per slice: first digit d1 of the budget-th score; count the
+//                scores above d1's bin and compact the ones inside it
+//   sel_resolve  per row: the remaining 21 bits over the compacted scores,
+//                the tie cut (by position), and each slice's output offset
+//   sel_emit     per slice: ordered write of the kept positions
+// The rule every kernel applies in the end is one predicate per score:
+// kept <=> key > prefix || (key == prefix && position <= cut), with
+// key = bits & pmask.
+// ---------------------------------------------------------------------------
+constexpr int kSliceThreads = 256;
+constexpr int kSlice = kSliceThreads * kPerThread;
+
+struct SelArgs {
+  const float* pooled;
+  int32_t* idx;
+  uint32_t* hist1;     // [rows][2048]
+  uint32_t* gtc;       // [rows][ns] scores above the first-digit bin
+  uint32_t* candc;     // [rows][ns] scores inside it
+  uint32_t* offs;      // [rows][ns] output offset of each slice
+  uint32_t* params;    // [rows][4] prefix, pmask, cut
+  uint32_t* cval;      // [rows][ns][kSlice] compacted score bits
+  int32_t* cidx;       // [rows][ns][kSlice] their positions
+  int S, lo, hi, budget, n_sink, W, n_keep, ns;
+};
+
+__device__ __forceinline__ int slice_base(const SelArgs& a, int row) {
+  const int ofs = (int)(((size_t)row * a.S) & 3u);
+  return a.lo - ((a.lo + ofs) & 3);
+}
+
+__global__ void __launch_bounds__(256) sel_init(SelArgs a) {
+  const int row = blockIdx.x, tid = threadIdx.x;
+  uint32_t* h = a.hist1 + (size_t)row * 2048;
+  for (int i = tid; i < 2048; i += 256) h[i] = 0u;
+  int32_t* out = a.idx + (size_t)row * a.n_keep;
+  for (int i = tid; i < a.n_sink; i += 256) out[i] = i;
+  for (int j = tid; j < a.W; j += 256) out[a.n_sink + a.budget + j] = a.S - a.W + j;
+}
+
+__global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
+  __shared__ uint32_t hist[2048];
+  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  for (int i = tid; i < 2048; i += kSliceThreads) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
+  const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) hist_add(hist, x[e] >> 21, (valid >> e) & 1u);
+  __syncthreads();
+  uint32_t* g = a.hist1 + (size_t)row * 2048;
+  for (int i = tid; i < 2048; i += kSliceThreads)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wsum[kSliceThreads / 64];
+  __shared__ uint32_t pick[3];
+  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const uint32_t* g = a.hist1 + (size_t)row * 2048;
+  for (int i = tid; i < 2048; i += kSliceThreads) hist[i] = g[i];
+  __syncthreads();
+  find_digit<kSliceThreads>(hist, 2048, (uint32_t)a.budget, wsum, pick);
+  const uint32_t d1 = pick[0];
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
+  const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  uint32_t gt = 0u, in = 0u;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool ok = (valid >> e) & 1u;
+    gt += ok && (x[e] >> 21) > d1;
+    in |= (uint32_t)(ok && (x[e] >> 21) == d1) << e;
+  }
+  uint32_t tot;
+  uint32_t pos = block_exclusive_scan<kSliceThreads>((gt << 16) | __popc(in), &tot, wsum) & 0xffffu;
+  const size_t cbase = ((size_t)row * a.ns + sl) * kSlice;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if ((in >> e) & 1u) {
+      a.cval[cbase + pos] = x[e];
+      a.cidx[cbase + pos] = i0 + e;
+      ++pos;
+    }
+  }
+  if (tid == 0) {
+    a.gtc[(size_t)row * a.ns + sl] = tot >> 16;
+    a.candc[(size_t)row * a.ns + sl] = tot & 0xffffu;
+  }
+}
+
+// Compacted scores held in LDS by sel_resolve (more spill to a slower path
+// that reads them from global memory on every pass).
+constexpr int kCandCap = 14336;
+
+// Slice of flat candidate number k, given the exclusive prefix of the
+// per-slice counts (cstart, ns entries, non-decreasing).
+__device__ __forceinline__ int slice_of(const uint32_t* cstart, int ns, uint32_t k) {
+  int lo = 0, hi = ns - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cstart[mid] <= k) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t selc[2048];
+  __shared__ uint32_t cstart[2048];
+  __shared__ uint32_t lval[kCandCap];
+  __shared__ int32_t lidx[kCandCap];
+  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t pick[3];
+  __shared__ uint32_t cut_s;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int ns = a.ns;
+  const uint32_t* g = a.hist1 + (size_t)row * 2048;
+  const uint32_t* cc = a.candc + (size_t)row * ns;
+  for (int i = tid; i < 2048; i += kSelThreads) {
+    hist[i] = g[i];
+    selc[i] = 0u;
+  }
+  if (tid == 0) cut_s = 0x7fffffffu;
+  // Flat numbering of the compacted scores (slice order = position order).
+  uint32_t c0 = 0u, c1 = 0u;
+  if (2 * tid < ns) c0 = cc[2 * tid];
+  if (2 * tid + 1 < ns) c1 = cc[2 * tid + 1];
+  uint32_t ncand;
+  const uint32_t ex = block_exclusive_scan<kSelThreads>(c0 + c1, &ncand, wsum);
+  if (2 * tid < ns) cstart[2 * tid] = ex;
+  if (2 * tid + 1 < ns) cstart[2 * tid + 1] = ex + c0;
+  __syncthreads();
+  find_digit<kSelThreads>(hist, 2048, (uint32_t)a.budget, wsum, pick);
+  uint32_t rem = (uint32_t)a.budget - pick[1];
+  uint32_t prefix = pick[0] << 21, pmask = 0x7ffu << 21;
+  bool whole = rem == pick[2];
+  __syncthreads();
+  const uint32_t* cv = a.cval + (size_t)row * ns * kSlice;
+  const int32_t* ci = a.cidx + (size_t)row * ns * kSlice;
+  const bool in_lds = ncand <= (uint32_t)kCandCap;
+  // Gather the compacted scores into LDS with independent loads.
+  if (!whole && in_lds) {
+    for (uint32_t k = tid; k < ncand; k += kSelThreads) {
+      const int sl = slice_of(cstart, ns, k);
+      const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
+      lval[k] = cv[at];
+      lidx[k] = ci[at];
+    }
+    __syncthreads();
+  }
+  auto cand = [&](uint32_t k, uint32_t& v, int32_t& i) {
+    if (in_lds) {
+      v = lval[k];
+      i = lidx[k];
+    } else {
+      const int sl = slice_of(cstart, ns, k);
+      const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
+      v = cv[at];
+      i = ci[at];
+    }
+  };
+  // Lower digits over the compacted scores (all share the first digit).
+  for (int r = 1; r < 3 && !whole; ++r) {
+    const int shift = r == 1 ? 10 : 0;
+    const int nb = r == 1 ? 2048 : 1024;
+    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t k0 = 0; k0 < ncand; k0 += kSelThreads) {
+      const uint32_t k = k0 + tid;
+      uint32_t x = 0u;
+      int32_t pos;
+      if (k < ncand) cand(k, x, pos);
+      hist_add(hist, (x >> shift) & (uint32_t)(nb - 1), k < ncand && (x & pmask) == prefix);
+    }
+    __syncthreads();
+    find_digit<kSelThreads>(hist, nb, rem, wsum, pick);
+    rem -= pick[1];
+    prefix |= pick[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    whole = rem == pick[2];
+    __syncthreads();
+  }
+  // Tie cut: position of the rem-th score equal to the prefix.  Each thread
+  // takes a contiguous run of candidates, so one scan orders them.
+  if (!whole) {
+    const uint32_t per = (ncand + kSelThreads - 1) / kSelThreads;
+    const uint32_t k0 = tid * per, k1 = min(ncand, k0 + per);
+    uint32_t neq = 0u;
+    for (uint32_t k = k0; k < k1; ++k) {
+      uint32_t x;
+      int32_t pos;
+      cand(k, x, pos);
+      neq += (x & pmask) == prefix;
+    }
+    uint32_t tot;
+    uint32_t seen = block_exclusive_scan<kSelThreads>(neq, &tot, wsum);
+    if (seen < rem && rem <= seen + neq) {
+      for (uint32_t k = k0; k < k1; ++k) {
+        uint32_t x;
+        int32_t pos;
+        cand(k, x, pos);
+        if ((x & pmask) == prefix && ++seen == rem) {
+          cut_s = (uint32_t)pos;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t cut = cut_s;
+  // Kept compacted scores per slice.  When the first digit's bin is kept
+  // whole every compacted score is kept; otherwise apply the predicate.
+  if (pmask == (0x7ffu << 21)) {
+    for (int sl = tid; sl < ns; sl += kSelThreads) selc[sl] = cc[sl];
+  } else {
+    for (uint32_t k0 = 0; k0 < ncand; k0 += kSelThreads) {
+      const uint32_t k = k0 + tid;
+      bool keep = false;
+      int sl = 0;
+      if (k < ncand) {
+        uint32_t x;
+        int32_t pos;
+        cand(k, x, pos);
+        const uint32_t key = x & pmask;
+        keep = key > prefix || (key == prefix && (uint32_t)pos <= cut);
+        sl = slice_of(cstart, ns, k);
+      }
+      hist_add(selc, (uint32_t)sl, keep);
+    }
+  }
+  __syncthreads();
+  // Exclusive prefix over slices of (above-bin + kept-inside-bin) counts.
+  const uint32_t* gt = a.gtc + (size_t)row * ns;
+  uint32_t k0c = 0u, k1c = 0u;
+  const int s0 = 2 * tid, s1 = 2 * tid + 1;
+  if (s0 < ns) k0c = gt[s0] + selc[s0];
+  if (s1 < ns) k1c = gt[s1] + selc[s1];
+  uint32_t tot;
+  const uint32_t exo = block_exclusive_scan<kSelThreads>(k0c + k1c, &tot, wsum);
+  uint32_t* of = a.offs + (size_t)row * ns;
+  if (s0 < ns) of[s0] = exo;
+  if (s1 < ns) of[s1] = exo + k0c;
+  if (tid == 0) {
+    uint32_t* pr = a.params + (size_t)row * 4;
+    pr[0] = prefix;
+    pr[1] = pmask;
+    pr[2] = cut;
+  }
+}
+
+__global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
+  __shared__ uint32_t wsum[kSliceThreads / 64];
+  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const uint32_t* pr = a.params + (size_t)row * 4;
+  const uint32_t prefix = pr[0], pmask = pr[1], cut = pr[2];
+  const uint32_t base_out = a.offs[(size_t)row * a.ns + sl];
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
+  const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const uint32_t key = x[e] & pmask;
+    const bool k = ((valid >> e) & 1u) &&
+                   (key > prefix || (key == prefix && (uint32_t)(i0 + e) <= cut));
+    keep |= (uint32_t)k << e;
+  }
+  uint32_t tot;
+  uint32_t pos = base_out + block_exclusive_scan<kSliceThreads>(__popc(keep), &tot, wsum);
+  int32_t* out = a.idx + (size_t)row * a.n_keep + a.n_sink;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if ((keep >> e) & 1u) {
+      // pos < budget for finite non-negative scores; guarded regardless.
+      if (pos < (uint32_t)a.budget) out[pos] = i0 + e;
+      ++pos;
+    }
+  }
+}
+
 }  // namespace
 
-kvsel_status launch_select(const kvsel_desc& d, const float* pooled, int budget, int32_t* idx,
-                           hipStream_t stream) {
-  const int nheads = d.batch * d.n_kv_heads;
+bool plan_select(const kvsel_desc& d, int budget, SelectPlan* p) {
+  const int rows = d.batch * d.n_kv_heads;
+  const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
+  const long ncand = (long)hi - lo;
+  // Short rows: one workgroup per row in one launch.  Long rows: the sliced
+  // multi-workgroup kernels (the slice count includes the alignment lead-in).
+  // (sel_resolve keeps per-slice counters for at most 2048 slices.)
+  const long ns = (ncand + 3 + kSlice - 1) / kSlice;
+  p->multi = budget > 0 && ncand > kBatch && ns <= 2048;
+  p->ns = p->multi ? (int)ns : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  if (p->multi) {
+    p->off_hist = take((size_t)rows * 2048 * 4);
+    p->off_gtc = take((size_t)rows * p->ns * 4);
+    p->off_candc = take((size_t)rows * p->ns * 4);
+    p->off_offs = take((size_t)rows * p->ns * 4);
+    p->off_params = take((size_t)rows * 4 * 4);
+    p->off_cval = take((size_t)rows * p->ns * kSlice * 4);
+    p->off_cidx = take((size_t)rows * p->ns * kSlice * 4);
+  }
+  p->total = off;
+  return true;
+}
+
+kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
+                           int budget, int32_t* idx, char* ws, hipStream_t stream) {
+  const int rows = d.batch * d.n_kv_heads;
   const int n_keep = budget + d.n_sink + d.obs_window;
-  hipLaunchKernelGGL(select_kernel, dim3(nheads), dim3(kSelThreads), 0, stream, pooled, idx,
-                     d.seq_len, d.n_sink, d.seq_len - d.obs_window, budget, d.n_sink,
-                     d.obs_window, n_keep);
+  const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
+  if (!p.multi) {
+    hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, pooled, idx,
+                       d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
+    return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+  }
+  SelArgs a;
+  a.pooled = pooled;
+  a.idx = idx;
+  a.hist1 = (uint32_t*)(ws + p.off_hist);
+  a.gtc = (uint32_t*)(ws + p.off_gtc);
+  a.candc = (uint32_t*)(ws + p.off_candc);
+  a.offs = (uint32_t*)(ws + p.off_offs);
+  a.params = (uint32_t*)(ws + p.off_params);
+  a.cval = (uint32_t*)(ws + p.off_cval);
+  a.cidx = (int32_t*)(ws + p.off_cidx);
+  a.S = d.seq_len;
+  a.lo = lo;
+  a.hi = hi;
+  a.budget = budget;
+  a.n_sink = d.n_sink;
+  a.W = d.obs_window;
+  a.n_keep = n_keep;
+  a.ns = p.ns;
+  const dim3 sg(p.ns, rows);
+  hipLaunchKernelGGL(sel_init, dim3(rows), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_resolve, dim3(rows), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 

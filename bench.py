@@ -116,6 +116,8 @@ def main() -> int:
     desc = kvsel.make_desc(q, k, n_sink=spec.n_sink, causal=bool(spec.causal))
     ws = torch.empty(max(kvsel.score_workspace_bytes(desc), 1), dtype=torch.uint8, device=dev)
     idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
+    sel_bytes = kvsel.select_workspace_bytes(desc, B)
+    sel_ws = torch.empty(max(sel_bytes, 1), dtype=torch.uint8, device=dev)
     k_hat = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=dev)
     v_hat = torch.empty_like(k_hat)
     stream = torch.cuda.current_stream()
@@ -127,7 +129,7 @@ def main() -> int:
     def select():
         kvsel.select(pooled, B, obs_window=W, n_q_heads=spec.n_q_heads, head_dim=D,
                      n_sink=spec.n_sink, causal=bool(spec.causal), idx=idx, dtype=k.dtype,
-                     stream=stream)
+                     workspace=sel_ws, stream=stream)
 
     def compact():
         kvsel.compact(k, v, idx, k_out=k_hat, v_out=v_hat, stream=stream)

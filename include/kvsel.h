@@ -124,7 +124,10 @@ kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* 
                          float* raw_scores, float* pooled, int32_t pool_kernel,
                          void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of scratch kvsel_select needs (currently always 0). */
+/* Bytes of scratch kvsel_select needs for `desc` and `budget` (0 when the
+ * rows are short enough for the single-workgroup kernel, or on invalid
+ * arguments).  Long rows use a sliced multi-workgroup radix select whose
+ * scratch is about 8 bytes per candidate position plus per-slice counters. */
 size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget);
 
 /*
@@ -146,6 +149,8 @@ size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget);
  */
 kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t budget,
                           int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+/* (kvsel_select: ws is device scratch of >= kvsel_select_workspace(desc,
+ * budget) bytes, may be NULL when that is 0; else KVSEL_ERR_WORKSPACE.) */
 
 /*
  * kvsel_compact -- GATHER of Algorithm 2: k_out[b,hk,r,:] = k[b,hk,idx[b,hk,r],:]

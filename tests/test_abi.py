@@ -99,7 +99,13 @@ def test_select_budget_checks(kv):
     assert sel(1000 - 40 - 4 + 1) == kv.ERR_BUDGET
     assert sel(10, p=None) == kv.ERR_ARG
     assert sel(10, i=FAKE + 2) == kv.ERR_ARG
-    assert L.kvsel_select_workspace(ctypes.byref(d), 10) == 0
+    assert L.kvsel_select_workspace(ctypes.byref(d), 10) == 0          # short rows
+    long_d = _desc(kv, seq_len=131072, obs_window=64)
+    need = L.kvsel_select_workspace(ctypes.byref(long_d), 4096)
+    assert 8 * 131072 * 8 <= need <= 8 * 131072 * 8 + (1 << 20)
+    assert L.kvsel_select_workspace(ctypes.byref(long_d), 0) == 0     # nothing to pick
+    assert L.kvsel_select(ctypes.byref(long_d), FAKE, 4096, FAKE, FAKE, need - 1, None) \
+        == kv.ERR_WORKSPACE
 
 
 def test_compact_checks(kv):

@@ -97,16 +97,21 @@ def test_score_is_deterministic():
     assert torch.equal(s1, s2) and torch.equal(p1, p2)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_select_exact_on_identical_inputs(seed):
+@pytest.mark.parametrize("seed,S", [(0, 9000), (1, 9777), (2, 10554), (3, 70001), (4, 131072),
+                                    (5, 50000)])
+def test_select_exact_on_identical_inputs(seed, S):
     """Given the same fp32 scores, the GPU selection is bit-exact with the
     oracle's (ties -> lowest positions), including heavy tie plateaus."""
     kvsel = _kvsel()
     rng = np.random.default_rng(seed)
-    Bt, Hkv, S, W, n_sink = 2, 3, 9000 + seed * 777, 40, seed
-    if seed == 0:
+    Bt, Hkv, W, n_sink = 2, 3, 40, seed % 3
+    if seed in (0, 4):
         p = rng.random((Bt, Hkv, S)).astype(np.float32)
-    elif seed == 1:
+    elif seed == 5:
+        # a dense band of near-equal values around the threshold
+        p = (np.float32(1.0) + rng.integers(0, 3000, size=(Bt, Hkv, S)).astype(np.float32)
+             * np.float32(2.0 ** -20)).astype(np.float32)
+    elif seed in (1, 3):
         p = rng.integers(0, 5, size=(Bt, Hkv, S)).astype(np.float32) * np.float32(0.25)
     else:
         p = np.full((Bt, Hkv, S), 0.125, np.float32)
@@ -115,7 +120,7 @@ def test_select_exact_on_identical_inputs(seed):
     p[..., :n_sink] = 0
     p[..., S - W:] = 0
     pt = torch.from_numpy(p).cuda()
-    for budget in [1, 7, 1000, S - W - n_sink]:
+    for budget in [1, 7, 1000, 4096, S - W - n_sink]:
         got = kvsel.select(pt, budget, obs_window=W, n_q_heads=Hkv, head_dim=128,
                            n_sink=n_sink).cpu().numpy()
         want = oracle.select(p.astype(np.float64), budget, n_sink, W)
