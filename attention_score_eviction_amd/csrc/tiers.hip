@@ -112,6 +112,7 @@ __global__ void __launch_bounds__(256) tier_move_kernel(
     uint16_t* __restrict__ k_full, uint16_t* __restrict__ v_full, uint8_t* __restrict__ k_codes,
     uint8_t* __restrict__ v_codes, float* __restrict__ k_meta, float* __restrict__ v_meta, int S,
     int nwin, int n_full, int n_quant) {
+#pragma clang fp contract(off)
   constexpr int VPW = kWin * D * 2 / 16;  // 16-byte vectors per window per tensor
   __shared__ uint16_t xs[2][kWin * D];
   __shared__ float lo_s[2][D], sc_s[2][D];
@@ -150,7 +151,7 @@ __global__ void __launch_bounds__(256) tier_move_kernel(
       lo = fminf(lo, x);
       hi = fmaxf(hi, x);
     }
-    const float sc = __fdiv_rn(__fsub_rn(hi, lo), 15.0f);
+    const float sc = (hi - lo) / 15.0f;
     lo_s[tn][ch] = lo;
     sc_s[tn][ch] = sc;
     float* meta = tn == 0 ? k_meta : v_meta;
@@ -181,7 +182,7 @@ __global__ void __launch_bounds__(256) tier_move_kernel(
           uint32_t code = 0u;
           if (sc != 0.f) {
             const float x = bf16_to_f32(xs[tn][r * D + ch]);
-            float qf = rintf(__fdiv_rn(__fsub_rn(x, lo_s[tn][ch]), sc));
+            float qf = rintf((x - lo_s[tn][ch]) / sc);
             qf = fminf(fmaxf(qf, 0.f), 15.f);
             code = (uint32_t)qf;
           }
@@ -203,6 +204,9 @@ __global__ void __launch_bounds__(256) tier_promote_kernel(
     const float* __restrict__ k_meta, const float* __restrict__ v_meta,
     const int32_t* __restrict__ promote, uint16_t* __restrict__ k_prom,
     uint16_t* __restrict__ v_prom, int n_quant, int n_promote) {
+  // The dequantised value is defined with two roundings (product, then sum):
+  // forbid fusing them into one multiply-add.
+#pragma clang fp contract(off)
   constexpr int BPT = D / 2;
   const int pi = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const int sl = promote[(size_t)head * n_promote + pi];
@@ -223,7 +227,8 @@ __global__ void __launch_bounds__(256) tier_promote_kernel(
         const int ch = c8 + e;
         const uint32_t code = (packed >> (4 * e)) & 0xfu;
         const float lo = meta[2 * ch], sc = meta[2 * ch + 1];
-        const float x = __fadd_rn(lo, __fmul_rn((float)code, sc));
+        const float prod = (float)code * sc;
+        const float x = lo + prod;
         out[e >> 1] |= (uint32_t)f32_to_bf16_rne(x) << (16 * (e & 1));
       }
     }

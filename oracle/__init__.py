@@ -27,5 +27,8 @@ from .reference import (  # noqa: F401
     route_tiers,
     quant_int4,
     dequant_int4,
+    round_bf16,
+    pack_nibbles,
+    tier_outputs,
     cache_bytes,
 )

@@ -230,6 +230,66 @@ def dequant_int4(codes: np.ndarray, lo: np.ndarray, scale: np.ndarray) -> np.nda
     return (lo.astype(np.float32) + prod).astype(np.float32)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to
+    even: keep the high 16 bits after adding half an ulp of bf16 plus the
+    parity of the kept least-significant bit.  Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    return ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)).astype(np.uint16)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes along the last axis two per byte, the even channel in
+    the low nibble: [..., D] -> [..., D/2] uint8."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 2 == 0 and int(c.max(initial=0)) <= 15
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def tier_outputs(k_bits: np.ndarray, v_bits: np.ndarray, tier: np.ndarray, win: int,
+                 promote: np.ndarray | None = None) -> dict:
+    """Tier payloads for a given window routing (QEvict Section 4.3).
+
+    k_bits/v_bits: bf16 bit patterns [Bt, Hkv, S, D]; tier: [Bt, Hkv, S/win]
+    with 0 = full precision, 1 = int4, 2 = evicted.  Within a tier the
+    windows keep ascending index order.  Returns k_full/v_full (copied bits),
+    k_codes/v_codes (packed int4 per window, [n_quant, win, D/2]),
+    k_meta/v_meta ([n_quant, D, 2] fp32 lo and scale) and, for the int4-tier
+    slots listed in `promote` ([Bt, Hkv, n_promote]), k_prom/v_prom: the
+    dequantised windows rounded to bf16 bit patterns.  Groups are one
+    channel of one window (win values); see quant_int4.
+    """
+    Bt, Hkv, S, D = k_bits.shape
+    out = {key: [] for key in ("k_full", "v_full", "k_codes", "v_codes", "k_meta", "v_meta",
+                               "k_prom", "v_prom")}
+    for b in range(Bt):
+        for h in range(Hkv):
+            full = [j for j in range(S // win) if tier[b, h, j] == 0]
+            quant = [j for j in range(S // win) if tier[b, h, j] == 1]
+            for name, x in (("k", k_bits), ("v", v_bits)):
+                rows = x[b, h].reshape(S // win, win, D)
+                out[name + "_full"].append(rows[full].reshape(-1, D))
+                codes, metas, deq = [], [], []
+                for j in quant:
+                    vals = (rows[j].astype(np.uint32) << np.uint32(16)).view(np.float32)
+                    c, lo, sc = quant_int4(vals)
+                    codes.append(pack_nibbles(c))
+                    metas.append(np.stack([lo, sc], axis=-1))
+                    deq.append(round_bf16(dequant_int4(c, lo, sc)))
+                out[name + "_codes"].append(np.array(codes, dtype=np.uint8).reshape(-1, win, D // 2))
+                out[name + "_meta"].append(np.array(metas, dtype=np.float32).reshape(-1, D, 2))
+                if promote is not None:
+                    out[name + "_prom"].append(
+                        np.concatenate([deq[int(p)] for p in promote[b, h]], axis=0)
+                        if promote.shape[-1] else np.zeros((0, D), np.uint16))
+    res = {}
+    for key, lst in out.items():
+        if lst:
+            res[key] = np.stack(lst).reshape((Bt, Hkv) + lst[0].shape)
+    return res
+
+
 # ---------------------------------------------------------------------------
 # Memory model
 # ---------------------------------------------------------------------------

@@ -314,3 +314,49 @@ def test_linear_budget_schedule():
     assert b[0] == 4096 and b[31] == 512
     assert all(x >= y for x, y in zip(b, b[1:]))
     assert sum(b) == 73743
+
+
+# ------------------------------------------------------------- tier output ---
+
+def test_round_bf16_matches_torch_conversion():
+    """Round-to-nearest-even to bfloat16, pinned to torch's own conversion,
+    including exact halfway cases in both parities."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 50,
+                        np.array([1.0, -2.5, 3.0e-30, 65504.0, 0.0, -0.0], np.float32)])
+    # halfway: low 16 bits exactly 0x8000 with even and odd kept parts
+    half = (np.arange(64, dtype=np.uint32) << 16 | 0x3F800000 | 0x8000).view(np.float32)
+    x = np.concatenate([x, half, -half])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.round_bf16(x), want)
+
+
+def test_pack_nibbles_layout():
+    codes = np.array([[1, 2, 15, 0, 7, 8]], dtype=np.uint8)
+    assert oracle.pack_nibbles(codes).tolist() == [[0x21, 0x0F, 0x87]]
+
+
+def test_tier_outputs_small_brute_force():
+    """Full-tier rows are the routed windows' bits in window order; int4 slots
+    follow window order; metadata is the per-channel min and range/15."""
+    rng = np.random.default_rng(22)
+    Bt, Hkv, win, nW, D = 1, 2, 4, 5, 6
+    kb = synth.f32_to_bf16_bits(rng.standard_normal((Bt, Hkv, nW * win, D)).astype(np.float32))
+    vb = synth.f32_to_bf16_bits(rng.standard_normal((Bt, Hkv, nW * win, D)).astype(np.float32))
+    tier = np.array([[[1, 0, 2, 1, 0], [2, 0, 0, 1, 1]]], dtype=np.int8)
+    prom = np.array([[[1], [0]]], dtype=np.int32)
+    out = oracle.tier_outputs(kb, vb, tier, win, prom)
+    assert out["k_full"][0, 0].tobytes() == np.concatenate([kb[0, 0, 4:8], kb[0, 0, 16:20]]).tobytes()
+    assert out["v_full"][0, 1].tobytes() == vb[0, 1, 4:12].tobytes()
+    assert out["k_codes"].shape == (1, 2, 2, win, D // 2)
+    f = synth.bf16_bits_to_f32(kb[0, 0, 12:16])            # window 3 = int4 slot 1 of head 0
+    lo, hi = f.min(0), f.max(0)
+    np.testing.assert_array_equal(out["k_meta"][0, 0, 1, :, 0], lo)
+    np.testing.assert_array_equal(out["k_meta"][0, 0, 1, :, 1],
+                                  ((hi - lo).astype(np.float32) / np.float32(15)).astype(np.float32))
+    # promoted slot 1 of head 0 is window 3 dequantised; every value within
+    # half a quantisation step (plus bf16 rounding) of the source
+    deq = synth.bf16_bits_to_f32(out["k_prom"][0, 0])
+    step = out["k_meta"][0, 0, 1, :, 1]
+    assert (np.abs(deq - f) <= step / 2 + np.abs(f) * 2 ** -8 + 1e-30).all()
