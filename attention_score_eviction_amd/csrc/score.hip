@@ -13,10 +13,12 @@
 //    qcap query rows.  The group's query rows are staged once in LDS in MFMA
 //    fragment order (each 16-row tile is 64 lanes x D*e/64 16-byte vectors,
 //    so every ds_read_b128 is a contiguous, conflict-free 1 KiB).
+//  * The query rows reach LDS by direct global->LDS copies (no registers).
 //  * Every wave streams its own 64-key blocks straight from HBM into
 //    registers (4 tiles of 16 keys; each lane reads D*e/4 contiguous bytes of
-//    one key row, which is exactly its MFMA operand fragment), then loops over
-//    the query tiles in LDS.  Waves never synchronise inside the key loop.
+//    one key row, which is exactly its MFMA operand fragment), prefetching the
+//    next block, then loops over the query tiles in LDS.  Waves never
+//    synchronise inside the key loop.
 //  * The contraction uses v_mfma_f32_16x16x32_bf16 (bf16 inputs) or
 //    v_mfma_f32_16x16x4_f32 (fp32 inputs), fp32 accumulation.  The operand
 //    roles are swapped between the passes so that the dimension each pass
@@ -71,20 +73,26 @@ __device__ __forceinline__ f32x4_t mma(const Frag<NV>& a, const Frag<NV>& b, f32
 
 // Stage query rows [0, nrows) of a group (row-major, D elements each) into LDS
 // in fragment order: vector (tile t, v, lane) at index (t*NV + v)*64 + lane.
+// Each wave copies whole 1 KiB fragment vectors straight from global memory
+// into LDS (global_load_lds_dwordx4), so no registers hold the data and all
+// copies are in flight together.  Rows past nrows repeat the last row; their
+// results are never used (pass 1 drops their statistics, pass 2 gives them an
+// infinite normaliser).
 template <typename T, int D, int NT>
 __device__ __forceinline__ void stage_queries(u32x4_t* qs, const T* qg, int nrows, int nqt) {
   constexpr int NV = nvec<T, D>();
-  const int total = nqt * NV * 64;
-  for (int id = threadIdx.x; id < total; id += NT) {
-    const int lane = id & 63;
-    const int v = (id >> 6) % NV;
-    const int t = (id >> 6) / NV;
-    const int row = t * 16 + (lane & 15);
-    const int g = lane >> 4;
-    u32x4_t val = {0u, 0u, 0u, 0u};
-    if (row < nrows) val = *(const u32x4_t*)((const char*)(qg + (size_t)row * D) + (4 * v + g) * 16);
-    qs[id] = val;
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  for (int tv = wave; tv < nqt * NV; tv += NW) {
+    const int t = tv / NV, v = tv - t * NV;
+    const int row = min(t * 16 + (lane & 15), nrows - 1);
+    const char* src = (const char*)(qg + (size_t)row * D) + (4 * v + g) * 16;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)(qs + tv * 64),
+                                     16, 0, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
@@ -106,18 +114,6 @@ __device__ __forceinline__ void load_key_block(Frag<NV> (&kf)[4], const char* kh
   for (int kt = 0; kt < 4; ++kt) {
     const int row = min(kb + kt * 16 + l16, S - 1);
     load_frag_global<NV>(kf[kt], kh + (size_t)row * row_bytes, g);
-  }
-}
-
-// Ask the scheduler to alternate the next tile's MFMAs with the current
-// tile's vector work (one MFMA, then a few VALU ops), so one wave keeps the
-// matrix pipe busy while it runs the exponentials.
-template <int NMFMA>
-__device__ __forceinline__ void interleave_mfma_valu() {
-#pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
   }
 }
 
@@ -158,21 +154,25 @@ __device__ __forceinline__ void pass1_block(const int* lims, const Frag<NV> (&kf
         for (int i = 0; i < 4; ++i)
           if (kb + kt * 16 + 4 * g + i > lim) cur[kt][i] = -INFINITY;
     }
-    float mx = fmaxf(cur[0][0], cur[0][1]);
+    float m4[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = (kt == 0 ? 2 : 0); i < 4; ++i) mx = fmaxf(mx, cur[kt][i]);
+      m4[kt] = fmaxf(fmaxf(cur[kt][0], cur[kt][1]), fmaxf(cur[kt][2], cur[kt][3]));
+    const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     const float mnew = fmaxf(m[t], mx * c);
     const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-    float sum = 0.f;
+    // All exponentials first, then the sums: no add waits on a fresh
+    // transcendental result.
+    float e[16];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mu));
+      for (int i = 0; i < 4; ++i) e[kt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mu));
+    const float sum = (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
+                      (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
     z[t] = z[t] * __builtin_amdgcn_exp2f(m[t] - mu) + sum;
     m[t] = mnew;
-    if (t + 1 < NQT) interleave_mfma_valu<4 * NV * (sizeof(T) == 2 ? 1 : 4)>();
+    
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -217,11 +217,15 @@ __device__ __forceinline__ void pass2_block(const int* lims, const Frag<NV> (&kf
         if (key > lim.w) cur[kt][3] = -INFINITY;
       }
     }
+    float e[16];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) as[kt] += __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -lq[i]));
-    if (t + 1 < NQT) interleave_mfma_valu<4 * NV * (sizeof(T) == 2 ? 1 : 4)>();
+      for (int i = 0; i < 4; ++i) e[kt * 4 + i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -lq[i]));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      as[kt] += (e[kt * 4] + e[kt * 4 + 1]) + (e[kt * 4 + 2] + e[kt * 4 + 3]);
+    
     __builtin_amdgcn_sched_barrier(0);
   }
 }

@@ -71,25 +71,27 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 // Among `nb` histogram bins read in descending value order, find the bin
 // holding the rem-th largest counted element.  pick[0] = that bin, pick[1] =
 // count strictly above it, pick[2] = its own count.  Every thread must call.
-template <int NT>
+template <int NT, int MAXNB = 2048>
 __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t rem,
                                            uint32_t* wsum, uint32_t* pick) {
-  constexpr int MAXPER = 2048 / NT;
-  const int per = nb / NT;
+  constexpr int MAXPER = (MAXNB + NT - 1) / NT;
+  const int per = (nb + NT - 1) / NT;   // bins per thread (nb <= MAXNB)
   const int t = threadIdx.x;
   uint32_t c[MAXPER];
   uint32_t local = 0u;
 #pragma unroll
   for (int j = 0; j < MAXPER; ++j) {
-    c[j] = j < per ? hist[nb - 1 - t * per - j] : 0u;
+    const int b = nb - 1 - t * per - j;
+    c[j] = (j < per && b >= 0) ? hist[b] : 0u;
     local += c[j];
   }
   uint32_t tot;
   uint32_t run = block_exclusive_scan<NT>(local, &tot, wsum);
 #pragma unroll
   for (int j = 0; j < MAXPER; ++j) {
-    if (j < per && run < rem && rem <= run + c[j]) {
-      pick[0] = (uint32_t)(nb - 1 - t * per - j);
+    const int b = nb - 1 - t * per - j;
+    if (j < per && b >= 0 && run < rem && rem <= run + c[j]) {
+      pick[0] = (uint32_t)b;
       pick[1] = run;
       pick[2] = c[j];
     }
@@ -147,6 +149,12 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
   const int ofs = (int)(((size_t)head * S) & 3u);
   const int base0 = lo - ((lo + ofs) & 3);
 
+  // A row that fits one batch is loaded once and kept in registers.
+  const bool one_batch = hi - base0 <= kBatch;
+  uint32_t x1[kPerThread];
+  uint32_t v1 = 0u;
+  if (one_batch) v1 = load16(u, base0 + tid * kPerThread, lo, hi, x1);
+
   // Radix select: digit r covers bits [shift, shift+nbits).
   uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)budget;
   for (int r = 0; r < 3; ++r) {
@@ -156,7 +164,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     __syncthreads();
     for (int base = base0; base < hi; base += kBatch) {
       uint32_t x[kPerThread];
-      const uint32_t valid = load16(u, base + tid * kPerThread, lo, hi, x);
+      const uint32_t valid = one_batch ? v1 : load16(u, base + tid * kPerThread, lo, hi, x);
+      if (one_batch) {
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) x[e] = x1[e];
+      }
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e)
         hist_add(hist, (x[e] >> shift) & (uint32_t)(nb - 1),
@@ -181,7 +193,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
   for (int base = base0; base < hi; base += kBatch) {
     const int i0 = base + tid * kPerThread;
     uint32_t x[kPerThread];
-    const uint32_t valid = load16(u, i0, lo, hi, x);
+    const uint32_t valid = one_batch ? v1 : load16(u, i0, lo, hi, x);
+    if (one_batch) {
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) x[e] = x1[e];
+    }
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -224,17 +240,20 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
 //   sel_resolve  per row: the remaining 21 bits over the compacted scores,
 //                the tie cut (by position), and each slice's output offset
 //   sel_emit     per slice: ordered write of the kept positions
+// The digits have 11, 11 and 10 bits (the first: sign, exponent and two
+// mantissa bits, a quarter octave per bin).
 // The rule every kernel applies in the end is one predicate per score:
 // kept <=> key > prefix || (key == prefix && position <= cut), with
 // key = bits & pmask.
 // ---------------------------------------------------------------------------
 constexpr int kSliceThreads = 256;
 constexpr int kSlice = kSliceThreads * kPerThread;
+constexpr int kD1Bits = 11, kD1Bins = 1 << kD1Bits, kD1Shift = 32 - kD1Bits;
 
 struct SelArgs {
   const float* pooled;
   int32_t* idx;
-  uint32_t* hist1;     // [rows][2048]
+  uint32_t* hist1;     // [rows][kD1Bins]
   uint32_t* gtc;       // [rows][ns] scores above the first-digit bin
   uint32_t* candc;     // [rows][ns] scores inside it
   uint32_t* offs;      // [rows][ns] output offset of each slice
@@ -251,39 +270,39 @@ __device__ __forceinline__ int slice_base(const SelArgs& a, int row) {
 
 __global__ void __launch_bounds__(256) sel_init(SelArgs a) {
   const int row = blockIdx.x, tid = threadIdx.x;
-  uint32_t* h = a.hist1 + (size_t)row * 2048;
-  for (int i = tid; i < 2048; i += 256) h[i] = 0u;
+  uint32_t* h = a.hist1 + (size_t)row * kD1Bins;
+  for (int i = tid; i < kD1Bins; i += 256) h[i] = 0u;
   int32_t* out = a.idx + (size_t)row * a.n_keep;
   for (int i = tid; i < a.n_sink; i += 256) out[i] = i;
   for (int j = tid; j < a.W; j += 256) out[a.n_sink + a.budget + j] = a.S - a.W + j;
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
-  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t hist[kD1Bins];
   const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  for (int i = tid; i < 2048; i += kSliceThreads) hist[i] = 0u;
+  for (int i = tid; i < kD1Bins; i += kSliceThreads) hist[i] = 0u;
   __syncthreads();
   const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
   const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) hist_add(hist, x[e] >> 21, (valid >> e) & 1u);
+  for (int e = 0; e < kPerThread; ++e) hist_add(hist, x[e] >> kD1Shift, (valid >> e) & 1u);
   __syncthreads();
-  uint32_t* g = a.hist1 + (size_t)row * 2048;
-  for (int i = tid; i < 2048; i += kSliceThreads)
+  uint32_t* g = a.hist1 + (size_t)row * kD1Bins;
+  for (int i = tid; i < kD1Bins; i += kSliceThreads)
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
-  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t hist[kD1Bins];
   __shared__ uint32_t wsum[kSliceThreads / 64];
   __shared__ uint32_t pick[3];
   const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  const uint32_t* g = a.hist1 + (size_t)row * 2048;
-  for (int i = tid; i < 2048; i += kSliceThreads) hist[i] = g[i];
+  const uint32_t* g = a.hist1 + (size_t)row * kD1Bins;
+  for (int i = tid; i < kD1Bins; i += kSliceThreads) hist[i] = g[i];
   __syncthreads();
-  find_digit<kSliceThreads>(hist, 2048, (uint32_t)a.budget, wsum, pick);
+  find_digit<kSliceThreads, kD1Bins>(hist, kD1Bins, (uint32_t)a.budget, wsum, pick);
   const uint32_t d1 = pick[0];
   const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
   const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
@@ -293,8 +312,8 @@ __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const bool ok = (valid >> e) & 1u;
-    gt += ok && (x[e] >> 21) > d1;
-    in |= (uint32_t)(ok && (x[e] >> 21) == d1) << e;
+    gt += ok && (x[e] >> kD1Shift) > d1;
+    in |= (uint32_t)(ok && (x[e] >> kD1Shift) == d1) << e;
   }
   uint32_t tot;
   uint32_t pos = block_exclusive_scan<kSliceThreads>((gt << 16) | __popc(in), &tot, wsum) & 0xffffu;
@@ -330,7 +349,7 @@ __device__ __forceinline__ int slice_of(const uint32_t* cstart, int ns, uint32_t
 }
 
 __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
-  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t hist[kD1Bins];
   __shared__ uint32_t selc[2048];
   __shared__ uint32_t cstart[2048];
   __shared__ uint32_t lval[kCandCap];
@@ -340,12 +359,10 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   __shared__ uint32_t cut_s;
   const int row = blockIdx.x, tid = threadIdx.x;
   const int ns = a.ns;
-  const uint32_t* g = a.hist1 + (size_t)row * 2048;
+  const uint32_t* g = a.hist1 + (size_t)row * kD1Bins;
   const uint32_t* cc = a.candc + (size_t)row * ns;
-  for (int i = tid; i < 2048; i += kSelThreads) {
-    hist[i] = g[i];
-    selc[i] = 0u;
-  }
+  for (int i = tid; i < kD1Bins; i += kSelThreads) hist[i] = g[i];
+  for (int i = tid; i < 2048; i += kSelThreads) selc[i] = 0u;
   if (tid == 0) cut_s = 0x7fffffffu;
   // Flat numbering of the compacted scores (slice order = position order).
   uint32_t c0 = 0u, c1 = 0u;
@@ -356,9 +373,9 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   if (2 * tid < ns) cstart[2 * tid] = ex;
   if (2 * tid + 1 < ns) cstart[2 * tid + 1] = ex + c0;
   __syncthreads();
-  find_digit<kSelThreads>(hist, 2048, (uint32_t)a.budget, wsum, pick);
+  find_digit<kSelThreads, kD1Bins>(hist, kD1Bins, (uint32_t)a.budget, wsum, pick);
   uint32_t rem = (uint32_t)a.budget - pick[1];
-  uint32_t prefix = pick[0] << 21, pmask = 0x7ffu << 21;
+  uint32_t prefix = pick[0] << kD1Shift, pmask = (uint32_t)(kD1Bins - 1) << kD1Shift;
   bool whole = rem == pick[2];
   __syncthreads();
   const uint32_t* cv = a.cval + (size_t)row * ns * kSlice;
@@ -436,7 +453,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   const uint32_t cut = cut_s;
   // Kept compacted scores per slice.  When the first digit's bin is kept
   // whole every compacted score is kept; otherwise apply the predicate.
-  if (pmask == (0x7ffu << 21)) {
+  if (pmask == (uint32_t)(kD1Bins - 1) << kD1Shift) {
     for (int sl = tid; sl < ns; sl += kSelThreads) selc[sl] = cc[sl];
   } else {
     for (uint32_t k0 = 0; k0 < ncand; k0 += kSelThreads) {
@@ -524,7 +541,7 @@ bool plan_select(const kvsel_desc& d, int budget, SelectPlan* p) {
     return o;
   };
   if (p->multi) {
-    p->off_hist = take((size_t)rows * 2048 * 4);
+    p->off_hist = take((size_t)rows * kD1Bins * 4);
     p->off_gtc = take((size_t)rows * p->ns * 4);
     p->off_candc = take((size_t)rows * p->ns * 4);
     p->off_offs = take((size_t)rows * p->ns * 4);

@@ -105,6 +105,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// One workgroup per window.  Full tier: 16-byte row copy.  int4 tier: thread
+// (tensor, 8-channel octet, token group) loads 8 tokens x 8 channels with
+// 16-byte loads, keeps them in registers, reduces per-channel min/max through
+// LDS, then writes its packed codes (4 bytes per token).
 template <int D>
 __global__ void __launch_bounds__(256) tier_move_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -113,8 +117,11 @@ __global__ void __launch_bounds__(256) tier_move_kernel(
     uint8_t* __restrict__ v_codes, float* __restrict__ k_meta, float* __restrict__ v_meta, int S,
     int nwin, int n_full, int n_quant) {
 #pragma clang fp contract(off)
-  constexpr int VPW = kWin * D * 2 / 16;  // 16-byte vectors per window per tensor
-  __shared__ uint16_t xs[2][kWin * D];
+  constexpr int VPW = kWin * D * 2 / 16;       // 16-byte vectors per window per tensor
+  constexpr int OCT = D / 8;                   // 8-channel octets per token
+  constexpr int TG = 256 / (2 * OCT);          // token groups (8 for D=128, 16 for D=64)
+  constexpr int TPT = kWin / TG;               // tokens per thread (8 or 4)
+  __shared__ float red_lo[TG][2][D], red_hi[TG][2][D];
   __shared__ float lo_s[2][D], sc_s[2][D];
   const int j = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const int t = tier[(size_t)head * nwin + j];
@@ -136,65 +143,73 @@ __global__ void __launch_bounds__(256) tier_move_kernel(
     }
     return;
   }
-  // int4 tier: stage the window of K and V in LDS.
-  for (int i = tid; i < VPW; i += 256) {
-    ((u32x4_t*)xs[0])[i] = ((const u32x4_t*)(k + src))[i];
-    ((u32x4_t*)xs[1])[i] = ((const u32x4_t*)(v + src))[i];
+  // int4 tier.
+  const int tn = tid / (OCT * TG);             // 0 = K, 1 = V
+  const int rem = tid - tn * (OCT * TG);
+  const int oct = rem % OCT, tg = rem / OCT;
+  const uint16_t* x = (tn == 0 ? k : v) + src;
+  float val[TPT][8];
+#pragma unroll
+  for (int r = 0; r < TPT; ++r) {
+    const u32x4_t w = *(const u32x4_t*)(x + (size_t)(tg * TPT + r) * D + oct * 8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      val[r][2 * h] = __uint_as_float(w[h] << 16);
+      val[r][2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float lo = val[0][c], hi = val[0][c];
+#pragma unroll
+    for (int r = 1; r < TPT; ++r) {
+      lo = fminf(lo, val[r][c]);
+      hi = fmaxf(hi, val[r][c]);
+    }
+    red_lo[tg][tn][oct * 8 + c] = lo;
+    red_hi[tg][tn][oct * 8 + c] = hi;
   }
   __syncthreads();
-  // Per-channel range: thread -> (tensor, channel).
+  // Per (tensor, channel): reduce the token groups, form (lo, scale).
   for (int id = tid; id < 2 * D; id += 256) {
-    const int tn = id / D, ch = id - tn * D;
-    float lo = bf16_to_f32(xs[tn][ch]), hi = lo;
-    for (int r = 1; r < kWin; ++r) {
-      const float x = bf16_to_f32(xs[tn][r * D + ch]);
-      lo = fminf(lo, x);
-      hi = fmaxf(hi, x);
+    const int tt = id / D, ch = id - tt * D;
+    float lo = red_lo[0][tt][ch], hi = red_hi[0][tt][ch];
+    for (int g2 = 1; g2 < TG; ++g2) {
+      lo = fminf(lo, red_lo[g2][tt][ch]);
+      hi = fmaxf(hi, red_hi[g2][tt][ch]);
     }
     const float sc = (hi - lo) / 15.0f;
-    lo_s[tn][ch] = lo;
-    sc_s[tn][ch] = sc;
-    float* meta = tn == 0 ? k_meta : v_meta;
+    lo_s[tt][ch] = lo;
+    sc_s[tt][ch] = sc;
+    float* meta = tt == 0 ? k_meta : v_meta;
     const size_t mo = (((size_t)head * n_quant + sl) * D + ch) * 2;
     meta[mo] = lo;
     meta[mo + 1] = sc;
   }
   __syncthreads();
-  // Codes: each thread packs 16 bytes = 32 channels of one token.
-  constexpr int BPT = D / 2;              // packed bytes per token
-  constexpr int VPT = BPT / 16;           // 16-byte vectors per token
-  for (int id = tid; id < 2 * kWin * VPT; id += 256) {
-    const int tn = id / (kWin * VPT);
-    const int rem = id - tn * (kWin * VPT);
-    const int r = rem / VPT, vc = rem - r * VPT;
-    uint32_t word[4];
+  // Codes for this thread's 8 channels of each of its tokens: 4 packed bytes.
+  float lo8[8], sc8[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t wv = 0u;
+  for (int c = 0; c < 8; ++c) {
+    lo8[c] = lo_s[tn][oct * 8 + c];
+    sc8[c] = sc_s[tn][oct * 8 + c];
+  }
+  constexpr int BPT = D / 2;  // packed bytes per token
+  uint8_t* codes = (tn == 0 ? k_codes : v_codes) + ((size_t)head * n_quant + sl) * kWin * BPT;
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const int ch0 = vc * 32 + q * 8 + bi * 2;
-        uint32_t cpair = 0u;
+  for (int r = 0; r < TPT; ++r) {
+    uint32_t word = 0u;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ch = ch0 + h;
-          const float sc = sc_s[tn][ch];
-          uint32_t code = 0u;
-          if (sc != 0.f) {
-            const float x = bf16_to_f32(xs[tn][r * D + ch]);
-            float qf = rintf((x - lo_s[tn][ch]) / sc);
-            qf = fminf(fmaxf(qf, 0.f), 15.f);
-            code = (uint32_t)qf;
-          }
-          cpair |= code << (4 * h);
-        }
-        wv |= cpair << (8 * bi);
+    for (int c = 0; c < 8; ++c) {
+      uint32_t code = 0u;
+      if (sc8[c] != 0.f) {
+        float qf = rintf((val[r][c] - lo8[c]) / sc8[c]);
+        qf = fminf(fmaxf(qf, 0.f), 15.f);
+        code = (uint32_t)qf;
       }
-      word[q] = wv;
+      word |= code << (4 * c);
     }
-    uint8_t* codes = tn == 0 ? k_codes : v_codes;
-    const size_t co = (((size_t)head * n_quant + sl) * kWin + r) * BPT + vc * 16;
-    *(u32x4_t*)(codes + co) = u32x4_t{word[0], word[1], word[2], word[3]};
+    *(uint32_t*)(codes + (size_t)(tg * TPT + r) * BPT + oct * 4) = word;
   }
 }
 
