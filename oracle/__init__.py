@@ -21,6 +21,8 @@ from .reference import (  # noqa: F401
     head_scores,
     max_pool,
     select,
+    select_head_adaptive,
+    compact_flat,
     compact_rows,
     layer_end_compress,
     window_sums,

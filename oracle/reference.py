@@ -16,7 +16,9 @@ pooling weights w_q = 1; GQA aggregation is a sum over the group with query
 head h mapped to KV head floor(h / G); the 1-D max-pool over key positions runs
 over the candidate range only, stride 1, window clipped at its edges; ties in
 the pooled score are broken by lowest position; the retained set is emitted in
-ascending position order; ``budget`` counts non-mandatory picks.
+ascending position order; ``budget`` counts non-mandatory picks.  Head-adaptive
+selection picks over all KV heads of a sequence with no per-head floor beyond
+the mandatory set, ties broken by (head, position) ascending.
 """
 from __future__ import annotations
 
@@ -145,6 +147,67 @@ def compact_rows(x: np.ndarray, idx: np.ndarray) -> np.ndarray:
     idx: [Bt, Hkv, n]. Returns [Bt, Hkv, n, D].
     """
     return np.take_along_axis(x, idx.astype(np.int64)[..., None], axis=2)
+
+
+def select_head_adaptive(p: np.ndarray, total_budget: int, n_sink: int, window: int):
+    """Head-adaptive retained positions per sequence, in a flattened layout with
+    per-head offsets   (TideKV Section 4.1, head-adaptive budget; Eq. (8)
+    applied to the union of a sequence's KV heads).
+
+    The sequence's candidates are the pairs (h, i) with n_sink <= i < S-W over
+    all of its KV heads; the ``total_budget`` largest pooled scores among them
+    are picked, ordered by (p descending, head ascending, position ascending),
+    so a head receives as many rows as it has scores above the sequence-wide
+    threshold.  Every head still keeps its own mandatory set (sinks and the
+    observation window).  Head h's retained positions, ascending, occupy rows
+    [off[b, h], off[b, h+1]) of the sequence's flattened index row.
+
+    p: [Bt, Hkv, S].  Returns (idx int32 [Bt, Hkv*(n_sink+W) + total_budget],
+    off int32 [Bt, Hkv+1]).
+    """
+    Bt, H, S = p.shape
+    lo, hi = n_sink, S - window
+    ncand = hi - lo
+    if not (0 <= n_sink and 1 <= window <= S and lo <= hi and 0 <= total_budget <= H * ncand):
+        raise ValueError("infeasible budget / window")
+    n_keep = H * (n_sink + window) + total_budget
+    idx = np.empty((Bt, n_keep), dtype=np.int32)
+    off = np.empty((Bt, H + 1), dtype=np.int32)
+    heads = np.repeat(np.arange(H), ncand)
+    pos = np.tile(np.arange(lo, hi), H)
+    for b in range(Bt):
+        score = p[b, :, lo:hi].reshape(-1)
+        order = np.lexsort((pos, heads, -score))      # last key is primary
+        chosen = order[:total_budget]
+        at = 0
+        for h in range(H):
+            mine = pos[chosen[heads[chosen] == h]]
+            keep = np.concatenate([np.arange(0, lo), mine, np.arange(hi, S)])
+            keep.sort()
+            off[b, h] = at
+            idx[b, at:at + keep.size] = keep
+            at += keep.size
+        off[b, H] = at
+        assert at == n_keep
+    return idx, off
+
+
+def compact_flat(x: np.ndarray, idx: np.ndarray, off: np.ndarray) -> np.ndarray:
+    """Gather a flattened head-adaptive cache: row r of sequence b, with
+    off[b, h] <= r < off[b, h+1], is x[b, h, idx[b, r], :]   (TideKV
+    Algorithm 2 GATHER into the flattened per-head-offset layout of Section
+    4.1).
+
+    x: [Bt, Hkv, S, D] (bit patterns copied unchanged).  Returns [Bt, n, D].
+    """
+    Bt, H = x.shape[:2]
+    n = idx.shape[1]
+    out = np.empty((Bt, n, x.shape[3]), dtype=x.dtype)
+    for b in range(Bt):
+        for h in range(H):
+            r0, r1 = int(off[b, h]), int(off[b, h + 1])
+            out[b, r0:r1] = x[b, h, idx[b, r0:r1].astype(np.int64)]
+    return out
 
 
 def layer_end_compress(q_obs, k, v, *, budget, window, pool_kernel, n_sink=0,

@@ -207,6 +207,101 @@ def test_select_rejects_infeasible(B, n_sink, W):
         oracle.select(np.zeros((1, 10)), B, n_sink, W)
 
 
+# ------------------------------------------------- head-adaptive select ----
+
+def _flat_heads(idx, off, b, H):
+    return [idx[b, off[b, h]:off[b, h + 1]].tolist() for h in range(H)]
+
+
+def test_head_adaptive_matches_subset_brute_force():
+    """With distinct scores the picked set is the unique T-subset of a
+    sequence's candidates (over all heads) with the largest score sum."""
+    import itertools
+    rng = np.random.default_rng(41)
+    H, S, n_sink, W = 3, 9, 1, 2
+    for T in [0, 1, 4, 7, 18]:
+        p = rng.permutation(2 * H * S).reshape(2, H, S)[:, :, :].astype(np.float64) + 0.5
+        idx, off = oracle.select_head_adaptive(p, T, n_sink, W)
+        assert idx.shape == (2, H * (n_sink + W) + T) and off.shape == (2, H + 1)
+        for b in range(2):
+            cand = [(h, i) for h in range(H) for i in range(n_sink, S - W)]
+            best = max(itertools.combinations(cand, T),
+                       key=lambda c: sum(p[b, h, i] for h, i in c)) if T else ()
+            for h in range(H):
+                want = sorted(list(range(n_sink)) + [i for g, i in best if g == h]
+                              + list(range(S - W, S)))
+                assert _flat_heads(idx, off, b, H)[h] == want
+            assert off[b, 0] == 0 and off[b, H] == idx.shape[1]
+
+
+def test_head_adaptive_ties_go_to_lower_head_then_position():
+    p = np.zeros((1, 2, 8))
+    p[0, 0] = [0, 5, 2, 5, 1, 0, 9, 9]
+    p[0, 1] = [0, 5, 5, 3, 5, 0, 9, 9]
+    # sinks 1, window 2 -> candidates 1..5; T = 4: the five 5s tie for four
+    # places -> head 0 positions 1, 3, then head 1 positions 1, 2.
+    idx, off = oracle.select_head_adaptive(p, 4, 1, 2)
+    assert off.tolist() == [[0, 5, 10]]
+    assert idx.tolist() == [[0, 1, 3, 6, 7, 0, 1, 2, 6, 7]]
+
+
+def test_head_adaptive_separable_scores_reduce_to_uniform_budget():
+    """When every head's top-B scores exceed all other candidates of the
+    sequence, the head-adaptive picks equal the per-head selection."""
+    rng = np.random.default_rng(42)
+    Bt, H, S, n_sink, W, B = 2, 4, 64, 2, 6, 5
+    p = rng.random((Bt, H, S))
+    for b in range(Bt):
+        for h in range(H):
+            top = rng.choice(np.arange(n_sink, S - W), B, replace=False)
+            p[b, h, top] += 10.0
+    idx, off = oracle.select_head_adaptive(p, H * B, n_sink, W)
+    uni = oracle.select(p, B, n_sink, W)
+    assert (off == np.arange(H + 1)[None] * (B + n_sink + W)).all()
+    assert (idx == uni.reshape(Bt, -1)).all()
+
+
+def test_head_adaptive_dominant_head_takes_every_pick():
+    p = np.full((1, 3, 20), 0.25)
+    p[0, 1, 2:17] = np.linspace(1.0, 2.0, 15)
+    idx, off = oracle.select_head_adaptive(p, 10, 0, 3)
+    segs = _flat_heads(idx, off, 0, 3)
+    assert segs[0] == [17, 18, 19] and segs[2] == [17, 18, 19]
+    assert segs[1] == list(range(7, 20))
+
+
+def test_head_adaptive_single_head_equals_select():
+    spec = synth.config(1)
+    x = synth.make_layer(spec, 1)
+    s = oracle.head_scores(synth.to_f64(x["q"], "f32"), synth.to_f64(x["k"], "f32"))
+    S, W = spec.seq_len, spec.obs_window
+    p = oracle.max_pool(s, 5, 4, S - W)
+    for h in range(2):
+        idx, off = oracle.select_head_adaptive(p[:, h:h + 1], 64, 4, W)
+        assert off.tolist() == [[0, 64 + 4 + W]]
+        assert (idx == oracle.select(p[:, h:h + 1], 64, 4, W)[:, 0]).all()
+
+
+@pytest.mark.parametrize("T,n_sink,W", [(-1, 0, 2), (2 * 8 + 1, 0, 2), (0, 0, 0), (0, 9, 2)])
+def test_head_adaptive_rejects_infeasible(T, n_sink, W):
+    with pytest.raises(ValueError):
+        oracle.select_head_adaptive(np.zeros((1, 2, 10)), T, n_sink, W)
+
+
+def test_compact_flat_rows_follow_their_head():
+    rng = np.random.default_rng(43)
+    kb = rng.integers(0, 65536, size=(2, 3, 30, 4), dtype=np.uint16)
+    p = rng.random((2, 3, 30))
+    idx, off = oracle.select_head_adaptive(p, 11, 1, 3)
+    out = oracle.compact_flat(kb, idx, off)
+    for b in range(2):
+        h = 0
+        for r in range(idx.shape[1]):
+            while r >= off[b, h + 1]:
+                h += 1
+            assert out[b, r].tobytes() == kb[b, h, idx[b, r]].tobytes()
+
+
 # ---------------------------------------------------------------- gather ----
 
 def test_compact_rows_are_byte_identical():
