@@ -164,3 +164,29 @@ def test_full_c3_layer0_64k_sampled_heads():
 def test_full_c4_qwen_128k_sampled_heads():
     """S = 131072, 40 query heads (G = 5, G*W = 320): heads 0 and 5 checked."""
     _run_and_check(synth.config(4), 4, heads=[0, 5])
+
+
+def test_scores_do_not_depend_on_key_blocking():
+    """TideKV Section 4.2: the block size only trades work for memory; the
+    result is the same.  One KV head scored alone (few, short key chunks) and
+    the same head inside a batch of 8 heads (different chunking and grid)
+    give scores within 1e-6 relative, and identical selections."""
+    kvsel = _kvsel()
+    spec = synth.config(2)
+    x = synth.make_layer(spec, 2, want_v=False)
+    q, k = dev_tensor(x["q"], "bf16"), dev_tensor(x["k"], "bf16")
+    p_all, s_all = kvsel.score(q, k, pool_kernel=7)
+    G = spec.group
+    for hk in (0, 5):
+        q1 = q[:, hk * G:(hk + 1) * G].contiguous()
+        k1 = k[:, hk:hk + 1].contiguous()
+        p1, s1 = kvsel.score(q1, k1, pool_kernel=7)
+        torch.cuda.synchronize()
+        rel = ((s1[:, 0] - s_all[:, hk]).abs() / s_all[:, hk].abs()).max().item()
+        assert rel <= 1e-6, rel
+        i1 = kvsel.select(p1, spec.budget, obs_window=spec.obs_window, n_q_heads=G, head_dim=128)
+        ia = kvsel.select(p_all, spec.budget, obs_window=spec.obs_window, n_q_heads=spec.n_q_heads,
+                          head_dim=128)
+        s_ref = p_all[:, hk:hk + 1].double().cpu().numpy()
+        check_selection(i1.cpu().numpy(), s_ref, spec.budget, 0, spec.obs_window)
+        check_selection(ia[:, hk:hk + 1].cpu().numpy(), s_ref, spec.budget, 0, spec.obs_window)
