@@ -80,6 +80,12 @@ def lib() -> ctypes.CDLL:
     L.kvsel_select.restype = ctypes.c_int
     L.kvsel_compact.argtypes = [DP, P, P, P, I32, P, P, P]
     L.kvsel_compact.restype = ctypes.c_int
+    L.kvsel_select_adaptive_workspace.argtypes = [DP, I32]
+    L.kvsel_select_adaptive_workspace.restype = SZ
+    L.kvsel_select_adaptive.argtypes = [DP, P, I32, P, P, P, SZ, P]
+    L.kvsel_select_adaptive.restype = ctypes.c_int
+    L.kvsel_compact_flat.argtypes = [DP, P, P, P, P, I32, P, P, P]
+    L.kvsel_compact_flat.restype = ctypes.c_int
     L.kvsel_route_tiers_workspace.argtypes = [TP]
     L.kvsel_route_tiers_workspace.restype = SZ
     L.kvsel_route_tiers.argtypes = [TP, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P]
@@ -204,6 +210,52 @@ def compact(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, *,
     return k_out, v_out
 
 
+def select_adaptive_workspace_bytes(desc: Desc, total_budget: int) -> int:
+    return int(lib().kvsel_select_adaptive_workspace(ctypes.byref(desc), int(total_budget)))
+
+
+def select_adaptive(pooled: torch.Tensor, total_budget: int, *, obs_window: int,
+                    n_q_heads: int, head_dim: int, n_sink: int = 0, causal: bool = True,
+                    idx: Optional[torch.Tensor] = None, head_off: Optional[torch.Tensor] = None,
+                    dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_select_adaptive: returns (idx [Bt, Hkv*(n_sink+W)+total_budget] int32,
+    head_off [Bt, Hkv+1] int32)."""
+    Bt, Hkv, S = pooled.shape
+    d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
+                dtype=dtype)
+    n_keep = Hkv * (n_sink + obs_window) + total_budget
+    if idx is None:
+        idx = torch.empty((Bt, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
+    if head_off is None:
+        head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=pooled.device)
+    nbytes = select_adaptive_workspace_bytes(d, total_budget)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=pooled.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    st = lib().kvsel_select_adaptive(ctypes.byref(d), _ptr(pooled), int(total_budget), _ptr(idx),
+                                     _ptr(head_off), ws_ptr, ws_n, _stream(stream))
+    _check(st, "kvsel_select_adaptive")
+    return idx, head_off
+
+
+def compact_flat(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor,
+                 head_off: torch.Tensor, *, k_out: Optional[torch.Tensor] = None,
+                 v_out: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_compact_flat: returns (k_hat, v_hat) [Bt, n_keep, D]."""
+    Bt, Hkv, S, D = k.shape
+    n_keep = idx.shape[-1]
+    d = Desc(Bt, Hkv, Hkv, D, S, 1, 0, 1, _dtype_code(k), 0.0)
+    if k_out is None:
+        k_out = torch.empty((Bt, n_keep, D), dtype=k.dtype, device=k.device)
+    if v is not None and v_out is None:
+        v_out = torch.empty((Bt, n_keep, D), dtype=v.dtype, device=v.device)
+    st = lib().kvsel_compact_flat(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(idx), _ptr(head_off),
+                                  int(n_keep), _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check(st, "kvsel_compact_flat")
+    return k_out, v_out
+
+
 def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
                        pool_kernel: int, n_sink: int = 0, causal: bool = True,
                        scale: float = 0.0, stream=None) -> dict:
@@ -215,6 +267,20 @@ def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                  n_sink=n_sink, causal=causal, dtype=k.dtype, stream=stream)
     k_hat, v_hat = compact(k, v, idx, stream=stream)
     return {"s": raw, "p": pooled, "idx": idx, "k_hat": k_hat, "v_hat": v_hat}
+
+
+def layer_end_compress_adaptive(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                                total_budget: int, pool_kernel: int, n_sink: int = 0,
+                                causal: bool = True, scale: float = 0.0, stream=None) -> dict:
+    """score -> head-adaptive select -> flattened compact on one stream."""
+    W = q_obs.shape[2]
+    pooled, raw = score(q_obs, k, pool_kernel=pool_kernel, n_sink=n_sink, causal=causal,
+                        scale=scale, stream=stream)
+    idx, off = select_adaptive(pooled, total_budget, obs_window=W, n_q_heads=q_obs.shape[1],
+                               head_dim=k.shape[3], n_sink=n_sink, causal=causal, dtype=k.dtype,
+                               stream=stream)
+    k_hat, v_hat = compact_flat(k, v, idx, off, stream=stream)
+    return {"s": raw, "p": pooled, "idx": idx, "head_off": off, "k_hat": k_hat, "v_hat": v_hat}
 
 
 @dataclass
@@ -268,4 +334,5 @@ def route_tiers(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, n_ful
 
 
 EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_select_workspace",
-           "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers")
+           "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers",
+           "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat")

@@ -46,6 +46,17 @@ kvsel_status check_tier_desc(const kvsel_tier_desc* d) {
   return KVSEL_OK;
 }
 
+// Head-adaptive selection: the sequence-wide pick count must be feasible,
+// and a sequence's flattened keys h*S + position must fit in 31 bits.
+kvsel_status check_adaptive(const kvsel_desc* d, int32_t total_budget) {
+  const kvsel_status st = check_desc(d);
+  if (st != KVSEL_OK) return st;
+  const int64_t ncand = (int64_t)d->seq_len - d->obs_window - d->n_sink;
+  if ((int64_t)d->n_kv_heads * d->seq_len >= ((int64_t)1 << 31)) return KVSEL_ERR_UNSUPPORTED;
+  if (total_budget < 0 || total_budget > (int64_t)d->n_kv_heads * ncand) return KVSEL_ERR_BUDGET;
+  return KVSEL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,7 +102,7 @@ size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget) {
   if (check_desc(desc) != KVSEL_OK) return 0;
   if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink) return 0;
   SelectPlan p;
-  plan_select(*desc, budget, &p);
+  plan_select(*desc, budget, 1, &p);
   return p.total;
 }
 
@@ -103,10 +114,31 @@ kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t b
     return KVSEL_ERR_BUDGET;
   if (!pooled || !idx || !aligned16(pooled) || !aligned16(idx)) return KVSEL_ERR_ARG;
   SelectPlan p;
-  plan_select(*desc, budget, &p);
+  plan_select(*desc, budget, 1, &p);
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
-  return launch_select(*desc, p, pooled, budget, idx, (char*)ws, (hipStream_t)stream);
+  return launch_select(*desc, p, pooled, budget, idx, nullptr, (char*)ws, (hipStream_t)stream);
+}
+
+size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget) {
+  if (check_adaptive(desc, total_budget) != KVSEL_OK) return 0;
+  SelectPlan p;
+  if (!plan_select(*desc, (int)total_budget, desc->n_kv_heads, &p)) return 0;
+  return p.total;
+}
+
+kvsel_status kvsel_select_adaptive(const kvsel_desc* desc, const float* pooled,
+                                   int32_t total_budget, int32_t* idx, int32_t* head_off,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_adaptive(desc, total_budget);
+  if (st != KVSEL_OK) return st;
+  if (!pooled || !idx || !head_off || !aligned16(pooled) || !aligned16(idx)) return KVSEL_ERR_ARG;
+  SelectPlan p;
+  if (!plan_select(*desc, (int)total_budget, desc->n_kv_heads, &p)) return KVSEL_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVSEL_ERR_ARG;
+  return launch_select(*desc, p, pooled, (int)total_budget, idx, head_off, (char*)ws,
+                       (hipStream_t)stream);
 }
 
 kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
@@ -121,6 +153,21 @@ kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
       !aligned16(v_out))
     return KVSEL_ERR_ARG;
   return launch_compact(*desc, k, v, idx, n_keep, k_out, v_out, (hipStream_t)stream);
+}
+
+kvsel_status kvsel_compact_flat(const kvsel_desc* desc, const void* k, const void* v,
+                                const int32_t* idx, const int32_t* head_off, int32_t n_keep,
+                                void* k_out, void* v_out, void* stream) {
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (n_keep < 0 || n_keep > (int64_t)desc->n_kv_heads * desc->seq_len) return KVSEL_ERR_ARG;
+  if (!k || !k_out || (n_keep > 0 && (!idx || !head_off))) return KVSEL_ERR_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVSEL_ERR_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(k_out) ||
+      !aligned16(v_out))
+    return KVSEL_ERR_ARG;
+  return launch_compact_flat(*desc, k, v, idx, head_off, (int)n_keep, k_out, v_out,
+                             (hipStream_t)stream);
 }
 
 size_t kvsel_route_tiers_workspace(const kvsel_tier_desc* desc) {

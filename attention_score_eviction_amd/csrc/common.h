@@ -51,17 +51,27 @@ struct ScoreArgs {
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
                           hipStream_t stream);
+// Selection groups: hg consecutive KV heads of a sequence share one budget
+// (hg = 1: per-head budget; hg = n_kv_heads: head-adaptive budget).
+constexpr int kMaxGroupSlices = 2048;
 struct SelectPlan {
-  bool multi;     // sliced multi-workgroup kernels (long rows)
-  int ns;         // slices per row
+  bool multi;     // sliced multi-workgroup kernels (long rows, head groups)
+  int hg;         // KV heads per selection group
+  int groups;     // batch * n_kv_heads / hg
+  int ns;         // slices per KV-head row
   size_t off_hist, off_gtc, off_candc, off_offs, off_params, off_cval, off_cidx, total;
 };
-bool plan_select(const kvsel_desc& d, int budget, SelectPlan* p);
+// False when a head group needs more than kMaxGroupSlices slices.
+bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p);
 kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
-                           int budget, int32_t* idx, char* ws, hipStream_t stream);
+                           int budget, int32_t* idx, int32_t* head_off, char* ws,
+                           hipStream_t stream);
 kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
                             const int32_t* idx, int n_keep, void* k_out, void* v_out,
                             hipStream_t stream);
+kvsel_status launch_compact_flat(const kvsel_desc& d, const void* k, const void* v,
+                                 const int32_t* idx, const int32_t* head_off, int n_keep,
+                                 void* k_out, void* v_out, hipStream_t stream);
 
 struct TierPlan {
   int nheads, nwin;

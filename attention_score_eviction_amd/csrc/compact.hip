@@ -37,6 +37,52 @@ __global__ void __launch_bounds__(256) compact_kernel(const u32x4_t* __restrict_
   }
 }
 
+// Flattened head-adaptive cache (TideKV Section 4.1): one row list per
+// sequence, head h owning rows [head_off[h], head_off[h+1]).  The first 64
+// threads resolve each row's head (binary search over the offsets) and
+// source row into LDS; then all threads move the rows as 16-byte vectors.
+__global__ void __launch_bounds__(256) compact_flat_kernel(const u32x4_t* __restrict__ k,
+                                                           const u32x4_t* __restrict__ v,
+                                                           const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ head_off,
+                                                           u32x4_t* __restrict__ ko,
+                                                           u32x4_t* __restrict__ vo, int S,
+                                                           int hkv, int n_keep, int vpr) {
+  __shared__ long long src_row[kRowsPerBlock];
+  const int b = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  if (threadIdx.x < kRowsPerBlock) {
+    const int r = r0 + threadIdx.x;
+    long long sr = -1;
+    if (r < n_keep) {
+      const int32_t* off = head_off + (size_t)b * (hkv + 1);
+      int lo = 0, hi = hkv - 1;   // last head whose first row is <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      const int src = idx[(size_t)b * n_keep + r];
+      if (src >= 0 && src < S) sr = ((long long)b * hkv + lo) * S + src;
+    }
+    src_row[threadIdx.x] = sr;
+  }
+  __syncthreads();
+  const size_t dst_base = (size_t)b * n_keep;
+  for (int t = threadIdx.x; t < kRowsPerBlock * vpr; t += 256) {
+    const int rr = t / vpr;
+    const int c = t - rr * vpr;
+    if (r0 + rr >= n_keep) break;
+    const long long sr = src_row[rr];
+    const bool ok = sr >= 0;
+    const size_t so = (size_t)(ok ? sr : 0) * vpr + c;
+    const size_t dsto = (dst_base + r0 + rr) * vpr + c;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    ko[dsto] = ok ? k[so] : zero;
+    if (v) vo[dsto] = ok ? v[so] : zero;
+  }
+}
+
 }  // namespace
 
 kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
@@ -49,6 +95,19 @@ kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
   hipLaunchKernelGGL(compact_kernel, dim3((n_keep + kRowsPerBlock - 1) / kRowsPerBlock, nheads),
                      dim3(256), 0, stream, (const u32x4_t*)k, (const u32x4_t*)v, idx,
                      (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, n_keep, vpr);
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+kvsel_status launch_compact_flat(const kvsel_desc& d, const void* k, const void* v,
+                                 const int32_t* idx, const int32_t* head_off, int n_keep,
+                                 void* k_out, void* v_out, hipStream_t stream) {
+  if (n_keep == 0) return KVSEL_OK;
+  const int e = d.dtype == KVSEL_F32 ? 4 : 2;
+  const int vpr = d.head_dim * e / 16;
+  hipLaunchKernelGGL(compact_flat_kernel,
+                     dim3((n_keep + kRowsPerBlock - 1) / kRowsPerBlock, d.batch), dim3(256), 0,
+                     stream, (const u32x4_t*)k, (const u32x4_t*)v, idx, head_off,
+                     (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, d.n_kv_heads, n_keep, vpr);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 

@@ -231,20 +231,29 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Multi-workgroup select for long rows.  A row's candidate range is cut into
-// slices of kSlice scores (256 threads x 16).  The kernels run in order:
-//   sel_init     zero the row's first-digit histogram, write the mandatory set
+// Multi-workgroup select for long rows and for head-adaptive selection.
+// A selection group is `hg` consecutive KV-head rows of one sequence (hg = 1:
+// one row, the per-head budget of Eq. (8); hg = Hkv: the sequence-wide budget
+// of TideKV Section 4.1's head-adaptive variant).  Each row's candidate range
+// is cut into ns slices of kSlice scores (256 threads x 16); the group's
+// slices are numbered head-major.  The kernels run in order:
+//   sel_init     zero the group's first-digit histogram
 //   sel_hist     per slice: 11-bit first-digit histogram -> global (atomics)
 //   sel_cand     per slice: first digit d1 of the budget-th score; count the
 //                scores above d1's bin and compact the ones inside it
-//   sel_resolve  per row: the remaining 21 bits over the compacted scores,
-//                the tie cut (by position), and each slice's output offset
+//   sel_resolve  per group: the remaining 21 bits over the compacted scores,
+//                the tie cut (by head, then position), each slice's output
+//                offset, the per-head offsets and the mandatory rows
 //   sel_emit     per slice: ordered write of the kept positions
 // The digits have 11, 11 and 10 bits (the first: sign, exponent and two
 // mantissa bits, a quarter octave per bin).
 // The rule every kernel applies in the end is one predicate per score:
-// kept <=> key > prefix || (key == prefix && position <= cut), with
-// key = bits & pmask.
+// kept <=> key > prefix || (key == prefix && h*S + position <= cut), with
+// key = bits & pmask and h the head's index inside its group.
+//
+// Output of a group: head h's rows start at h*(n_sink+W) + (picks of heads
+// before h); they are its sinks, its picks in ascending position order and its
+// observation window.  With hg = 1 this is the [sinks | picks | window] row.
 // ---------------------------------------------------------------------------
 constexpr int kSliceThreads = 256;
 constexpr int kSlice = kSliceThreads * kPerThread;
@@ -252,16 +261,29 @@ constexpr int kD1Bits = 11, kD1Bins = 1 << kD1Bits, kD1Shift = 32 - kD1Bits;
 
 struct SelArgs {
   const float* pooled;
-  int32_t* idx;
-  uint32_t* hist1;     // [rows][kD1Bins]
-  uint32_t* gtc;       // [rows][ns] scores above the first-digit bin
-  uint32_t* candc;     // [rows][ns] scores inside it
-  uint32_t* offs;      // [rows][ns] output offset of each slice
-  uint32_t* params;    // [rows][4] prefix, pmask, cut
-  uint32_t* cval;      // [rows][ns][kSlice] compacted score bits
-  int32_t* cidx;       // [rows][ns][kSlice] their positions
-  int S, lo, hi, budget, n_sink, W, n_keep, ns;
+  int32_t* idx;        // [groups][n_keep]
+  int32_t* head_off;   // [groups][hg+1] or null
+  uint32_t* hist1;     // [groups][kD1Bins]
+  uint32_t* gtc;       // [groups][nst] scores above the first-digit bin
+  uint32_t* candc;     // [groups][nst] scores inside it
+  uint32_t* offs;      // [groups][nst] output offset (among picks) of each slice
+  uint32_t* params;    // [groups][4] prefix, pmask, cut
+  uint32_t* cval;      // [groups][nst][kSlice] compacted score bits
+  int32_t* cidx;       // [groups][nst][kSlice] their keys h*S + position
+  int S, lo, hi, budget, n_sink, W, n_keep, ns, hg, nst;
 };
+
+// Slice sg of group grp: its KV-head row and its slice number inside the row.
+struct SliceAt {
+  int h, row, sl;
+};
+__device__ __forceinline__ SliceAt slice_at(const SelArgs& a, int grp, int sg) {
+  SliceAt r;
+  r.h = sg / a.ns;
+  r.sl = sg - r.h * a.ns;
+  r.row = grp * a.hg + r.h;
+  return r;
+}
 
 __device__ __forceinline__ int slice_base(const SelArgs& a, int row) {
   const int ofs = (int)(((size_t)row * a.S) & 3u);
@@ -269,27 +291,25 @@ __device__ __forceinline__ int slice_base(const SelArgs& a, int row) {
 }
 
 __global__ void __launch_bounds__(256) sel_init(SelArgs a) {
-  const int row = blockIdx.x, tid = threadIdx.x;
-  uint32_t* h = a.hist1 + (size_t)row * kD1Bins;
+  const int grp = blockIdx.x, tid = threadIdx.x;
+  uint32_t* h = a.hist1 + (size_t)grp * kD1Bins;
   for (int i = tid; i < kD1Bins; i += 256) h[i] = 0u;
-  int32_t* out = a.idx + (size_t)row * a.n_keep;
-  for (int i = tid; i < a.n_sink; i += 256) out[i] = i;
-  for (int j = tid; j < a.W; j += 256) out[a.n_sink + a.budget + j] = a.S - a.W + j;
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
   __shared__ uint32_t hist[kD1Bins];
-  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int grp = blockIdx.y, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, blockIdx.x);
   for (int i = tid; i < kD1Bins; i += kSliceThreads) hist[i] = 0u;
   __syncthreads();
-  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
-  const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) hist_add(hist, x[e] >> kD1Shift, (valid >> e) & 1u);
   __syncthreads();
-  uint32_t* g = a.hist1 + (size_t)row * kD1Bins;
+  uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
   for (int i = tid; i < kD1Bins; i += kSliceThreads)
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
@@ -298,14 +318,16 @@ __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
   __shared__ uint32_t hist[kD1Bins];
   __shared__ uint32_t wsum[kSliceThreads / 64];
   __shared__ uint32_t pick[3];
-  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  const uint32_t* g = a.hist1 + (size_t)row * kD1Bins;
+  const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, sg);
+  const uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
   for (int i = tid; i < kD1Bins; i += kSliceThreads) hist[i] = g[i];
   __syncthreads();
   find_digit<kSliceThreads, kD1Bins>(hist, kD1Bins, (uint32_t)a.budget, wsum, pick);
   const uint32_t d1 = pick[0];
-  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
-  const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
+  const int key0 = at.h * a.S + i0;
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
   uint32_t gt = 0u, in = 0u;
@@ -317,18 +339,18 @@ __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
   }
   uint32_t tot;
   uint32_t pos = block_exclusive_scan<kSliceThreads>((gt << 16) | __popc(in), &tot, wsum) & 0xffffu;
-  const size_t cbase = ((size_t)row * a.ns + sl) * kSlice;
+  const size_t cbase = ((size_t)grp * a.nst + sg) * kSlice;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if ((in >> e) & 1u) {
       a.cval[cbase + pos] = x[e];
-      a.cidx[cbase + pos] = i0 + e;
+      a.cidx[cbase + pos] = key0 + e;
       ++pos;
     }
   }
   if (tid == 0) {
-    a.gtc[(size_t)row * a.ns + sl] = tot >> 16;
-    a.candc[(size_t)row * a.ns + sl] = tot & 0xffffu;
+    a.gtc[(size_t)grp * a.nst + sg] = tot >> 16;
+    a.candc[(size_t)grp * a.nst + sg] = tot & 0xffffu;
   }
 }
 
@@ -350,19 +372,19 @@ __device__ __forceinline__ int slice_of(const uint32_t* cstart, int ns, uint32_t
 
 __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   __shared__ uint32_t hist[kD1Bins];
-  __shared__ uint32_t selc[2048];
-  __shared__ uint32_t cstart[2048];
+  __shared__ uint32_t selc[kMaxGroupSlices];
+  __shared__ uint32_t cstart[kMaxGroupSlices];
   __shared__ uint32_t lval[kCandCap];
   __shared__ int32_t lidx[kCandCap];
   __shared__ uint32_t wsum[kSelThreads / 64];
   __shared__ uint32_t pick[3];
   __shared__ uint32_t cut_s;
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int ns = a.ns;
-  const uint32_t* g = a.hist1 + (size_t)row * kD1Bins;
-  const uint32_t* cc = a.candc + (size_t)row * ns;
+  const int grp = blockIdx.x, tid = threadIdx.x;
+  const int ns = a.nst;   // slices of the whole group
+  const uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
+  const uint32_t* cc = a.candc + (size_t)grp * ns;
   for (int i = tid; i < kD1Bins; i += kSelThreads) hist[i] = g[i];
-  for (int i = tid; i < 2048; i += kSelThreads) selc[i] = 0u;
+  for (int i = tid; i < kMaxGroupSlices; i += kSelThreads) selc[i] = 0u;
   if (tid == 0) cut_s = 0x7fffffffu;
   // Flat numbering of the compacted scores (slice order = position order).
   uint32_t c0 = 0u, c1 = 0u;
@@ -378,8 +400,8 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   uint32_t prefix = pick[0] << kD1Shift, pmask = (uint32_t)(kD1Bins - 1) << kD1Shift;
   bool whole = rem == pick[2];
   __syncthreads();
-  const uint32_t* cv = a.cval + (size_t)row * ns * kSlice;
-  const int32_t* ci = a.cidx + (size_t)row * ns * kSlice;
+  const uint32_t* cv = a.cval + (size_t)grp * ns * kSlice;
+  const int32_t* ci = a.cidx + (size_t)grp * ns * kSlice;
   const bool in_lds = ncand <= (uint32_t)kCandCap;
   // Gather the compacted scores into LDS with independent loads.
   if (!whole && in_lds) {
@@ -423,8 +445,8 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
     whole = rem == pick[2];
     __syncthreads();
   }
-  // Tie cut: position of the rem-th score equal to the prefix.  Each thread
-  // takes a contiguous run of candidates, so one scan orders them.
+  // Tie cut: key (h*S + position) of the rem-th score equal to the prefix.
+  // Each thread takes a contiguous run of candidates, so one scan orders them.
   if (!whole) {
     const uint32_t per = (ncand + kSelThreads - 1) / kSelThreads;
     const uint32_t k0 = tid * per, k1 = min(ncand, k0 + per);
@@ -473,32 +495,58 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   }
   __syncthreads();
   // Exclusive prefix over slices of (above-bin + kept-inside-bin) counts.
-  const uint32_t* gt = a.gtc + (size_t)row * ns;
+  const uint32_t* gt = a.gtc + (size_t)grp * ns;
   uint32_t k0c = 0u, k1c = 0u;
   const int s0 = 2 * tid, s1 = 2 * tid + 1;
   if (s0 < ns) k0c = gt[s0] + selc[s0];
   if (s1 < ns) k1c = gt[s1] + selc[s1];
   uint32_t tot;
   const uint32_t exo = block_exclusive_scan<kSelThreads>(k0c + k1c, &tot, wsum);
-  uint32_t* of = a.offs + (size_t)row * ns;
+  uint32_t* of = a.offs + (size_t)grp * ns;
   if (s0 < ns) of[s0] = exo;
   if (s1 < ns) of[s1] = exo + k0c;
+  // Slice offsets also kept in LDS (cstart is free again) for the head offsets.
+  if (s0 < ns) cstart[s0] = exo;
+  if (s1 < ns) cstart[s1] = exo + k0c;
   if (tid == 0) {
-    uint32_t* pr = a.params + (size_t)row * 4;
+    uint32_t* pr = a.params + (size_t)grp * 4;
     pr[0] = prefix;
     pr[1] = pmask;
     pr[2] = cut;
+  }
+  __syncthreads();
+  // Head h's picks occupy [cstart[h*ns_row], next head's start) among the
+  // group's picks; its rows start after the mandatory rows of earlier heads.
+  const int seg = a.n_sink + a.W;
+  auto picks_before = [&](int h) -> uint32_t {
+    return h < a.hg ? min(cstart[h * a.ns], (uint32_t)a.budget) : (uint32_t)a.budget;
+  };
+  if (a.head_off)
+    for (int h = tid; h <= a.hg; h += kSelThreads)
+      a.head_off[(size_t)grp * (a.hg + 1) + h] = (int32_t)(h * seg + picks_before(h));
+  int32_t* out = a.idx + (size_t)grp * a.n_keep;
+  for (int t = tid; t < a.hg * seg; t += kSelThreads) {
+    const int h = t / seg, j = t - h * seg;
+    const uint32_t start = h * seg + picks_before(h);
+    if (j < a.n_sink) {
+      out[start + j] = j;
+    } else {
+      const int w = j - a.n_sink;
+      out[start + a.n_sink + (picks_before(h + 1) - picks_before(h)) + w] = a.S - a.W + w;
+    }
   }
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
   __shared__ uint32_t wsum[kSliceThreads / 64];
-  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  const uint32_t* pr = a.params + (size_t)row * 4;
+  const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, sg);
+  const uint32_t* pr = a.params + (size_t)grp * 4;
   const uint32_t prefix = pr[0], pmask = pr[1], cut = pr[2];
-  const uint32_t base_out = a.offs[(size_t)row * a.ns + sl];
-  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)row * a.S;
-  const int i0 = slice_base(a, row) + sl * kSlice + tid * kPerThread;
+  const uint32_t base_out = a.offs[(size_t)grp * a.nst + sg];
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
+  const uint32_t key0 = (uint32_t)(at.h * a.S + i0);
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
   uint32_t keep = 0u;
@@ -506,12 +554,12 @@ __global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
   for (int e = 0; e < kPerThread; ++e) {
     const uint32_t key = x[e] & pmask;
     const bool k = ((valid >> e) & 1u) &&
-                   (key > prefix || (key == prefix && (uint32_t)(i0 + e) <= cut));
+                   (key > prefix || (key == prefix && key0 + e <= cut));
     keep |= (uint32_t)k << e;
   }
   uint32_t tot;
   uint32_t pos = base_out + block_exclusive_scan<kSliceThreads>(__popc(keep), &tot, wsum);
-  int32_t* out = a.idx + (size_t)row * a.n_keep + a.n_sink;
+  int32_t* out = a.idx + (size_t)grp * a.n_keep + at.h * (a.n_sink + a.W) + a.n_sink;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     if ((keep >> e) & 1u) {
@@ -522,18 +570,43 @@ __global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
   }
 }
 
+// Budget 0: each head of a group keeps its sinks and its observation window,
+// and head h's rows start at h*(n_sink+W).
+__global__ void __launch_bounds__(256) mandatory_only_kernel(int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ head_off,
+                                                             int S, int n_sink, int W, int hg) {
+  const int grp = blockIdx.x, tid = threadIdx.x;
+  const int seg = n_sink + W;
+  int32_t* out = idx + (size_t)grp * hg * seg;
+  for (int t = tid; t < hg * seg; t += 256) {
+    const int j = t % seg;
+    out[t] = j < n_sink ? j : S - W + (j - n_sink);
+  }
+  if (head_off)
+    for (int h = tid; h <= hg; h += 256) head_off[(size_t)grp * (hg + 1) + h] = h * seg;
+}
+
 }  // namespace
 
-bool plan_select(const kvsel_desc& d, int budget, SelectPlan* p) {
-  const int rows = d.batch * d.n_kv_heads;
+bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p) {
+  const int groups = d.batch * d.n_kv_heads / hg;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
   const long ncand = (long)hi - lo;
-  // Short rows: one workgroup per row in one launch.  Long rows: the sliced
-  // multi-workgroup kernels (the slice count includes the alignment lead-in).
-  // (sel_resolve keeps per-slice counters for at most 2048 slices.)
+  // Per-head short rows: one workgroup per row in one launch.  Long rows and
+  // head groups: the sliced multi-workgroup kernels (the slice count includes
+  // the alignment lead-in; sel_resolve keeps per-slice counters for at most
+  // kMaxGroupSlices slices of a group).
   const long ns = (ncand + 3 + kSlice - 1) / kSlice;
-  p->multi = budget > 0 && ncand > kBatch && ns <= 2048;
+  p->hg = hg;
+  p->groups = groups;
+  if (hg == 1) {
+    p->multi = budget > 0 && ncand > kBatch && ns <= kMaxGroupSlices;
+  } else {
+    if (ns * hg > kMaxGroupSlices) return false;
+    p->multi = budget > 0;
+  }
   p->ns = p->multi ? (int)ns : 0;
+  const size_t nst = (size_t)p->ns * hg;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -541,31 +614,40 @@ bool plan_select(const kvsel_desc& d, int budget, SelectPlan* p) {
     return o;
   };
   if (p->multi) {
-    p->off_hist = take((size_t)rows * kD1Bins * 4);
-    p->off_gtc = take((size_t)rows * p->ns * 4);
-    p->off_candc = take((size_t)rows * p->ns * 4);
-    p->off_offs = take((size_t)rows * p->ns * 4);
-    p->off_params = take((size_t)rows * 4 * 4);
-    p->off_cval = take((size_t)rows * p->ns * kSlice * 4);
-    p->off_cidx = take((size_t)rows * p->ns * kSlice * 4);
+    p->off_hist = take((size_t)groups * kD1Bins * 4);
+    p->off_gtc = take((size_t)groups * nst * 4);
+    p->off_candc = take((size_t)groups * nst * 4);
+    p->off_offs = take((size_t)groups * nst * 4);
+    p->off_params = take((size_t)groups * 4 * 4);
+    p->off_cval = take((size_t)groups * nst * kSlice * 4);
+    p->off_cidx = take((size_t)groups * nst * kSlice * 4);
   }
   p->total = off;
   return true;
 }
 
 kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
-                           int budget, int32_t* idx, char* ws, hipStream_t stream) {
-  const int rows = d.batch * d.n_kv_heads;
-  const int n_keep = budget + d.n_sink + d.obs_window;
+                           int budget, int32_t* idx, int32_t* head_off, char* ws,
+                           hipStream_t stream) {
+  const int hg = p.hg, groups = p.groups;
+  const int seg = d.n_sink + d.obs_window;
+  const int n_keep = hg * seg + budget;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
-  if (!p.multi) {
-    hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, pooled, idx,
+  if (!p.multi && hg == 1) {
+    hipLaunchKernelGGL(select_kernel, dim3(groups), dim3(kSelThreads), 0, stream, pooled, idx,
                        d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
+    return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+  }
+  if (!p.multi) {
+    // Nothing to pick: every head keeps exactly its mandatory rows.
+    hipLaunchKernelGGL(mandatory_only_kernel, dim3(groups), dim3(256), 0, stream, idx, head_off,
+                       d.seq_len, d.n_sink, d.obs_window, hg);
     return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   }
   SelArgs a;
   a.pooled = pooled;
   a.idx = idx;
+  a.head_off = head_off;
   a.hist1 = (uint32_t*)(ws + p.off_hist);
   a.gtc = (uint32_t*)(ws + p.off_gtc);
   a.candc = (uint32_t*)(ws + p.off_candc);
@@ -581,11 +663,13 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   a.W = d.obs_window;
   a.n_keep = n_keep;
   a.ns = p.ns;
-  const dim3 sg(p.ns, rows);
-  hipLaunchKernelGGL(sel_init, dim3(rows), dim3(256), 0, stream, a);
+  a.hg = hg;
+  a.nst = p.ns * hg;
+  const dim3 sg(a.nst, groups);
+  hipLaunchKernelGGL(sel_init, dim3(groups), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_resolve, dim3(rows), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_resolve, dim3(groups), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }

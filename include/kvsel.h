@@ -152,6 +152,59 @@ kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t b
 /* (kvsel_select: ws is device scratch of >= kvsel_select_workspace(desc,
  * budget) bytes, may be NULL when that is 0; else KVSEL_ERR_WORKSPACE.) */
 
+/* Bytes of scratch kvsel_select_adaptive needs (0 when total_budget is 0 or
+ * the arguments are invalid): about 8 bytes per candidate position of every
+ * KV head plus per-slice counters. */
+size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget);
+
+/*
+ * kvsel_select_adaptive -- head-adaptive retained sets in a flattened layout
+ * with per-head offsets (TideKV Section 4.1: a head-adaptive budget gives a
+ * variable-length cache, flattened, with per-head offsets; Eq. (8) applied to
+ * all KV heads of a sequence at once).
+ *
+ * For each sequence b the candidates are the pairs (hk, i), i in
+ * [n_sink, S-W), over all Hkv heads; the total_budget largest pooled scores
+ * are picked, ordered by (score descending, head ascending, position
+ * ascending).  There is no per-head floor beyond the mandatory set: every
+ * head keeps its sinks [0, n_sink) and its window [S-W, S).
+ *
+ *   pooled    [Bt,Hkv,S] float32, device; candidates finite and >= 0
+ *   total_budget  0 <= total_budget <= Hkv*(S-W-n_sink), else
+ *             KVSEL_ERR_BUDGET (callers counting the mandatory rows inside
+ *             a per-sequence budget pass that budget minus Hkv*(n_sink+W))
+ *   idx       [Bt, n_keep] int32 out, n_keep = Hkv*(n_sink+W) + total_budget:
+ *             head hk's positions, ascending, in rows
+ *             [head_off[b,hk], head_off[b,hk+1])
+ *   head_off  [Bt, Hkv+1] int32 out; head_off[b,0] = 0, head_off[b,Hkv] = n_keep
+ *   ws        device scratch of >= kvsel_select_adaptive_workspace bytes
+ * Needs Hkv*S < 2^31 and at most 2048 slices of 4096 candidates per
+ * sequence (KVSEL_ERR_UNSUPPORTED otherwise).  Selection is exact as in
+ * kvsel_select.
+ */
+kvsel_status kvsel_select_adaptive(const kvsel_desc* desc, const float* pooled,
+                                   int32_t total_budget, int32_t* idx, int32_t* head_off,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_compact_flat -- GATHER into the flattened per-head-offset layout:
+ * for head_off[b,hk] <= r < head_off[b,hk+1],
+ * k_out[b,r,:] = k[b,hk,idx[b,r],:], and the same for v, byte for byte.
+ *
+ *   k, v         [Bt,Hkv,S,D] dtype, device
+ *   idx          [Bt,n_keep] int32, head_off [Bt,Hkv+1] int32, device (as
+ *                written by kvsel_select_adaptive)
+ *   n_keep       0 <= n_keep <= Hkv*S
+ *   k_out, v_out [Bt,n_keep,D] dtype, device
+ * A row whose index is outside [0, S) is written as zeros; a row below
+ * head_off[b,0] or at/after head_off[b,Hkv] is taken from the first or the
+ * last head, so malformed offsets never read out of bounds.  v may be NULL
+ * together with v_out.
+ */
+kvsel_status kvsel_compact_flat(const kvsel_desc* desc, const void* k, const void* v,
+                                const int32_t* idx, const int32_t* head_off, int32_t n_keep,
+                                void* k_out, void* v_out, void* stream);
+
 /*
  * kvsel_compact -- GATHER of Algorithm 2: k_out[b,hk,r,:] = k[b,hk,idx[b,hk,r],:]
  * and the same for v, byte for byte.  The position metadata of the compact

@@ -68,6 +68,56 @@ def check_selection(idx_gpu: np.ndarray, p_ref: np.ndarray, budget: int, n_sink:
         assert not extra, f"row {r}: clearly-dropped positions kept: {extra[:10]}"
 
 
+def check_adaptive_selection(idx_g: np.ndarray, off_g: np.ndarray, p_ref: np.ndarray,
+                             total: int, n_sink: int, W: int, band: float = 1e-4):
+    """Head-adaptive selection in the flattened layout: per-head segments are
+    ascending, hold their head's mandatory set, and the picks over all heads
+    of a sequence equal the oracle's except at candidates whose oracle score
+    lies within `band` (relative) of the sequence's total-th score."""
+    Bt, H, S = p_ref.shape
+    lo, hi = n_sink, S - W
+    n_keep = H * (n_sink + W) + total
+    assert idx_g.shape == (Bt, n_keep) and off_g.shape == (Bt, H + 1)
+    for b in range(Bt):
+        off = off_g[b].astype(np.int64)
+        assert off[0] == 0 and off[H] == n_keep and (np.diff(off) >= n_sink + W).all()
+        picked = np.zeros((H, S), bool)
+        for h in range(H):
+            g = idx_g[b, off[h]:off[h + 1]].astype(np.int64)
+            assert (np.diff(g) > 0).all(), f"seq {b} head {h}: not ascending"
+            assert g[:n_sink].tolist() == list(range(n_sink))
+            assert g[g.size - W:].tolist() == list(range(hi, S))
+            picks = g[n_sink:g.size - W]
+            assert ((picks >= lo) & (picks < hi)).all()
+            picked[h, picks] = True
+        assert picked.sum() == total
+        if total == 0:
+            continue
+        cand = p_ref[b, :, lo:hi]
+        kth = np.sort(cand.reshape(-1))[::-1][total - 1]
+        sure_in = cand > kth * (1 + band)
+        sure_out = cand < kth * (1 - band)
+        got = picked[:, lo:hi]
+        assert not (sure_in & ~got).any(), f"seq {b}: clearly-kept candidates missing"
+        assert not (sure_out & got).any(), f"seq {b}: clearly-dropped candidates kept"
+
+
+def rows_gathered(out_bits: np.ndarray, src_bits: np.ndarray, idx: np.ndarray,
+                  head_off: np.ndarray = None) -> bool:
+    """Every output row is the source row its index names, byte for byte
+    (per-head layout [Bt,Hkv,n,D], or flattened [Bt,n,D] with head offsets)."""
+    if head_off is None:
+        want = np.take_along_axis(src_bits, idx.astype(np.int64)[..., None], axis=2)
+        return out_bits.tobytes() == want.tobytes()
+    H = src_bits.shape[1]
+    for b in range(idx.shape[0]):
+        for h in range(H):
+            r0, r1 = int(head_off[b, h]), int(head_off[b, h + 1])
+            if out_bits[b, r0:r1].tobytes() != src_bits[b, h, idx[b, r0:r1]].tobytes():
+                return False
+    return True
+
+
 def layer_inputs(spec: synth.LayerSpec, config_id: int, layer: int = 0, want_v: bool = True):
     x = synth.make_layer(spec, config_id, layer, want_v=want_v)
     return x

@@ -108,6 +108,40 @@ def test_select_budget_checks(kv):
         == kv.ERR_WORKSPACE
 
 
+def test_select_adaptive_checks(kv):
+    L = kv.lib()
+    d = _desc(kv, seq_len=1000, obs_window=40, n_sink=4)
+    sel = lambda T, p=FAKE, i=FAKE, o=FAKE, ws=FAKE, n=1 << 30: L.kvsel_select_adaptive(  # noqa
+        ctypes.byref(d), p, T, i, o, ws, n, None)
+    ncand = 1000 - 40 - 4
+    assert sel(-1) == kv.ERR_BUDGET
+    assert sel(8 * ncand + 1) == kv.ERR_BUDGET
+    assert sel(10, p=None) == kv.ERR_ARG
+    assert sel(10, o=None) == kv.ERR_ARG
+    assert sel(10, i=FAKE + 4) == kv.ERR_ARG
+    need = L.kvsel_select_adaptive_workspace(ctypes.byref(d), 10)
+    assert need >= 8 * ncand * 8
+    assert sel(10, n=need - 1) == kv.ERR_WORKSPACE
+    assert L.kvsel_select_adaptive_workspace(ctypes.byref(d), 0) == 0
+    # more than 2048 slices of 4096 candidates in one sequence
+    big = _desc(kv, seq_len=1 << 21, obs_window=64)
+    assert L.kvsel_select_adaptive_workspace(ctypes.byref(big), 100) == 0
+    assert L.kvsel_select_adaptive(ctypes.byref(big), FAKE, 100, FAKE, FAKE, FAKE, 1 << 40,
+                                   None) == kv.ERR_UNSUPPORTED
+
+
+def test_compact_flat_checks(kv):
+    L = kv.lib()
+    d = _desc(kv, seq_len=100)
+    c = lambda n, i=FAKE, o=FAKE, v=FAKE, vo=FAKE: L.kvsel_compact_flat(  # noqa
+        ctypes.byref(d), FAKE, v, i, o, n, FAKE, vo, None)
+    assert c(-1) == kv.ERR_ARG
+    assert c(8 * 100 + 1) == kv.ERR_ARG
+    assert c(10, o=None) == kv.ERR_ARG
+    assert c(10, i=None) == kv.ERR_ARG
+    assert c(10, vo=None) == kv.ERR_ARG
+
+
 def test_compact_checks(kv):
     L = kv.lib()
     d = _desc(kv)

@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_scores_close, check_selection, dev_tensor, host_bits
+from helpers import (assert_scores_close, check_adaptive_selection, check_selection, dev_tensor,
+                     host_bits, rows_gathered)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -72,11 +73,9 @@ def _run_and_check(spec, cid, heads=None):
         assert_scores_close(p_g[:, hk:hk + 1], p_ref, what=f"pooled scores head {hk}")
         np.testing.assert_allclose(s_g[:, hk].astype(np.float64).sum(-1), G * W, rtol=1e-5)
         check_selection(idx_g[:, hk:hk + 1], p_ref, spec.budget, spec.n_sink, W)
-    # compaction of the GPU's own indices is byte-exact
-    k_ref = oracle.compact_rows(x["k"], idx_g)
-    v_ref = oracle.compact_rows(x["v"], idx_g)
-    assert host_bits(out["k_hat"]).tobytes() == k_ref.tobytes()
-    assert host_bits(out["v_hat"]).tobytes() == v_ref.tobytes()
+    # every gathered row is, byte for byte, the source row its index names
+    assert rows_gathered(host_bits(out["k_hat"]), x["k"], idx_g)
+    assert rows_gathered(host_bits(out["v_hat"]), x["v"], idx_g)
     return out
 
 
@@ -190,3 +189,102 @@ def test_scores_do_not_depend_on_key_blocking():
         s_ref = p_all[:, hk:hk + 1].double().cpu().numpy()
         check_selection(i1.cpu().numpy(), s_ref, spec.budget, 0, spec.obs_window)
         check_selection(ia[:, hk:hk + 1].cpu().numpy(), s_ref, spec.budget, 0, spec.obs_window)
+
+
+# ----------------------------------------------- head-adaptive selection ----
+
+def _tie_heavy_scores(rng, kind, shape):
+    if kind == "uniform":
+        return rng.random(shape).astype(np.float32)
+    if kind == "quarters":
+        return rng.integers(0, 5, size=shape).astype(np.float32) * np.float32(0.25)
+    if kind == "band":
+        return (np.float32(1.0) + rng.integers(0, 3000, size=shape).astype(np.float32)
+                * np.float32(2.0 ** -20)).astype(np.float32)
+    p = np.full(shape, 0.125, np.float32)       # plateau with sparse spikes
+    p[..., ::97] = 3.0
+    p[..., 5::11] = 0.0
+    return p
+
+
+@pytest.mark.parametrize("seed,Bt,Hkv,S,W,n_sink,kind", [
+    (0, 2, 8, 1000, 40, 0, "uniform"),
+    (1, 1, 8, 8192, 32, 4, "quarters"),
+    (2, 2, 3, 9777, 64, 1, "plateau"),
+    (3, 1, 8, 20000, 64, 0, "band"),
+    (4, 3, 2, 5, 2, 1, "uniform"),
+    (5, 1, 8, 131072, 64, 4, "uniform"),
+])
+def test_select_adaptive_exact_on_identical_inputs(seed, Bt, Hkv, S, W, n_sink, kind):
+    """Given the same fp32 scores, the head-adaptive picks and per-head
+    offsets are bit-exact with the oracle's (ties -> lower head, then lower
+    position), from one pick to every candidate of the sequence."""
+    kvsel = _kvsel()
+    rng = np.random.default_rng(200 + seed)
+    p = _tie_heavy_scores(rng, kind, (Bt, Hkv, S))
+    if kind == "uniform" and Hkv > 1:
+        p[:, 1] *= np.float32(3.0)          # one head dominates the budget
+    p[..., :n_sink] = 0
+    p[..., S - W:] = 0
+    ncand = S - W - n_sink
+    print(f"case adaptive seed {seed} Bt={Bt} Hkv={Hkv} S={S} kind={kind}", flush=True)
+    pt = torch.from_numpy(p).cuda()
+    for T in sorted({min(t, Hkv * ncand) for t in (0, 1, 7, 1000, Hkv * 1024, Hkv * ncand)}):
+        idx, off = kvsel.select_adaptive(pt, T, obs_window=W, n_q_heads=Hkv, head_dim=128,
+                                         n_sink=n_sink)
+        torch.cuda.synchronize()
+        want_idx, want_off = oracle.select_head_adaptive(p.astype(np.float64), T, n_sink, W)
+        np.testing.assert_array_equal(off.cpu().numpy(), want_off)
+        np.testing.assert_array_equal(idx.cpu().numpy(), want_idx)
+
+
+def test_compact_flat_exact_with_oracle_selection():
+    kvsel = _kvsel()
+    rng = np.random.default_rng(7)
+    Bt, Hkv, S, D, W = 2, 4, 900, 64, 16
+    kb = rng.integers(0, 65536, size=(Bt, Hkv, S, D), dtype=np.uint16)
+    vb = rng.integers(0, 65536, size=(Bt, Hkv, S, D), dtype=np.uint16)
+    p = rng.random((Bt, Hkv, S))
+    p[:, 2] *= 4.0
+    idx, off = oracle.select_head_adaptive(p, 777, 2, W)
+    kh, vh = kvsel.compact_flat(dev_tensor(kb, "bf16"), dev_tensor(vb, "bf16"),
+                                torch.from_numpy(idx).cuda(), torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    assert host_bits(kh).tobytes() == oracle.compact_flat(kb, idx, off).tobytes()
+    assert host_bits(vh).tobytes() == oracle.compact_flat(vb, idx, off).tobytes()
+    # an index outside [0, S) gives a zero row
+    bad = idx.copy()
+    bad[0, 5] = -3
+    bad[1, 40] = S
+    kh2, _ = kvsel.compact_flat(dev_tensor(kb, "bf16"), None, torch.from_numpy(bad).cuda(),
+                                torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    got = host_bits(kh2)
+    assert not got[0, 5].any() and not got[1, 40].any()
+    want = oracle.compact_flat(kb, idx, off)
+    want[0, 5] = 0
+    want[1, 40] = 0
+    assert got.tobytes() == want.tobytes()
+
+
+@pytest.mark.parametrize("cid,heads_for_scores", [(2, None), (1, None)])
+def test_adaptive_layer_end_against_oracle(cid, heads_for_scores):
+    """Score -> head-adaptive select (sequence budget Hkv*B) -> flattened
+    compact, against the oracle's scores and head-adaptive selection."""
+    kvsel = _kvsel()
+    spec = synth.config(cid)
+    x = synth.make_layer(spec, cid)
+    q, k, v = (dev_tensor(x[n], spec.dtype) for n in ("q", "k", "v"))
+    T = spec.n_kv_heads * spec.budget
+    print(f"case adaptive layer-end config {cid} T={T}", flush=True)
+    out = kvsel.layer_end_compress_adaptive(q, k, v, total_budget=T,
+                                            pool_kernel=spec.pool_kernel, n_sink=spec.n_sink)
+    torch.cuda.synchronize()
+    S, W = spec.seq_len, spec.obs_window
+    s_ref = oracle.head_scores(synth.to_f64(x["q"], spec.dtype), synth.to_f64(x["k"], spec.dtype))
+    p_ref = oracle.max_pool(s_ref, spec.pool_kernel, spec.n_sink, S - W)
+    assert_scores_close(out["p"].cpu().numpy(), p_ref, what="pooled scores")
+    idx_g, off_g = out["idx"].cpu().numpy(), out["head_off"].cpu().numpy()
+    check_adaptive_selection(idx_g, off_g, p_ref, T, spec.n_sink, W)
+    assert rows_gathered(host_bits(out["k_hat"]), x["k"], idx_g, off_g)
+    assert rows_gathered(host_bits(out["v_hat"]), x["v"], idx_g, off_g)
