@@ -237,16 +237,20 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
 // of TideKV Section 4.1's head-adaptive variant).  Each row's candidate range
 // is cut into ns slices of kSlice scores (256 threads x 16); the group's
 // slices are numbered head-major.  The kernels run in order:
-//   sel_init     zero the group's first-digit histogram
-//   sel_hist     per slice: 11-bit first-digit histogram -> global (atomics)
-//   sel_cand     per slice: first digit d1 of the budget-th score; count the
-//                scores above d1's bin and compact the ones inside it
-//   sel_resolve  per group: the remaining 21 bits over the compacted scores,
-//                the tie cut (by head, then position), each slice's output
+//   sel_init     zero the group's two digit histograms
+//   sel_hist     per slice: first-digit (top 11 bits) histogram -> global
+//   sel_hist2    per slice: first digit d1 of the budget-th score; histogram
+//                of the second digit (next 11 bits) of the scores in d1's bin
+//   sel_cand     per slice: the 22-bit prefix of the budget-th score; count
+//                the scores above it and compact the ones that share it
+//   sel_resolve  per group: the last 10 bits over the compacted scores, the
+//                tie cut (by head, then position), each slice's output
 //                offset, the per-head offsets and the mandatory rows
 //   sel_emit     per slice: ordered write of the kept positions
-// The digits have 11, 11 and 10 bits (the first: sign, exponent and two
-// mantissa bits, a quarter octave per bin).
+// Both wide digits are settled by every slice in parallel, so the single
+// resolve workgroup only sees scores equal to the budget-th one in their top
+// 22 bits (a handful, unless values repeat).  A digit whose boundary bin is
+// kept whole ends the search early.
 // The rule every kernel applies in the end is one predicate per score:
 // kept <=> key > prefix || (key == prefix && h*S + position <= cut), with
 // key = bits & pmask and h the head's index inside its group.
@@ -258,14 +262,17 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
 constexpr int kSliceThreads = 256;
 constexpr int kSlice = kSliceThreads * kPerThread;
 constexpr int kD1Bits = 11, kD1Bins = 1 << kD1Bits, kD1Shift = 32 - kD1Bits;
+constexpr int kD2Bits = 11, kD2Bins = 1 << kD2Bits, kD2Shift = kD1Shift - kD2Bits;
+constexpr int kD3Bins = 1 << kD2Shift;
 
 struct SelArgs {
   const float* pooled;
   int32_t* idx;        // [groups][n_keep]
   int32_t* head_off;   // [groups][hg+1] or null
   uint32_t* hist1;     // [groups][kD1Bins]
-  uint32_t* gtc;       // [groups][nst] scores above the first-digit bin
-  uint32_t* candc;     // [groups][nst] scores inside it
+  uint32_t* hist2;     // [groups][kD2Bins]
+  uint32_t* gtc;       // [groups][nst] scores kept outright (above the prefix)
+  uint32_t* candc;     // [groups][nst] scores sharing the prefix (compacted)
   uint32_t* offs;      // [groups][nst] output offset (among picks) of each slice
   uint32_t* params;    // [groups][4] prefix, pmask, cut
   uint32_t* cval;      // [groups][nst][kSlice] compacted score bits
@@ -290,10 +297,44 @@ __device__ __forceinline__ int slice_base(const SelArgs& a, int row) {
   return a.lo - ((a.lo + ofs) & 3);
 }
 
+// The digits settled from the global histograms: prefix / pmask of the
+// budget-th score over the first one or two digits, the rank still to place
+// inside that prefix, and whether every score sharing it is kept.
+struct Prefix {
+  uint32_t prefix, pmask, rem;
+  bool whole;
+};
+
+// hist1 / hist2 are LDS copies; hist2 is read only when the first digit's
+// bin is not kept whole.  Every thread of the block must call.
+template <int NT>
+__device__ __forceinline__ Prefix settle_prefix(const uint32_t* hist1, const uint32_t* hist2,
+                                                uint32_t budget, uint32_t* wsum,
+                                                uint32_t* pick) {
+  Prefix p;
+  find_digit<NT, kD1Bins>(hist1, kD1Bins, budget, wsum, pick);
+  p.rem = budget - pick[1];
+  p.prefix = pick[0] << kD1Shift;
+  p.pmask = (uint32_t)(kD1Bins - 1) << kD1Shift;
+  p.whole = p.rem == pick[2];
+  __syncthreads();
+  if (!p.whole) {
+    find_digit<NT, kD2Bins>(hist2, kD2Bins, p.rem, wsum, pick);
+    p.rem -= pick[1];
+    p.prefix |= pick[0] << kD2Shift;
+    p.pmask |= (uint32_t)(kD2Bins - 1) << kD2Shift;
+    p.whole = p.rem == pick[2];
+    __syncthreads();
+  }
+  return p;
+}
+
 __global__ void __launch_bounds__(256) sel_init(SelArgs a) {
   const int grp = blockIdx.x, tid = threadIdx.x;
-  uint32_t* h = a.hist1 + (size_t)grp * kD1Bins;
-  for (int i = tid; i < kD1Bins; i += 256) h[i] = 0u;
+  uint32_t* h1 = a.hist1 + (size_t)grp * kD1Bins;
+  uint32_t* h2 = a.hist2 + (size_t)grp * kD2Bins;
+  for (int i = tid; i < kD1Bins; i += 256) h1[i] = 0u;
+  for (int i = tid; i < kD2Bins; i += 256) h2[i] = 0u;
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
@@ -314,17 +355,47 @@ __global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
+__global__ void __launch_bounds__(kSliceThreads) sel_hist2(SelArgs a) {
+  __shared__ uint32_t h1[kD1Bins];
+  __shared__ uint32_t hist[kD2Bins];
+  __shared__ uint32_t wsum[kSliceThreads / 64];
+  __shared__ uint32_t pick[3];
+  const int grp = blockIdx.y, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, blockIdx.x);
+  const uint32_t* g1 = a.hist1 + (size_t)grp * kD1Bins;
+  for (int i = tid; i < kD1Bins; i += kSliceThreads) h1[i] = g1[i];
+  for (int i = tid; i < kD2Bins; i += kSliceThreads) hist[i] = 0u;
+  __syncthreads();
+  find_digit<kSliceThreads, kD1Bins>(h1, kD1Bins, (uint32_t)a.budget, wsum, pick);
+  const uint32_t d1 = pick[0];
+  if ((uint32_t)a.budget - pick[1] == pick[2]) return;   // d1's bin kept whole
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    hist_add(hist, (x[e] >> kD2Shift) & (uint32_t)(kD2Bins - 1),
+             ((valid >> e) & 1u) && (x[e] >> kD1Shift) == d1);
+  __syncthreads();
+  uint32_t* g2 = a.hist2 + (size_t)grp * kD2Bins;
+  for (int i = tid; i < kD2Bins; i += kSliceThreads)
+    if (hist[i]) atomicAdd(&g2[i], hist[i]);
+}
+
 __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
-  __shared__ uint32_t hist[kD1Bins];
+  __shared__ uint32_t h1[kD1Bins];
+  __shared__ uint32_t h2[kD2Bins];
   __shared__ uint32_t wsum[kSliceThreads / 64];
   __shared__ uint32_t pick[3];
   const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
   const SliceAt at = slice_at(a, grp, sg);
-  const uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
-  for (int i = tid; i < kD1Bins; i += kSliceThreads) hist[i] = g[i];
+  const uint32_t* g1 = a.hist1 + (size_t)grp * kD1Bins;
+  const uint32_t* g2 = a.hist2 + (size_t)grp * kD2Bins;
+  for (int i = tid; i < kD1Bins; i += kSliceThreads) h1[i] = g1[i];
+  for (int i = tid; i < kD2Bins; i += kSliceThreads) h2[i] = g2[i];
   __syncthreads();
-  find_digit<kSliceThreads, kD1Bins>(hist, kD1Bins, (uint32_t)a.budget, wsum, pick);
-  const uint32_t d1 = pick[0];
+  const Prefix pf = settle_prefix<kSliceThreads>(h1, h2, (uint32_t)a.budget, wsum, pick);
   const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
   const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
   const int key0 = at.h * a.S + i0;
@@ -334,8 +405,9 @@ __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const bool ok = (valid >> e) & 1u;
-    gt += ok && (x[e] >> kD1Shift) > d1;
-    in |= (uint32_t)(ok && (x[e] >> kD1Shift) == d1) << e;
+    const uint32_t key = x[e] & pf.pmask;
+    gt += ok && (key > pf.prefix || (pf.whole && key == pf.prefix));
+    in |= (uint32_t)(ok && !pf.whole && key == pf.prefix) << e;
   }
   uint32_t tot;
   uint32_t pos = block_exclusive_scan<kSliceThreads>((gt << 16) | __popc(in), &tot, wsum) & 0xffffu;
@@ -371,7 +443,8 @@ __device__ __forceinline__ int slice_of(const uint32_t* cstart, int ns, uint32_t
 }
 
 __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
-  __shared__ uint32_t hist[kD1Bins];
+  __shared__ uint32_t h1[kD1Bins];
+  __shared__ uint32_t h2[kD2Bins];
   __shared__ uint32_t selc[kMaxGroupSlices];
   __shared__ uint32_t cstart[kMaxGroupSlices];
   __shared__ uint32_t lval[kCandCap];
@@ -381,12 +454,14 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   __shared__ uint32_t cut_s;
   const int grp = blockIdx.x, tid = threadIdx.x;
   const int ns = a.nst;   // slices of the whole group
-  const uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
+  const uint32_t* g1 = a.hist1 + (size_t)grp * kD1Bins;
+  const uint32_t* g2 = a.hist2 + (size_t)grp * kD2Bins;
   const uint32_t* cc = a.candc + (size_t)grp * ns;
-  for (int i = tid; i < kD1Bins; i += kSelThreads) hist[i] = g[i];
+  for (int i = tid; i < kD1Bins; i += kSelThreads) h1[i] = g1[i];
+  for (int i = tid; i < kD2Bins; i += kSelThreads) h2[i] = g2[i];
   for (int i = tid; i < kMaxGroupSlices; i += kSelThreads) selc[i] = 0u;
   if (tid == 0) cut_s = 0x7fffffffu;
-  // Flat numbering of the compacted scores (slice order = position order).
+  // Flat numbering of the compacted scores (slice order = key order).
   uint32_t c0 = 0u, c1 = 0u;
   if (2 * tid < ns) c0 = cc[2 * tid];
   if (2 * tid + 1 < ns) c1 = cc[2 * tid + 1];
@@ -395,106 +470,98 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   if (2 * tid < ns) cstart[2 * tid] = ex;
   if (2 * tid + 1 < ns) cstart[2 * tid + 1] = ex + c0;
   __syncthreads();
-  find_digit<kSelThreads, kD1Bins>(hist, kD1Bins, (uint32_t)a.budget, wsum, pick);
-  uint32_t rem = (uint32_t)a.budget - pick[1];
-  uint32_t prefix = pick[0] << kD1Shift, pmask = (uint32_t)(kD1Bins - 1) << kD1Shift;
-  bool whole = rem == pick[2];
-  __syncthreads();
+  Prefix pf = settle_prefix<kSelThreads>(h1, h2, (uint32_t)a.budget, wsum, pick);
+  uint32_t prefix = pf.prefix, pmask = pf.pmask, rem = pf.rem;
   const uint32_t* cv = a.cval + (size_t)grp * ns * kSlice;
   const int32_t* ci = a.cidx + (size_t)grp * ns * kSlice;
   const bool in_lds = ncand <= (uint32_t)kCandCap;
-  // Gather the compacted scores into LDS with independent loads.
-  if (!whole && in_lds) {
-    for (uint32_t k = tid; k < ncand; k += kSelThreads) {
-      const int sl = slice_of(cstart, ns, k);
-      const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
-      lval[k] = cv[at];
-      lidx[k] = ci[at];
-    }
-    __syncthreads();
-  }
-  auto cand = [&](uint32_t k, uint32_t& v, int32_t& i) {
+  if (!pf.whole) {
+    // Gather the compacted scores into LDS with independent loads.
     if (in_lds) {
-      v = lval[k];
-      i = lidx[k];
-    } else {
-      const int sl = slice_of(cstart, ns, k);
-      const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
-      v = cv[at];
-      i = ci[at];
+      for (uint32_t k = tid; k < ncand; k += kSelThreads) {
+        const int sl = slice_of(cstart, ns, k);
+        const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
+        lval[k] = cv[at];
+        lidx[k] = ci[at];
+      }
+      __syncthreads();
     }
-  };
-  // Lower digits over the compacted scores (all share the first digit).
-  for (int r = 1; r < 3 && !whole; ++r) {
-    const int shift = r == 1 ? 10 : 0;
-    const int nb = r == 1 ? 2048 : 1024;
-    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0u;
+    auto cand = [&](uint32_t k, uint32_t& v, int32_t& i) {
+      if (in_lds) {
+        v = lval[k];
+        i = lidx[k];
+      } else {
+        const int sl = slice_of(cstart, ns, k);
+        const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
+        v = cv[at];
+        i = ci[at];
+      }
+    };
+    // Last digit (10 bits) over the compacted scores, which all share the
+    // 22-bit prefix.  The histogram reuses h1.
+    for (int i = tid; i < kD3Bins; i += kSelThreads) h1[i] = 0u;
     __syncthreads();
     for (uint32_t k0 = 0; k0 < ncand; k0 += kSelThreads) {
       const uint32_t k = k0 + tid;
       uint32_t x = 0u;
-      int32_t pos;
-      if (k < ncand) cand(k, x, pos);
-      hist_add(hist, (x >> shift) & (uint32_t)(nb - 1), k < ncand && (x & pmask) == prefix);
+      int32_t key;
+      if (k < ncand) cand(k, x, key);
+      hist_add(h1, x & (uint32_t)(kD3Bins - 1), k < ncand);
     }
     __syncthreads();
-    find_digit<kSelThreads>(hist, nb, rem, wsum, pick);
+    find_digit<kSelThreads>(h1, kD3Bins, rem, wsum, pick);
     rem -= pick[1];
-    prefix |= pick[0] << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    whole = rem == pick[2];
+    prefix |= pick[0];
+    pmask = 0xffffffffu;
+    const bool whole3 = rem == pick[2];
     __syncthreads();
-  }
-  // Tie cut: key (h*S + position) of the rem-th score equal to the prefix.
-  // Each thread takes a contiguous run of candidates, so one scan orders them.
-  if (!whole) {
-    const uint32_t per = (ncand + kSelThreads - 1) / kSelThreads;
-    const uint32_t k0 = tid * per, k1 = min(ncand, k0 + per);
-    uint32_t neq = 0u;
-    for (uint32_t k = k0; k < k1; ++k) {
-      uint32_t x;
-      int32_t pos;
-      cand(k, x, pos);
-      neq += (x & pmask) == prefix;
-    }
-    uint32_t tot;
-    uint32_t seen = block_exclusive_scan<kSelThreads>(neq, &tot, wsum);
-    if (seen < rem && rem <= seen + neq) {
+    // Tie cut: key (h*S + position) of the rem-th score equal to the prefix.
+    // Each thread takes a contiguous run of candidates, so one scan orders
+    // them.
+    if (!whole3) {
+      const uint32_t per = (ncand + kSelThreads - 1) / kSelThreads;
+      const uint32_t k0 = tid * per, k1 = min(ncand, k0 + per);
+      uint32_t neq = 0u;
       for (uint32_t k = k0; k < k1; ++k) {
         uint32_t x;
-        int32_t pos;
-        cand(k, x, pos);
-        if ((x & pmask) == prefix && ++seen == rem) {
-          cut_s = (uint32_t)pos;
-          break;
+        int32_t key;
+        cand(k, x, key);
+        neq += x == prefix;
+      }
+      uint32_t tot;
+      uint32_t seen = block_exclusive_scan<kSelThreads>(neq, &tot, wsum);
+      if (seen < rem && rem <= seen + neq) {
+        for (uint32_t k = k0; k < k1; ++k) {
+          uint32_t x;
+          int32_t key;
+          cand(k, x, key);
+          if (x == prefix && ++seen == rem) {
+            cut_s = (uint32_t)key;
+            break;
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  const uint32_t cut = cut_s;
-  // Kept compacted scores per slice.  When the first digit's bin is kept
-  // whole every compacted score is kept; otherwise apply the predicate.
-  if (pmask == (uint32_t)(kD1Bins - 1) << kD1Shift) {
-    for (int sl = tid; sl < ns; sl += kSelThreads) selc[sl] = cc[sl];
-  } else {
+    const uint32_t cut = cut_s;
+    // Kept compacted scores per slice.
     for (uint32_t k0 = 0; k0 < ncand; k0 += kSelThreads) {
       const uint32_t k = k0 + tid;
       bool keep = false;
       int sl = 0;
       if (k < ncand) {
         uint32_t x;
-        int32_t pos;
-        cand(k, x, pos);
-        const uint32_t key = x & pmask;
-        keep = key > prefix || (key == prefix && (uint32_t)pos <= cut);
+        int32_t key;
+        cand(k, x, key);
+        keep = x > prefix || (x == prefix && (uint32_t)key <= cut);
         sl = slice_of(cstart, ns, k);
       }
       hist_add(selc, (uint32_t)sl, keep);
     }
   }
   __syncthreads();
-  // Exclusive prefix over slices of (above-bin + kept-inside-bin) counts.
+  const uint32_t cut = cut_s;
+  // Exclusive prefix over slices of (kept outright + kept compacted) counts.
   const uint32_t* gt = a.gtc + (size_t)grp * ns;
   uint32_t k0c = 0u, k1c = 0u;
   const int s0 = 2 * tid, s1 = 2 * tid + 1;
@@ -614,7 +681,7 @@ bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p) {
     return o;
   };
   if (p->multi) {
-    p->off_hist = take((size_t)groups * kD1Bins * 4);
+    p->off_hist = take((size_t)groups * (kD1Bins + kD2Bins) * 4);
     p->off_gtc = take((size_t)groups * nst * 4);
     p->off_candc = take((size_t)groups * nst * 4);
     p->off_offs = take((size_t)groups * nst * 4);
@@ -649,6 +716,7 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   a.idx = idx;
   a.head_off = head_off;
   a.hist1 = (uint32_t*)(ws + p.off_hist);
+  a.hist2 = a.hist1 + (size_t)groups * kD1Bins;
   a.gtc = (uint32_t*)(ws + p.off_gtc);
   a.candc = (uint32_t*)(ws + p.off_candc);
   a.offs = (uint32_t*)(ws + p.off_offs);
@@ -668,6 +736,7 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   const dim3 sg(a.nst, groups);
   hipLaunchKernelGGL(sel_init, dim3(groups), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
+  hipLaunchKernelGGL(sel_hist2, sg, dim3(kSliceThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_resolve, dim3(groups), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_emit, sg, dim3(kSliceThreads), 0, stream, a);

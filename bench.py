@@ -15,6 +15,9 @@ Workloads (one JSON line each):
   qwen128k     one Qwen3-14B-shaped layer (40 q / 8 kv heads), 131072 tokens
   sweep64k     32 layers at 65536 tokens, budget 4096 -> 512, one layer resident
   qevict32k    16 x 32768-token caches, 256 decode queries, window tiers
+  llama8k-adaptive / qwen128k-adaptive
+               the same layers with a head-adaptive budget: Hkv*B picks per
+               sequence over all KV heads, flattened output with head offsets
 """
 from __future__ import annotations
 
@@ -41,6 +44,8 @@ WORKLOADS = {
     "qwen128k": (4, "qwen3-14b-layer-128k"),
     "sweep64k": (3, "llama3-8b-32-layer-sweep-64k"),
     "qevict32k": (5, "qevict-decode-tiers-16x32k"),
+    "llama8k-adaptive": (2, "llama3-8b-layer-8k-head-adaptive"),
+    "qwen128k-adaptive": (4, "qwen3-14b-layer-128k-head-adaptive"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "common.h"]
@@ -85,7 +90,8 @@ def tier_bytes(spec: synth.LayerSpec, n_full: int, n_quant: int, n_prom: int, wi
     return read + write
 
 
-def cpu_baseline(spec: synth.LayerSpec, x: dict, budget_s: float = 12.0) -> dict:
+def cpu_baseline(spec: synth.LayerSpec, x: dict, budget_s: float = 12.0,
+                 adaptive: bool = False) -> dict:
     """The oracle, as it stands, timed on this host on the same layer."""
     import oracle
     try:
@@ -96,11 +102,20 @@ def cpu_baseline(spec: synth.LayerSpec, x: dict, budget_s: float = 12.0) -> dict
     q64 = synth.to_f64(x["q"], spec.dtype)
     k64 = synth.to_f64(x["k"], spec.dtype)
     reps, t0 = 0, time.perf_counter()
+    S, W = spec.seq_len, spec.obs_window
     while True:
-        oracle.layer_end_compress(q64, k64, x["v"], budget=spec.budget,
-                                  window=spec.obs_window, pool_kernel=spec.pool_kernel,
-                                  n_sink=spec.n_sink, causal=bool(spec.causal),
-                                  k_store=x["k"], v_store=x["v"])
+        if adaptive:
+            s = oracle.head_scores(q64, k64, causal=bool(spec.causal))
+            p = oracle.max_pool(s, spec.pool_kernel, spec.n_sink, S - W)
+            idx, off = oracle.select_head_adaptive(p, spec.n_kv_heads * spec.budget,
+                                                   spec.n_sink, W)
+            oracle.compact_flat(x["k"], idx, off)
+            oracle.compact_flat(x["v"], idx, off)
+        else:
+            oracle.layer_end_compress(q64, k64, x["v"], budget=spec.budget,
+                                      window=W, pool_kernel=spec.pool_kernel,
+                                      n_sink=spec.n_sink, causal=bool(spec.causal),
+                                      k_store=x["k"], v_store=x["v"])
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
@@ -138,8 +153,9 @@ def event_time_us(torch, stream, fn, reps: int) -> float:
 class Layer:
     """Device buffers of one resident layer and its preallocated outputs."""
 
-    def __init__(self, kvsel, torch, spec, x, dev):
+    def __init__(self, kvsel, torch, spec, x, dev, adaptive=False):
         self.kvsel, self.torch, self.spec = kvsel, torch, spec
+        self.adaptive = adaptive
         if spec.dtype == "bf16":
             up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
         else:
@@ -159,10 +175,17 @@ class Layer:
         dev = self.k.device
         self.budget = budget
         n_keep = budget + self.spec.n_sink + self.spec.obs_window
-        self.idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
-        self.sel_ws = torch.empty(max(kvsel.select_workspace_bytes(self.desc, budget), 1),
-                                  dtype=torch.uint8, device=dev)
-        self.k_hat = torch.empty((Bt, Hkv, n_keep, D), dtype=self.k.dtype, device=dev)
+        if self.adaptive:
+            # the same rows in total, chosen over all KV heads of a sequence
+            self.idx = torch.empty((Bt, Hkv * n_keep), dtype=torch.int32, device=dev)
+            self.head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=dev)
+            nb = kvsel.select_adaptive_workspace_bytes(self.desc, Hkv * budget)
+            self.k_hat = torch.empty((Bt, Hkv * n_keep, D), dtype=self.k.dtype, device=dev)
+        else:
+            self.idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
+            nb = kvsel.select_workspace_bytes(self.desc, budget)
+            self.k_hat = torch.empty((Bt, Hkv, n_keep, D), dtype=self.k.dtype, device=dev)
+        self.sel_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
         self.v_hat = torch.empty_like(self.k_hat)
 
     def load(self, x):
@@ -179,12 +202,23 @@ class Layer:
 
     def select(self, stream):
         s = self.spec
+        if self.adaptive:
+            self.kvsel.select_adaptive(
+                self.pooled, self.k.shape[1] * self.budget, obs_window=s.obs_window,
+                n_q_heads=s.n_q_heads, head_dim=self.k.shape[3], n_sink=s.n_sink,
+                causal=bool(s.causal), idx=self.idx, head_off=self.head_off, dtype=self.k.dtype,
+                workspace=self.sel_ws, stream=stream)
+            return
         self.kvsel.select(self.pooled, self.budget, obs_window=s.obs_window,
                           n_q_heads=s.n_q_heads, head_dim=self.k.shape[3], n_sink=s.n_sink,
                           causal=bool(s.causal), idx=self.idx, dtype=self.k.dtype,
                           workspace=self.sel_ws, stream=stream)
 
     def compact(self, stream):
+        if self.adaptive:
+            self.kvsel.compact_flat(self.k, self.v, self.idx, self.head_off, k_out=self.k_hat,
+                                    v_out=self.v_hat, stream=stream)
+            return
         self.kvsel.compact(self.k, self.v, self.idx, k_out=self.k_hat, v_out=self.v_hat,
                            stream=stream)
 
@@ -214,6 +248,9 @@ CALL_KERNELS = {
     "kvsel_select": ("select_kernel", "sel_init", "sel_hist", "sel_cand", "sel_resolve",
                      "sel_emit"),
     "kvsel_compact": ("compact_kernel",),
+    "kvsel_select_adaptive": ("sel_init", "sel_hist", "sel_cand", "sel_resolve", "sel_emit",
+                              "mandatory_only_kernel"),
+    "kvsel_compact_flat": ("compact_flat_kernel",),
     "kvsel_route_tiers": ("tier_rank_kernel", "tier_move_kernel", "tier_promote_kernel"),
 }
 
@@ -301,7 +338,8 @@ def main() -> int:
     if args.workload == "qevict32k":
         return bench_tiers(args, kvsel, torch, spec, wname, dev, stream)
     x = synth.make_layer(spec, cid)
-    L = Layer(kvsel, torch, spec, x, dev)
+    adaptive = args.workload.endswith("-adaptive")
+    L = Layer(kvsel, torch, spec, x, dev, adaptive=adaptive)
     if args.workload == "sweep64k":
         return bench_sweep(args, torch, spec, wname, L, stream)
 
@@ -319,10 +357,16 @@ def main() -> int:
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
     reps = max(args.steps, 50)
+    sel_name = "kvsel_select_adaptive" if adaptive else "kvsel_select"
+    cmp_name = "kvsel_compact_flat" if adaptive else "kvsel_compact"
     us = {"kvsel_score": event_time_us(torch, stream, lambda: L.score(stream), reps),
-          "kvsel_select": event_time_us(torch, stream, lambda: L.select(stream), reps),
-          "kvsel_compact": event_time_us(torch, stream, lambda: L.compact(stream), reps)}
+          sel_name: event_time_us(torch, stream, lambda: L.select(stream), reps),
+          cmp_name: event_time_us(torch, stream, lambda: L.compact(stream), reps)}
     ab = algorithmic_bytes(spec)
+    if adaptive:
+        ab[sel_name] = ab.pop("kvsel_select") + spec.batch * (spec.n_kv_heads + 1) * 4
+        ab[cmp_name] = ab.pop("kvsel_compact") + spec.batch * (spec.n_kv_heads + 1) * 4
+        ab["path"] = ab["kvsel_score"] + ab[sel_name] + ab[cmp_name]
     Bt, S = spec.batch, spec.seq_len
     value = Bt * S / (ms_step * 1e-3)
     path_gbs = ab["path"] / (ms_step * 1e-3) / 1e9
@@ -336,7 +380,8 @@ def main() -> int:
         "config": {"workload": wname, "batch": Bt, "seq_len": S, "n_q_heads": spec.n_q_heads,
                    "n_kv_heads": spec.n_kv_heads, "head_dim": spec.head_dim,
                    "obs_window": spec.obs_window, "pool_kernel": spec.pool_kernel,
-                   "budget": spec.budget, "parallelism": "none"},
+                   "budget": (f"{spec.n_kv_heads * spec.budget} per sequence over all KV heads"
+                              if adaptive else spec.budget), "parallelism": "none"},
         "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
         "path_algorithmic_bytes": ab["path"],
         "us_per_call": {k: round(v, 2) for k, v in us.items()},
@@ -347,7 +392,7 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": ab[dom]},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(spec, x)
+        out["cpu_baseline"] = cpu_baseline(spec, x, adaptive=adaptive)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -4,8 +4,9 @@ quantisation, promotion by dequantisation) with the CPU oracle.
 Routing: exact when window sums are exact in fp32 (integer-valued scores);
 otherwise identical except for windows whose oracle sum lies within 1e-4
 relative of a tier-boundary sum.  Payloads (full-tier rows, int4 codes,
-(lo, scale) metadata, promoted bf16 rows) are bit-exact against the oracle
-applied to the routing the GPU chose.
+(lo, scale) metadata, promoted bf16 rows) are bit-exact against the oracle's
+payloads for its own routing, window by window, for every window both sides
+put in the same tier (all of them when the routings agree).
 """
 import numpy as np
 import pytest
@@ -30,14 +31,53 @@ def _rand_bf16(rng, shape, scale=1.0):
     return synth.f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
-def _payload_check(out, kb, vb, tier, promote):
-    want = oracle.tier_outputs(kb, vb, tier, WIN, promote)
-    for name in ("k_full", "v_full", "k_codes", "v_codes", "k_prom", "v_prom"):
-        got = host_bits(getattr(out, name))
-        assert got.tobytes() == want[name].reshape(got.shape).tobytes(), name
-    for name in ("k_meta", "v_meta"):
-        got = getattr(out, name).cpu().numpy()
-        assert got.tobytes() == want[name].reshape(got.shape).tobytes(), name
+def _payload_check(got, want, tier_g, tier_ref, promote, min_agree=0.9):
+    """got / want: payload dicts (GPU outputs as numpy, oracle outputs for the
+    oracle's routing tier_ref) for the same [Bt, Hkv] rows.  Each window that
+    both routings put in the full or int4 tier must carry identical bytes in
+    its slot on each side; promoted slots are compared where both sides'
+    promoted window is the same."""
+    Bt, Hkv, nW = tier_ref.shape
+    D = got["k_full"].shape[-1] if got["k_full"].size else got["k_meta"].shape[-2]
+    per_win = {"k_full": (WIN, D), "v_full": (WIN, D), "k_codes": (WIN, D // 2),
+               "v_codes": (WIN, D // 2), "k_meta": (D, 2), "v_meta": (D, 2),
+               "k_prom": (WIN, D), "v_prom": (WIN, D)}
+    view = lambda a, name: a.reshape((Bt, Hkv, -1) + per_win[name])  # noqa
+    agree = 0
+    for b in range(Bt):
+        for h in range(Hkv):
+            agree += int((tier_g[b, h] == tier_ref[b, h]).sum())
+            for t, names in ((0, ("k_full", "v_full")),
+                             (1, ("k_codes", "v_codes", "k_meta", "v_meta"))):
+                wg = np.flatnonzero(tier_g[b, h] == t)
+                wr = np.flatnonzero(tier_ref[b, h] == t)
+                common = np.intersect1d(wg, wr)
+                sg, sr = np.searchsorted(wg, common), np.searchsorted(wr, common)
+                for name in names:
+                    g = view(got[name], name)[b, h][sg]
+                    w = view(want[name], name)[b, h][sr]
+                    assert g.tobytes() == w.tobytes(), f"{name} row ({b},{h})"
+            qg = np.flatnonzero(tier_g[b, h] == 1)
+            qr = np.flatnonzero(tier_ref[b, h] == 1)
+            for i, slot in enumerate(promote[b, h]):
+                if qg[slot] != qr[slot]:
+                    continue
+                for name in ("k_prom", "v_prom"):
+                    g = view(got[name], name)[b, h][i]
+                    w = view(want[name], name)[b, h][i]
+                    assert g.tobytes() == w.tobytes(), f"{name} row ({b},{h}) slot {i}"
+    assert agree >= min_agree * Bt * Hkv * nW
+
+
+def _gpu_payloads(out, rows=None):
+    res = {}
+    for name in ("k_full", "v_full", "k_codes", "v_codes", "k_prom", "v_prom", "k_meta",
+                 "v_meta"):
+        t = getattr(out, name)
+        if rows is not None:
+            t = t[rows]
+        res[name] = t.cpu().numpy() if name.endswith("meta") else host_bits(t)
+    return res
 
 
 def _check_routing_band(tier_g, rank_g, w_ref, n_full, n_quant, band=1e-4):
@@ -84,7 +124,8 @@ def test_route_tiers_exact_on_integer_scores(D):
     tier, rank = oracle.route_tiers(w, n_full, n_quant)
     np.testing.assert_array_equal(out.tier.cpu().numpy(), tier)
     np.testing.assert_array_equal(out.rank.cpu().numpy(), rank)
-    _payload_check(out, kb, vb, tier, promote)
+    want = oracle.tier_outputs(kb, vb, tier, WIN, promote)
+    _payload_check(_gpu_payloads(out), want, tier, tier, promote, min_agree=1.0)
 
 
 def test_route_tiers_float_scores_and_edges():
@@ -105,8 +146,10 @@ def test_route_tiers_float_scores_and_edges():
         tier_g = out.tier.cpu().numpy()
         w = oracle.window_sums(scores.astype(np.float64), WIN)
         _check_routing_band(tier_g, out.rank.cpu().numpy(), w, n_full, n_quant)
-        _payload_check(out, kb, vb, tier_g, promote if promote is not None
-                       else np.zeros((Bt, Hkv, 0), np.int32))
+        prom = promote if promote is not None else np.zeros((Bt, Hkv, 0), np.int32)
+        tier_ref, _ = oracle.route_tiers(w, n_full, n_quant)
+        want = oracle.tier_outputs(kb, vb, tier_ref, WIN, prom)
+        _payload_check(_gpu_payloads(out), want, tier_g, tier_ref, prom)
 
 
 def test_full_c5_decode_tiers_sampled_rows():
@@ -137,11 +180,8 @@ def test_full_c5_decode_tiers_sampled_rows():
         tier_g = out.tier[b:b + 1, h:h + 1].cpu().numpy()
         _check_routing_band(tier_g, out.rank[b:b + 1, h:h + 1].cpu().numpy(), w_ref, n_full,
                             n_quant)
-        want = oracle.tier_outputs(x["k"][b:b + 1, h:h + 1], x["v"][b:b + 1, h:h + 1], tier_g,
+        tier_ref, _ = oracle.route_tiers(w_ref, n_full, n_quant)
+        want = oracle.tier_outputs(x["k"][b:b + 1, h:h + 1], x["v"][b:b + 1, h:h + 1], tier_ref,
                                    WIN, promote[b:b + 1, h:h + 1])
-        for name in ("k_full", "v_full", "k_codes", "v_codes", "k_prom", "v_prom"):
-            got = host_bits(getattr(out, name)[b:b + 1, h:h + 1])
-            assert got.tobytes() == want[name].reshape(got.shape).tobytes(), name
-        for name in ("k_meta", "v_meta"):
-            got = getattr(out, name)[b:b + 1, h:h + 1].cpu().numpy()
-            assert got.tobytes() == want[name].reshape(got.shape).tobytes(), name
+        got = _gpu_payloads(out, (slice(b, b + 1), slice(h, h + 1)))
+        _payload_check(got, want, tier_g, tier_ref, promote[b:b + 1, h:h + 1])
