@@ -1,16 +1,20 @@
-// Exact top-B selection with the mandatory set (kvsel_select) for gfx950.
+// Exact top-B selection with the mandatory set (kvsel_select,
+// kvsel_select_adaptive) for gfx950.
 //
 // TideKV ("Delayed KV Eviction via Layer-Wise Chunked Prefill ..."),
-// Section 4.2, Eq. (8): R = Top_k{p_i : i not mandatory} U mandatory.  The
-// pages keep the top-k in a streaming heap inside pass 2 (Algorithm 2); here
-// the per-key scores are already a compact fp32 vector per KV head (a few
-// MiB, resident in the last-level cache), so the k-th largest value is found
-// exactly by a three-digit radix select over the fp32 bit patterns
-// (11 + 11 + 10 bits; scores are >= 0, so bit order equals value order).
-// Ties at the threshold keep the lowest positions.  The retained positions
-// are emitted in ascending order with a block-wide prefix count.
+// Section 4.2, Eq. (8): R = Top_k{p_i : i not mandatory} U mandatory.
+// TideKV keeps the top-k in a streaming heap inside pass 2 (Algorithm 2);
+// here the per-key scores are already a compact fp32 vector per KV head (a
+// few MiB, resident in the last-level cache), so the k-th largest value is
+// found exactly by a three-digit radix select over the fp32 bit patterns.
+// Scores are >= 0, so the sign bit is always clear and bit order equals value
+// order; the digits are bits 30..20 (exponent and three mantissa bits, an
+// eighth of an octave per bin), 19..10 and 9..0.  Ties at the threshold keep
+// the lowest positions.  The retained positions are emitted in ascending
+// order with a block-wide prefix count.
 //
-// One 1024-thread workgroup per (batch, KV head); histograms live in LDS.
+// Short rows: one workgroup per (batch, KV head), the row held in registers,
+// histograms in LDS.  Long rows and head groups: the sliced kernels below.
 #include "common.h"
 
 namespace kvsel {
@@ -18,85 +22,114 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 
+// Inclusive prefix sum across the 64 lanes of a wave: DPP row shifts build
+// the sums inside each row of 16 lanes, two row broadcasts carry them across
+// rows (no LDS round trips).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over a workgroup of NT threads; *total receives the
-// sum of all.  wsum must hold NT/64 entries.
+// sum of all.  wsum must hold NT/64 entries.  Two barriers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total,
                                                          uint32_t* wsum) {
   constexpr int NWV = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t w = lane < NWV ? wsum[lane] : 0u;
+  uint32_t before = 0u, tot = 0u;
 #pragma unroll
-    for (int off = 1; off < NWV; off <<= 1) {
-      const uint32_t t = __shfl_up(w, off);
-      if (lane >= off) w += t;
-    }
-    if (lane < NWV) wsum[lane] = w;
+  for (int w = 0; w < NWV; ++w) {
+    const uint32_t sw = wsum[w];
+    before += w < wave ? sw : 0u;
+    tot += sw;
   }
-  __syncthreads();
-  const uint32_t before = wave > 0 ? wsum[wave - 1] : 0u;
-  *total = wsum[NWV - 1];
-  __syncthreads();
+  *total = tot;
+  __syncthreads();   // wsum may be reused after this
   return before + incl - v;
 }
 
-// Histogram update with wave-level aggregation: scores cluster in a few
-// bins, so lanes sharing a bin are counted by one leader lane (up to two
-// distinct bins per wave per call) before the remaining lanes add one each.
+// Histogram update: one LDS atomic per counted score.  (Aggregating equal
+// bins across a wave first costs more in cross-lane latency than the atomic
+// conflicts it saves, at every row length measured.)
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const unsigned long long act = __ballot(active);
-    if (act == 0ull) return;
-    const int leader = __ffsll((long long)act) - 1;
-    const uint32_t lb = __shfl(bin, leader);
-    const bool same = active && bin == lb;
-    const unsigned long long mk = __ballot(same);
-    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(mk));
-    active = active && !same;
-  }
   if (active) atomicAdd(&hist[bin], 1u);
 }
 
-// Among `nb` histogram bins read in descending value order, find the bin
-// holding the rem-th largest counted element.  pick[0] = that bin, pick[1] =
-// count strictly above it, pick[2] = its own count.  Every thread must call.
-template <int NT, int MAXNB = 2048>
-__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t rem,
-                                           uint32_t* wsum, uint32_t* pick) {
-  constexpr int MAXPER = (MAXNB + NT - 1) / NT;
-  const int per = (nb + NT - 1) / NT;   // bins per thread (nb <= MAXNB)
-  const int t = threadIdx.x;
-  uint32_t c[MAXPER];
+// Histogram update for a thread's kPerThread consecutive scores: runs of
+// equal bins (common, since max-pooling repeats a local maximum over its
+// neighbours) are counted in registers and added with one atomic per run,
+// which cuts same-address conflicts on the crowded bins.
+template <int N>
+__device__ __forceinline__ void hist_add_runs(uint32_t* hist, const uint32_t (&bin)[N],
+                                              uint32_t active) {
+  uint32_t cur = bin[0], cnt = active & 1u;
+#pragma unroll
+  for (int e = 1; e < N; ++e) {
+    const bool a = (active >> e) & 1u;
+    if (a && bin[e] == cur) {
+      ++cnt;
+    } else {
+      if (cnt) atomicAdd(&hist[cur], cnt);
+      cur = bin[e];
+      cnt = a ? 1u : 0u;
+    }
+  }
+  if (cnt) atomicAdd(&hist[cur], cnt);
+}
+
+// Among the NB bins of `hist` (16-byte aligned), read in descending value
+// order, find the bin holding the rem-th largest counted element (rem >= 1
+// and at most the total count).  pick[0] = that bin, pick[1] = count strictly
+// above it, pick[2] = its own count.  One wave: each lane sums NB/64
+// consecutive bins, a wave scan orders the lanes, and the lane whose range
+// holds the rank walks its bins from the top.
+template <int NB>
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t rem,
+                                                uint32_t* pick) {
+  constexpr int PER = NB / 64;
+  const int lane = threadIdx.x & 63;
+  const int b0 = NB - (lane + 1) * PER;
+  uint32_t c[PER];
   uint32_t local = 0u;
 #pragma unroll
-  for (int j = 0; j < MAXPER; ++j) {
-    const int b = nb - 1 - t * per - j;
-    c[j] = (j < per && b >= 0) ? hist[b] : 0u;
-    local += c[j];
+  for (int j = 0; j < PER; j += 4) {
+    const u32x4_t w = *(const u32x4_t*)(hist + b0 + j);
+    c[j] = w[0];
+    c[j + 1] = w[1];
+    c[j + 2] = w[2];
+    c[j + 3] = w[3];
+    local += (w[0] + w[1]) + (w[2] + w[3]);
   }
-  uint32_t tot;
-  uint32_t run = block_exclusive_scan<NT>(local, &tot, wsum);
+  const uint32_t incl = wave_incl_scan(local);
+  uint32_t run = incl - local;
+  if (run < rem && rem <= incl) {
 #pragma unroll
-  for (int j = 0; j < MAXPER; ++j) {
-    const int b = nb - 1 - t * per - j;
-    if (j < per && b >= 0 && run < rem && rem <= run + c[j]) {
-      pick[0] = (uint32_t)b;
-      pick[1] = run;
-      pick[2] = c[j];
+    for (int j = PER - 1; j >= 0; --j) {
+      if (run < rem && rem <= run + c[j]) {
+        pick[0] = (uint32_t)(b0 + j);
+        pick[1] = run;
+        pick[2] = c[j];
+      }
+      run += c[j];
     }
-    run += c[j];
   }
+}
+
+// wave_find_digit by the first wave, then a barrier so every thread can
+// read pick.  Every thread of the block must call.
+template <int NB>
+__device__ __forceinline__ void block_find_digit(const uint32_t* hist, uint32_t rem,
+                                                 uint32_t* pick) {
+  if (threadIdx.x < 64) wave_find_digit<NB>(hist, rem, pick);
   __syncthreads();
 }
 
@@ -104,6 +137,8 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_
 // (scalar loads only at the unaligned ends), so a sweep keeps many bytes in
 // flight per CU.  Elements outside [lo, hi) come back invalid.
 constexpr int kPerThread = 16;
+// Longest row the single-workgroup kernel takes (one register batch of its
+// largest block); longer rows go to the sliced multi-workgroup kernels.
 constexpr int kBatch = kSelThreads * kPerThread;
 
 __device__ __forceinline__ uint32_t load16(const uint32_t* row, int p0, int lo, int hi,
@@ -132,65 +167,73 @@ __device__ __forceinline__ uint32_t load16(const uint32_t* row, int p0, int lo, 
   return valid;
 }
 
-__global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __restrict__ pooled,
-                                                             int32_t* __restrict__ idx, int S,
-                                                             int lo, int hi, int budget,
-                                                             int n_sink, int W, int n_keep) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wsum[kSelThreads / 64];
+template <int NT>
+__global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ pooled,
+                                                    int32_t* __restrict__ idx, int S, int lo,
+                                                    int hi, int budget, int n_sink, int W,
+                                                    int n_keep) {
+  constexpr int kRowBatch = NT * kPerThread;
+  // One histogram per digit, all cleared up front: a round is then one
+  // barrier after its counts and one after the digit search.
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2048 + 1024 + 1024];
+  __shared__ uint32_t wsum[NT / 64];
   __shared__ uint32_t pick[3];
   const int head = blockIdx.x, tid = threadIdx.x;
   const uint32_t* u = (const uint32_t*)pooled + (size_t)head * S;
   int32_t* out = idx + (size_t)head * n_keep;
-  for (int i = tid; i < n_sink; i += kSelThreads) out[i] = i;
-  for (int j = tid; j < W; j += kSelThreads) out[n_sink + budget + j] = S - W + j;
+  for (int i = tid; i < n_sink; i += NT) out[i] = i;
+  for (int j = tid; j < W; j += NT) out[n_sink + budget + j] = S - W + j;
   if (budget == 0) return;
   // First batch start: at or below lo, on a 16-byte boundary of the buffer.
   const int ofs = (int)(((size_t)head * S) & 3u);
   const int base0 = lo - ((lo + ofs) & 3);
 
   // A row that fits one batch is loaded once and kept in registers.
-  const bool one_batch = hi - base0 <= kBatch;
+  const bool one_batch = hi - base0 <= kRowBatch;
   uint32_t x1[kPerThread];
   uint32_t v1 = 0u;
   if (one_batch) v1 = load16(u, base0 + tid * kPerThread, lo, hi, x1);
+  for (int i = tid; i < 2048 + 1024 + 1024; i += NT) hist[i] = 0u;
+  __syncthreads();
 
   // Radix select: digit r covers bits [shift, shift+nbits).
   uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)budget;
   for (int r = 0; r < 3; ++r) {
-    const int shift = r == 0 ? 21 : (r == 1 ? 10 : 0);
-    const int nb = r == 2 ? 1024 : 2048;
-    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0u;
-    __syncthreads();
-    for (int base = base0; base < hi; base += kBatch) {
+    const int shift = r == 0 ? 20 : (r == 1 ? 10 : 0);
+    const int nb = r == 0 ? 2048 : 1024;
+    uint32_t* h = hist + (r == 0 ? 0 : (r == 1 ? 2048 : 3072));
+    for (int base = base0; base < hi; base += kRowBatch) {
       uint32_t x[kPerThread];
       const uint32_t valid = one_batch ? v1 : load16(u, base + tid * kPerThread, lo, hi, x);
       if (one_batch) {
 #pragma unroll
         for (int e = 0; e < kPerThread; ++e) x[e] = x1[e];
       }
+      uint32_t bin[kPerThread];
+      uint32_t act = 0u;
 #pragma unroll
-      for (int e = 0; e < kPerThread; ++e)
-        hist_add(hist, (x[e] >> shift) & (uint32_t)(nb - 1),
-                 ((valid >> e) & 1u) && (x[e] & pmask) == prefix);
+      for (int e = 0; e < kPerThread; ++e) {
+        bin[e] = (x[e] >> shift) & (uint32_t)(nb - 1);
+        act |= (uint32_t)(((valid >> e) & 1u) && (x[e] & pmask) == prefix) << e;
+      }
+      hist_add_runs(h, bin, act);
     }
     __syncthreads();
-    find_digit<kSelThreads>(hist, nb, rem, wsum, pick);
+    if (r == 0) block_find_digit<2048>(h, rem, pick);
+    else block_find_digit<1024>(h, rem, pick);
     const uint32_t digit = pick[0];
     rem -= pick[1];
     prefix |= digit << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
-    const bool whole_bin = rem == pick[2];
-    __syncthreads();
     // The whole boundary bin is kept: no need to resolve the lower bits.
-    if (whole_bin) break;
+    if (rem == pick[2]) break;
   }
   // Kept: (x & pmask) > prefix, and the first `rem` elements (by position)
   // with (x & pmask) == prefix.  After three rounds pmask covers every bit
   // and prefix is the exact bit pattern of the budget-th largest score.
   const uint32_t need_eq = rem;
   uint32_t cgt = 0u, ceq = 0u;
-  for (int base = base0; base < hi; base += kBatch) {
+  for (int base = base0; base < hi; base += kRowBatch) {
     const int i0 = base + tid * kPerThread;
     uint32_t x[kPerThread];
     const uint32_t valid = one_batch ? v1 : load16(u, i0, lo, hi, x);
@@ -208,7 +251,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     }
     const uint32_t ngt = __popc(gt), neq = __popc(eq);
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<kSelThreads>((ngt << 16) | neq, &tot, wsum);
+    const uint32_t ex = block_exclusive_scan<NT>((ngt << 16) | neq, &tot, wsum);
     uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
@@ -238,18 +281,18 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
 // is cut into ns slices of kSlice scores (256 threads x 16); the group's
 // slices are numbered head-major.  The kernels run in order:
 //   sel_init     zero the group's two digit histograms
-//   sel_hist     per slice: first-digit (top 11 bits) histogram -> global
+//   sel_hist     per slice: first-digit (bits 30..20) histogram -> global
 //   sel_hist2    per slice: first digit d1 of the budget-th score; histogram
-//                of the second digit (next 11 bits) of the scores in d1's bin
-//   sel_cand     per slice: the 22-bit prefix of the budget-th score; count
+//                of the second digit (bits 19..10) of the scores in d1's bin
+//   sel_cand     per slice: the 21-bit prefix of the budget-th score; count
 //                the scores above it and compact the ones that share it
 //   sel_resolve  per group: the last 10 bits over the compacted scores, the
 //                tie cut (by head, then position), each slice's output
 //                offset, the per-head offsets and the mandatory rows
 //   sel_emit     per slice: ordered write of the kept positions
 // Both wide digits are settled by every slice in parallel, so the single
-// resolve workgroup only sees scores equal to the budget-th one in their top
-// 22 bits (a handful, unless values repeat).  A digit whose boundary bin is
+// resolve workgroup only sees scores equal to the budget-th one in their
+// bits 30..10 (a handful, unless values repeat).  A digit whose boundary bin is
 // kept whole ends the search early.
 // The rule every kernel applies in the end is one predicate per score:
 // kept <=> key > prefix || (key == prefix && h*S + position <= cut), with
@@ -261,8 +304,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
 // ---------------------------------------------------------------------------
 constexpr int kSliceThreads = 256;
 constexpr int kSlice = kSliceThreads * kPerThread;
-constexpr int kD1Bits = 11, kD1Bins = 1 << kD1Bits, kD1Shift = 32 - kD1Bits;
-constexpr int kD2Bits = 11, kD2Bins = 1 << kD2Bits, kD2Shift = kD1Shift - kD2Bits;
+constexpr int kD1Bits = 11, kD1Bins = 1 << kD1Bits, kD1Shift = 31 - kD1Bits;
+constexpr int kD2Bits = 10, kD2Bins = 1 << kD2Bits, kD2Shift = kD1Shift - kD2Bits;
 constexpr int kD3Bins = 1 << kD2Shift;
 
 struct SelArgs {
@@ -309,17 +352,16 @@ struct Prefix {
 // bin is not kept whole.  Every thread of the block must call.
 template <int NT>
 __device__ __forceinline__ Prefix settle_prefix(const uint32_t* hist1, const uint32_t* hist2,
-                                                uint32_t budget, uint32_t* wsum,
-                                                uint32_t* pick) {
+                                                uint32_t budget, uint32_t* pick) {
   Prefix p;
-  find_digit<NT, kD1Bins>(hist1, kD1Bins, budget, wsum, pick);
+  block_find_digit<kD1Bins>(hist1, budget, pick);
   p.rem = budget - pick[1];
   p.prefix = pick[0] << kD1Shift;
   p.pmask = (uint32_t)(kD1Bins - 1) << kD1Shift;
   p.whole = p.rem == pick[2];
   __syncthreads();
   if (!p.whole) {
-    find_digit<NT, kD2Bins>(hist2, kD2Bins, p.rem, wsum, pick);
+    block_find_digit<kD2Bins>(hist2, p.rem, pick);
     p.rem -= pick[1];
     p.prefix |= pick[0] << kD2Shift;
     p.pmask |= (uint32_t)(kD2Bins - 1) << kD2Shift;
@@ -347,8 +389,12 @@ __global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
   const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  {
+    uint32_t bin[kPerThread];
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) hist_add(hist, x[e] >> kD1Shift, (valid >> e) & 1u);
+    for (int e = 0; e < kPerThread; ++e) bin[e] = (x[e] >> kD1Shift) & (uint32_t)(kD1Bins - 1);
+    hist_add_runs(hist, bin, valid);
+  }
   __syncthreads();
   uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
   for (int i = tid; i < kD1Bins; i += kSliceThreads)
@@ -356,9 +402,8 @@ __global__ void __launch_bounds__(kSliceThreads) sel_hist(SelArgs a) {
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_hist2(SelArgs a) {
-  __shared__ uint32_t h1[kD1Bins];
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kD1Bins];
   __shared__ uint32_t hist[kD2Bins];
-  __shared__ uint32_t wsum[kSliceThreads / 64];
   __shared__ uint32_t pick[3];
   const int grp = blockIdx.y, tid = threadIdx.x;
   const SliceAt at = slice_at(a, grp, blockIdx.x);
@@ -366,17 +411,22 @@ __global__ void __launch_bounds__(kSliceThreads) sel_hist2(SelArgs a) {
   for (int i = tid; i < kD1Bins; i += kSliceThreads) h1[i] = g1[i];
   for (int i = tid; i < kD2Bins; i += kSliceThreads) hist[i] = 0u;
   __syncthreads();
-  find_digit<kSliceThreads, kD1Bins>(h1, kD1Bins, (uint32_t)a.budget, wsum, pick);
+  block_find_digit<kD1Bins>(h1, (uint32_t)a.budget, pick);
   const uint32_t d1 = pick[0];
   if ((uint32_t)a.budget - pick[1] == pick[2]) return;   // d1's bin kept whole
   const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
   const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  uint32_t bin[kPerThread];
+  uint32_t act = 0u;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e)
-    hist_add(hist, (x[e] >> kD2Shift) & (uint32_t)(kD2Bins - 1),
-             ((valid >> e) & 1u) && (x[e] >> kD1Shift) == d1);
+  for (int e = 0; e < kPerThread; ++e) {
+    bin[e] = (x[e] >> kD2Shift) & (uint32_t)(kD2Bins - 1);
+    act |= (uint32_t)(((valid >> e) & 1u) && ((x[e] >> kD1Shift) & (uint32_t)(kD1Bins - 1)) == d1)
+           << e;
+  }
+  hist_add_runs(hist, bin, act);
   __syncthreads();
   uint32_t* g2 = a.hist2 + (size_t)grp * kD2Bins;
   for (int i = tid; i < kD2Bins; i += kSliceThreads)
@@ -384,8 +434,8 @@ __global__ void __launch_bounds__(kSliceThreads) sel_hist2(SelArgs a) {
 }
 
 __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
-  __shared__ uint32_t h1[kD1Bins];
-  __shared__ uint32_t h2[kD2Bins];
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kD1Bins];
+  __shared__ __attribute__((aligned(16))) uint32_t h2[kD2Bins];
   __shared__ uint32_t wsum[kSliceThreads / 64];
   __shared__ uint32_t pick[3];
   const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
@@ -395,7 +445,7 @@ __global__ void __launch_bounds__(kSliceThreads) sel_cand(SelArgs a) {
   for (int i = tid; i < kD1Bins; i += kSliceThreads) h1[i] = g1[i];
   for (int i = tid; i < kD2Bins; i += kSliceThreads) h2[i] = g2[i];
   __syncthreads();
-  const Prefix pf = settle_prefix<kSliceThreads>(h1, h2, (uint32_t)a.budget, wsum, pick);
+  const Prefix pf = settle_prefix<kSliceThreads>(h1, h2, (uint32_t)a.budget, pick);
   const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
   const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
   const int key0 = at.h * a.S + i0;
@@ -443,8 +493,8 @@ __device__ __forceinline__ int slice_of(const uint32_t* cstart, int ns, uint32_t
 }
 
 __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
-  __shared__ uint32_t h1[kD1Bins];
-  __shared__ uint32_t h2[kD2Bins];
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kD1Bins];
+  __shared__ __attribute__((aligned(16))) uint32_t h2[kD2Bins];
   __shared__ uint32_t selc[kMaxGroupSlices];
   __shared__ uint32_t cstart[kMaxGroupSlices];
   __shared__ uint32_t lval[kCandCap];
@@ -470,7 +520,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
   if (2 * tid < ns) cstart[2 * tid] = ex;
   if (2 * tid + 1 < ns) cstart[2 * tid + 1] = ex + c0;
   __syncthreads();
-  Prefix pf = settle_prefix<kSelThreads>(h1, h2, (uint32_t)a.budget, wsum, pick);
+  Prefix pf = settle_prefix<kSelThreads>(h1, h2, (uint32_t)a.budget, pick);
   uint32_t prefix = pf.prefix, pmask = pf.pmask, rem = pf.rem;
   const uint32_t* cv = a.cval + (size_t)grp * ns * kSlice;
   const int32_t* ci = a.cidx + (size_t)grp * ns * kSlice;
@@ -498,7 +548,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
       }
     };
     // Last digit (10 bits) over the compacted scores, which all share the
-    // 22-bit prefix.  The histogram reuses h1.
+    // 21-bit prefix.  The histogram reuses h1.
     for (int i = tid; i < kD3Bins; i += kSelThreads) h1[i] = 0u;
     __syncthreads();
     for (uint32_t k0 = 0; k0 < ncand; k0 += kSelThreads) {
@@ -509,7 +559,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_resolve(SelArgs a) {
       hist_add(h1, x & (uint32_t)(kD3Bins - 1), k < ncand);
     }
     __syncthreads();
-    find_digit<kSelThreads>(h1, kD3Bins, rem, wsum, pick);
+    block_find_digit<kD3Bins>(h1, rem, pick);
     rem -= pick[1];
     prefix |= pick[0];
     pmask = 0xffffffffu;
@@ -701,8 +751,18 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   const int n_keep = hg * seg + budget;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
   if (!p.multi && hg == 1) {
-    hipLaunchKernelGGL(select_kernel, dim3(groups), dim3(kSelThreads), 0, stream, pooled, idx,
-                       d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
+    // Smallest block that holds the row in one register batch (16 scores per
+    // thread): no idle threads on short rows, fewer waves at each barrier.
+    const int need = hi - lo + 3;
+    if (need <= 256 * kPerThread)
+      hipLaunchKernelGGL(select_kernel<256>, dim3(groups), dim3(256), 0, stream, pooled, idx,
+                         d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
+    else if (need <= 512 * kPerThread)
+      hipLaunchKernelGGL(select_kernel<512>, dim3(groups), dim3(512), 0, stream, pooled, idx,
+                         d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
+    else
+      hipLaunchKernelGGL(select_kernel<1024>, dim3(groups), dim3(1024), 0, stream, pooled, idx,
+                         d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
     return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   }
   if (!p.multi) {
