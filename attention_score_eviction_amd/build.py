@@ -33,6 +33,10 @@ def command(out: str = LIB) -> list[str]:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep the compiler from forming packed-fp32 instructions by itself
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results straight into VGPRs: the score passes read every
+        # logit with VALU instructions, so accumulator-register copies would
+        # cost one extra instruction per logit
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
         *srcs, "-o", out,

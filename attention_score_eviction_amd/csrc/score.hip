@@ -95,6 +95,10 @@ __device__ __forceinline__ void stage_queries(u32x4_t* qs, const T* qg, int nrow
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(fmaxf(a, b), c);
+}
+
 __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
   const float mn = fmaxf(m, mo);
   const float mu = (mn == -INFINITY) ? 0.f : mn;
@@ -154,11 +158,13 @@ __device__ __forceinline__ void pass1_block(const int* lims, const Frag<NV> (&kf
         for (int i = 0; i < 4; ++i)
           if (kb + kt * 16 + 4 * g + i > lim) cur[kt][i] = -INFINITY;
     }
-    float m4[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      m4[kt] = fmaxf(fmaxf(cur[kt][0], cur[kt][1]), fmaxf(cur[kt][2], cur[kt][3]));
-    const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    // Maximum of the 16 logits as three-input maxima (v_max3_f32): 8 ops.
+    const float a0 = max3f(cur[0][0], cur[0][1], cur[0][2]);
+    const float a1 = max3f(cur[0][3], cur[1][0], cur[1][1]);
+    const float a2 = max3f(cur[1][2], cur[1][3], cur[2][0]);
+    const float a3 = max3f(cur[2][1], cur[2][2], cur[2][3]);
+    const float a4 = max3f(cur[3][0], cur[3][1], cur[3][2]);
+    const float mx = max3f(max3f(a0, a1, a2), max3f(a3, a4, cur[3][3]), -INFINITY);
     const float mnew = fmaxf(m[t], mx * c);
     const float mu = (mnew == -INFINITY) ? 0.f : mnew;
     // All exponentials first, then the sums: no add waits on a fresh
