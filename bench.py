@@ -281,7 +281,12 @@ def ingest_counters(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
     per_call = {}
+    adaptive = workload.endswith("-adaptive")
     for call, kernels in CALL_KERNELS.items():
+        if (call in ("kvsel_select_adaptive", "kvsel_compact_flat")) != adaptive and \
+                call in ("kvsel_select", "kvsel_compact", "kvsel_select_adaptive",
+                         "kvsel_compact_flat"):
+            continue
         tot, seen = 0.0, False
         for name in set(fetch) | set(write):
             if any(kn in name for kn in kernels):
