@@ -58,7 +58,8 @@ struct SelectPlan {
   bool multi;     // sliced multi-workgroup kernels (long rows, head groups)
   int hg;         // KV heads per selection group
   int groups;     // batch * n_kv_heads / hg
-  int ns;         // slices per KV-head row
+  int ns;         // slices of kSlice scores per KV-head row (sliced kernels)
+  int nsl;        // slices of 16 scores per KV-head row (single-workgroup kernel)
   size_t off_hist, off_gtc, off_candc, off_offs, off_params, off_cval, off_cidx, total;
 };
 // False when a head group needs more than kMaxGroupSlices slices.

@@ -89,38 +89,40 @@ __device__ __forceinline__ void hist_add_runs(uint32_t* hist, const uint32_t (&b
 // Among the NB bins of `hist` (16-byte aligned), read in descending value
 // order, find the bin holding the rem-th largest counted element (rem >= 1
 // and at most the total count).  pick[0] = that bin, pick[1] = count strictly
-// above it, pick[2] = its own count.  One wave: each lane sums NB/64
-// consecutive bins, a wave scan orders the lanes, and the lane whose range
-// holds the rank walks its bins from the top.
+// above it, pick[2] = its own count.  One wave, two levels: each lane sums
+// NB/64 consecutive bins and a wave scan finds the lane whose range holds
+// the rank; then the wave reads that lane's bins, one per lane, highest
+// first, and a second scan finds the bin.  (Keeping a lane's bins in
+// registers and walking them serially costs ~100 VGPRs in the kernels that
+// inline this.)
 template <int NB>
 __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t rem,
                                                 uint32_t* pick) {
   constexpr int PER = NB / 64;
+  static_assert(PER <= 64 && PER % 4 == 0, "bins per lane");
   const int lane = threadIdx.x & 63;
-  const int b0 = NB - (lane + 1) * PER;
-  uint32_t c[PER];
   uint32_t local = 0u;
+  {
+    const int b0 = NB - (lane + 1) * PER;
 #pragma unroll
-  for (int j = 0; j < PER; j += 4) {
-    const u32x4_t w = *(const u32x4_t*)(hist + b0 + j);
-    c[j] = w[0];
-    c[j + 1] = w[1];
-    c[j + 2] = w[2];
-    c[j + 3] = w[3];
-    local += (w[0] + w[1]) + (w[2] + w[3]);
+    for (int j = 0; j < PER; j += 4) {
+      const u32x4_t w = *(const u32x4_t*)(hist + b0 + j);
+      local += (w[0] + w[1]) + (w[2] + w[3]);
+    }
   }
   const uint32_t incl = wave_incl_scan(local);
-  uint32_t run = incl - local;
-  if (run < rem && rem <= incl) {
-#pragma unroll
-    for (int j = PER - 1; j >= 0; --j) {
-      if (run < rem && rem <= run + c[j]) {
-        pick[0] = (uint32_t)(b0 + j);
-        pick[1] = run;
-        pick[2] = c[j];
-      }
-      run += c[j];
-    }
+  const uint32_t excl = incl - local;
+  const unsigned long long hit = __ballot(excl < rem && rem <= incl);
+  if (hit == 0ull) return;
+  const int L = __ffsll((long long)hit) - 1;
+  const uint32_t run = __builtin_amdgcn_readlane(excl, L);
+  const int bin = NB - L * PER - 1 - lane;   // lane 0: lane L's highest bin
+  const uint32_t c = lane < PER ? hist[bin] : 0u;
+  const uint32_t i2 = wave_incl_scan(c);
+  if (lane < PER && run + (i2 - c) < rem && rem <= run + i2) {
+    pick[0] = (uint32_t)bin;
+    pick[1] = run + (i2 - c);
+    pick[2] = c;
   }
 }
 
@@ -137,9 +139,6 @@ __device__ __forceinline__ void block_find_digit(const uint32_t* hist, uint32_t 
 // (scalar loads only at the unaligned ends), so a sweep keeps many bytes in
 // flight per CU.  Elements outside [lo, hi) come back invalid.
 constexpr int kPerThread = 16;
-// Longest row the single-workgroup kernel takes (one register batch of its
-// largest block); longer rows go to the sliced multi-workgroup kernels.
-constexpr int kBatch = kSelThreads * kPerThread;
 
 __device__ __forceinline__ uint32_t load16(const uint32_t* row, int p0, int lo, int hi,
                                            uint32_t (&x)[kPerThread]) {
@@ -167,109 +166,185 @@ __device__ __forceinline__ uint32_t load16(const uint32_t* row, int p0, int lo, 
   return valid;
 }
 
-template <int NT>
+// Heads of one selection group the single-workgroup kernel takes.
+constexpr int kMaxWgHeads = 64;
+
+// Single-workgroup select for one selection group: hg consecutive KV-head
+// rows (hg = 1: a per-head budget; hg = Hkv: the head-adaptive budget of one
+// sequence).  Each row's candidates are cut into nsl slices of 16 scores
+// (from a 16-byte aligned start at or below lo); slice j of the group is row
+// j / nsl, slice j % nsl.  Batch b is slices [b*NT, (b+1)*NT), one per
+// thread, so thread order within a batch is (head, position) order.  The
+// first NB batches stay in registers for the whole kernel; later ones (only
+// for rows longer than the sliced kernels take) are reloaded per pass.
+template <int NT, int NB>
 __global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ pooled,
-                                                    int32_t* __restrict__ idx, int S, int lo,
-                                                    int hi, int budget, int n_sink, int W,
-                                                    int n_keep) {
-  constexpr int kRowBatch = NT * kPerThread;
+                                                    int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ head_off, int S,
+                                                    int lo, int hi, int budget, int n_sink,
+                                                    int W, int n_keep, int hg, int nsl) {
   // One histogram per digit, all cleared up front: a round is then one
   // barrier after its counts and one after the digit search.
   __shared__ __attribute__((aligned(16))) uint32_t hist[2048 + 1024 + 1024];
   __shared__ uint32_t wsum[NT / 64];
   __shared__ uint32_t pick[3];
-  const int head = blockIdx.x, tid = threadIdx.x;
-  const uint32_t* u = (const uint32_t*)pooled + (size_t)head * S;
-  int32_t* out = idx + (size_t)head * n_keep;
-  for (int i = tid; i < n_sink; i += NT) out[i] = i;
-  for (int j = tid; j < W; j += NT) out[n_sink + budget + j] = S - W + j;
-  if (budget == 0) return;
-  // First batch start: at or below lo, on a 16-byte boundary of the buffer.
-  const int ofs = (int)(((size_t)head * S) & 3u);
-  const int base0 = lo - ((lo + ofs) & 3);
+  __shared__ uint32_t kept[kMaxWgHeads];
+  const int grp = blockIdx.x, tid = threadIdx.x;
+  const int seg = n_sink + W;
+  int32_t* out = idx + (size_t)grp * n_keep;
+  const int nbatch = (hg * nsl + NT - 1) / NT;
 
-  // A row that fits one batch is loaded once and kept in registers.
-  const bool one_batch = hi - base0 <= kRowBatch;
-  uint32_t x1[kPerThread];
-  uint32_t v1 = 0u;
-  if (one_batch) v1 = load16(u, base0 + tid * kPerThread, lo, hi, x1);
+  // Slice of batch b for this thread: its head, first position and scores.
+  auto slice_load = [&](int bt, uint32_t (&x)[kPerThread], int& h, int& p0) -> uint32_t {
+    const int j = bt * NT + tid;
+    h = j / nsl;
+    if (h >= hg) {
+      h = hg - 1;
+      p0 = hi;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) x[e] = 0u;
+      return 0u;
+    }
+    const size_t row = (size_t)grp * hg + h;
+    const int base0 = lo - ((lo + (int)((row * S) & 3u)) & 3);
+    p0 = base0 + (j - h * nsl) * kPerThread;
+    return load16((const uint32_t*)pooled + row * S, p0, lo, hi, x);
+  };
+  uint32_t xr[NB][kPerThread];
+  uint32_t vr[NB];
+  if (budget > 0) {
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) {
+      int h, p0;
+      vr[bt] = slice_load(bt, xr[bt], h, p0);
+    }
+  }
+  // Head and first position of this thread's slice in batch bt (recomputed
+  // rather than kept: fewer live registers).
+  auto slice_at = [&](int bt, int& h, int& p0) {
+    const int j = bt * NT + tid;
+    h = j / nsl;
+    if (h >= hg) {
+      h = hg - 1;
+      p0 = hi;
+      return;
+    }
+    const size_t row = (size_t)grp * hg + h;
+    const int base0 = lo - ((lo + (int)((row * S) & 3u)) & 3);
+    p0 = base0 + (j - h * nsl) * kPerThread;
+  };
+  // Visit every batch in order: the register-resident ones unrolled, the
+  // rest reloaded.
+  auto for_batches = [&](auto&& fn) {
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) {
+      if (bt < nbatch) {
+        int h, p0;
+        slice_at(bt, h, p0);
+        fn(xr[bt], vr[bt], h, p0);
+      }
+    }
+    for (int bt = NB; bt < nbatch; ++bt) {
+      uint32_t x[kPerThread];
+      int h, p0;
+      const uint32_t v = slice_load(bt, x, h, p0);
+      fn(x, v, h, p0);
+    }
+  };
   for (int i = tid; i < 2048 + 1024 + 1024; i += NT) hist[i] = 0u;
+  for (int i = tid; i < hg; i += NT) kept[i] = 0u;
   __syncthreads();
 
-  // Radix select: digit r covers bits [shift, shift+nbits).
-  uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)budget;
-  for (int r = 0; r < 3; ++r) {
-    const int shift = r == 0 ? 20 : (r == 1 ? 10 : 0);
-    const int nb = r == 0 ? 2048 : 1024;
-    uint32_t* h = hist + (r == 0 ? 0 : (r == 1 ? 2048 : 3072));
-    for (int base = base0; base < hi; base += kRowBatch) {
-      uint32_t x[kPerThread];
-      const uint32_t valid = one_batch ? v1 : load16(u, base + tid * kPerThread, lo, hi, x);
-      if (one_batch) {
+  if (budget > 0) {
+    // Radix select: digit r covers bits [shift, shift+nbits).
+    uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)budget;
+    for (int r = 0; r < 3; ++r) {
+      const int shift = r == 0 ? 20 : (r == 1 ? 10 : 0);
+      const int nb = r == 0 ? 2048 : 1024;
+      uint32_t* hh = hist + (r == 0 ? 0 : (r == 1 ? 2048 : 3072));
+      for_batches([&](const uint32_t (&x)[kPerThread], uint32_t valid, int, int) {
+        uint32_t bin[kPerThread];
+        uint32_t act = 0u;
 #pragma unroll
-        for (int e = 0; e < kPerThread; ++e) x[e] = x1[e];
-      }
-      uint32_t bin[kPerThread];
-      uint32_t act = 0u;
+        for (int e = 0; e < kPerThread; ++e) {
+          bin[e] = (x[e] >> shift) & (uint32_t)(nb - 1);
+          act |= (uint32_t)(((valid >> e) & 1u) && (x[e] & pmask) == prefix) << e;
+        }
+        hist_add_runs(hh, bin, act);
+      });
+      __syncthreads();
+      if (r == 0) block_find_digit<2048>(hh, rem, pick);
+      else block_find_digit<1024>(hh, rem, pick);
+      const uint32_t digit = pick[0];
+      rem -= pick[1];
+      prefix |= digit << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
+      // The whole boundary bin is kept: no need to resolve the lower bits.
+      if (rem == pick[2]) break;
+    }
+    // Kept: (x & pmask) > prefix, and the first `rem` elements in (head,
+    // position) order with (x & pmask) == prefix.  After three rounds pmask
+    // covers every bit below the sign and prefix is the exact bit pattern of
+    // the budget-th largest score.  Pick number `slot` of the group goes to
+    // row h*(n_sink+W) + n_sink + slot: the rows of earlier heads' picks and
+    // mandatory sets come before it.
+    const uint32_t need_eq = rem;
+    uint32_t cgt = 0u, ceq = 0u;
+    for_batches([&](const uint32_t (&x)[kPerThread], uint32_t valid, int h, int p0) {
+      uint32_t gt = 0u, eq = 0u;
 #pragma unroll
       for (int e = 0; e < kPerThread; ++e) {
-        bin[e] = (x[e] >> shift) & (uint32_t)(nb - 1);
-        act |= (uint32_t)(((valid >> e) & 1u) && (x[e] & pmask) == prefix) << e;
+        const uint32_t km = x[e] & pmask;
+        const bool ok = (valid >> e) & 1u;
+        gt |= (uint32_t)(ok && km > prefix) << e;
+        eq |= (uint32_t)(ok && km == prefix) << e;
       }
-      hist_add_runs(h, bin, act);
-    }
-    __syncthreads();
-    if (r == 0) block_find_digit<2048>(h, rem, pick);
-    else block_find_digit<1024>(h, rem, pick);
-    const uint32_t digit = pick[0];
-    rem -= pick[1];
-    prefix |= digit << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    // The whole boundary bin is kept: no need to resolve the lower bits.
-    if (rem == pick[2]) break;
+      const uint32_t ngt = __popc(gt), neq = __popc(eq);
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_scan<NT>((ngt << 16) | neq, &tot, wsum);
+      uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
+      int32_t* oh = out + h * seg + n_sink;
+      uint32_t nw = 0u;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        // slot < budget always holds for finite non-negative scores; the
+        // guard keeps malformed input from writing outside this group.
+        if ((gt >> e) & 1u) {
+          const uint32_t slot = gtb + min(eqb, need_eq);
+          if (slot < (uint32_t)budget) {
+            oh[slot] = p0 + e;
+            ++nw;
+          }
+          ++gtb;
+        } else if ((eq >> e) & 1u) {
+          const uint32_t slot = gtb + eqb;
+          if (eqb < need_eq && slot < (uint32_t)budget) {
+            oh[slot] = p0 + e;
+            ++nw;
+          }
+          ++eqb;
+        }
+      }
+      if (nw) atomicAdd(&kept[h], nw);
+      cgt += tot >> 16;
+      ceq += tot & 0xffffu;
+    });
   }
-  // Kept: (x & pmask) > prefix, and the first `rem` elements (by position)
-  // with (x & pmask) == prefix.  After three rounds pmask covers every bit
-  // and prefix is the exact bit pattern of the budget-th largest score.
-  const uint32_t need_eq = rem;
-  uint32_t cgt = 0u, ceq = 0u;
-  for (int base = base0; base < hi; base += kRowBatch) {
-    const int i0 = base + tid * kPerThread;
-    uint32_t x[kPerThread];
-    const uint32_t valid = one_batch ? v1 : load16(u, i0, lo, hi, x);
-    if (one_batch) {
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) x[e] = x1[e];
-    }
-    uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const uint32_t km = x[e] & pmask;
-      const bool ok = (valid >> e) & 1u;
-      gt |= (uint32_t)(ok && km > prefix) << e;
-      eq |= (uint32_t)(ok && km == prefix) << e;
-    }
-    const uint32_t ngt = __popc(gt), neq = __popc(eq);
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<NT>((ngt << 16) | neq, &tot, wsum);
-    uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      // slot < budget always holds for finite non-negative scores; the
-      // guard keeps malformed input from writing outside this row.
-      if ((gt >> e) & 1u) {
-        const uint32_t slot = gtb + min(eqb, need_eq);
-        if (slot < (uint32_t)budget) out[n_sink + slot] = i0 + e;
-        ++gtb;
-      } else if ((eq >> e) & 1u) {
-        const uint32_t slot = gtb + eqb;
-        if (eqb < need_eq && slot < (uint32_t)budget) out[n_sink + slot] = i0 + e;
-        ++eqb;
-      }
-    }
-    cgt += tot >> 16;
-    ceq += tot & 0xffffu;
-    if (cgt + min(ceq, need_eq) >= (uint32_t)budget && ceq >= need_eq) break;
+  __syncthreads();
+  // Mandatory rows and head offsets from the per-head pick counts.
+  auto picks_before = [&](int h) -> uint32_t {
+    uint32_t c = 0u;
+    for (int k = 0; k < h; ++k) c += kept[k];
+    return c;
+  };
+  if (head_off)
+    for (int h = tid; h <= hg; h += NT)
+      head_off[(size_t)grp * (hg + 1) + h] = (int32_t)(h * seg + picks_before(h));
+  for (int t = tid; t < hg * seg; t += NT) {
+    const int h = t / seg, j = t - h * seg;
+    const uint32_t start = h * seg + picks_before(h);
+    if (j < n_sink) out[start + j] = j;
+    else out[start + n_sink + kept[h] + (j - n_sink)] = S - W + (j - n_sink);
   }
 }
 
@@ -687,40 +762,31 @@ __global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
   }
 }
 
-// Budget 0: each head of a group keeps its sinks and its observation window,
-// and head h's rows start at h*(n_sink+W).
-__global__ void __launch_bounds__(256) mandatory_only_kernel(int32_t* __restrict__ idx,
-                                                             int32_t* __restrict__ head_off,
-                                                             int S, int n_sink, int W, int hg) {
-  const int grp = blockIdx.x, tid = threadIdx.x;
-  const int seg = n_sink + W;
-  int32_t* out = idx + (size_t)grp * hg * seg;
-  for (int t = tid; t < hg * seg; t += 256) {
-    const int j = t % seg;
-    out[t] = j < n_sink ? j : S - W + (j - n_sink);
-  }
-  if (head_off)
-    for (int h = tid; h <= hg; h += 256) head_off[(size_t)grp * (hg + 1) + h] = h * seg;
-}
-
 }  // namespace
 
 bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p) {
   const int groups = d.batch * d.n_kv_heads / hg;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
   const long ncand = (long)hi - lo;
-  // Per-head short rows: one workgroup per row in one launch.  Long rows and
-  // head groups: the sliced multi-workgroup kernels (the slice count includes
-  // the alignment lead-in; sel_resolve keeps per-slice counters for at most
-  // kMaxGroupSlices slices of a group).
+  // Single workgroup per group when the group's slices of 16 scores fit two
+  // register batches of 512 threads (16K scores); otherwise the sliced
+  // multi-workgroup kernels (the slice count includes the alignment lead-in;
+  // sel_resolve keeps per-slice counters for at most kMaxGroupSlices slices
+  // of a group).  One workgroup over 64K scores measured slower than the
+  // sliced kernels (58 vs 33 us for eight 64K rows): its histogram atomics
+  // and passes all run on one CU.
+  const long nsl = (ncand + 3 + kPerThread - 1) / kPerThread;
+  const bool single = nsl * hg <= 2L * 512;
   const long ns = (ncand + 3 + kSlice - 1) / kSlice;
   p->hg = hg;
   p->groups = groups;
+  p->nsl = (int)nsl;
+  if (hg > kMaxWgHeads) return false;
   if (hg == 1) {
-    p->multi = budget > 0 && ncand > kBatch && ns <= kMaxGroupSlices;
+    p->multi = budget > 0 && !single && ns <= kMaxGroupSlices;
   } else {
-    if (ns * hg > kMaxGroupSlices) return false;
-    p->multi = budget > 0;
+    if (!single && ns * hg > kMaxGroupSlices) return false;
+    p->multi = budget > 0 && !single;
   }
   p->ns = p->multi ? (int)ns : 0;
   const size_t nst = (size_t)p->ns * hg;
@@ -750,25 +816,18 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   const int seg = d.n_sink + d.obs_window;
   const int n_keep = hg * seg + budget;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
-  if (!p.multi && hg == 1) {
-    // Smallest block that holds the row in one register batch (16 scores per
-    // thread): no idle threads on short rows, fewer waves at each barrier.
-    const int need = hi - lo + 3;
-    if (need <= 256 * kPerThread)
-      hipLaunchKernelGGL(select_kernel<256>, dim3(groups), dim3(256), 0, stream, pooled, idx,
-                         d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
-    else if (need <= 512 * kPerThread)
-      hipLaunchKernelGGL(select_kernel<512>, dim3(groups), dim3(512), 0, stream, pooled, idx,
-                         d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
-    else
-      hipLaunchKernelGGL(select_kernel<1024>, dim3(groups), dim3(1024), 0, stream, pooled, idx,
-                         d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep);
-    return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
-  }
   if (!p.multi) {
-    // Nothing to pick: every head keeps exactly its mandatory rows.
-    hipLaunchKernelGGL(mandatory_only_kernel, dim3(groups), dim3(256), 0, stream, idx, head_off,
-                       d.seq_len, d.n_sink, d.obs_window, hg);
+    // Smallest block whose register batches hold the group (16 scores per
+    // thread): no idle threads on short rows, fewer waves at each barrier.
+    const long tot = (long)p.nsl * hg;
+    const dim3 g(groups);
+#define KVSEL_SELECT_1WG(NT, NB)                                                            \
+  hipLaunchKernelGGL((select_kernel<NT, NB>), g, dim3(NT), 0, stream, pooled, idx, head_off, \
+                     d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep, hg, p.nsl)
+    if (tot <= 256) KVSEL_SELECT_1WG(256, 1);
+    else if (tot <= 512) KVSEL_SELECT_1WG(512, 1);
+    else KVSEL_SELECT_1WG(512, 2);   // beyond 1024 slices: later batches reloaded
+#undef KVSEL_SELECT_1WG
     return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   }
   SelArgs a;

@@ -124,9 +124,9 @@ kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* 
                          float* raw_scores, float* pooled, int32_t pool_kernel,
                          void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of scratch kvsel_select needs for `desc` and `budget` (0 when the
- * rows are short enough for the single-workgroup kernel, or on invalid
- * arguments).  Long rows use a sliced multi-workgroup radix select whose
+/* Bytes of scratch kvsel_select needs for `desc` and `budget` (0 when rows
+ * have up to about 16384 candidates and fit the single-workgroup kernel, or on
+ * invalid arguments).  Long rows use a sliced multi-workgroup radix select whose
  * scratch is about 8 bytes per candidate position plus per-slice counters. */
 size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget);
 
@@ -152,9 +152,10 @@ kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t b
 /* (kvsel_select: ws is device scratch of >= kvsel_select_workspace(desc,
  * budget) bytes, may be NULL when that is 0; else KVSEL_ERR_WORKSPACE.) */
 
-/* Bytes of scratch kvsel_select_adaptive needs (0 when total_budget is 0 or
- * the arguments are invalid): about 8 bytes per candidate position of every
- * KV head plus per-slice counters. */
+/* Bytes of scratch kvsel_select_adaptive needs: 0 when a sequence has up to about
+ * 16384 candidates (one workgroup per sequence), when total_budget is 0, or
+ * on invalid arguments; otherwise about 8 bytes per candidate position of
+ * every KV head plus per-slice counters. */
 size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget);
 
 /*
@@ -178,9 +179,9 @@ size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_bud
  *             [head_off[b,hk], head_off[b,hk+1])
  *   head_off  [Bt, Hkv+1] int32 out; head_off[b,0] = 0, head_off[b,Hkv] = n_keep
  *   ws        device scratch of >= kvsel_select_adaptive_workspace bytes
- * Needs Hkv*S < 2^31 and at most 2048 slices of 4096 candidates per
- * sequence (KVSEL_ERR_UNSUPPORTED otherwise).  Selection is exact as in
- * kvsel_select.
+ * Needs Hkv <= 64, Hkv*S < 2^31 and, when a sequence has more than 16384
+ * candidates, at most 2048 slices of 4096 candidates per sequence
+ * (KVSEL_ERR_UNSUPPORTED otherwise).  Selection is exact as in kvsel_select.
  */
 kvsel_status kvsel_select_adaptive(const kvsel_desc* desc, const float* pooled,
                                    int32_t total_budget, int32_t* idx, int32_t* head_off,

@@ -119,15 +119,24 @@ def test_select_adaptive_checks(kv):
     assert sel(10, p=None) == kv.ERR_ARG
     assert sel(10, o=None) == kv.ERR_ARG
     assert sel(10, i=FAKE + 4) == kv.ERR_ARG
-    need = L.kvsel_select_adaptive_workspace(ctypes.byref(d), 10)
-    assert need >= 8 * ncand * 8
-    assert sel(10, n=need - 1) == kv.ERR_WORKSPACE
-    assert L.kvsel_select_adaptive_workspace(ctypes.byref(d), 0) == 0
+    # a sequence whose 8 heads fit one workgroup needs no scratch
+    small = _desc(kv, seq_len=2000, obs_window=40)
+    assert L.kvsel_select_adaptive_workspace(ctypes.byref(small), 10) == 0
+    long_d = _desc(kv, seq_len=131072, obs_window=64)
+    need = L.kvsel_select_adaptive_workspace(ctypes.byref(long_d), 10)
+    assert need >= 8 * 131008 * 8
+    assert L.kvsel_select_adaptive(ctypes.byref(long_d), FAKE, 10, FAKE, FAKE, FAKE, need - 1,
+                                   None) == kv.ERR_WORKSPACE
+    assert L.kvsel_select_adaptive_workspace(ctypes.byref(long_d), 0) == 0
     # more than 2048 slices of 4096 candidates in one sequence
     big = _desc(kv, seq_len=1 << 21, obs_window=64)
     assert L.kvsel_select_adaptive_workspace(ctypes.byref(big), 100) == 0
     assert L.kvsel_select_adaptive(ctypes.byref(big), FAKE, 100, FAKE, FAKE, FAKE, 1 << 40,
                                    None) == kv.ERR_UNSUPPORTED
+    many = _desc(kv, n_q_heads=65, n_kv_heads=65, seq_len=1000)
+    for T in (0, 10):
+        assert L.kvsel_select_adaptive(ctypes.byref(many), FAKE, T, FAKE, FAKE, FAKE, 1 << 40,
+                                       None) == kv.ERR_UNSUPPORTED
 
 
 def test_compact_flat_checks(kv):
