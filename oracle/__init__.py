@@ -25,6 +25,8 @@ from .reference import (  # noqa: F401
     compact_flat,
     compact_rows,
     layer_end_compress,
+    kara_scores,
+    kara_select,
     window_sums,
     route_tiers,
     quant_int4,

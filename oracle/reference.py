@@ -229,6 +229,73 @@ def layer_end_compress(q_obs, k, v, *, budget, window, pool_kernel, n_sink=0,
 
 
 # ---------------------------------------------------------------------------
+# Kara: sliding-window bidirectional scoring and Token2Chunk
+# ---------------------------------------------------------------------------
+
+def kara_scores(q_win: np.ndarray, k_comp: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """Importance A_j of each compressible key of a decode window   (Kara,
+    Section 3.1, Eq. 4): every query of the window (bidirectional: no causal
+    mask) takes a softmax over the compressible keys (W minus U) only, and A_j sums
+    the weights key j receives over the window's queries and, per KV head,
+    over the GQA group (the same group reading as head_scores).
+
+    q_win: [Bt, Hq, |W|, D]; k_comp: [Bt, Hkv, |W|-|U|, D].  Returns
+    [Bt, Hkv, |W|-|U|] float64.
+    """
+    return head_scores(q_win, k_comp, causal=False, scale=scale)
+
+
+def kara_select(A: np.ndarray, keep: int, gamma: int, alpha: int, buffer: int) -> np.ndarray:
+    """Retained window positions per (b, h_kv)   (Kara Section 3.2, Eqs. 5-8,
+    and the fill-up rule that follows them).
+
+    A: [Bt, Hkv, n] importance of the compressible positions 0..n-1 (the
+    buffer U occupies n..n+buffer-1 and is always kept).
+      I  = the `keep` largest A (Eq. 5; ties -> lower position), ascending;
+      R_k = (A[I[k]] + A[I[k+1]]) * (I[k+1] - I[k] - 1)  for consecutive
+            picks with I[k+1] - I[k] <= gamma (Eq. 6), evaluated in float32
+            because the kernel decides in float32;
+      P  = the floor(alpha / gamma) largest R_k (Eq. 7; ties -> lower k);
+      I^ = I plus the interior positions of the chunks in P (Eq. 8);
+      fill-up: while fewer than alpha positions were added, add the highest-A
+            positions not yet kept (ties -> lower position).
+    Returns int32 [Bt, Hkv, min(n, keep + alpha) + buffer], ascending.
+    """
+    Bt, H, n = A.shape
+    if not (0 <= keep <= n and gamma >= 1 and alpha >= 0 and buffer >= 0):
+        raise ValueError("invalid Kara parameters")
+    n_out = min(n, keep + alpha)
+    out = np.empty((Bt, H, n_out + buffer), dtype=np.int32)
+    pos = np.arange(n)
+    for b in range(Bt):
+        for h in range(H):
+            a = A[b, h]
+            order = np.lexsort((pos, -a))
+            chosen = np.zeros(n, bool)
+            chosen[order[:keep]] = True
+            I = np.flatnonzero(chosen)
+            a32 = a.astype(np.float32)
+            chunks = []
+            for k in range(len(I) - 1):
+                gap = int(I[k + 1] - I[k])
+                if gap <= gamma:
+                    r = np.float32(np.float32(a32[I[k]] + a32[I[k + 1]]) * np.float32(gap - 1))
+                    chunks.append((-float(r), k))
+            chunks.sort()
+            added = np.zeros(n, bool)
+            for _, k in chunks[:alpha // gamma]:
+                added[I[k] + 1:I[k + 1]] = True
+            n_add = int(added.sum())
+            rest = [j for j in order if not chosen[j] and not added[j]]
+            for j in rest[:max(0, alpha - n_add)]:
+                added[j] = True
+            keep_pos = np.flatnonzero(chosen | added)
+            assert keep_pos.size == n_out
+            out[b, h] = np.concatenate([keep_pos, np.arange(n, n + buffer)])
+    return out
+
+
+# ---------------------------------------------------------------------------
 # QEvict-style window tiers
 # ---------------------------------------------------------------------------
 

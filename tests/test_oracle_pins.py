@@ -302,6 +302,87 @@ def test_compact_flat_rows_follow_their_head():
             assert out[b, r].tobytes() == kb[b, h, idx[b, r]].tobytes()
 
 
+# --------------------------------------------------------------- Kara ----
+
+def test_kara_scores_brute_force_more_queries_than_keys():
+    """Kara Eq. 4 written out with math.exp: |W| = 7 window queries (two
+    query heads per KV head) against the n = 5 compressible keys, no mask."""
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((1, 4, 7, 8))
+    k = rng.standard_normal((1, 2, 5, 8))
+    A = oracle.kara_scores(q, k)
+    for hk in range(2):
+        for j in range(5):
+            tot = 0.0
+            for h in (2 * hk, 2 * hk + 1):
+                for i in range(7):
+                    num = math.exp(sum(q[0, h, i, d] * k[0, hk, j, d] for d in range(8)) / math.sqrt(8))
+                    den = sum(math.exp(sum(q[0, h, i, d] * k[0, hk, jj, d] for d in range(8))
+                                       / math.sqrt(8)) for jj in range(5))
+                    tot += num / den
+            assert abs(A[0, hk, j] - tot) <= 1e-12 * tot
+        # every window query's weights over the compressible keys sum to one
+        assert abs(A[0, hk].sum() - 2 * 7) <= 1e-12
+
+
+def test_kara_scores_identical_keys_are_uniform():
+    q = np.random.default_rng(52).standard_normal((1, 3, 9, 4))
+    k = np.tile(np.array([0.3, -1.0, 2.0, 0.5]), (1, 1, 6, 1))
+    assert np.allclose(oracle.kara_scores(q, k), 3 * 9 / 6, rtol=1e-13)
+
+
+def test_kara_select_worked_example():
+    """TopK 4 -> I = {0, 3, 5, 9}; chunk (0,3) scores (0.9+0.8)*2, chunk (3,5)
+    (0.8+0.7)*1, chunk (5,9) is wider than gamma = 3; floor(4/3) = 1 chunk
+    adds {1, 2}; fill-up adds the two best remaining, 10 and 6; the buffer
+    (12, 13) is kept."""
+    A = np.array([[[0.9, 0.1, 0.2, 0.8, 0.05, 0.7, 0.3, 0.01, 0.02, 0.6, 0.4, 0.03]]])
+    out = oracle.kara_select(A, keep=4, gamma=3, alpha=4, buffer=2)
+    assert out.tolist() == [[[0, 1, 2, 3, 5, 6, 9, 10, 12, 13]]]
+
+
+def test_kara_select_gamma_one_reduces_to_top_k():
+    """gamma = 1 leaves no chunk interior, so the fill-up makes the result the
+    plain top-(keep + alpha) set."""
+    rng = np.random.default_rng(53)
+    A = rng.random((2, 3, 40))
+    out = oracle.kara_select(A, keep=10, gamma=1, alpha=6, buffer=0)
+    for b in range(2):
+        for h in range(3):
+            want = sorted(sorted(range(40), key=lambda j: (-A[b, h, j], j))[:16])
+            assert out[b, h].tolist() == want
+
+
+def test_kara_select_ties_and_edges():
+    flat = np.full((1, 1, 10), 0.5)
+    # all equal: I = first positions, chunks add nothing, fill-up by position
+    assert oracle.kara_select(flat, 3, 4, 2, 1).tolist() == [[[0, 1, 2, 3, 4, 10]]]
+    rng = np.random.default_rng(54)
+    A = rng.random((1, 2, 30))
+    # alpha = 0: exactly the top-k set, ascending
+    out = oracle.kara_select(A, 7, 8, 0, 3)
+    for h in range(2):
+        assert out[0, h, :7].tolist() == sorted(np.argsort(-A[0, h], kind="stable")[:7].tolist())
+        assert out[0, h, 7:].tolist() == [30, 31, 32]
+    # keep everything
+    assert oracle.kara_select(A, 30, 8, 16, 0)[0, 0].tolist() == list(range(30))
+    # near the end: fewer unselected positions than alpha
+    assert oracle.kara_select(A, 25, 8, 16, 0).shape == (1, 2, 30)
+
+
+def test_kara_select_chunks_are_contiguous_and_bounded():
+    rng = np.random.default_rng(55)
+    A = rng.random((3, 4, 448)) ** 4
+    keep, gamma, alpha = 179, 8, 32
+    out = oracle.kara_select(A, keep, gamma, alpha, 64)
+    for b in range(3):
+        for h in range(4):
+            row = out[b, h]
+            assert row.size == keep + alpha + 64 and (np.diff(row) > 0).all()
+            top = set(sorted(range(448), key=lambda j: (-A[b, h, j], j))[:keep])
+            assert top <= set(row.tolist())
+
+
 # ---------------------------------------------------------------- gather ----
 
 def test_compact_rows_are_byte_identical():
