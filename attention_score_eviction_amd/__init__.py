@@ -14,6 +14,7 @@ There is no CPU fallback: without the built library every call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -54,6 +55,18 @@ class TierDesc(ctypes.Structure):
     ]
 
 
+class KaraDesc(ctypes.Structure):
+    """kvsel_kara_desc."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("buffer", ctypes.c_int32),
+        ("keep", ctypes.c_int32), ("gamma", ctypes.c_int32),
+        ("alpha", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -86,6 +99,13 @@ def lib() -> ctypes.CDLL:
     L.kvsel_select_adaptive.restype = ctypes.c_int
     L.kvsel_compact_flat.argtypes = [DP, P, P, P, P, I32, P, P, P]
     L.kvsel_compact_flat.restype = ctypes.c_int
+    KP = ctypes.POINTER(KaraDesc)
+    L.kvsel_kara_score_workspace.argtypes = [KP]
+    L.kvsel_kara_score_workspace.restype = SZ
+    L.kvsel_kara_score.argtypes = [KP, P, P, P, P, SZ, P]
+    L.kvsel_kara_score.restype = ctypes.c_int
+    L.kvsel_kara_select.argtypes = [KP, P, P, P]
+    L.kvsel_kara_select.restype = ctypes.c_int
     L.kvsel_route_tiers_workspace.argtypes = [TP]
     L.kvsel_route_tiers_workspace.restype = SZ
     L.kvsel_route_tiers.argtypes = [TP, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P]
@@ -283,6 +303,59 @@ def layer_end_compress_adaptive(q_obs: torch.Tensor, k: torch.Tensor, v: torch.T
     return {"s": raw, "p": pooled, "idx": idx, "head_off": off, "k_hat": k_hat, "v_hat": v_hat}
 
 
+def kara_desc(q_win: torch.Tensor, k_win: torch.Tensor, *, buffer: int, keep: int, gamma: int,
+              alpha: int, scale: float = 0.0) -> KaraDesc:
+    Bt, Hq, Wn, D = q_win.shape
+    return KaraDesc(Bt, Hq, k_win.shape[1], D, Wn, int(buffer), int(keep), int(gamma),
+                    int(alpha), _dtype_code(k_win), float(scale))
+
+
+def kara_keep(window: int, buffer: int, ratio: float) -> int:
+    """|I| = ceil(r * (|W| - |U|))   (Kara Eq. 5)."""
+    return int(math.ceil(ratio * (window - buffer) - 1e-9))
+
+
+def kara_score(q_win: torch.Tensor, k_win: torch.Tensor, kd: KaraDesc, *,
+               scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """kvsel_kara_score: importance [Bt,Hkv,window-buffer] float32."""
+    n = kd.window - kd.buffer
+    if scores is None:
+        scores = torch.empty((kd.batch, kd.n_kv_heads, n), dtype=torch.float32,
+                             device=k_win.device)
+    nbytes = int(lib().kvsel_kara_score_workspace(ctypes.byref(kd)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k_win.device)
+    st = lib().kvsel_kara_score(ctypes.byref(kd), _ptr(q_win), _ptr(k_win), _ptr(scores),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kvsel_kara_score")
+    return scores
+
+
+def kara_select(scores: torch.Tensor, kd: KaraDesc, *, idx: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """kvsel_kara_select: window-relative kept positions [Bt,Hkv,n_out+buffer]."""
+    n = kd.window - kd.buffer
+    n_out = min(n, kd.keep + kd.alpha)
+    if idx is None:
+        idx = torch.empty((kd.batch, kd.n_kv_heads, n_out + kd.buffer), dtype=torch.int32,
+                          device=scores.device)
+    st = lib().kvsel_kara_select(ctypes.byref(kd), _ptr(scores), _ptr(idx), _stream(stream))
+    _check(st, "kvsel_kara_select")
+    return idx
+
+
+def kara_compress(q_win: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor, *,
+                  buffer: int, ratio: float, gamma: int, alpha: int, stream=None) -> dict:
+    """One Kara window compression: score -> Token2Chunk select -> gather."""
+    kd = kara_desc(q_win, k_win, buffer=buffer, keep=kara_keep(q_win.shape[2], buffer, ratio),
+                   gamma=gamma, alpha=alpha)
+    A = kara_score(q_win, k_win, kd, stream=stream)
+    idx = kara_select(A, kd, stream=stream)
+    k_hat, v_hat = compact(k_win, v_win, idx, stream=stream)
+    return {"A": A, "idx": idx, "k_hat": k_hat, "v_hat": v_hat, "desc": kd}
+
+
 @dataclass
 class TierOutputs:
     tier: torch.Tensor
@@ -335,4 +408,5 @@ def route_tiers(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, n_ful
 
 EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_select_workspace",
            "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers",
-           "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat")
+           "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat",
+           "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select")

@@ -57,6 +57,39 @@ kvsel_status check_adaptive(const kvsel_desc* d, int32_t total_budget) {
   return KVSEL_OK;
 }
 
+kvsel_status check_kara_desc(const kvsel_kara_desc* k) {
+  if (!k) return KVSEL_ERR_ARG;
+  if (k->batch < 1 || k->n_q_heads < 1 || k->n_kv_heads < 1) return KVSEL_ERR_ARG;
+  if (k->n_q_heads % k->n_kv_heads != 0) return KVSEL_ERR_ARG;
+  if ((int64_t)k->batch * k->n_kv_heads > 65535) return KVSEL_ERR_ARG;
+  if (k->window < 2 || k->window > kMaxSeq || k->buffer < 0 || k->buffer >= k->window)
+    return KVSEL_ERR_ARG;
+  const int n = k->window - k->buffer;
+  if (k->keep < 0 || k->keep > n || k->gamma < 1 || k->alpha < 0) return KVSEL_ERR_ARG;
+  if (k->dtype != KVSEL_BF16 && k->dtype != KVSEL_F32) return KVSEL_ERR_ARG;
+  if (!(k->scale >= 0.f) || isinf(k->scale)) return KVSEL_ERR_ARG;
+  if ((int64_t)(k->n_q_heads / k->n_kv_heads) * k->window > (1 << 20)) return KVSEL_ERR_ARG;
+  if (k->head_dim != 64 && k->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
+  return KVSEL_OK;
+}
+
+// Scoring problem of a Kara window: every window token queries the
+// compressible keys (the first window - buffer rows of each head), no mask.
+kvsel_desc kara_score_desc(const kvsel_kara_desc& k) {
+  kvsel_desc d;
+  d.batch = k.batch;
+  d.n_q_heads = k.n_q_heads;
+  d.n_kv_heads = k.n_kv_heads;
+  d.head_dim = k.head_dim;
+  d.seq_len = k.window - k.buffer;
+  d.obs_window = k.window;
+  d.n_sink = 0;
+  d.causal = 0;
+  d.dtype = (kvsel_dtype)k.dtype;
+  d.scale = k.scale;
+  return d;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,7 +128,7 @@ kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* 
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
   return launch_score(*desc, p, q_obs, k, raw_scores, pooled, pool_kernel, (char*)ws,
-                      (hipStream_t)stream);
+                      (hipStream_t)stream, desc->seq_len);
 }
 
 size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget) {
@@ -168,6 +201,40 @@ kvsel_status kvsel_compact_flat(const kvsel_desc* desc, const void* k, const voi
     return KVSEL_ERR_ARG;
   return launch_compact_flat(*desc, k, v, idx, head_off, (int)n_keep, k_out, v_out,
                              (hipStream_t)stream);
+}
+
+size_t kvsel_kara_score_workspace(const kvsel_kara_desc* kdesc) {
+  if (check_kara_desc(kdesc) != KVSEL_OK) return 0;
+  const kvsel_desc d = kara_score_desc(*kdesc);
+  ScorePlan p;
+  plan_score(d, &p);
+  return p.total;
+}
+
+kvsel_status kvsel_kara_score(const kvsel_kara_desc* kdesc, const void* q_win, const void* k_win,
+                              float* scores, void* ws, size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_kara_desc(kdesc);
+  if (st != KVSEL_OK) return st;
+  if (!q_win || !k_win || !scores) return KVSEL_ERR_ARG;
+  if (!aligned16(q_win) || !aligned16(k_win) || !aligned16(scores)) return KVSEL_ERR_ARG;
+  const kvsel_desc d = kara_score_desc(*kdesc);
+  ScorePlan p;
+  plan_score(d, &p);
+  if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVSEL_ERR_ARG;
+  return launch_score(d, p, q_win, k_win, scores, nullptr, 1, (char*)ws, (hipStream_t)stream,
+                      kdesc->window);
+}
+
+kvsel_status kvsel_kara_select(const kvsel_kara_desc* kdesc, const float* scores, int32_t* idx,
+                               void* stream) {
+  const kvsel_status st = check_kara_desc(kdesc);
+  if (st != KVSEL_OK) return st;
+  if (!scores || !idx) return KVSEL_ERR_ARG;
+  const int n = kdesc->window - kdesc->buffer;
+  if (!kara_supported(n)) return KVSEL_ERR_UNSUPPORTED;
+  return launch_kara_select(scores, idx, kdesc->batch * kdesc->n_kv_heads, n, kdesc->buffer,
+                            kdesc->keep, kdesc->gamma, kdesc->alpha, (hipStream_t)stream);
 }
 
 size_t kvsel_route_tiers_workspace(const kvsel_tier_desc* desc) {

@@ -45,12 +45,16 @@ struct ScoreArgs {
   float* lse;          // [nheads][GWr] row log2-sum-exp
   float* s_out;        // [ngroups][nheads][S] (ngroups == 1: the raw scores)
   int Hq, Hkv, G, W, S, GW, GWr, qcap, chunk, nchunk, causal;
+  int kstride;         // key rows between consecutive KV heads in k (>= S)
   float c;             // scale * log2(e)
 };
 
+// kstride: key rows per KV head in k (the head's first seq_len rows are
+// scored); pooled may be null (no max-pool launched) for callers that only
+// need the raw scores.
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
-                          hipStream_t stream);
+                          hipStream_t stream, int kstride);
 // Selection groups: hg consecutive KV heads of a sequence share one budget
 // (hg = 1: per-head budget; hg = n_kv_heads: head-adaptive budget).
 constexpr int kMaxGroupSlices = 2048;
@@ -73,6 +77,10 @@ kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
 kvsel_status launch_compact_flat(const kvsel_desc& d, const void* k, const void* v,
                                  const int32_t* idx, const int32_t* head_off, int n_keep,
                                  void* k_out, void* v_out, hipStream_t stream);
+
+bool kara_supported(int n);
+kvsel_status launch_kara_select(const float* scores, int32_t* idx, int rows, int n, int buffer,
+                                int keep, int gamma, int alpha, hipStream_t stream);
 
 struct TierPlan {
   int nheads, nwin;

@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
   const int nrows = min(a.qcap, a.GW - row0);
   const int S = a.S;
   const float c = a.c;
-  const char* kh = (const char*)((const T*)a.k + (size_t)head * S * D);
+  const char* kh = (const char*)((const T*)a.k + (size_t)head * a.kstride * D);
   const int k0 = chunk * a.chunk;
   const int kend = min(S, k0 + a.chunk);
   const int mask_from = a.causal ? (S - a.W + 1) : S;
@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(NW * 64) score_pass2(ScoreArgs a) {
   const int nrows = min(a.qcap, a.GW - row0);
   const int S = a.S;
   const float c = a.c;
-  const char* kh = (const char*)((const T*)a.k + (size_t)head * S * D);
+  const char* kh = (const char*)((const T*)a.k + (size_t)head * a.kstride * D);
   const int k0 = chunk * a.chunk;
   const int kend = min(S, k0 + a.chunk);
   const int mask_from = a.causal ? (S - a.W + 1) : S;
@@ -525,7 +525,7 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
 
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, int kstride) {
   ScoreArgs a;
   a.q = q;
   a.k = k;
@@ -538,6 +538,7 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   a.G = p.G;
   a.W = d.obs_window;
   a.S = d.seq_len;
+  a.kstride = kstride;
   a.GW = p.GW;
   a.GWr = p.GWr;
   a.qcap = p.qcap;
@@ -561,6 +562,7 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
     hipLaunchKernelGGL(score_group_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                        a.s_out, s, n, p.ngroups);
   }
+  if (!pooled) return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
   hipLaunchKernelGGL(maxpool_kernel, dim3((d.seq_len + 255) / 256, p.nheads), dim3(256), 0, stream,
                      s, pooled, d.seq_len, lo, hi, (pool_kernel - 1) / 2);

@@ -222,6 +222,64 @@ kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
                            const int32_t* idx, int32_t n_keep, void* k_out, void* v_out,
                            void* stream);
 
+/*
+ * Kara decode-window compression (Kara, "Kara: Efficient Reasoning LLM
+ * Serving via Sliding-Window KV Cache Compression", Section 3).  A window of
+ * `window` recent tokens per (sequence, KV head); its last `buffer` tokens
+ * (U) are never compressed; the first n = window - buffer are the
+ * compressible region.
+ */
+typedef struct {
+  int32_t batch;       /* Bt >= 1 */
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t window;      /* |W| >= 2 */
+  int32_t buffer;      /* |U|, 0 <= buffer < window */
+  int32_t keep;        /* size of I, ceil(r * (window - buffer)) for ratio r (Eq. 5) */
+  int32_t gamma;       /* maximum chunk length, >= 1 (Eq. 7) */
+  int32_t alpha;       /* chunk budget: extra positions added, >= 0 (Eq. 7, fill-up) */
+  int32_t dtype;       /* kvsel_dtype of q and k */
+  float scale;         /* logit scale; 0 => 1/sqrt(head_dim) */
+} kvsel_kara_desc;
+
+/* Bytes of scratch kvsel_kara_score needs (0 on invalid arguments). */
+size_t kvsel_kara_score_workspace(const kvsel_kara_desc* desc);
+
+/*
+ * kvsel_kara_score -- sliding-window bidirectional importance (Kara Eq. 4):
+ * scores[b,hk,j] = sum over the window queries i of the G query heads of KV
+ * head hk of softmax_j'(<Q_i, K_j'> * scale) at j, the softmax running over
+ * the compressible keys j' < n only, with no causal mask.
+ *
+ *   q_win   [Bt,Hq,window,D] dtype, device: the queries of every window token
+ *   k_win   [Bt,Hkv,window,D] dtype, device: the window's keys (rows >= n,
+ *           the buffer, are not read)
+ *   scores  [Bt,Hkv,n] float32 out, device
+ * Same kernels and numerics as kvsel_score (fp32 products and sums).
+ */
+kvsel_status kvsel_kara_score(const kvsel_kara_desc* desc, const void* q_win, const void* k_win,
+                              float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_kara_select -- Token2Chunk selection (Kara Eqs. 5-8 and the fill-up
+ * rule after them).  Per (b, hk): I = the `keep` highest scores (ties to the
+ * lower position); for consecutive members of I (ascending) at most gamma
+ * apart, chunk k scores (A[I[k]] + A[I[k+1]]) * (I[k+1] - I[k] - 1) in fp32;
+ * the floor(alpha/gamma) best chunks (ties to the lower k) add their interior
+ * positions; then, while fewer than alpha positions were added, the best
+ * remaining positions by score are added (ties to the lower position).
+ *
+ *   scores  [Bt,Hkv,n] float32, device (kvsel_kara_score), finite
+ *   idx     [Bt,Hkv,min(n, keep+alpha) + buffer] int32 out, device: the kept
+ *           compressible positions ascending, then n..window-1 (the buffer);
+ *           window-relative, so kvsel_compact with seq_len = window gathers
+ *           the compressed window
+ * n = window - buffer must be at most 2048 (KVSEL_ERR_UNSUPPORTED).
+ */
+kvsel_status kvsel_kara_select(const kvsel_kara_desc* desc, const float* scores, int32_t* idx,
+                               void* stream);
+
 /* Shape of a window-tier routing problem (QEvict Sections 4.1-4.3). */
 typedef struct {
   int32_t batch;       /* Bt >= 1 */

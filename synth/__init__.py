@@ -196,6 +196,24 @@ def _apply_spans(k32: np.ndarray, spec: LayerSpec, rng) -> None:
                 k32[b, h, a:a + L] = (spec.span_boost * nk * u[None, :]).astype(np.float32)
 
 
+def decode_window(seed: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
+                  head_dim: int, dtype: str = "bf16") -> dict:
+    """Queries, keys and values of the most recent `window` decode tokens:
+    Q [Bt,Hq,W,D], K and V [Bt,Hkv,W,D], fp32 N(0,1) rounded to the storage
+    dtype.  Structure: per (sequence, KV head), round(0.05 W) seeded-uniform
+    window positions get their key scaled by 2, so a few keys stand out."""
+    base = (900, seed)
+    q32 = _normal(base + (TENSOR_Q,), (batch, n_q_heads, window, head_dim))
+    k32 = _normal(base + (TENSOR_K,), (batch, n_kv_heads, window, head_dim))
+    v32 = _normal(base + (TENSOR_V,), (batch, n_kv_heads, window, head_dim))
+    rng = _rng(base + (TENSOR_PROMOTE,))
+    n_boost = int(round(0.05 * window))
+    for b in range(batch):
+        for h in range(n_kv_heads):
+            k32[b, h, rng.choice(window, size=n_boost, replace=False)] *= np.float32(2.0)
+    return {"q": _round(q32, dtype), "k": _round(k32, dtype), "v": _round(v32, dtype)}
+
+
 def promote_list(config_id: int, n_rows: int, n_quant: int, n_promote: int,
                  layer: int = 0) -> np.ndarray:
     """Seeded-uniform choice (without replacement, ascending) of n_promote of

@@ -151,6 +151,28 @@ def test_compact_flat_checks(kv):
     assert c(10, vo=None) == kv.ERR_ARG
 
 
+def test_kara_checks(kv):
+    L = kv.lib()
+    K = lambda **kw: kv.KaraDesc(**{**dict(batch=2, n_q_heads=40, n_kv_heads=8, head_dim=128,  # noqa
+                                            window=512, buffer=64, keep=180, gamma=8, alpha=32,
+                                            dtype=kv.BF16, scale=0.0), **kw})
+    good = K()
+    need = L.kvsel_kara_score_workspace(ctypes.byref(good))
+    assert need > 0
+    score = lambda d, ws_bytes=need: L.kvsel_kara_score(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE,  # noqa
+                                                        ws_bytes, None)
+    sel = lambda d: L.kvsel_kara_select(ctypes.byref(d), FAKE, FAKE, None)  # noqa
+    for bad in (K(buffer=512), K(buffer=-1), K(keep=449), K(keep=-1), K(gamma=0), K(alpha=-1),
+                K(window=1), K(n_q_heads=30), K(dtype=5), K(scale=-1.0)):
+        assert score(bad, 1 << 30) == kv.ERR_ARG and sel(bad) == kv.ERR_ARG
+    assert score(K(head_dim=96), 1 << 30) == kv.ERR_UNSUPPORTED
+    assert score(good, need - 1) == kv.ERR_WORKSPACE
+    assert sel(K(window=4000, buffer=64, keep=100)) == kv.ERR_UNSUPPORTED   # n > 2048
+    assert L.kvsel_kara_select(ctypes.byref(good), None, FAKE, None) == kv.ERR_ARG
+    # the window queries need no more scratch than O(Hkv * n + rows * chunks)
+    assert need < 64 * 1024 * 1024
+
+
 def test_compact_checks(kv):
     L = kv.lib()
     d = _desc(kv)

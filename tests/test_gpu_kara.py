@@ -1,0 +1,134 @@
+"""Parity of the Kara decode-window path (kvsel_kara_score, kvsel_kara_select,
+then kvsel_compact on the window) with the CPU oracle.
+
+Scores: within 1e-3 relative of the oracle's float64 definition.
+Selection: bit-exact with the oracle on identical float32 scores.  End to
+end (GPU scores vs oracle scores), a row must match the oracle exactly
+unless one of the oracle's own decisions (the keep-th score, the chunk cut,
+the fill-up cut) is a near tie, within 1e-5 relative; every row is checked
+for size, order, the buffer and the clearly-kept positions.  Gathered rows
+are byte copies of the window rows their indices name.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_scores_close, dev_tensor, host_bits, rows_gathered
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _kvsel():
+    import attention_score_eviction_amd as kvsel
+    kvsel.lib()
+    return kvsel
+
+
+def _ties_kind(rng, kind, shape):
+    if kind == "uniform":
+        return rng.random(shape).astype(np.float32)
+    if kind == "quarters":
+        return (rng.integers(0, 6, size=shape) * 0.25).astype(np.float32)
+    if kind == "peaks":
+        p = (rng.random(shape) * 0.01).astype(np.float32)
+        p[..., ::9] += np.float32(1.0)
+        return p
+    return np.full(shape, 0.5, np.float32)
+
+
+@pytest.mark.parametrize("seed,n,buffer,keep,gamma,alpha,kind", [
+    (0, 448, 64, 180, 8, 32, "uniform"),
+    (1, 448, 64, 90, 8, 16, "quarters"),
+    (2, 320, 64, 64, 8, 32, "peaks"),
+    (3, 200, 0, 40, 4, 12, "flat"),
+    (4, 17, 3, 5, 3, 4, "uniform"),
+    (5, 448, 32, 0, 8, 32, "uniform"),
+    (6, 448, 32, 448, 8, 32, "uniform"),
+    (7, 300, 10, 100, 1, 20, "uniform"),
+    (8, 2048, 16, 700, 8, 32, "uniform"),
+    (9, 1, 1, 1, 8, 32, "uniform"),
+])
+def test_kara_select_exact_on_identical_scores(seed, n, buffer, keep, gamma, alpha, kind):
+    kvsel = _kvsel()
+    rng = np.random.default_rng(300 + seed)
+    Bt, Hkv = 3, 4
+    A = _ties_kind(rng, kind, (Bt, Hkv, n))
+    print(f"case kara select seed {seed} n={n} keep={keep} gamma={gamma} alpha={alpha}",
+          flush=True)
+    kd = kvsel.KaraDesc(Bt, Hkv, Hkv, 128, n + buffer, buffer, keep, gamma, alpha, kvsel.BF16,
+                        0.0)
+    got = kvsel.kara_select(torch.from_numpy(A).cuda(), kd).cpu().numpy()
+    want = oracle.kara_select(A.astype(np.float64), keep, gamma, alpha, buffer)
+    np.testing.assert_array_equal(got, want)
+
+
+def _margins_ok(a, keep, gamma, alpha, rel=1e-5):
+    """True when none of the oracle's three cuts on score row `a` is a near
+    tie: the keep-th score (Eq. 5), the chunk cut (Eq. 7) and the fill-up
+    cut.  Orders inside a kept set do not matter, only the cuts."""
+    n = a.size
+    order = np.lexsort((np.arange(n), -a))
+
+    def gap_ok(vals, k):
+        if k <= 0 or k >= len(vals):
+            return True
+        return abs(vals[k - 1] - vals[k]) > rel * max(abs(vals[k - 1]), 1e-30)
+    if not gap_ok(a[order], keep):
+        return False
+    I = np.sort(order[:keep])
+    a32 = a.astype(np.float32)
+    chunks = sorted(((float(np.float32(a32[I[k]] + a32[I[k + 1]])
+                             * np.float32(I[k + 1] - I[k] - 1)), k)
+                     for k in range(len(I) - 1) if I[k + 1] - I[k] <= gamma),
+                    key=lambda t: (-t[0], t[1]))
+    if not gap_ok([c[0] for c in chunks], alpha // gamma):
+        return False
+    taken = set(I.tolist())
+    for _, k in chunks[:alpha // gamma]:
+        taken.update(range(I[k] + 1, I[k + 1]))
+    need = alpha - (len(taken) - len(I))
+    rest = [a[j] for j in order if j not in taken]
+    return gap_ok(rest, need)
+
+
+@pytest.mark.parametrize("shape,dtype,seed", [
+    # (Bt, Hq, Hkv, window, buffer, D), as Qwen3-14B and R1-Llama-8B decode windows
+    ((4, 40, 8, 512, 64, 128), "bf16", 1),
+    ((2, 32, 8, 384, 32, 128), "bf16", 2),
+    ((2, 8, 2, 256, 32, 64), "bf16", 3),
+    ((1, 4, 2, 97, 13, 64), "f32", 4),
+])
+def test_kara_window_end_to_end(shape, dtype, seed):
+    kvsel = _kvsel()
+    Bt, Hq, Hkv, Wn, U, D = shape
+    x = synth.decode_window(seed, Bt, Hq, Hkv, Wn, D, dtype)
+    q, k, v = (dev_tensor(x[t], dtype) for t in ("q", "k", "v"))
+    ratio, gamma, alpha = 0.4, 8, 32
+    print(f"case kara window seed {seed} shape {shape} {dtype}", flush=True)
+    out = kvsel.kara_compress(q, k, v, buffer=U, ratio=ratio, gamma=gamma, alpha=alpha)
+    torch.cuda.synchronize()
+    n = Wn - U
+    A_ref = oracle.kara_scores(synth.to_f64(x["q"], dtype), synth.to_f64(x["k"], dtype)[:, :, :n])
+    assert_scores_close(out["A"].cpu().numpy(), A_ref, what="Kara importance")
+    keep = out["desc"].keep
+    assert keep == int(np.ceil(ratio * n - 1e-9))
+    want = oracle.kara_select(A_ref, keep, gamma, alpha, U)
+    got = out["idx"].cpu().numpy()
+    assert got.shape == want.shape
+    exact_rows = 0
+    for b in range(Bt):
+        for h in range(Hkv):
+            row = got[b, h]
+            assert (np.diff(row) > 0).all() and row[-U:].tolist() == list(range(n, Wn)) if U \
+                else (np.diff(row) > 0).all()
+            top = np.sort(A_ref[b, h])[::-1]
+            assert set(np.flatnonzero(A_ref[b, h] > top[keep - 1] * (1 + 1e-4)).tolist()) \
+                <= set(row.tolist())
+            if _margins_ok(A_ref[b, h], keep, gamma, alpha):
+                assert row.tolist() == want[b, h].tolist(), (b, h)
+                exact_rows += 1
+    assert exact_rows >= max(1, Bt * Hkv // 4)
+    assert rows_gathered(host_bits(out["k_hat"]), x["k"], got)
+    assert rows_gathered(host_bits(out["v_hat"]), x["v"], got)
