@@ -315,6 +315,10 @@ def kara_keep(window: int, buffer: int, ratio: float) -> int:
     return int(math.ceil(ratio * (window - buffer) - 1e-9))
 
 
+def kara_score_workspace_bytes(kd: KaraDesc) -> int:
+    return int(lib().kvsel_kara_score_workspace(ctypes.byref(kd)))
+
+
 def kara_score(q_win: torch.Tensor, k_win: torch.Tensor, kd: KaraDesc, *,
                scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
@@ -323,7 +327,7 @@ def kara_score(q_win: torch.Tensor, k_win: torch.Tensor, kd: KaraDesc, *,
     if scores is None:
         scores = torch.empty((kd.batch, kd.n_kv_heads, n), dtype=torch.float32,
                              device=k_win.device)
-    nbytes = int(lib().kvsel_kara_score_workspace(ctypes.byref(kd)))
+    nbytes = kara_score_workspace_bytes(kd)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k_win.device)
     st = lib().kvsel_kara_score(ctypes.byref(kd), _ptr(q_win), _ptr(k_win), _ptr(scores),

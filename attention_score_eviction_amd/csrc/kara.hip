@@ -57,32 +57,58 @@ __device__ __forceinline__ uint32_t kara_block_scan(uint32_t v, uint32_t* total,
 // Position states.
 constexpr uint8_t kNone = 0, kTop = 1, kChunk = 2, kFill = 3;
 
+// How many of v[0..n4) are ordered before (x0, j0) and before (x1, j1) by
+// (value desc, index asc); with STATE only entries whose state is kNone
+// count.  Four entries per broadcast LDS read, both probes per read.
+// Padding entries hold -inf (never before a finite value) and a state other
+// than kNone.
+template <bool STATE>
+__device__ __forceinline__ void count_before2(const float* v, const uint8_t* st, int n4, float x0,
+                                              int j0, float x1, int j1, int& r0, int& r1) {
+  int c0 = 0, c1 = 0;
+  for (int i = 0; i < n4; i += 4) {
+    const float4 q = *(const float4*)&v[i];
+    uint32_t sw = 0u;
+    if constexpr (STATE) sw = *(const uint32_t*)&st[i];
+    const float qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = !STATE || ((sw >> (8 * u)) & 0xffu) == kNone;
+      const int ii = i + u;
+      c0 += (ok && (qv[u] > x0 || (qv[u] == x0 && ii < j0))) ? 1 : 0;
+      c1 += (ok && (qv[u] > x1 || (qv[u] == x1 && ii < j1))) ? 1 : 0;
+    }
+  }
+  r0 = c0;
+  r1 = c1;
+}
+
 __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ idx, int n, int buffer, int keep,
     int gamma, int alpha, int n_out) {
-  __shared__ float a[kKaraMax];
-  __shared__ float rk[kKaraMax];       // chunk scores, < 0 when a chunk does not qualify
-  __shared__ int32_t ilist[kKaraMax];  // I in ascending position order
-  __shared__ uint8_t state[kKaraMax];
+  __shared__ __align__(16) float a[kKaraMax];
+  __shared__ __align__(16) float rk[kKaraMax];  // chunk scores, < 0 when a chunk does not qualify
+  __shared__ int32_t ilist[kKaraMax];           // I in ascending position order
+  __shared__ __align__(16) uint8_t state[kKaraMax];
   __shared__ uint32_t wsum[kKaraThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* s = scores + (size_t)row * n;
   int32_t* out = idx + (size_t)row * (n_out + buffer);
-  for (int j = tid; j < n; j += kKaraThreads) {
-    a[j] = s[j];
-    state[j] = kNone;
+  const int n4 = (n + 3) & ~3;
+  for (int j = tid; j < n4; j += kKaraThreads) {
+    a[j] = j < n ? s[j] : -INFINITY;
+    state[j] = j < n ? kNone : kTop;   // padding never counts as a free position
   }
   __syncthreads();
 
   // Eq. 5: rank by (score desc, position asc); the first `keep` form I.
-  for (int j = tid; j < n; j += kKaraThreads) {
-    const float aj = a[j];
-    int r = 0;
-    for (int i = 0; i < n; ++i) {
-      const float ai = a[i];
-      r += (ai > aj) || (ai == aj && i < j);
-    }
-    if (r < keep) state[j] = kTop;
+  for (int base = 0; base < n; base += 2 * kKaraThreads) {
+    const int j0 = base + tid, j1 = j0 + kKaraThreads;
+    const float x0 = j0 < n ? a[j0] : 0.f, x1 = j1 < n ? a[j1] : 0.f;
+    int r0, r1;
+    count_before2<false>(a, state, n4, x0, j0, x1, j1, r0, r1);
+    if (j0 < n && r0 < keep) state[j0] = kTop;
+    if (j1 < n && r1 < keep) state[j1] = kTop;
   }
   __syncthreads();
 
@@ -101,26 +127,31 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   // Eq. 6: chunk k spans (I[k], I[k+1]); it qualifies when its end points are
   // at most gamma apart.  Scores in fp32: (A + A) * interior length.
   const int nchunk = nI > 1u ? (int)nI - 1 : 0;
-  for (int k = tid; k < nchunk; k += kKaraThreads) {
-    const int i0 = ilist[k], i1 = ilist[k + 1];
-    const int gap = i1 - i0;
-    rk[k] = gap <= gamma ? (a[i0] + a[i1]) * (float)(gap - 1) : -1.f;
+  const int nc4 = (nchunk + 3) & ~3;
+  for (int k = tid; k < nc4; k += kKaraThreads) {
+    float r = -INFINITY;   // padding and non-qualifying chunks rank after every qualifying one
+    if (k < nchunk) {
+      const int i0 = ilist[k], i1 = ilist[k + 1];
+      const int gap = i1 - i0;
+      if (gap <= gamma) r = (a[i0] + a[i1]) * (float)(gap - 1);
+    }
+    rk[k] = r;
   }
   __syncthreads();
 
   // Eq. 7: the floor(alpha / gamma) best qualifying chunks (score desc, chunk
-  // asc); Eq. 8: their interiors join the retained set.
+  // asc); Eq. 8: their interiors join the retained set.  A non-qualifying
+  // chunk (-inf) is never counted before a qualifying (finite) one.
   const int want_chunks = alpha / gamma;
-  for (int k = tid; k < nchunk; k += kKaraThreads) {
-    const float rkk = rk[k];
-    if (rkk < 0.f) continue;
-    int r = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const float rc = rk[c];
-      r += rc >= 0.f && ((rc > rkk) || (rc == rkk && c < k));
-    }
-    if (r < want_chunks)
-      for (int j = ilist[k] + 1; j < ilist[k + 1]; ++j) state[j] = kChunk;
+  for (int base = 0; base < nchunk; base += 2 * kKaraThreads) {
+    const int k0 = base + tid, k1 = k0 + kKaraThreads;
+    const float x0 = k0 < nchunk ? rk[k0] : -INFINITY, x1 = k1 < nchunk ? rk[k1] : -INFINITY;
+    int r0, r1;
+    count_before2<false>(rk, state, nc4, x0, k0, x1, k1, r0, r1);
+    if (k0 < nchunk && x0 > -INFINITY && r0 < want_chunks)
+      for (int j = ilist[k0] + 1; j < ilist[k0 + 1]; ++j) state[j] = kChunk;
+    if (k1 < nchunk && x1 > -INFINITY && r1 < want_chunks)
+      for (int j = ilist[k1] + 1; j < ilist[k1 + 1]; ++j) state[j] = kChunk;
   }
   __syncthreads();
 
@@ -137,15 +168,14 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   // ranking reads a state array nobody writes.
   uint32_t fill = 0u;
   if (need > 0) {
-    for (int m = 0, j = tid; j < n; ++m, j += kKaraThreads) {
-      if (state[j] != kNone) continue;
-      const float aj = a[j];
-      int r = 0;
-      for (int i = 0; i < n; ++i) {
-        const float ai = a[i];
-        r += state[i] == kNone && ((ai > aj) || (ai == aj && i < j));
-      }
-      if (r < need) fill |= 1u << m;
+    for (int m = 0, base = 0; base < n; m += 2, base += 2 * kKaraThreads) {
+      const int j0 = base + tid, j1 = j0 + kKaraThreads;
+      const bool f0 = j0 < n && state[j0] == kNone, f1 = j1 < n && state[j1] == kNone;
+      if (!f0 && !f1) continue;
+      int r0, r1;
+      count_before2<true>(a, state, n4, f0 ? a[j0] : 0.f, j0, f1 ? a[j1] : 0.f, j1, r0, r1);
+      if (f0 && r0 < need) fill |= 1u << m;
+      if (f1 && r1 < need) fill |= 1u << (m + 1);
     }
   }
   __syncthreads();

@@ -323,29 +323,36 @@ __global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine the per-chunk partials of each query row (one wave per row, fixed
-// merge tree): lse = max + log2(sum).
+// Combine the per-chunk partials of each query row: lse = max + log2(sum).
+// 2^tpr_log2 consecutive lanes share a row (just enough for about four
+// partials each, so short chunk lists do not leave a wave per row mostly
+// idle); each lane merges its strided partials in order, then a fixed
+// butterfly merges the lanes.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) score_combine(const float2* __restrict__ part,
                                                      float* __restrict__ lse, int nheads,
-                                                     int nchunk, int GW, int GWr) {
-  const int row_id = (blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  if (row_id >= nheads * GW) return;
-  const int head = row_id / GW, r = row_id - head * GW;
-  const float2* p = part + ((size_t)head * GWr + r) * nchunk;
+                                                     int nchunk, int GW, int GWr, int tpr_log2) {
+  const int tpr = 1 << tpr_log2;
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row_id = gid >> tpr_log2;
+  const int sub = (int)(gid & (tpr - 1));
+  const bool valid = row_id < (long)nheads * GW;
+  const int head = valid ? (int)(row_id / GW) : 0;
+  const int r = valid ? (int)(row_id - (long)head * GW) : 0;
   float m = -INFINITY, z = 0.f;
-  for (int ch = lane; ch < nchunk; ch += 64) {
-    const float2 pz = p[ch];
-    lse_merge(m, z, pz.x, pz.y);
+  if (valid) {
+    const float2* p = part + ((size_t)head * GWr + r) * nchunk;
+    for (int ch = sub; ch < nchunk; ch += tpr) {
+      const float2 pz = p[ch];
+      lse_merge(m, z, pz.x, pz.y);
+    }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
+  for (int off = tpr >> 1; off >= 1; off >>= 1) {
     const float mo = __shfl_xor(m, off);
     const float zo = __shfl_xor(z, off);
     lse_merge(m, z, mo, zo);
   }
-  if (lane == 0) lse[(size_t)head * GWr + r] = m + log2f(z);
+  if (valid && sub == 0) lse[(size_t)head * GWr + r] = m + log2f(z);
 }
 
 // ---------------------------------------------------------------------------
@@ -441,9 +448,11 @@ __global__ void __launch_bounds__(256) maxpool_kernel(const float* __restrict__ 
 template <typename T, int D, int NQT, int NW>
 void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
   hipLaunchKernelGGL((score_pass1<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
-  const int n = p.nheads * p.GW;   // rows, one wave each
-  hipLaunchKernelGGL(score_combine, dim3((n + 3) / 4), dim3(256), 0, stream, args.part,
-                     args.lse, p.nheads, p.nchunk, p.GW, p.GWr);
+  int tl = 0;
+  while ((4 << tl) < p.nchunk && tl < 6) ++tl;
+  const long lanes = ((long)p.nheads * p.GW) << tl;
+  hipLaunchKernelGGL(score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
+                     args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl);
   hipLaunchKernelGGL((score_pass2<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 

@@ -15,6 +15,8 @@ Workloads (one JSON line each):
   qwen128k     one Qwen3-14B-shaped layer (40 q / 8 kv heads), 131072 tokens
   sweep64k     32 layers at 65536 tokens, budget 4096 -> 512, one layer resident
   qevict32k    16 x 32768-token caches, 256 decode queries, window tiers
+  kara512      Kara decode-window compression: 64 sequences, Llama-3-8B shape,
+               512-token window, 64-token buffer, r = 40%, gamma 8, alpha 32
   llama8k-adaptive / qwen128k-adaptive
                the same layers with a head-adaptive budget: Hkv*B picks per
                sequence over all KV heads, flattened output with head offsets
@@ -46,9 +48,10 @@ WORKLOADS = {
     "qevict32k": (5, "qevict-decode-tiers-16x32k"),
     "llama8k-adaptive": (2, "llama3-8b-layer-8k-head-adaptive"),
     "qwen128k-adaptive": (4, "qwen3-14b-layer-128k-head-adaptive"),
+    "kara512": (0, "kara-decode-window-64x512"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "common.h"]
+KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "common.h"]
 
 
 def source_hash() -> str:
@@ -337,6 +340,8 @@ def main() -> int:
     import attention_score_eviction_amd as kvsel
 
     cid, wname = WORKLOADS[args.workload]
+    if args.workload == "kara512":
+        return bench_kara(args, kvsel, torch, wname)
     spec = synth.config(cid)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -496,6 +501,80 @@ def bench_tiers(args, kvsel, torch, spec, wname, dev, stream) -> int:
                      "kernel": "kvsel_score", "algorithmic_flops_per_launch": flops},
         "route_tiers_hbm_frac": round(tb / (us["kvsel_route_tiers"] * 1e-6) / 1e9
                                       / HBM_PEAK_GBS, 4),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_kara(args, kvsel, torch, wname) -> int:
+    """Kara decode-window compression of one layer for a decode batch: the
+    window's queries score its compressible keys (no mask), Token2Chunk picks
+    the kept positions, the kept K/V rows are gathered.  Shapes follow the
+    Kara page's settings: |W| = 512, |U| = 64, r = 40%, gamma = 8, alpha = 32,
+    an 8B Llama-shaped layer (32 query / 8 KV heads, D = 128)."""
+    Bt, Hq, Hkv, Wn, D, U, ratio, gamma, alpha = 64, 32, 8, 512, 128, 64, 0.4, 8, 32
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    x = synth.decode_window(7, Bt, Hq, Hkv, Wn, D)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    kd = kvsel.kara_desc(q, k, buffer=U, keep=kvsel.kara_keep(Wn, U, ratio), gamma=gamma,
+                         alpha=alpha)
+    n = Wn - U
+    n_keep = min(n, kd.keep + alpha) + U
+    A = torch.empty((Bt, Hkv, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kvsel.kara_score_workspace_bytes(kd), 1), dtype=torch.uint8,
+                     device=dev)
+    idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
+    k_hat = torch.empty((Bt, Hkv, n_keep, D), dtype=torch.bfloat16, device=dev)
+    v_hat = torch.empty_like(k_hat)
+
+    def score():
+        kvsel.kara_score(q, k, kd, scores=A, workspace=ws, stream=stream)
+
+    def select():
+        kvsel.kara_select(A, kd, idx=idx, stream=stream)
+
+    def compact():
+        kvsel.compact(k, v, idx, k_out=k_hat, v_out=v_hat, stream=stream)
+
+    def step():
+        score()
+        select()
+        compact()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    step_us = event_time_us(torch, stream, step, args.steps)
+    reps = max(args.steps, 50)
+    us = {"kvsel_kara_score": event_time_us(torch, stream, score, reps),
+          "kvsel_kara_select": event_time_us(torch, stream, select, reps),
+          "kvsel_compact": event_time_us(torch, stream, compact, reps)}
+    H = Bt * Hkv
+    ab = {"kvsel_kara_score": Bt * Hq * Wn * D * 2 + 2 * H * n * D * 2 + H * n * 4,
+          "kvsel_kara_select": H * n * 4 + H * n_keep * 4,
+          "kvsel_compact": 2 * 2 * H * n_keep * D * 2 + H * n_keep * 4}
+    path = sum(ab.values())
+    # The scoring contraction has G*|W| = 2048 query rows per key: it is bound
+    # by the matrix cores (and the exponentials), not by HBM.
+    flops = 2 * 2 * Bt * Hq * Wn * n * D
+    tflops = flops / (us["kvsel_kara_score"] * 1e-6) / 1e12
+    out = {
+        "metric": METRIC, "value": round(Bt * Wn / (step_us * 1e-6), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wname, "batch": Bt, "window": Wn, "buffer": U,
+                   "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "keep": kd.keep,
+                   "gamma": gamma, "alpha": alpha, "parallelism": "none"},
+        "path_hbm_frac": round(path / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "path_algorithmic_bytes": path,
+        "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                     "traffic": traffic_for(args.workload, "kvsel_kara_score"),
+                     "kernel": "kvsel_kara_score", "algorithmic_flops_per_launch": flops},
     }
     print(json.dumps(out), flush=True)
     return 0
