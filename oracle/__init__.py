@@ -35,4 +35,13 @@ from .reference import (  # noqa: F401
     pack_nibbles,
     tier_outputs,
     cache_bytes,
+    TIER_FULL,
+    TIER_QUANT,
+    TIER_EVICT,
+    quant_lowbit,
+    pack_codes,
+    unpack_codes,
+    qevict_windows,
+    qevict_init,
+    qevict_step,
 )

@@ -429,3 +429,136 @@ def cache_bytes(n_layers: int, batch: int, n_kv_heads: int, tokens: int,
     """Bytes of a K+V cache: 2 * N * B * H_kv * tokens * D * b
     (TideKV §3, prompt KV size; §4.3 active-layer KV with N = 1)."""
     return 2 * n_layers * batch * n_kv_heads * tokens * head_dim * elem_bytes
+
+
+# ---------------------------------------------------------------------------
+# QEvict: recoverable routing repeated over decode steps
+# ---------------------------------------------------------------------------
+
+TIER_FULL, TIER_QUANT, TIER_EVICT = 0, 1, 2
+
+
+def quant_lowbit(x: np.ndarray, bits: int):
+    """Asymmetric codes of `bits` bits (2 or 4) of one group along axis 0:
+    the int4 rule of quant_int4 with 2^bits - 1 steps between the group's
+    minimum and maximum (QEvict's recoverable tier is INT2 by default, §B.5;
+    §G.3 compares INT4).  float32, fixed operation order, round half to even.
+    """
+    levels = np.float32((1 << bits) - 1)
+    x = np.asarray(x, dtype=np.float32)
+    lo = x.min(axis=0)
+    hi = x.max(axis=0)
+    scale = np.asarray(np.float32(hi - lo) / levels, dtype=np.float32)
+    safe = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    q = np.rint((x - lo).astype(np.float32) / safe).astype(np.float32)
+    q = np.clip(q, 0, levels)
+    q = np.where(scale == 0, np.float32(0.0), q)
+    return q.astype(np.uint8), lo.astype(np.float32), scale
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack `bits`-bit codes along the last axis, 8/bits per byte, channel c
+    at bit offset bits*(c mod (8/bits)) of byte c // (8/bits) (the lowest
+    channel in the lowest bits): [..., D] -> [..., D*bits/8] uint8."""
+    per = 8 // bits
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % per == 0 and int(c.max(initial=0)) < (1 << bits)
+    out = np.zeros(c.shape[:-1] + (c.shape[-1] // per,), dtype=np.uint8)
+    for u in range(per):
+        out |= (c[..., u::per] << np.uint8(bits * u)).astype(np.uint8)
+    return out
+
+
+def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_codes."""
+    per = 8 // bits
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * per,), dtype=np.uint8)
+    for u in range(per):
+        out[..., u::per] = (p >> np.uint8(bits * u)) & np.uint8((1 << bits) - 1)
+    return out
+
+
+def qevict_windows(seq_len: int, n_sink: int, n_recent: int, win: int) -> int:
+    """Routed windows of a cache of seq_len tokens: the historical region
+    between the protected sinks and the protected recent tokens (§4.1) cut
+    into whole windows from its start; a partial window at its end stays
+    with the protected recent tokens."""
+    return max(0, (seq_len - n_sink - n_recent) // win)
+
+
+def qevict_init(batch: int, heads: int, max_windows: int, head_dim: int, win: int,
+                bits: int) -> dict:
+    """Routing state before the first step: every window full precision,
+    no backing-store entry, zero accumulated score."""
+    bpt = head_dim * bits // 8
+    return {
+        "w_acc": np.zeros((batch, heads, max_windows), dtype=np.float64),
+        "tier": np.zeros((batch, heads, max_windows), dtype=np.int8),
+        "has_codes": np.zeros((batch, heads, max_windows), dtype=np.uint8),
+        "k_codes": np.zeros((batch, heads, max_windows, win, bpt), dtype=np.uint8),
+        "v_codes": np.zeros((batch, heads, max_windows, win, bpt), dtype=np.uint8),
+        "k_meta": np.zeros((batch, heads, max_windows, head_dim, 2), dtype=np.float32),
+        "v_meta": np.zeros((batch, heads, max_windows, head_dim, 2), dtype=np.float32),
+    }
+
+
+def qevict_step(state: dict, token_scores: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                *, seq_len: int, n_sink: int, n_recent: int, win: int, n_full: int,
+                n_quant: int, bits: int) -> dict:
+    """One routing step of QEvict's recoverable hierarchy (§4.1-4.3,
+    Appendix A), run every Omega decode tokens (§4.2), with the persistent
+    backing store of §1.  Returns a new state; k_bits / v_bits (bf16 bit
+    patterns [Bt, Hkv, capacity, D]) are updated in place by promotions.
+
+    Per (sequence, KV head), for the nW = qevict_windows(...) routed windows
+    (window j = tokens n_sink + win*j .. n_sink + win*(j+1) - 1):
+      1. accumulate: w_acc[j] += sum of this step's token scores over window j
+         (the prompt's attention initialises the scores at the first step);
+      2. rank the windows that are not evicted by (w_acc desc, j asc): the
+         first n_full are full precision, the next n_quant quantised, the rest
+         evicted; eviction is permanent (an evicted window never ranks again);
+      3. a window entering the quantised tier from full precision is
+         quantised from its cache rows only at its first demotion; later
+         demotions reuse that backing-store entry unchanged, so repeated
+         transitions do not accumulate error;
+      4. a window promoted from the quantised tier back to full precision has
+         its cache rows rewritten with the dequantised values (bf16 RNE of
+         lo + code*scale, two roundings): promotion restores residency, not
+         the original values (Appendix K).
+    Groups are one channel of one window, K and V separately (quant_lowbit).
+    """
+    st = {key: val.copy() for key, val in state.items()}
+    Bt, H, _ = st["tier"].shape
+    nW = qevict_windows(seq_len, n_sink, n_recent, win)
+    for b in range(Bt):
+        for h in range(H):
+            for j in range(nW):
+                a = n_sink + win * j
+                st["w_acc"][b, h, j] += float(np.sum(token_scores[b, h, a:a + win],
+                                                     dtype=np.float64))
+            live = [j for j in range(nW) if st["tier"][b, h, j] != TIER_EVICT]
+            order = sorted(live, key=lambda j: (-st["w_acc"][b, h, j], j))
+            new = {}
+            for r, j in enumerate(order):
+                new[j] = TIER_FULL if r < n_full else (
+                    TIER_QUANT if r < n_full + n_quant else TIER_EVICT)
+            for j in live:
+                old, nt = int(st["tier"][b, h, j]), new[j]
+                a = n_sink + win * j
+                if old == TIER_FULL and nt == TIER_QUANT and not st["has_codes"][b, h, j]:
+                    for name, x in (("k", k_bits), ("v", v_bits)):
+                        vals = (x[b, h, a:a + win].astype(np.uint32) << np.uint32(16)).view(
+                            np.float32)
+                        c, lo, sc = quant_lowbit(vals, bits)
+                        st[name + "_codes"][b, h, j] = pack_codes(c, bits)
+                        st[name + "_meta"][b, h, j] = np.stack([lo, sc], axis=-1)
+                    st["has_codes"][b, h, j] = 1
+                elif old == TIER_QUANT and nt == TIER_FULL:
+                    for name, x in (("k", k_bits), ("v", v_bits)):
+                        c = unpack_codes(st[name + "_codes"][b, h, j], bits)
+                        meta = st[name + "_meta"][b, h, j]
+                        x[b, h, a:a + win] = round_bf16(
+                            dequant_int4(c, meta[:, 0][None, :], meta[:, 1][None, :]))
+                st["tier"][b, h, j] = nt
+    return st

@@ -536,3 +536,159 @@ def test_tier_outputs_small_brute_force():
     deq = synth.bf16_bits_to_f32(out["k_prom"][0, 0])
     step = out["k_meta"][0, 0, 1, :, 1]
     assert (np.abs(deq - f) <= step / 2 + np.abs(f) * 2 ** -8 + 1e-30).all()
+
+
+# ------------------------------------------------- QEvict routing steps ----
+
+def _bf16_bits(vals):
+    """Exactly representable float32 values -> bf16 bit patterns."""
+    u = np.asarray(vals, dtype=np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_int2_extremes_constant_identity_and_half_even():
+    """INT2 rule written out: min -> 0, max -> 3, a constant group gives
+    zeros, lo + c*scale with an exact scale gives c, and half-way values
+    round to even (lo + 0.5 s -> 0, lo + 1.5 s -> 2, lo + 2.5 s -> 2)."""
+    x = _rand((64, 8), 31).astype(np.float32)
+    c, lo, sc = oracle.quant_lowbit(x, 2)
+    assert c.max() <= 3
+    assert np.all(c[np.argmin(x, axis=0), np.arange(8)] == 0)
+    assert np.all(c[np.argmax(x, axis=0), np.arange(8)] == 3)
+    c0, lo0, sc0 = oracle.quant_lowbit(np.full((64, 1), 1.25, np.float32), 2)
+    assert np.all(c0 == 0) and sc0[0] == 0 and lo0[0] == np.float32(1.25)
+    # lo = 1, hi = 2.5 -> scale = 0.5 exactly
+    g = np.array([1.0, 1.5, 2.0, 2.5, 1.25, 1.75, 2.25, 2.5], np.float32)[:, None]
+    c1, lo1, sc1 = oracle.quant_lowbit(g, 2)
+    assert sc1[0] == np.float32(0.5) and lo1[0] == np.float32(1.0)
+    assert c1[:, 0].tolist() == [0, 1, 2, 3, 0, 2, 2, 3]
+
+
+def test_lowbit_four_bits_is_the_int4_rule():
+    x = _rand((64, 16), 32).astype(np.float32)
+    a = oracle.quant_lowbit(x, 4)
+    b = oracle.quant_int4(x)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_pack_codes_layout():
+    """Lowest channel in the lowest bits: [1, 2, 3, 0] -> 1 | 2<<2 | 3<<4 = 57;
+    4-bit packing equals the nibble layout."""
+    assert oracle.pack_codes(np.array([[1, 2, 3, 0]], np.uint8), 2).tolist() == [[57]]
+    c = np.random.default_rng(3).integers(0, 16, (5, 32)).astype(np.uint8)
+    assert np.array_equal(oracle.pack_codes(c, 4), oracle.pack_nibbles(c))
+    c2 = np.random.default_rng(4).integers(0, 4, (5, 32)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(c2, 2), 2), c2)
+
+
+def _qe_setup(nW=6, win=4, D=8, n_sink=2, n_recent=3, seed=5, bits=2):
+    S = n_sink + nW * win + n_recent + 1          # one leftover token joins the recent region
+    rng = np.random.default_rng(seed)
+    vals = (rng.integers(-64, 64, (1, 1, S, D)) / 16.0).astype(np.float32)
+    k = _bf16_bits(vals)
+    v = _bf16_bits(-vals)
+    st = oracle.qevict_init(1, 1, nW + 2, D, win, bits)
+    return S, k, v, st
+
+
+def _window_scores(S, n_sink, win, per_window):
+    s = np.zeros((1, 1, S), np.float32)
+    for j, w in enumerate(per_window):
+        s[0, 0, n_sink + win * j] = w          # the whole window's mass on its first token
+    return s
+
+
+def test_qevict_routing_steps_by_hand():
+    """Six windows, capacities 2 full / 2 quantised.  Step 1 ranks 5,4 | 3,2 |
+    1,0; step 2 makes windows 0 and 1 the strongest, but eviction is
+    permanent, so the live windows 2..5 are re-ranked among themselves."""
+    S, k, v, st = _qe_setup()
+    kw = dict(seq_len=S, n_sink=2, n_recent=3, win=4, n_full=2, n_quant=2, bits=2)
+    st = oracle.qevict_step(st, _window_scores(S, 2, 4, [1, 2, 3, 4, 5, 6]), k, v, **kw)
+    assert st["tier"][0, 0, :6].tolist() == [2, 2, 1, 1, 0, 0]
+    assert st["has_codes"][0, 0, :6].tolist() == [0, 0, 1, 1, 0, 0]
+    # step 2: accumulated 0+100, 2+100, 3+10, 4, 5, 6+1 -> live order 2 (13), 5 (7), 4, 3
+    st = oracle.qevict_step(st, _window_scores(S, 2, 4, [100, 100, 10, 0, 0, 1]), k, v, **kw)
+    assert st["w_acc"][0, 0, :6].tolist() == [101, 102, 13, 4, 5, 7]
+    assert st["tier"][0, 0, :6].tolist() == [2, 2, 0, 1, 1, 0]
+    # windows beyond nW are never touched
+    assert st["tier"][0, 0, 6:].tolist() == [0, 0] and st["w_acc"][0, 0, 6:].tolist() == [0, 0]
+
+
+def test_qevict_backing_store_is_reused_and_promotion_writes_dequantised_rows():
+    """F -> Q quantises the window once; Q -> F writes the dequantised values
+    (brute force per value) into the cache rows; a second demotion keeps the
+    first codes although the rows changed; protected rows never change."""
+    S, k, v, st = _qe_setup()
+    k0, v0 = k.copy(), v.copy()
+    kw = dict(seq_len=S, n_sink=2, n_recent=3, win=4, n_full=5, n_quant=1, bits=2)
+    # step 1: window 0 weakest -> quantised
+    st = oracle.qevict_step(st, _window_scores(S, 2, 4, [1, 9, 9, 9, 9, 9]), k, v, **kw)
+    assert st["tier"][0, 0, :6].tolist() == [1, 0, 0, 0, 0, 0]
+    codes1 = st["k_codes"][0, 0, 0].copy()
+    meta1 = st["k_meta"][0, 0, 0].copy()
+    rows = (k0[0, 0, 2:6].astype(np.uint32) << 16).view(np.float32)
+    lo = rows.min(axis=0)
+    sc = (rows.max(axis=0) - lo) / np.float32(3)
+    assert np.array_equal(meta1[:, 0], lo) and np.array_equal(meta1[:, 1], sc.astype(np.float32))
+    # step 2: window 0 strongest, window 1 weakest -> 0 promoted, 1 quantised
+    st = oracle.qevict_step(st, _window_scores(S, 2, 4, [100, 0, 1, 1, 1, 1]), k, v, **kw)
+    assert st["tier"][0, 0, :6].tolist() == [0, 1, 0, 0, 0, 0]
+    cu = oracle.unpack_codes(codes1, 2)
+    for t in range(4):
+        for ch in range(8):
+            x = float(np.float32(meta1[ch, 0]) + np.float32(np.float32(cu[t, ch]) * meta1[ch, 1]))
+            want = oracle.round_bf16(np.array([x], np.float32))[0]
+            assert k[0, 0, 2 + t, ch] == want
+    promoted = k[0, 0, 2:6].copy()
+    # Re-quantising the dequantised rows would give the same codes here, so
+    # make reuse observable: overwrite the window's cache rows; a re-demotion
+    # must still hold the first codes, and the next promotion restores the
+    # rows from them.
+    k[0, 0, 2:6] = 0
+    v[0, 0, 2:6] = 0
+    # step 3: accumulated 101, 1009, 210 x 4 -> window 0 is the weakest and is
+    # demoted again: the first codes, not a re-quantisation of its new rows
+    st = oracle.qevict_step(st, _window_scores(S, 2, 4, [0, 1000, 200, 200, 200, 200]), k, v, **kw)
+    assert st["tier"][0, 0, 0] == 1
+    assert np.array_equal(st["k_codes"][0, 0, 0], codes1)
+    assert np.array_equal(st["k_meta"][0, 0, 0], meta1)
+    # step 4: promoted again -> the same rows as after the first promotion
+    st = oracle.qevict_step(st, _window_scores(S, 2, 4, [10000, 0, 0, 0, 0, 0]), k, v, **kw)
+    assert st["tier"][0, 0, 0] == 0 and np.array_equal(k[0, 0, 2:6], promoted)
+    # protected sinks and recent rows (incl. the partial window) untouched
+    assert np.array_equal(k[0, 0, :2], k0[0, 0, :2]) and np.array_equal(k[0, 0, 26:], k0[0, 0, 26:])
+    assert np.array_equal(v[0, 0, :2], v0[0, 0, :2])
+
+
+def test_qevict_capacities_and_permanent_eviction_random():
+    """Over random steps: at most n_full full and n_quant quantised windows,
+    the full tier holds the best live windows, evicted windows stay evicted,
+    and with enough capacity nothing is ever evicted."""
+    rng = np.random.default_rng(9)
+    S, k, v, st = _qe_setup(nW=12, seed=11, bits=4)
+    kw = dict(seq_len=S, n_sink=2, n_recent=3, win=4, n_full=3, n_quant=4, bits=4)
+    evicted = np.zeros(12, bool)
+    for _ in range(6):
+        sc = rng.integers(0, 5, (1, 1, S)).astype(np.float32)
+        st = oracle.qevict_step(st, sc, k, v, **kw)
+        t = st["tier"][0, 0, :12]
+        assert np.sum(t == 0) <= 3 and np.sum(t == 1) <= 4
+        assert np.all(t[evicted] == 2)
+        evicted = t == 2
+        live = np.flatnonzero(t != 2)
+        w = st["w_acc"][0, 0]
+        best = sorted(live, key=lambda j: (-w[j], j))[:3]
+        assert sorted(best) == sorted(np.flatnonzero(t == 0).tolist())
+    S, k, v, st = _qe_setup(nW=5, seed=12)
+    st = oracle.qevict_step(st, rng.random((1, 1, S)).astype(np.float32), k, v, seq_len=S,
+                            n_sink=2, n_recent=3, win=4, n_full=2, n_quant=3, bits=2)
+    assert not np.any(st["tier"][0, 0, :5] == 2)
+
+
+def test_qevict_window_count():
+    assert oracle.qevict_windows(32768, 5, 64, 64) == 510      # 32699 // 64
+    assert oracle.qevict_windows(100, 5, 64, 64) == 0
+    assert oracle.qevict_windows(5 + 64 + 64, 5, 64, 64) == 1
