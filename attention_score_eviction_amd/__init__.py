@@ -55,6 +55,19 @@ class TierDesc(ctypes.Structure):
     ]
 
 
+class QevictDesc(ctypes.Structure):
+    """kvsel_qevict_desc."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+        ("capacity", ctypes.c_int32), ("max_windows", ctypes.c_int32),
+        ("win", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+        ("n_recent", ctypes.c_int32), ("n_full", ctypes.c_int32),
+        ("n_quant", ctypes.c_int32), ("bits", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
 class KaraDesc(ctypes.Structure):
     """kvsel_kara_desc."""
     _fields_ = [
@@ -110,6 +123,11 @@ def lib() -> ctypes.CDLL:
     L.kvsel_route_tiers_workspace.restype = SZ
     L.kvsel_route_tiers.argtypes = [TP, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, P, P, SZ, P]
     L.kvsel_route_tiers.restype = ctypes.c_int
+    QP = ctypes.POINTER(QevictDesc)
+    L.kvsel_qevict_step_workspace.argtypes = [QP]
+    L.kvsel_qevict_step_workspace.restype = SZ
+    L.kvsel_qevict_step.argtypes = [QP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.kvsel_qevict_step.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -413,4 +431,53 @@ def route_tiers(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, n_ful
 EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_select_workspace",
            "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers",
            "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat",
-           "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select")
+           "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select",
+           "kvsel_qevict_step_workspace", "kvsel_qevict_step")
+
+
+# ---------------------------------------------------------------------------
+# Repeated recoverable routing (kvsel_qevict_step)
+# ---------------------------------------------------------------------------
+
+def qevict_desc(k: torch.Tensor, *, seq_len: int, max_windows: int, n_sink: int,
+                n_recent: int, n_full: int, n_quant: int, bits: int = 2) -> QevictDesc:
+    """Descriptor for a cache k [Bt, Hkv, capacity, D] (bf16)."""
+    Bt, Hkv, cap, D = k.shape
+    return QevictDesc(Bt, Hkv, D, int(seq_len), cap, int(max_windows), 64, int(n_sink),
+                      int(n_recent), int(n_full), int(n_quant), int(bits), _dtype_code(k))
+
+
+def qevict_state(qd: QevictDesc, device) -> dict:
+    """Zeroed routing state: every window full precision, no backing-store
+    entry, accumulated score 0."""
+    Bt, H, M, D = qd.batch, qd.n_kv_heads, qd.max_windows, qd.head_dim
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+    return {
+        "w_acc": z((Bt, H, M), torch.float32),
+        "tier": z((Bt, H, M), torch.int8),
+        "has_codes": z((Bt, H, M), torch.uint8),
+        "k_codes": z((Bt, H, M, 64, D * qd.bits // 8), torch.uint8),
+        "v_codes": z((Bt, H, M, 64, D * qd.bits // 8), torch.uint8),
+        "k_meta": z((Bt, H, M, D, 2), torch.float32),
+        "v_meta": z((Bt, H, M, D, 2), torch.float32),
+    }
+
+
+def qevict_step_workspace_bytes(qd: QevictDesc) -> int:
+    return int(lib().kvsel_qevict_step_workspace(ctypes.byref(qd)))
+
+
+def qevict_step(qd: QevictDesc, token_scores: torch.Tensor, state: dict, k: torch.Tensor,
+                v: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> dict:
+    """kvsel_qevict_step: updates state (and promoted rows of k, v) in place."""
+    if workspace is None:
+        workspace = torch.empty(max(qevict_step_workspace_bytes(qd), 1), dtype=torch.uint8,
+                                device=k.device)
+    st = lib().kvsel_qevict_step(
+        ctypes.byref(qd), _ptr(token_scores), _ptr(state["w_acc"]), _ptr(state["tier"]),
+        _ptr(state["has_codes"]), _ptr(k), _ptr(v), _ptr(state["k_codes"]),
+        _ptr(state["v_codes"]), _ptr(state["k_meta"]), _ptr(state["v_meta"]), _ptr(workspace),
+        workspace.numel(), _stream(stream))
+    _check(st, "kvsel_qevict_step")
+    return state

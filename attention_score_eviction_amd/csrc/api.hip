@@ -46,6 +46,21 @@ kvsel_status check_tier_desc(const kvsel_tier_desc* d) {
   return KVSEL_OK;
 }
 
+kvsel_status check_qevict_desc(const kvsel_qevict_desc* d) {
+  if (!d) return KVSEL_ERR_ARG;
+  if (d->batch < 1 || d->n_kv_heads < 1 || d->head_dim < 1) return KVSEL_ERR_ARG;
+  if ((int64_t)d->batch * d->n_kv_heads > 65535) return KVSEL_ERR_ARG;
+  if (d->seq_len < 0 || d->capacity < d->seq_len || d->capacity > kMaxSeq) return KVSEL_ERR_ARG;
+  if (d->n_sink < 0 || d->n_recent < 0 || d->n_full < 0 || d->n_quant < 0) return KVSEL_ERR_ARG;
+  if (d->max_windows < 1) return KVSEL_ERR_ARG;
+  if (d->win != 64 || (d->bits != 2 && d->bits != 4) || d->max_windows > 4096)
+    return KVSEL_ERR_UNSUPPORTED;
+  if (d->dtype != KVSEL_BF16) return d->dtype == KVSEL_F32 ? KVSEL_ERR_UNSUPPORTED : KVSEL_ERR_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return KVSEL_ERR_UNSUPPORTED;
+  if (qevict_windows(*d) > d->max_windows) return KVSEL_ERR_ARG;
+  return KVSEL_OK;
+}
+
 // Head-adaptive selection: the sequence-wide pick count must be feasible,
 // and a sequence's flattened keys h*S + position must fit in 31 bits.
 kvsel_status check_adaptive(const kvsel_desc* d, int32_t total_budget) {
@@ -267,6 +282,26 @@ kvsel_status kvsel_route_tiers(const kvsel_tier_desc* desc, const float* token_s
   return launch_tiers(*desc, p, token_scores, k, v, tier, win_rank, k_full, v_full, k_codes,
                       v_codes, k_meta, v_meta, promote, n_promote, k_prom, v_prom, (char*)ws,
                       (hipStream_t)stream);
+}
+
+size_t kvsel_qevict_step_workspace(const kvsel_qevict_desc* desc) {
+  if (check_qevict_desc(desc) != KVSEL_OK) return 0;
+  return qevict_workspace(*desc);
+}
+
+kvsel_status kvsel_qevict_step(const kvsel_qevict_desc* desc, const float* token_scores,
+                               float* w_acc, int8_t* tier, uint8_t* has_codes, void* k, void* v,
+                               uint8_t* k_codes, uint8_t* v_codes, float* k_meta, float* v_meta,
+                               void* ws, size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_qevict_desc(desc);
+  if (st != KVSEL_OK) return st;
+  const void* ptrs[] = {token_scores, w_acc, tier, has_codes, k, v, k_codes, v_codes, k_meta,
+                        v_meta, ws};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return KVSEL_ERR_ARG;
+  if (ws_bytes < qevict_workspace(*desc)) return KVSEL_ERR_WORKSPACE;
+  return launch_qevict(*desc, token_scores, w_acc, tier, has_codes, k, v, k_codes, v_codes,
+                       k_meta, v_meta, (char*)ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -87,6 +87,14 @@ struct TierPlan {
   size_t off_slot, total;
 };
 bool plan_tiers(const kvsel_tier_desc& d, TierPlan* p);
+// Repeated recoverable routing: routed windows of the desc's cache, the
+// workspace (one action byte per window slot) and the launch.
+int qevict_windows(const kvsel_qevict_desc& d);
+size_t qevict_workspace(const kvsel_qevict_desc& d);
+kvsel_status launch_qevict(const kvsel_qevict_desc& d, const float* scores, float* w_acc,
+                           int8_t* tier, uint8_t* has_codes, void* k, void* v, uint8_t* k_codes,
+                           uint8_t* v_codes, float* k_meta, float* v_meta, char* ws,
+                           hipStream_t stream);
 kvsel_status launch_tiers(const kvsel_tier_desc& d, const TierPlan& p, const float* scores,
                           const void* k, const void* v, int8_t* tier, int32_t* rank,
                           void* k_full, void* v_full, uint8_t* k_codes, uint8_t* v_codes,

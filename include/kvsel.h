@@ -334,6 +334,70 @@ kvsel_status kvsel_route_tiers(const kvsel_tier_desc* desc, const float* token_s
                                int32_t n_promote, void* k_prom, void* v_prom,
                                void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Repeated recoverable routing (QEvict, "Recoverable Quantized KV Eviction for
+ * Attention-Drift-Robust Long-Context Decoding": Sections 4.1-4.3 and
+ * Appendix A, repeated every Omega decode tokens as in Section 4.2, with the
+ * persistent quantised backing store of Section 1).  Per (sequence, KV head)
+ * the cache rows [n_sink, n_sink + 64*nW) are cut into nW = floor((seq_len -
+ * n_sink - n_recent) / 64) windows; the sinks, the recent tokens and a
+ * partial window before them are protected (never routed, never changed).
+ */
+typedef struct {
+  int32_t batch;        /* Bt >= 1 */
+  int32_t n_kv_heads;   /* Hkv >= 1, Bt*Hkv <= 65535 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t seq_len;      /* tokens currently in the cache (<= capacity) */
+  int32_t capacity;     /* cache rows per (sequence, KV head) in k, v */
+  int32_t max_windows;  /* window slots per (sequence, KV head) in the state (<= 4096) */
+  int32_t win;          /* tokens per window: 64 */
+  int32_t n_sink;       /* protected leading tokens (QEvict's default: 5) */
+  int32_t n_recent;     /* protected trailing tokens */
+  int32_t n_full;       /* full-precision window capacity */
+  int32_t n_quant;      /* quantised window capacity */
+  int32_t bits;         /* 2 (QEvict's default tier) or 4 */
+  int32_t dtype;        /* kvsel_dtype of k, v: KVSEL_BF16 only */
+} kvsel_qevict_desc;
+
+/* Bytes of scratch kvsel_qevict_step needs (0 on invalid arguments). */
+size_t kvsel_qevict_step_workspace(const kvsel_qevict_desc* desc);
+
+/*
+ * kvsel_qevict_step -- one routing step.  State buffers persist across steps
+ * (caller-owned device memory; zero them before the first step: every window
+ * full precision, no backing-store entry, score 0).  For every routed window j:
+ *   w_acc[j] += the sum of token_scores over its 64 tokens (fp32, a fixed
+ *     reduction order); the prompt's attention initialises the scores;
+ *   windows not evicted are ranked by (w_acc desc, j asc): the first n_full
+ *     are full precision (0), the next n_quant quantised (1), the rest evicted
+ *     (2); eviction is permanent;
+ *   full -> quantised: if has_codes[j] == 0 the window's K and V rows are
+ *     quantised into slot j of the backing store and has_codes[j] = 1;
+ *     otherwise the stored codes are kept as they are (no re-quantisation);
+ *   quantised -> full: the window's K and V cache rows are overwritten with
+ *     bf16_rne(lo + code*scale) (two fp32 roundings, no FMA).
+ * Code rule per (window, channel) group of 64 values, K and V separately:
+ *   lo = min, scale = (max - lo) / (2^bits - 1) in fp32, code =
+ *   clip(rint((x - lo) / scale), 0, 2^bits - 1) (0 when scale == 0); channel c
+ *   at bit offset bits*(c mod (8/bits)) of byte c / (8/bits).
+ *
+ *   token_scores [Bt,Hkv,seq_len] float32, device: this step's attention mass
+ *   w_acc        [Bt,Hkv,max_windows] float32 in/out
+ *   tier         [Bt,Hkv,max_windows] int8 in/out
+ *   has_codes    [Bt,Hkv,max_windows] uint8 in/out
+ *   k, v         [Bt,Hkv,capacity,D] bf16 in/out (promotions write rows)
+ *   k_codes, v_codes [Bt,Hkv,max_windows,64,D*bits/8] uint8 in/out
+ *   k_meta, v_meta   [Bt,Hkv,max_windows,D,2] float32 (lo, scale) in/out
+ * Slots j >= nW are not touched.  Errors: KVSEL_ERR_ARG for a bad shape or
+ * pointer, nW > max_windows, or negative capacities; KVSEL_ERR_UNSUPPORTED
+ * for win != 64, bits not 2 or 4, D not 64/128, a dtype other than bf16, or
+ * max_windows > 4096.  Overlapping calls on the same state race.
+ */
+kvsel_status kvsel_qevict_step(const kvsel_qevict_desc* desc, const float* token_scores,
+                               float* w_acc, int8_t* tier, uint8_t* has_codes, void* k, void* v,
+                               uint8_t* k_codes, uint8_t* v_codes, float* k_meta, float* v_meta,
+                               void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

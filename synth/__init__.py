@@ -223,3 +223,26 @@ def promote_list(config_id: int, n_rows: int, n_quant: int, n_promote: int,
     for r in range(n_rows):
         out[r] = np.sort(rng.choice(n_quant, size=n_promote, replace=False))
     return out
+
+
+def qevict_cache(seed: int, batch: int, n_kv_heads: int, capacity: int, head_dim: int) -> dict:
+    """K and V cache rows [Bt, Hkv, capacity, D] as bf16 bit patterns, N(0,1)."""
+    base = (950, seed)
+    return {"k": _round(_normal(base + (TENSOR_K,), (batch, n_kv_heads, capacity, head_dim)),
+                        "bf16"),
+            "v": _round(_normal(base + (TENSOR_V,), (batch, n_kv_heads, capacity, head_dim)),
+                        "bf16")}
+
+
+def qevict_token_scores(seed: int, step: int, batch: int, n_kv_heads: int, seq_len: int,
+                        integer: bool = True) -> np.ndarray:
+    """Per-step attention mass per token [Bt, Hkv, seq_len] float32 with drift:
+    a fixed per-token importance (heavy-tailed) plus a fresh per-step part, so
+    window rankings change between steps.  integer=True gives small integers
+    (sums stay exact in fp32); otherwise positive reals."""
+    base = _rng((960, seed, TENSOR_STRUCT)).gamma(0.5, 2.0, size=(batch, n_kv_heads, seq_len))
+    fresh = _rng((960, seed, step)).gamma(0.5, 2.0, size=(batch, n_kv_heads, seq_len))
+    s = base + 1.5 * fresh
+    if integer:
+        return np.minimum(np.floor(s), 15).astype(np.float32)
+    return (s / seq_len).astype(np.float32)

@@ -204,6 +204,29 @@ def test_tier_checks(kv):
     assert call(td, ws_bytes=need - 1) == kv.ERR_WORKSPACE
 
 
+def test_qevict_checks(kv):
+    L = kv.lib()
+    Q = lambda **kw: kv.QevictDesc(**{**dict(batch=16, n_kv_heads=8, head_dim=128,  # noqa
+                                             seq_len=32768, capacity=32768, max_windows=512,
+                                             win=64, n_sink=5, n_recent=64, n_full=153,
+                                             n_quant=357, bits=2, dtype=kv.BF16), **kw})
+    good = Q()
+    need = L.kvsel_qevict_step_workspace(ctypes.byref(good))
+    assert need >= 16 * 8 * 512
+    call = lambda d, ws_bytes=need, first=FAKE: L.kvsel_qevict_step(  # noqa
+        ctypes.byref(d), first, *([FAKE] * 10), ws_bytes, None)
+    for bad in (Q(batch=0), Q(seq_len=40000), Q(max_windows=500), Q(n_sink=-1), Q(n_full=-1),
+                Q(n_quant=-1), Q(max_windows=0), Q(dtype=7)):
+        assert call(bad) == kv.ERR_ARG
+        assert L.kvsel_qevict_step_workspace(ctypes.byref(bad)) == 0
+    for bad in (Q(win=32), Q(bits=3), Q(bits=8), Q(head_dim=96), Q(dtype=kv.F32),
+                Q(max_windows=5000)):
+        assert call(bad) == kv.ERR_UNSUPPORTED
+    assert call(good, first=None) == kv.ERR_ARG
+    assert call(good, first=FAKE + 4) == kv.ERR_ARG
+    assert call(good, ws_bytes=need - 1) == kv.ERR_WORKSPACE
+
+
 def test_workspace_is_linear_in_prompt_not_window_times_prompt(kv):
     """The dense [Hq, W, S] score tensor is never formed (TideKV Section 4.2
     temporary-memory bound): scratch is the per-key score vector plus small
