@@ -15,6 +15,9 @@ Workloads (one JSON line each):
   qwen128k     one Qwen3-14B-shaped layer (40 q / 8 kv heads), 131072 tokens
   sweep64k     32 layers at 65536 tokens, budget 4096 -> 512, one layer resident
   qevict32k    16 x 32768-token caches, 256 decode queries, window tiers
+  qevict-steps QEvict decode-time routing every 8 tokens: 16 x 32768-token caches,
+               8 decode queries scored per step, INT2 backing store, 5 sinks,
+               64 recent tokens, half the routed windows kept (30% full, 70% INT2)
   kara512      Kara decode-window compression: 64 sequences, Llama-3-8B shape,
                512-token window, 64-token buffer, r = 40%, gamma 8, alpha 32
   llama8k-adaptive / qwen128k-adaptive
@@ -49,9 +52,11 @@ WORKLOADS = {
     "llama8k-adaptive": (2, "llama3-8b-layer-8k-head-adaptive"),
     "qwen128k-adaptive": (4, "qwen3-14b-layer-128k-head-adaptive"),
     "kara512": (0, "kara-decode-window-64x512"),
+    "qevict-steps": (5, "qevict-routing-steps-16x32k-int2"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "common.h"]
+KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "qevict.hip",
+                  "common.h"]
 
 
 def source_hash() -> str:
@@ -342,7 +347,9 @@ def main() -> int:
     cid, wname = WORKLOADS[args.workload]
     if args.workload == "kara512":
         return bench_kara(args, kvsel, torch, wname)
-    spec = synth.config(cid)
+    spec = synth.config(cid) if cid else None
+    if args.workload == "qevict-steps":
+        return bench_qevict_steps(args, kvsel, torch, spec, wname)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     if args.workload == "qevict32k":
@@ -575,6 +582,80 @@ def bench_kara(args, kvsel, torch, wname) -> int:
                      "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
                      "traffic": traffic_for(args.workload, "kvsel_kara_score"),
                      "kernel": "kvsel_kara_score", "algorithmic_flops_per_launch": flops},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_qevict_steps(args, kvsel, torch, spec, wname) -> int:
+    """QEvict's decode-time routing, repeated every Omega = 8 generated tokens:
+    the 8 newest decode queries are scored against the whole cache (no mask),
+    then kvsel_qevict_step accumulates the window scores, re-ranks the live
+    windows and moves data for the transitions (first demotions into the INT2
+    backing store, promotions back into the cache rows).  Query sets cycle
+    so that rankings drift between steps."""
+    Bt, Hq, Hkv, D, S = spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.seq_len
+    omega, n_sink, n_recent, bits, n_sets = 8, 5, 64, 2, 4
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    x = synth.qevict_cache(7, Bt, Hkv, S, D)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
+    k, v = up(x["k"]), up(x["v"])
+    qs = [up(synth.decode_window(40 + i, Bt, Hq, Hkv, omega, D)["q"]) for i in range(n_sets)]
+    nW = max(0, (S - n_sink - n_recent) // 64)
+    keep = nW // 2
+    n_quant = int(round(0.7 * keep))
+    n_full = keep - n_quant
+    qd = kvsel.qevict_desc(k, seq_len=S, max_windows=nW, n_sink=n_sink, n_recent=n_recent,
+                           n_full=n_full, n_quant=n_quant, bits=bits)
+    state = kvsel.qevict_state(qd, dev)
+    qws = torch.empty(kvsel.qevict_step_workspace_bytes(qd), dtype=torch.uint8, device=dev)
+    desc = kvsel.make_desc(qs[0], k, causal=False)
+    sws = torch.empty(kvsel.score_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    raw = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev)
+    pooled = torch.empty_like(raw)
+    it = [0]
+
+    def score():
+        q = qs[it[0] % n_sets]
+        kvsel.score(q, k, pool_kernel=1, causal=False, pooled=pooled, raw=raw, workspace=sws,
+                    stream=stream)
+
+    def route():
+        kvsel.qevict_step(qd, raw, state, k, v, workspace=qws, stream=stream)
+
+    def step():
+        score()
+        route()
+        it[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(args.steps // 4, 10)
+    step_us = event_time_us(torch, stream, step, steps)
+    us = {"kvsel_score": event_time_us(torch, stream, score, steps),
+          "kvsel_qevict_step": event_time_us(torch, stream, route, steps)}
+    H = Bt * Hkv
+    t = state["tier"].cpu().numpy()
+    score_bytes = 2 * H * S * D * 2 + 2 * H * S * 4
+    dom_gbs = score_bytes / (us["kvsel_score"] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC, "value": round(Bt * S / (step_us * 1e-6), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(step_us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wname, "batch": Bt, "seq_len": S, "n_q_heads": Hq,
+                   "n_kv_heads": Hkv, "head_dim": D, "queries_per_step": omega,
+                   "sinks": n_sink, "recent": n_recent, "windows": nW, "full": n_full,
+                   "quant": n_quant, "bits": bits, "parallelism": "none"},
+        "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
+        "final_tiers": {"full": int((t == 0).sum()), "quant": int((t == 1).sum()),
+                        "evicted": int((t == 2).sum())},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for(args.workload, "kvsel_score"),
+                     "kernel": "kvsel_score", "algorithmic_bytes_per_launch": score_bytes},
     }
     print(json.dumps(out), flush=True)
     return 0
