@@ -10,8 +10,11 @@
 namespace kvsel {
 namespace {
 
-constexpr int kRowsPerBlock = 64;
+constexpr int kRowsPerBlock = 64;   // flattened gather
 
+// One 16-byte vector of K and one of V per thread: a workgroup moves
+// 256 / vpr whole rows, so every thread has a single index -> row load chain
+// and all of a workgroup's loads are in flight together.
 __global__ void __launch_bounds__(256) compact_kernel(const u32x4_t* __restrict__ k,
                                                       const u32x4_t* __restrict__ v,
                                                       const int32_t* __restrict__ idx,
@@ -19,21 +22,22 @@ __global__ void __launch_bounds__(256) compact_kernel(const u32x4_t* __restrict_
                                                       u32x4_t* __restrict__ vo, int S,
                                                       int n_keep, int vpr) {
   const int head = blockIdx.y;
-  const int r0 = blockIdx.x * kRowsPerBlock;
-  const int32_t* ih = idx + (size_t)head * n_keep;
-  const size_t src_base = (size_t)head * S;
-  const size_t dst_base = (size_t)head * n_keep;
-  for (int t = threadIdx.x; t < kRowsPerBlock * vpr; t += 256) {
-    const int r = r0 + t / vpr;
-    const int c = t - (t / vpr) * vpr;
-    if (r >= n_keep) break;
-    const int src = ih[r];
-    const bool ok = src >= 0 && src < S;
-    const size_t so = (src_base + (ok ? src : 0)) * vpr + c;
-    const size_t dsto = (dst_base + r) * vpr + c;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    ko[dsto] = ok ? k[so] : zero;
-    if (v) vo[dsto] = ok ? v[so] : zero;
+  const int rpb = 256 / vpr;
+  const int r = blockIdx.x * rpb + threadIdx.x / vpr;
+  const int c = threadIdx.x - (threadIdx.x / vpr) * vpr;
+  if (r >= n_keep || threadIdx.x >= rpb * vpr) return;
+  const int src = idx[(size_t)head * n_keep + r];
+  const bool ok = src >= 0 && src < S;
+  const size_t so = ((size_t)head * S + (ok ? src : 0)) * vpr + c;
+  const size_t dsto = ((size_t)head * n_keep + r) * vpr + c;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const u32x4_t kx = ok ? k[so] : zero;
+  if (v) {
+    const u32x4_t vx = ok ? v[so] : zero;
+    ko[dsto] = kx;
+    vo[dsto] = vx;
+  } else {
+    ko[dsto] = kx;
   }
 }
 
@@ -92,7 +96,8 @@ kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
   const int e = d.dtype == KVSEL_F32 ? 4 : 2;
   const int vpr = d.head_dim * e / 16;
   const int nheads = d.batch * d.n_kv_heads;
-  hipLaunchKernelGGL(compact_kernel, dim3((n_keep + kRowsPerBlock - 1) / kRowsPerBlock, nheads),
+  const int rpb = 256 / vpr;   // vpr <= 32 (D * e <= 512 bytes)
+  hipLaunchKernelGGL(compact_kernel, dim3((n_keep + rpb - 1) / rpb, nheads),
                      dim3(256), 0, stream, (const u32x4_t*)k, (const u32x4_t*)v, idx,
                      (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, n_keep, vpr);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
