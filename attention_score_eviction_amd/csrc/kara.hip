@@ -13,9 +13,11 @@
 // Ties go to the lower position (I, fill-up) and to the lower chunk (Eq. 7).
 //
 // A window holds a few hundred positions, so one 256-thread workgroup takes
-// one (sequence, KV head) row entirely in LDS and ranks by counting: every
-// position (chunk) counts the ones ordered before it, with broadcast LDS
-// reads.  Ascending order for I and for the output comes from block scans.
+// one (sequence, KV head) row entirely in LDS.  The positions, and then the
+// chunks, are put in (score desc, index asc) order by a bitonic sort of
+// 64-bit keys (the order is exact: every key is unique); ascending order for
+// I and for the output, and the fill-up's count of free positions, come from
+// block scans.
 #include "common.h"
 
 namespace kvsel {
@@ -57,59 +59,65 @@ __device__ __forceinline__ uint32_t kara_block_scan(uint32_t v, uint32_t* total,
 // Position states.
 constexpr uint8_t kNone = 0, kTop = 1, kChunk = 2, kFill = 3;
 
-// How many of v[0..n4) are ordered before (x0, j0) and before (x1, j1) by
-// (value desc, index asc); with STATE only entries whose state is kNone
-// count.  Four entries per broadcast LDS read, both probes per read.
-// Padding entries hold -inf (never before a finite value) and a state other
-// than kNone.
-template <bool STATE>
-__device__ __forceinline__ void count_before2(const float* v, const uint8_t* st, int n4, float x0,
-                                              int j0, float x1, int j1, int& r0, int& r1) {
-  int c0 = 0, c1 = 0;
-  for (int i = 0; i < n4; i += 4) {
-    const float4 q = *(const float4*)&v[i];
-    uint32_t sw = 0u;
-    if constexpr (STATE) sw = *(const uint32_t*)&st[i];
-    const float qv[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = !STATE || ((sw >> (8 * u)) & 0xffu) == kNone;
-      const int ii = i + u;
-      c0 += (ok && (qv[u] > x0 || (qv[u] == x0 && ii < j0))) ? 1 : 0;
-      c1 += (ok && (qv[u] > x1 || (qv[u] == x1 && ii < j1))) ? 1 : 0;
+// Sort key for (value desc, index asc) as one ascending 64-bit integer: the
+// value's bits mapped to an order-preserving unsigned form, complemented for
+// descending order, above the index.  -0.0 is folded into +0.0 so that equal
+// values tie; -inf sorts after every finite value.
+__device__ __forceinline__ uint64_t desc_key(float x, int idx) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending in x
+  return ((uint64_t)(~ord) << 32) | (uint32_t)idx;
+}
+
+// Ascending bitonic sort of key[0, n2) (n2 a power of two) by the workgroup.
+__device__ __forceinline__ void bitonic_sort(uint64_t* key, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += kKaraThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = key[i], y = key[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            key[i] = y;
+            key[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
     }
   }
-  r0 = c0;
-  r1 = c1;
 }
 
 __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ idx, int n, int buffer, int keep,
     int gamma, int alpha, int n_out) {
-  __shared__ __align__(16) float a[kKaraMax];
-  __shared__ __align__(16) float rk[kKaraMax];  // chunk scores, < 0 when a chunk does not qualify
-  __shared__ int32_t ilist[kKaraMax];           // I in ascending position order
-  __shared__ __align__(16) uint8_t state[kKaraMax];
+  __shared__ float a[kKaraMax];
+  __shared__ float rk[kKaraMax];       // chunk scores, -inf when a chunk does not qualify
+  __shared__ int32_t ilist[kKaraMax];  // I in ascending position order
+  __shared__ uint8_t state[kKaraMax];
+  __shared__ uint64_t key[kKaraMax];   // sorted (score desc, position asc), then chunks
   __shared__ uint32_t wsum[kKaraThreads / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* s = scores + (size_t)row * n;
   int32_t* out = idx + (size_t)row * (n_out + buffer);
-  const int n4 = (n + 3) & ~3;
-  for (int j = tid; j < n4; j += kKaraThreads) {
-    a[j] = j < n ? s[j] : -INFINITY;
-    state[j] = j < n ? kNone : kTop;   // padding never counts as a free position
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int j = tid; j < n2; j += kKaraThreads) {
+    if (j < n) {
+      const float x = s[j];
+      a[j] = x;
+      state[j] = kNone;
+      key[j] = desc_key(x, j);
+    } else {
+      key[j] = ~0ull;   // padding sorts last
+    }
   }
   __syncthreads();
 
-  // Eq. 5: rank by (score desc, position asc); the first `keep` form I.
-  for (int base = 0; base < n; base += 2 * kKaraThreads) {
-    const int j0 = base + tid, j1 = j0 + kKaraThreads;
-    const float x0 = j0 < n ? a[j0] : 0.f, x1 = j1 < n ? a[j1] : 0.f;
-    int r0, r1;
-    count_before2<false>(a, state, n4, x0, j0, x1, j1, r0, r1);
-    if (j0 < n && r0 < keep) state[j0] = kTop;
-    if (j1 < n && r1 < keep) state[j1] = kTop;
-  }
+  // Eq. 5: the first `keep` positions in (score desc, position asc) order form I.
+  bitonic_sort(key, n2);
+  for (int r = tid; r < keep; r += kKaraThreads) state[(uint32_t)key[r]] = kTop;
   __syncthreads();
 
   // I in ascending order.
@@ -124,39 +132,52 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   }
   __syncthreads();
 
+  // Fill-up candidates, decided later: the free positions in sorted order.
+  // Their sorted order is read now, before the key array is reused.
+  constexpr int kPer = kKaraMax / kKaraThreads;
+  uint32_t fpos[kPer];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int r = m * kKaraThreads + tid;
+    fpos[m] = r < n ? (uint32_t)key[r] : 0xffffffffu;
+  }
+  __syncthreads();
+
   // Eq. 6: chunk k spans (I[k], I[k+1]); it qualifies when its end points are
   // at most gamma apart.  Scores in fp32: (A + A) * interior length.
   const int nchunk = nI > 1u ? (int)nI - 1 : 0;
-  const int nc4 = (nchunk + 3) & ~3;
-  for (int k = tid; k < nc4; k += kKaraThreads) {
-    float r = -INFINITY;   // padding and non-qualifying chunks rank after every qualifying one
+  int nc2 = 1;
+  while (nc2 < nchunk) nc2 <<= 1;
+  for (int k = tid; k < nc2; k += kKaraThreads) {
     if (k < nchunk) {
       const int i0 = ilist[k], i1 = ilist[k + 1];
       const int gap = i1 - i0;
-      if (gap <= gamma) r = (a[i0] + a[i1]) * (float)(gap - 1);
+      const float r = gap <= gamma ? (a[i0] + a[i1]) * (float)(gap - 1) : -INFINITY;
+      rk[k] = r;
+      key[k] = desc_key(r, k);
+    } else {
+      key[k] = ~0ull;
     }
-    rk[k] = r;
   }
   __syncthreads();
 
   // Eq. 7: the floor(alpha / gamma) best qualifying chunks (score desc, chunk
   // asc); Eq. 8: their interiors join the retained set.  A non-qualifying
-  // chunk (-inf) is never counted before a qualifying (finite) one.
+  // chunk (-inf) sorts after every qualifying one.
   const int want_chunks = alpha / gamma;
-  for (int base = 0; base < nchunk; base += 2 * kKaraThreads) {
-    const int k0 = base + tid, k1 = k0 + kKaraThreads;
-    const float x0 = k0 < nchunk ? rk[k0] : -INFINITY, x1 = k1 < nchunk ? rk[k1] : -INFINITY;
-    int r0, r1;
-    count_before2<false>(rk, state, nc4, x0, k0, x1, k1, r0, r1);
-    if (k0 < nchunk && x0 > -INFINITY && r0 < want_chunks)
-      for (int j = ilist[k0] + 1; j < ilist[k0 + 1]; ++j) state[j] = kChunk;
-    if (k1 < nchunk && x1 > -INFINITY && r1 < want_chunks)
-      for (int j = ilist[k1] + 1; j < ilist[k1 + 1]; ++j) state[j] = kChunk;
+  if (nchunk > 0) {
+    bitonic_sort(key, nc2);
+    for (int r = tid; r < want_chunks && r < nchunk; r += kKaraThreads) {
+      const int k = (int)(uint32_t)key[r];
+      if (rk[k] > -INFINITY)
+        for (int j = ilist[k] + 1; j < ilist[k + 1]; ++j) state[j] = kChunk;
+    }
   }
   __syncthreads();
 
   // Fill-up: while fewer than alpha positions were added, the best remaining
-  // positions by score (ties to the lower position).
+  // positions by score (ties to the lower position): a prefix count of the
+  // free positions in sorted order.
   uint32_t added;
   {
     uint32_t mine = 0u;
@@ -164,23 +185,23 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
     kara_block_scan(mine, &added, wsum);
   }
   const int need = alpha - (int)added;
-  // Decisions are held in registers until every rank is computed, so the
-  // ranking reads a state array nobody writes.
   uint32_t fill = 0u;
   if (need > 0) {
-    for (int m = 0, base = 0; base < n; m += 2, base += 2 * kKaraThreads) {
-      const int j0 = base + tid, j1 = j0 + kKaraThreads;
-      const bool f0 = j0 < n && state[j0] == kNone, f1 = j1 < n && state[j1] == kNone;
-      if (!f0 && !f1) continue;
-      int r0, r1;
-      count_before2<true>(a, state, n4, f0 ? a[j0] : 0.f, j0, f1 ? a[j1] : 0.f, j1, r0, r1);
-      if (f0 && r0 < need) fill |= 1u << m;
-      if (f1 && r1 < need) fill |= 1u << (m + 1);
+    uint32_t seen = 0u;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      if (m * kKaraThreads >= n) break;
+      const bool f = fpos[m] != 0xffffffffu && state[fpos[m]] == kNone;
+      uint32_t tot;
+      const uint32_t ex = kara_block_scan(f ? 1u : 0u, &tot, wsum);
+      if (f && seen + ex < (uint32_t)need) fill |= 1u << m;
+      seen += tot;
     }
   }
   __syncthreads();
-  for (int m = 0, j = tid; j < n; ++m, j += kKaraThreads)
-    if ((fill >> m) & 1u) state[j] = kFill;
+#pragma unroll
+  for (int m = 0; m < kPer; ++m)
+    if ((fill >> m) & 1u) state[fpos[m]] = kFill;
   __syncthreads();
 
   // Retained positions in ascending order, then the buffer.
