@@ -15,6 +15,38 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Sort key for (value desc, index asc) as one ascending 64-bit integer: the
+// value's bits mapped to an order-preserving unsigned form, complemented for
+// descending order, above the index.  -0.0 is folded into +0.0 so equal
+// values tie; -inf sorts after every finite value; ~0 (padding) after all.
+__device__ __forceinline__ uint64_t desc_key(float x, int idx) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending in x
+  return ((uint64_t)(~ord) << 32) | (uint32_t)idx;
+}
+
+// Ascending bitonic sort of key[0, n2) in LDS (n2 a power of two) by a
+// workgroup of NT threads.  Every thread of the block must call.
+template <int NT>
+__device__ __forceinline__ void block_bitonic_sort(uint64_t* key, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = key[i], y = key[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            key[i] = y;
+            key[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Score launch plan.  Keys of one (batch, KV head) are split into chunks of
 // `chunk` keys (a multiple of the per-step key count); query rows of the head

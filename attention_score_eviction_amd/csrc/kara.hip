@@ -59,36 +59,6 @@ __device__ __forceinline__ uint32_t kara_block_scan(uint32_t v, uint32_t* total,
 // Position states.
 constexpr uint8_t kNone = 0, kTop = 1, kChunk = 2, kFill = 3;
 
-// Sort key for (value desc, index asc) as one ascending 64-bit integer: the
-// value's bits mapped to an order-preserving unsigned form, complemented for
-// descending order, above the index.  -0.0 is folded into +0.0 so that equal
-// values tie; -inf sorts after every finite value.
-__device__ __forceinline__ uint64_t desc_key(float x, int idx) {
-  const uint32_t u = __float_as_uint(x + 0.0f);
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // ascending in x
-  return ((uint64_t)(~ord) << 32) | (uint32_t)idx;
-}
-
-// Ascending bitonic sort of key[0, n2) (n2 a power of two) by the workgroup.
-__device__ __forceinline__ void bitonic_sort(uint64_t* key, int n2) {
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += kKaraThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = key[i], y = key[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            key[i] = y;
-            key[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ idx, int n, int buffer, int keep,
     int gamma, int alpha, int n_out) {
@@ -116,7 +86,7 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   __syncthreads();
 
   // Eq. 5: the first `keep` positions in (score desc, position asc) order form I.
-  bitonic_sort(key, n2);
+  block_bitonic_sort<kKaraThreads>(key, n2);
   for (int r = tid; r < keep; r += kKaraThreads) state[(uint32_t)key[r]] = kTop;
   __syncthreads();
 
@@ -166,7 +136,7 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   // chunk (-inf) sorts after every qualifying one.
   const int want_chunks = alpha / gamma;
   if (nchunk > 0) {
-    bitonic_sort(key, nc2);
+    block_bitonic_sort<kKaraThreads>(key, nc2);
     for (int r = tid; r < want_chunks && r < nchunk; r += kKaraThreads) {
       const int k = (int)(uint32_t)key[r];
       if (rk[k] > -INFINITY)

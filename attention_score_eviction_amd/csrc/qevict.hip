@@ -20,9 +20,9 @@
 //
 // Kernels:
 //   qe_rank_kernel  one workgroup per (sequence, KV head): window sums in a
-//                   fixed reduction order, accumulation, exact rank by counting
-//                   over the live windows, new tier, and the data action of each
-//                   window (none / first demotion / promotion)
+//                   fixed reduction order, accumulation, exact rank among the
+//                   live windows by a bitonic sort, new tier, and the data
+//                   action of each window (none / first demotion / promotion)
 //   qe_move_kernel  one workgroup per window with an action: quantise the
 //                   window into its backing-store slot, or dequantise the slot
 //                   into the cache rows
@@ -42,10 +42,13 @@ __global__ void __launch_bounds__(kQeRankThreads) qe_rank_kernel(
     const float* __restrict__ scores, float* __restrict__ w_acc, int8_t* __restrict__ tier,
     uint8_t* __restrict__ has_codes, int8_t* __restrict__ act, int S, int n_sink, int nwin,
     int max_windows, int n_full, int n_quant) {
-  __shared__ __align__(16) float w[kQeMaxWindows];   // live score, -inf when evicted
+  __shared__ uint64_t key[kQeMaxWindows];   // (live score desc, index asc); evicted last
+  __shared__ int32_t rk[kQeMaxWindows];
   const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* s = scores + (size_t)head * S + n_sink;
   const size_t so = (size_t)head * max_windows;
+  int n2 = 1;
+  while (n2 < nwin) n2 <<= 1;
   // Window sums: one wave per window, lane l adds token l, a fixed butterfly.
   for (int j = wave; j < nwin; j += kQeRankThreads / 64) {
     float x = s[(size_t)j * kQeWin + lane];
@@ -54,30 +57,26 @@ __global__ void __launch_bounds__(kQeRankThreads) qe_rank_kernel(
     if (lane == 0) {
       const float acc = w_acc[so + j] + x;
       w_acc[so + j] = acc;
-      w[j] = tier[so + j] == 2 ? -INFINITY : acc;
+      // an evicted window sorts after every live one (its key's top bits are
+      // all ones, above -inf's)
+      key[j] = tier[so + j] == 2 ? (0xffffffff00000000ull | (uint32_t)j) : desc_key(acc, j);
     }
   }
-  const int n4 = (nwin + 3) & ~3;
-  for (int j = nwin + tid; j < n4; j += kQeRankThreads) w[j] = -INFINITY;
+  for (int j = nwin + tid; j < n2; j += kQeRankThreads) key[j] = ~0ull;
   __syncthreads();
-  // Rank among the live windows: an evicted window (-inf) never counts
-  // before a live one (finite).
+  block_bitonic_sort<kQeRankThreads>(key, n2);
+  for (int r = tid; r < nwin; r += kQeRankThreads) rk[(uint32_t)key[r]] = r;
+  __syncthreads();
+  // Live windows occupy the first sorted positions, so a live window's sorted
+  // position is its rank among the live windows.
   for (int j = tid; j < nwin; j += kQeRankThreads) {
     const int8_t told = tier[so + j];
     if (told == 2) {
       act[so + j] = kActNone;
       continue;
     }
-    const float wj = w[j];
-    int rk = 0;
-    for (int i = 0; i < n4; i += 4) {
-      const float4 q = *(const float4*)&w[i];
-      rk += (q.x > wj || (q.x == wj && i < j)) ? 1 : 0;
-      rk += (q.y > wj || (q.y == wj && i + 1 < j)) ? 1 : 0;
-      rk += (q.z > wj || (q.z == wj && i + 2 < j)) ? 1 : 0;
-      rk += (q.w > wj || (q.w == wj && i + 3 < j)) ? 1 : 0;
-    }
-    const int8_t tnew = rk < n_full ? 0 : (rk < n_full + n_quant ? 1 : 2);
+    const int r = rk[j];
+    const int8_t tnew = r < n_full ? 0 : (r < n_full + n_quant ? 1 : 2);
     int8_t a = kActNone;
     if (told == 0 && tnew == 1 && has_codes[so + j] == 0) {
       a = kActQuant;

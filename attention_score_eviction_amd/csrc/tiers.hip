@@ -10,8 +10,8 @@
 //
 // Kernels:
 //   tier_rank_kernel     one workgroup per (batch, KV head): window sums in a
-//                        fixed reduction order, exact rank by counting, tier
-//                        id, and each window's slot inside its tier
+//                        fixed reduction order, exact rank by a bitonic sort,
+//                        tier id, and each window's slot inside its tier
 //   tier_move_kernel     one workgroup per window: full tier -> 16 B/lane row
 //                        copy; int4 tier -> LDS-staged per-channel min/max,
 //                        codes, nibble packing
@@ -53,35 +53,39 @@ __device__ __forceinline__ uint32_t block_excl_scan_1024(uint32_t v, uint32_t* t
   return before + incl - v;
 }
 
-// nwin <= 4096 windows per head.
+// nwin <= 4096 windows per head.  Window sums in a fixed order, then the
+// windows sorted by (sum desc, index asc) with a bitonic sort of unique 64-bit
+// keys: a window's rank is its sorted position.
 __global__ void __launch_bounds__(kRankThreads) tier_rank_kernel(
     const float* __restrict__ scores, int8_t* __restrict__ tier, int32_t* __restrict__ rank,
     int32_t* __restrict__ slot, int S, int nwin, int n_full, int n_quant) {
-  __shared__ float w[4096];
+  __shared__ uint64_t key[4096];
+  __shared__ int32_t rk[4096];
   __shared__ uint32_t wsum[16];
   const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* s = scores + (size_t)head * S;
+  int n2 = 1;
+  while (n2 < nwin) n2 <<= 1;
   // Window sums: one wave per window, lane l adds tokens l; tree in fixed order.
   for (int j = wave; j < nwin; j += kRankThreads / 64) {
     float x = s[(size_t)j * kWin + lane];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) w[j] = x;
+    if (lane == 0) key[j] = desc_key(x, j);
   }
+  for (int j = nwin + tid; j < n2; j += kRankThreads) key[j] = ~0ull;
+  __syncthreads();
+  block_bitonic_sort<kRankThreads>(key, n2);
+  for (int r = tid; r < nwin; r += kRankThreads) rk[(uint32_t)key[r]] = r;
   __syncthreads();
   uint32_t cf = 0u, cq = 0u;
   for (int base = 0; base < nwin; base += kRankThreads) {
     const int j = base + tid;
     int t = 2;
     if (j < nwin) {
-      const float wj = w[j];
-      int rk = 0;
-      for (int i = 0; i < nwin; ++i) {
-        const float wi = w[i];
-        rk += (wi > wj) || (wi == wj && i < j);
-      }
-      t = rk < n_full ? 0 : (rk < n_full + n_quant ? 1 : 2);
-      rank[(size_t)head * nwin + j] = rk;
+      const int r = rk[j];
+      t = r < n_full ? 0 : (r < n_full + n_quant ? 1 : 2);
+      rank[(size_t)head * nwin + j] = r;
       tier[(size_t)head * nwin + j] = (int8_t)t;
     }
     uint32_t tot;
