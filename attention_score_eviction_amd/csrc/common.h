@@ -12,6 +12,7 @@ namespace kvsel {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
@@ -61,6 +62,7 @@ struct ScorePlan {
   int GWr;        // GW rounded up to 16
   int maxqt;      // 16-row query tiles per workgroup (template choice)
   int nwaves;     // waves per workgroup
+  bool mfma32;    // bf16: 32-row query tiles on 32x32x16 matrix products (maxqt counts them)
   int qcap;       // rows per group = 16 * maxqt
   int ngroups;    // ceil(GW / qcap)
   int chunk;      // keys per workgroup

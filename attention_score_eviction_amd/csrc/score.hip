@@ -323,6 +323,301 @@ __global__ void __launch_bounds__(NW * 64) score_pass1(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 passes on v_mfma_f32_32x32x16_bf16.  A 32x32 matrix product keeps the
+// matrix core busy twice as long per instruction as the 16x16x32 form and
+// overlaps far better with the exponential / sum VALU work of the passes
+// (in-wave probe: MFMA stream + softmax VALU 548 cycles vs 705 for the same
+// work on 16x16x32; the VALU alone 504).
+//  * Query tiles are 32 rows, key tiles 32 keys; a 64-key block is two key
+//    tiles.  Lane (r = lane % 32, h = lane / 32) holds, of its tile's row r,
+//    the D/2 contiguous elements [h*D/2, (h+1)*D/2): its D bytes are its
+//    operand for all D/16 k-steps (step s takes elements h*D/2 + 8s .. +7, the
+//    same on both operands, so every d is covered once).
+//  * Result element i of lane l is (row 8*(i/4) + 4*h + i%4, column l % 32).
+// ---------------------------------------------------------------------------
+template <int NV>
+__device__ __forceinline__ f32x16_t mma32(const Frag<NV>& a, const Frag<NV>& b, f32x16_t c) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v[i]),
+                                                __builtin_bit_cast(bf16x8_t, b.v[i]), c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Two 32-key tiles starting at kb (rows past the end repeat the last key).
+template <int D>
+__device__ __forceinline__ void load_key_block32(Frag<D / 16> (&kf)[2], const char* kh, int kb,
+                                                 int S, int lane) {
+  constexpr int RB = D * 2;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int row = min(kb + kt * 32 + r, S - 1);
+    const char* src = kh + (size_t)row * RB + h * D;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) kf[kt].v[i] = *(const u32x4_t*)(src + 16 * i);
+  }
+}
+
+// Query rows [0, nrows) of a group into LDS in fragment order: vector
+// (tile t, v, lane) at (t*NV + v)*64 + lane; direct global->LDS copies.
+template <int D, int NT>
+__device__ __forceinline__ void stage_queries32(u32x4_t* qs, const uint16_t* qg, int nrows,
+                                                int nqt) {
+  constexpr int NV = D / 16;
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int tv = wave; tv < nqt * NV; tv += NW) {
+    const int t = tv / NV, v = tv - t * NV;
+    const int row = min(t * 32 + (lane & 31), nrows - 1);
+    const char* src = (const char*)(qg + (size_t)row * D) + (lane >> 5) * D + 16 * v;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)(qs + tv * 64),
+                                     16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+__device__ __forceinline__ float max16(const f32x16_t& x) {
+  const float a0 = max3f(x[0], x[1], x[2]), a1 = max3f(x[3], x[4], x[5]);
+  const float a2 = max3f(x[6], x[7], x[8]), a3 = max3f(x[9], x[10], x[11]);
+  const float a4 = max3f(x[12], x[13], x[14]);
+  return max3f(max3f(a0, a1, a2), max3f(a3, a4, x[15]), -INFINITY);
+}
+
+// Pass 1 on one 64-key block: lane (r, h) keeps the running (max, sum) of
+// query row t*32 + r over its 16 keys per key tile.
+template <int NV, int NQ, bool MASK>
+__device__ __forceinline__ void pass1_block32(const int* lims, const Frag<NV> (&kf)[2],
+                                              const u32x4_t* qs, float (&m)[NQ], float (&z)[NQ],
+                                              int kb, int lane, float c) {
+  const int r = lane & 31, h = lane >> 5;
+  f32x16_t acc[2][2];
+  {
+    Frag<NV> qf;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qf.v[i] = qs[i * 64 + lane];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) acc[0][kt] = mma32<NV>(kf[kt], qf, zero16());
+  }
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    f32x16_t(&cur)[2] = acc[t & 1];
+    if (t + 1 < NQ) {
+      Frag<NV> qf;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) qf.v[i] = qs[((t + 1) * NV + i) * 64 + lane];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[(t + 1) & 1][kt] = mma32<NV>(kf[kt], qf, zero16());
+    }
+    // cur[kt][i]: key kb + kt*32 + 8*(i/4) + 4h + i%4, query row t*32 + r
+    if constexpr (MASK) {
+      const int lim = lims[t * 32 + r];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3) > lim) cur[kt][i] = -INFINITY;
+    }
+    const float mx = fmaxf(max16(cur[0]), max16(cur[1]));
+    const float mnew = fmaxf(m[t], mx * c);
+    const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+    float e[32];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) e[kt * 16 + i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mu));
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) e[i] += e[i + w];
+    z[t] = z[t] * __builtin_amdgcn_exp2f(m[t] - mu) + e[0];
+    m[t] = mnew;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Pass 2 on one 64-key block: as[kt] collects, for key kb + kt*32 + r, the
+// normalised weights of the query rows 8j + 4h + q (j, q < 4) of every tile.
+template <int NV, int NQ, bool MASK>
+__device__ __forceinline__ void pass2_block32(const int* lims, const Frag<NV> (&kf)[2],
+                                              const u32x4_t* qs, const float* ls, float (&as)[2],
+                                              int kb, int lane, float c) {
+  const int r = lane & 31, h = lane >> 5;
+  f32x16_t acc[2][2];
+  {
+    Frag<NV> qf;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qf.v[i] = qs[i * 64 + lane];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) acc[0][kt] = mma32<NV>(qf, kf[kt], zero16());
+  }
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    f32x16_t(&cur)[2] = acc[t & 1];
+    if (t + 1 < NQ) {
+      Frag<NV> qf;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) qf.v[i] = qs[((t + 1) * NV + i) * 64 + lane];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[(t + 1) & 1][kt] = mma32<NV>(qf, kf[kt], zero16());
+    }
+    // cur[kt][i]: query row t*32 + 8*(i/4) + 4h + i%4, key kb + kt*32 + r
+    f32x4_t lq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lq[j] = *(const f32x4_t*)&ls[t * 32 + 8 * j + 4 * h];
+    if constexpr (MASK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int4 lim = *(const int4*)&lims[t * 32 + 8 * j + 4 * h];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int key = kb + kt * 32 + r;
+          if (key > lim.x) cur[kt][4 * j] = -INFINITY;
+          if (key > lim.y) cur[kt][4 * j + 1] = -INFINITY;
+          if (key > lim.z) cur[kt][4 * j + 2] = -INFINITY;
+          if (key > lim.w) cur[kt][4 * j + 3] = -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float e[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        e[i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -lq[i >> 2][i & 3]));
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) e[i] += e[i + w];
+      as[kt] += e[0];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D, int NQ, int NW>
+__global__ void __launch_bounds__(NW * 64) score_pass1_32(ScoreArgs a) {
+  constexpr int NV = D / 16;
+  constexpr int NT = NW * 64;
+  __shared__ u32x4_t qs[NQ * NV * 64];
+  __shared__ int lims[NQ * 32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, head = blockIdx.y, grp = blockIdx.z;
+  const int b = head / a.Hkv, hk = head - b * a.Hkv;
+  const int row0 = grp * a.qcap;
+  const int nrows = min(a.qcap, a.GW - row0);
+  const int S = a.S;
+  const float c = a.c;
+  const char* kh = (const char*)((const uint16_t*)a.k + (size_t)head * a.kstride * D);
+  const int k0 = chunk * a.chunk;
+  const int kend = min(S, k0 + a.chunk);
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+
+  int kb = k0 + wave * 64;
+  Frag<NV> kf[2];
+  if (kb < kend) load_key_block32<D>(kf, kh, kb, S, lane);
+  const uint16_t* qg = (const uint16_t*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
+  stage_queries32<D, NT>(qs, qg, nrows, NQ);
+  for (int r = tid; r < NQ * 32; r += NT) lims[r] = key_limit(a, row0 + r);
+  __syncthreads();
+
+  float m[NQ], z[NQ];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) { m[t] = -INFINITY; z[t] = 0.f; }
+  for (; kb < kend; kb += NW * 64) {
+    int lds_off = 0;
+    asm volatile("" : "+v"(lds_off));
+    const u32x4_t* qsv = qs + lds_off;
+    if (kb + 64 > mask_from)
+      pass1_block32<NV, NQ, true>(lims, kf, qsv, m, z, kb, lane, c);
+    else
+      pass1_block32<NV, NQ, false>(lims, kf, qsv, m, z, kb, lane, c);
+    if (kb + NW * 64 < kend) load_key_block32<D>(kf, kh, kb + NW * 64, S, lane);
+  }
+  // Lanes r and r + 32 hold partials of the same query row.
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const float mo = __shfl_xor(m[t], 32);
+    const float zo = __shfl_xor(z[t], 32);
+    lse_merge(m[t], z[t], mo, zo);
+  }
+  __syncthreads();  // the query tiles are no longer read
+  float2* red = (float2*)qs;  // [NW][NQ*32]
+  if (lane < 32) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) red[wave * NQ * 32 + t * 32 + lane] = make_float2(m[t], z[t]);
+  }
+  __syncthreads();
+  for (int r = tid; r < nrows; r += NT) {
+    float mm = -INFINITY, zz = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      const float2 pz = red[w * NQ * 32 + r];
+      lse_merge(mm, zz, pz.x, pz.y);
+    }
+    a.part[((size_t)head * a.GWr + row0 + r) * a.nchunk + chunk] = make_float2(mm, zz);
+  }
+}
+
+template <int D, int NQ, int NW>
+__global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
+  constexpr int NV = D / 16;
+  constexpr int NT = NW * 64;
+  __shared__ u32x4_t qs[NQ * NV * 64];
+  __shared__ float ls[NQ * 32];
+  __shared__ int lims[NQ * 32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, head = blockIdx.y, grp = blockIdx.z;
+  const int b = head / a.Hkv, hk = head - b * a.Hkv;
+  const int row0 = grp * a.qcap;
+  const int nrows = min(a.qcap, a.GW - row0);
+  const int S = a.S;
+  const float c = a.c;
+  const char* kh = (const char*)((const uint16_t*)a.k + (size_t)head * a.kstride * D);
+  const int k0 = chunk * a.chunk;
+  const int kend = min(S, k0 + a.chunk);
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+
+  int kb = k0 + wave * 64;
+  Frag<NV> kf[2];
+  if (kb < kend) load_key_block32<D>(kf, kh, kb, S, lane);
+  const uint16_t* qg = (const uint16_t*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
+  stage_queries32<D, NT>(qs, qg, nrows, NQ);
+  for (int r = tid; r < NQ * 32; r += NT) {
+    // rows past the group's end get an infinite normaliser (weight 0)
+    ls[r] = (r < nrows) ? a.lse[(size_t)head * a.GWr + row0 + r] : INFINITY;
+    lims[r] = key_limit(a, row0 + r);
+  }
+  __syncthreads();
+
+  float* out = a.s_out + ((size_t)grp * gridDim.y + head) * S;
+  for (; kb < kend; kb += NW * 64) {
+    int lds_off = 0;
+    asm volatile("" : "+v"(lds_off));
+    const u32x4_t* qsv = qs + lds_off;
+    const float* lsv = ls + lds_off;
+    float as[2] = {0.f, 0.f};
+    if (kb + 64 > mask_from)
+      pass2_block32<NV, NQ, true>(lims, kf, qsv, lsv, as, kb, lane, c);
+    else
+      pass2_block32<NV, NQ, false>(lims, kf, qsv, lsv, as, kb, lane, c);
+    if (kb + NW * 64 < kend) load_key_block32<D>(kf, kh, kb + NW * 64, S, lane);
+    as[0] += __shfl_xor(as[0], 32);
+    as[1] += __shfl_xor(as[1], 32);
+    // lane l writes key kb + l: key tile l / 32, column l % 32
+    const float mine = (lane >> 5) ? as[1] : as[0];
+    if (kb + lane < kend) out[kb + lane] = mine;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Combine the per-chunk partials of each query row: lse = max + log2(sum).
 // 2^tpr_log2 consecutive lanes share a row (just enough for about four
 // partials each, so short chunk lists do not leave a wave per row mostly
@@ -456,6 +751,30 @@ void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const S
   hipLaunchKernelGGL((score_pass2<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 
+template <int D, int NQ, int NW>
+void launch_passes32(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
+  hipLaunchKernelGGL((score_pass1_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
+  int tl = 0;
+  while ((4 << tl) < p.nchunk && tl < 6) ++tl;
+  const long lanes = ((long)p.nheads * p.GW) << tl;
+  hipLaunchKernelGGL(score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
+                     args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl);
+  hipLaunchKernelGGL((score_pass2_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
+}
+
+template <int D>
+bool dispatch_qt32(int nq, const ScoreArgs& args, dim3 grid, hipStream_t stream,
+                   const ScorePlan& p) {
+  switch (nq) {
+    case 1: launch_passes32<D, 1, 4>(args, grid, stream, p); return true;
+    case 2: launch_passes32<D, 2, 4>(args, grid, stream, p); return true;
+    case 4: launch_passes32<D, 4, 4>(args, grid, stream, p); return true;
+    case 8: launch_passes32<D, 8, 4>(args, grid, stream, p); return true;
+    case 10: launch_passes32<D, 10, 8>(args, grid, stream, p); return true;
+    default: return false;
+  }
+}
+
 template <typename T, int D>
 bool dispatch_qt(int nqt, const ScoreArgs& args, dim3 grid, hipStream_t stream,
                  const ScorePlan& p) {
@@ -477,6 +796,8 @@ bool dispatch_qt(int nqt, const ScoreArgs& args, dim3 grid, hipStream_t stream,
 
 }  // namespace
 
+static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes);
+
 bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   const int e = d.dtype == KVSEL_F32 ? 4 : 2;
   const int tile_bytes = 16 * d.head_dim * e;
@@ -489,6 +810,18 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   // count, when it fits in about 80 KiB of LDS (20 tiles of 4 KiB run 8 waves
   // per workgroup, one workgroup per CU); otherwise groups of 16 tiles, each
   // re-reading its key chunk.
+  p->mfma32 = d.dtype == KVSEL_BF16;
+  if (p->mfma32) {
+    // 32-row tiles: the whole group when it fits 10 tiles (8 waves), else
+    // groups of 8 tiles (4 waves); 32*D*2 bytes of LDS per tile.
+    const int nq = (p->GW + 31) / 32;
+    const int maxq = nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : nq <= 10 ? 10 : 8;
+    p->maxqt = maxq;
+    p->nwaves = maxq == 10 ? 8 : 4;
+    p->qcap = 32 * maxq;
+    p->ngroups = (p->GW + p->qcap - 1) / p->qcap;
+    return plan_chunks(d, p, maxq * 32 * d.head_dim * 2 + maxq * 32 * 8);
+  }
   int maxqt;
   if (nqt <= 1) maxqt = 1;
   else if (nqt <= 2) maxqt = 2;
@@ -502,11 +835,15 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   p->nwaves = (maxqt == 20) ? 8 : 4;
   p->qcap = 16 * maxqt;
   p->ngroups = (p->GW + p->qcap - 1) / p->qcap;
+  return plan_chunks(d, p, maxqt * tile_bytes + maxqt * 16 * 8);
+}
+
+// Key chunks and the workspace layout for a plan whose tiles are chosen.
+static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes) {
   // Key chunk: a multiple of one workgroup step, sized so the grid is about
   // one full wave of resident workgroups (fewer, longer workgroups amortise
   // the query staging and keep the key prefetch busy).
   const int step = p->nwaves * 64;
-  const int lds_bytes = maxqt * tile_bytes + maxqt * 16 * 8;
   int wg_per_cu = (160 * 1024) / lds_bytes;
   const int wave_cap = 8 / p->nwaves;     // about two waves per SIMD
   if (wg_per_cu > wave_cap) wg_per_cu = wave_cap;
@@ -558,7 +895,10 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   a.c = scale * kLog2e;
   const dim3 grid(p.nchunk, p.nheads, p.ngroups);
   bool ok = false;
-  if (d.dtype == KVSEL_BF16) {
+  if (p.mfma32) {
+    ok = d.head_dim == 128 ? dispatch_qt32<128>(p.maxqt, a, grid, stream, p)
+                           : dispatch_qt32<64>(p.maxqt, a, grid, stream, p);
+  } else if (d.dtype == KVSEL_BF16) {
     ok = d.head_dim == 128 ? dispatch_qt<uint16_t, 128>(p.maxqt, a, grid, stream, p)
                            : dispatch_qt<uint16_t, 64>(p.maxqt, a, grid, stream, p);
   } else {
