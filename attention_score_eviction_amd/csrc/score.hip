@@ -771,6 +771,7 @@ bool dispatch_qt32(int nq, const ScoreArgs& args, dim3 grid, hipStream_t stream,
     case 4: launch_passes32<D, 4, 4>(args, grid, stream, p); return true;
     case 8: launch_passes32<D, 8, 4>(args, grid, stream, p); return true;
     case 10: launch_passes32<D, 10, 8>(args, grid, stream, p); return true;
+    case 16: launch_passes32<D, 16, 8>(args, grid, stream, p); return true;
     default: return false;
   }
 }
@@ -813,11 +814,12 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   p->mfma32 = d.dtype == KVSEL_BF16;
   if (p->mfma32) {
     // 32-row tiles: the whole group when it fits 10 tiles (8 waves), else
-    // groups of 8 tiles (4 waves); 32*D*2 bytes of LDS per tile.
+    // groups of 16 tiles (8 waves, 128 KiB of LDS at D = 128: fewer groups
+    // re-reading each key chunk); 32*D*2 bytes of LDS per tile.
     const int nq = (p->GW + 31) / 32;
-    const int maxq = nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : nq <= 10 ? 10 : 8;
+    const int maxq = nq <= 1 ? 1 : nq <= 2 ? 2 : nq <= 4 ? 4 : nq <= 8 ? 8 : nq <= 10 ? 10 : 16;
     p->maxqt = maxq;
-    p->nwaves = maxq == 10 ? 8 : 4;
+    p->nwaves = maxq >= 10 ? 8 : 4;
     p->qcap = 32 * maxq;
     p->ngroups = (p->GW + p->qcap - 1) / p->qcap;
     return plan_chunks(d, p, maxq * 32 * d.head_dim * 2 + maxq * 32 * 8);
