@@ -811,7 +811,9 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   // count, when it fits in about 80 KiB of LDS (20 tiles of 4 KiB run 8 waves
   // per workgroup, one workgroup per CU); otherwise groups of 16 tiles, each
   // re-reading its key chunk.
-  p->mfma32 = d.dtype == KVSEL_BF16;
+  // 32x32 tiles for bf16 prompts of 4096 keys or more; the 16x16 form is
+  // faster on short key ranges (the 448-key decode window: 304 vs 353 us).
+  p->mfma32 = d.dtype == KVSEL_BF16 && d.seq_len >= 4096;
   if (p->mfma32) {
     // 32-row tiles: the whole group when it fits 10 tiles (8 waves), else
     // groups of 16 tiles (8 waves, 128 KiB of LDS at D = 128: fewer groups

@@ -43,6 +43,12 @@ SMALL = [
     ("bf16-window-is-all", L(1, 2, 1, 128, 64, 64, 5, 0), 110),
     ("bf16-single-key", L(1, 2, 2, 64, 1, 1, 1, 0), 111),
     ("bf16-spans", L(1, 5, 1, 128, 4096, 64, 7, 512, structure="spans", n_spans=8), 112),
+    # prompts of 4096 keys or more run the 32x32 tiling: D = 64, a ragged
+    # tail, sinks, no mask, and two query groups (640 rows: 512 + 128)
+    ("bf16-long-d64-ragged", L(1, 4, 2, 64, 4500, 24, 5, 300, n_sink=2, structure="heavy"), 113),
+    ("bf16-long-gw640-groups", L(1, 20, 2, 128, 4160, 64, 7, 256), 114),
+    ("bf16-long-noncausal", L(1, 8, 2, 128, 5000, 40, 3, 100, causal=0, structure="heavy"), 115),
+    ("bf16-long-gw320", L(1, 10, 2, 128, 4100, 64, 7, 128, n_sink=4), 116),
 ]
 
 
