@@ -132,3 +132,33 @@ def test_kara_window_end_to_end(shape, dtype, seed):
     assert exact_rows >= max(1, Bt * Hkv // 4)
     assert rows_gathered(host_bits(out["k_hat"]), x["k"], got)
     assert rows_gathered(host_bits(out["v_hat"]), x["v"], got)
+
+
+def test_kara_bench_config_sampled_rows():
+    """The benchmarked configuration in full (64 sequences of a 32/8-head,
+    D = 128 layer, 512-token windows, 64-token buffer, r = 40%, gamma 8,
+    alpha 32); three sequences replayed through the oracle."""
+    kvsel = _kvsel()
+    Bt, Hq, Hkv, Wn, U, D = 64, 32, 8, 512, 64, 128
+    x = synth.decode_window(7, Bt, Hq, Hkv, Wn, D)
+    q, k, v = (dev_tensor(x[t], "bf16") for t in ("q", "k", "v"))
+    ratio, gamma, alpha = 0.4, 8, 32
+    print("case kara bench config 64 x 512", flush=True)
+    out = kvsel.kara_compress(q, k, v, buffer=U, ratio=ratio, gamma=gamma, alpha=alpha)
+    torch.cuda.synchronize()
+    n = Wn - U
+    keep = out["desc"].keep
+    A = out["A"].cpu().numpy()
+    got = out["idx"].cpu().numpy()
+    exact = 0
+    for b in (0, 31, 63):
+        A_ref = oracle.kara_scores(synth.to_f64(x["q"][b:b + 1], "bf16"),
+                                   synth.to_f64(x["k"][b:b + 1], "bf16")[:, :, :n])
+        assert_scores_close(A[b:b + 1], A_ref, what=f"Kara importance, sequence {b}")
+        want = oracle.kara_select(A_ref, keep, gamma, alpha, U)
+        for h in range(Hkv):
+            if _margins_ok(A_ref[0, h], keep, gamma, alpha):
+                assert got[b, h].tolist() == want[0, h].tolist(), (b, h)
+                exact += 1
+        assert rows_gathered(host_bits(out["k_hat"][b:b + 1]), x["k"][b:b + 1], got[b:b + 1])
+    assert exact >= 6
