@@ -192,11 +192,15 @@ def select_workspace_bytes(desc: Desc, budget: int) -> int:
 def score(q_obs: torch.Tensor, k: torch.Tensor, *, pool_kernel: int, n_sink: int = 0,
           causal: bool = True, scale: float = 0.0, pooled: Optional[torch.Tensor] = None,
           raw: Optional[torch.Tensor] = None, want_raw: bool = True,
-          workspace: Optional[torch.Tensor] = None, stream=None):
-    """kvsel_score: returns (pooled [Bt,Hkv,S] fp32, raw [Bt,Hkv,S] fp32 or None)."""
+          want_pooled: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_score: returns (pooled [Bt,Hkv,S] fp32 or None, raw [Bt,Hkv,S] fp32 or
+    None).  want_pooled=False skips the max filter (raw scores only)."""
     d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
     shape = (d.batch, d.n_kv_heads, d.seq_len)
-    if pooled is None:
+    if not want_pooled:
+        pooled = None
+        want_raw = True
+    elif pooled is None:
         pooled = torch.empty(shape, dtype=torch.float32, device=k.device)
     if raw is None and want_raw:
         raw = torch.empty(shape, dtype=torch.float32, device=k.device)

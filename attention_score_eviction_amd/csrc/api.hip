@@ -133,7 +133,7 @@ kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* 
                          size_t ws_bytes, void* stream) {
   const kvsel_status st = check_desc(desc);
   if (st != KVSEL_OK) return st;
-  if (!q_obs || !k || !pooled) return KVSEL_ERR_ARG;
+  if (!q_obs || !k || (!pooled && !raw_scores)) return KVSEL_ERR_ARG;
   if (!aligned16(q_obs) || !aligned16(k) || !aligned16(pooled) || !aligned16(raw_scores))
     return KVSEL_ERR_ARG;
   if (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 1 + 2 * (1 << 20))

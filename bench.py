@@ -466,15 +466,14 @@ def bench_tiers(args, kvsel, torch, spec, wname, dev, stream) -> int:
         synth.promote_list(5, Bt * Hkv, n_quant, n_prom).reshape(Bt, Hkv, n_prom)).to(dev)
     desc = kvsel.make_desc(q, k, causal=False)
     ws = torch.empty(kvsel.score_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    pooled = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev)
-    raw = torch.empty_like(pooled)
+    raw = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev)
     outs = kvsel.route_tiers(raw, k, v, n_full=n_full, n_quant=n_quant, promote=promote)
     tws = torch.empty(kvsel.route_tiers_workspace_bytes(
         kvsel.TierDesc(Bt, Hkv, D, S, 64, n_full, n_quant, kvsel.BF16)), dtype=torch.uint8,
         device=dev)
 
     def score():
-        kvsel.score(q, k, pool_kernel=1, causal=False, pooled=pooled, raw=raw, workspace=ws,
+        kvsel.score(q, k, pool_kernel=1, causal=False, want_pooled=False, raw=raw, workspace=ws,
                     stream=stream)
 
     def tiers():
@@ -613,12 +612,11 @@ def bench_qevict_steps(args, kvsel, torch, spec, wname) -> int:
     desc = kvsel.make_desc(qs[0], k, causal=False)
     sws = torch.empty(kvsel.score_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     raw = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev)
-    pooled = torch.empty_like(raw)
     it = [0]
 
     def score():
         q = qs[it[0] % n_sets]
-        kvsel.score(q, k, pool_kernel=1, causal=False, pooled=pooled, raw=raw, workspace=sws,
+        kvsel.score(q, k, pool_kernel=1, causal=False, want_pooled=False, raw=raw, workspace=sws,
                     stream=stream)
 
     def route():
@@ -638,7 +636,7 @@ def bench_qevict_steps(args, kvsel, torch, spec, wname) -> int:
           "kvsel_qevict_step": event_time_us(torch, stream, route, steps)}
     H = Bt * Hkv
     t = state["tier"].cpu().numpy()
-    score_bytes = 2 * H * S * D * 2 + 2 * H * S * 4
+    score_bytes = 2 * H * S * D * 2 + H * S * 4   # two K sweeps + the raw scores
     dom_gbs = score_bytes / (us["kvsel_score"] * 1e-6) / 1e9
     out = {
         "metric": METRIC, "value": round(Bt * S / (step_us * 1e-6), 1), "unit": "tokens/s",

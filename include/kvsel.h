@@ -110,12 +110,14 @@ size_t kvsel_score_workspace(const kvsel_desc* desc);
  *   q_obs       [Bt,Hq,W,D] dtype, device
  *   k           [Bt,Hkv,S,D] dtype, device
  *   raw_scores  [Bt,Hkv,S] float32, device, may be NULL (then kept in ws)
- *   pooled      [Bt,Hkv,S] float32, device, required
+ *   pooled      [Bt,Hkv,S] float32, device; may be NULL when raw_scores is
+ *               given (callers that rank the raw scores themselves, as the
+ *               decode-time window routers do, skip the max filter)
  *   pool_kernel odd, >= 1
  *   ws          device scratch of >= kvsel_score_workspace(desc) bytes
  *               (may be NULL when that size is 0)
- * Errors: KVSEL_ERR_ARG (shape, pointer, pool_kernel even or < 1),
- *         KVSEL_ERR_UNSUPPORTED (head_dim), KVSEL_ERR_WORKSPACE,
+ * Errors: KVSEL_ERR_ARG (shape, pointer, both outputs NULL, pool_kernel even
+ *         or < 1), KVSEL_ERR_UNSUPPORTED (head_dim), KVSEL_ERR_WORKSPACE,
  *         KVSEL_ERR_DEVICE.
  * Numerics: bf16 or fp32 inputs, fp32 products and sums; the result does
  * not depend on how the keys are blocked; repeated calls are bitwise equal.

@@ -90,6 +90,20 @@ def test_small_parity(name, spec, cid):
     _run_and_check(dataclasses.replace(spec, name=name), cid)
 
 
+def test_raw_only_scores_equal_pooled_call():
+    """kvsel_score with pooled = NULL (raw scores only, no max filter) gives
+    the same raw scores, bit for bit, as the full call."""
+    kvsel = _kvsel()
+    spec = dataclasses.replace(synth.config(2), seq_len=5000, obs_window=32)
+    x = synth.make_layer(spec, 2)
+    q, k = dev_tensor(x["q"], "bf16"), dev_tensor(x["k"], "bf16")
+    _, raw_full = kvsel.score(q, k, pool_kernel=7)
+    pooled, raw_only = kvsel.score(q, k, pool_kernel=7, want_pooled=False)
+    torch.cuda.synchronize()
+    assert pooled is None
+    assert torch.equal(raw_full, raw_only)
+
+
 def test_score_is_deterministic():
     kvsel = _kvsel()
     spec = synth.config(2)
