@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.kvsel_select.restype = ctypes.c_int
     L.kvsel_compact.argtypes = [DP, P, P, P, I32, P, P, P]
     L.kvsel_compact.restype = ctypes.c_int
+    L.kvsel_select_compact.argtypes = [DP, P, I32, P, P, P, P, P, P, SZ, P]
+    L.kvsel_select_compact.restype = ctypes.c_int
     L.kvsel_select_adaptive_workspace.argtypes = [DP, I32]
     L.kvsel_select_adaptive_workspace.restype = SZ
     L.kvsel_select_adaptive.argtypes = [DP, P, I32, P, P, P, SZ, P]
@@ -252,6 +254,32 @@ def compact(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, *,
     return k_out, v_out
 
 
+def select_compact(pooled: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
+                   budget: int, *, obs_window: int, n_q_heads: int, n_sink: int = 0,
+                   causal: bool = True, idx: Optional[torch.Tensor] = None,
+                   k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_select_compact: returns (idx, k_hat, v_hat), the outputs of
+    select() followed by compact()."""
+    Bt, Hkv, S, D = k.shape
+    d = Desc(Bt, n_q_heads, Hkv, D, S, obs_window, n_sink, int(causal), _dtype_code(k), 0.0)
+    n_keep = budget + n_sink + obs_window
+    if idx is None:
+        idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=k.device)
+    if k_out is None:
+        k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
+    if v is not None and v_out is None:
+        v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
+    if workspace is None:
+        workspace = torch.empty(max(select_workspace_bytes(d, budget), 1), dtype=torch.uint8,
+                                device=k.device)
+    st = lib().kvsel_select_compact(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx),
+                                    _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "kvsel_select_compact")
+    return idx, k_out, v_out
+
+
 def select_adaptive_workspace_bytes(desc: Desc, total_budget: int) -> int:
     return int(lib().kvsel_select_adaptive_workspace(ctypes.byref(desc), int(total_budget)))
 
@@ -301,13 +329,14 @@ def compact_flat(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor,
 def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
                        pool_kernel: int, n_sink: int = 0, causal: bool = True,
                        scale: float = 0.0, stream=None) -> dict:
-    """score -> select -> compact on one stream (TideKV's layer-end step)."""
+    """score -> select + compact (kvsel_select_compact) on one stream: TideKV's
+    layer-end step."""
     W = q_obs.shape[2]
     pooled, raw = score(q_obs, k, pool_kernel=pool_kernel, n_sink=n_sink, causal=causal,
                         scale=scale, stream=stream)
-    idx = select(pooled, budget, obs_window=W, n_q_heads=q_obs.shape[1], head_dim=k.shape[3],
-                 n_sink=n_sink, causal=causal, dtype=k.dtype, stream=stream)
-    k_hat, v_hat = compact(k, v, idx, stream=stream)
+    idx, k_hat, v_hat = select_compact(pooled, k, v, budget, obs_window=W,
+                                       n_q_heads=q_obs.shape[1], n_sink=n_sink, causal=causal,
+                                       stream=stream)
     return {"s": raw, "p": pooled, "idx": idx, "k_hat": k_hat, "v_hat": v_hat}
 
 
@@ -436,7 +465,7 @@ EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_se
            "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers",
            "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat",
            "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select",
-           "kvsel_qevict_step_workspace", "kvsel_qevict_step")
+           "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact")
 
 
 # ---------------------------------------------------------------------------

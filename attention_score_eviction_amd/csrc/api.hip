@@ -168,6 +168,26 @@ kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t b
   return launch_select(*desc, p, pooled, budget, idx, nullptr, (char*)ws, (hipStream_t)stream);
 }
 
+kvsel_status kvsel_select_compact(const kvsel_desc* desc, const float* pooled, int32_t budget,
+                                  int32_t* idx, const void* k, const void* v, void* k_out,
+                                  void* v_out, void* ws, size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink)
+    return KVSEL_ERR_BUDGET;
+  if (!pooled || !idx || !k || !k_out) return KVSEL_ERR_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVSEL_ERR_ARG;
+  const void* ptrs[] = {pooled, idx, k, v, k_out, v_out};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return KVSEL_ERR_ARG;
+  SelectPlan p;
+  plan_select(*desc, budget, 1, &p);
+  if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVSEL_ERR_ARG;
+  return launch_select_compact(*desc, p, pooled, budget, idx, k, v, k_out, v_out, (char*)ws,
+                               (hipStream_t)stream);
+}
+
 size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget) {
   if (check_adaptive(desc, total_budget) != KVSEL_OK) return 0;
   SelectPlan p;

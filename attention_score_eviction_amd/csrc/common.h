@@ -105,6 +105,10 @@ bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p);
 kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
                            int budget, int32_t* idx, int32_t* head_off, char* ws,
                            hipStream_t stream);
+// Per-head select and gather in one launch for short rows (else the two).
+kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
+                                   int budget, int32_t* idx, const void* k, const void* v,
+                                   void* k_out, void* v_out, char* ws, hipStream_t stream);
 kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
                             const int32_t* idx, int n_keep, void* k_out, void* v_out,
                             hipStream_t stream);

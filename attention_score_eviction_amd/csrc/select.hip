@@ -177,19 +177,41 @@ constexpr int kMaxWgHeads = 64;
 // thread, so thread order within a batch is (head, position) order.  The
 // first NB batches stay in registers for the whole kernel; later ones (only
 // for rows longer than the sliced kernels take) are reloaded per pass.
-template <int NT, int NB>
+//
+// GATHER (kvsel_select_compact, per-head groups, n_keep <= kMaxFusedKeep):
+// `reps` workgroups per group each run the same selection (it is
+// deterministic), keep the retained positions in LDS, and copy their share
+// of the retained K/V rows; replica 0 also writes the index row.  The short
+// rows this serves leave most CUs idle, so the repeated selection costs
+// nothing extra and the separate gather launch disappears.
+constexpr int kMaxFusedKeep = 4096;
+
+struct GatherArgs {
+  const u32x4_t* k;   // [groups][S][vpr]
+  const u32x4_t* v;   // nullable
+  u32x4_t* ko;        // [groups][n_keep][vpr]
+  u32x4_t* vo;
+  int vpr;            // 16-byte vectors per row
+  int reps;           // workgroups per group
+};
+
+template <int NT, int NB, bool GATHER>
 __global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ pooled,
                                                     int32_t* __restrict__ idx,
                                                     int32_t* __restrict__ head_off, int S,
                                                     int lo, int hi, int budget, int n_sink,
-                                                    int W, int n_keep, int hg, int nsl) {
+                                                    int W, int n_keep, int hg, int nsl,
+                                                    GatherArgs ga) {
   // One histogram per digit, all cleared up front: a round is then one
   // barrier after its counts and one after the digit search.
   __shared__ __attribute__((aligned(16))) uint32_t hist[2048 + 1024 + 1024];
   __shared__ uint32_t wsum[NT / 64];
   __shared__ uint32_t pick[3];
   __shared__ uint32_t kept[kMaxWgHeads];
-  const int grp = blockIdx.x, tid = threadIdx.x;
+  __shared__ int32_t sidx[GATHER ? kMaxFusedKeep : 1];   // retained positions, in order
+  const int grp = GATHER ? (int)blockIdx.x / ga.reps : (int)blockIdx.x, tid = threadIdx.x;
+  const int rep = GATHER ? (int)blockIdx.x - grp * ga.reps : 0;
+  const bool writer = rep == 0;   // the replica that writes the index row
   const int seg = n_sink + W;
   int32_t* out = idx + (size_t)grp * n_keep;
   const int nbatch = (hg * nsl + NT - 1) / NT;
@@ -312,14 +334,16 @@ __global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ po
         if ((gt >> e) & 1u) {
           const uint32_t slot = gtb + min(eqb, need_eq);
           if (slot < (uint32_t)budget) {
-            oh[slot] = p0 + e;
+            if (writer) oh[slot] = p0 + e;
+            if constexpr (GATHER) sidx[h * seg + n_sink + slot] = p0 + e;
             ++nw;
           }
           ++gtb;
         } else if ((eq >> e) & 1u) {
           const uint32_t slot = gtb + eqb;
           if (eqb < need_eq && slot < (uint32_t)budget) {
-            oh[slot] = p0 + e;
+            if (writer) oh[slot] = p0 + e;
+            if constexpr (GATHER) sidx[h * seg + n_sink + slot] = p0 + e;
             ++nw;
           }
           ++eqb;
@@ -337,14 +361,39 @@ __global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ po
     for (int k = 0; k < h; ++k) c += kept[k];
     return c;
   };
-  if (head_off)
+  if (head_off && writer)
     for (int h = tid; h <= hg; h += NT)
       head_off[(size_t)grp * (hg + 1) + h] = (int32_t)(h * seg + picks_before(h));
   for (int t = tid; t < hg * seg; t += NT) {
     const int h = t / seg, j = t - h * seg;
     const uint32_t start = h * seg + picks_before(h);
-    if (j < n_sink) out[start + j] = j;
-    else out[start + n_sink + kept[h] + (j - n_sink)] = S - W + (j - n_sink);
+    const uint32_t row = j < n_sink ? start + j : start + n_sink + kept[h] + (j - n_sink);
+    const int32_t pos = j < n_sink ? j : S - W + (j - n_sink);
+    if (writer) out[row] = pos;
+    if constexpr (GATHER) sidx[row] = pos;
+  }
+  if constexpr (GATHER) {
+    // This replica's share of the retained rows (one KV head per group).
+    __syncthreads();
+    const int share = (n_keep + ga.reps - 1) / ga.reps;
+    const int r0 = rep * share, r1 = min(n_keep, r0 + share);
+    const int vpr = ga.vpr;
+    for (int t = tid; t < (r1 - r0) * vpr; t += NT) {
+      const int r = r0 + t / vpr, c = t - (t / vpr) * vpr;
+      const int src = sidx[r];
+      const bool ok = src >= 0 && src < S;
+      const size_t so = ((size_t)grp * S + (ok ? src : 0)) * vpr + c;
+      const size_t dst = ((size_t)grp * n_keep + r) * vpr + c;
+      const u32x4_t zero = {0u, 0u, 0u, 0u};
+      const u32x4_t kx = ok ? ga.k[so] : zero;
+      if (ga.v) {
+        const u32x4_t vx = ok ? ga.v[so] : zero;
+        ga.ko[dst] = kx;
+        ga.vo[dst] = vx;
+      } else {
+        ga.ko[dst] = kx;
+      }
+    }
   }
 }
 
@@ -821,9 +870,11 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
     // thread): no idle threads on short rows, fewer waves at each barrier.
     const long tot = (long)p.nsl * hg;
     const dim3 g(groups);
-#define KVSEL_SELECT_1WG(NT, NB)                                                            \
-  hipLaunchKernelGGL((select_kernel<NT, NB>), g, dim3(NT), 0, stream, pooled, idx, head_off, \
-                     d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep, hg, p.nsl)
+    const GatherArgs none = {nullptr, nullptr, nullptr, nullptr, 0, 1};
+#define KVSEL_SELECT_1WG(NT, NB)                                                              \
+  hipLaunchKernelGGL((select_kernel<NT, NB, false>), g, dim3(NT), 0, stream, pooled, idx,      \
+                     head_off, d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep, hg, \
+                     p.nsl, none)
     if (tot <= 256) KVSEL_SELECT_1WG(256, 1);
     else if (tot <= 512) KVSEL_SELECT_1WG(512, 1);
     else KVSEL_SELECT_1WG(512, 2);   // beyond 1024 slices: later batches reloaded
@@ -859,6 +910,42 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   hipLaunchKernelGGL(sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_resolve, dim3(groups), dim3(kSelThreads), 0, stream, a);
   hipLaunchKernelGGL(sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
+                                   int budget, int32_t* idx, const void* k, const void* v,
+                                   void* k_out, void* v_out, char* ws, hipStream_t stream) {
+  const int seg = d.n_sink + d.obs_window;
+  const int n_keep = seg + budget;
+  const int e = d.dtype == KVSEL_F32 ? 4 : 2;
+  if (p.multi || p.hg != 1 || n_keep > kMaxFusedKeep) {
+    const kvsel_status st = launch_select(d, p, pooled, budget, idx, nullptr, ws, stream);
+    if (st != KVSEL_OK) return st;
+    return launch_compact(d, k, v, idx, n_keep, k_out, v_out, stream);
+  }
+  // Enough replicas to spread the gather over the chip, at least 16 rows each.
+  int reps = 256 / p.groups;
+  if (reps > n_keep / 16) reps = n_keep / 16;
+  if (reps < 1) reps = 1;
+  GatherArgs ga;
+  ga.k = (const u32x4_t*)k;
+  ga.v = (const u32x4_t*)v;
+  ga.ko = (u32x4_t*)k_out;
+  ga.vo = (u32x4_t*)v_out;
+  ga.vpr = d.head_dim * e / 16;
+  ga.reps = reps;
+  const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
+  const long tot = (long)p.nsl;
+  const dim3 g(p.groups * reps);
+#define KVSEL_SELECT_GATHER(NT, NB)                                                          \
+  hipLaunchKernelGGL((select_kernel<NT, NB, true>), g, dim3(NT), 0, stream, pooled, idx,      \
+                     (int32_t*)nullptr, d.seq_len, lo, hi, budget, d.n_sink, d.obs_window,    \
+                     n_keep, 1, p.nsl, ga)
+  if (tot <= 256) KVSEL_SELECT_GATHER(256, 1);
+  else if (tot <= 512) KVSEL_SELECT_GATHER(512, 1);
+  else KVSEL_SELECT_GATHER(512, 2);
+#undef KVSEL_SELECT_GATHER
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 

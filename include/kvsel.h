@@ -225,6 +225,25 @@ kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
                            void* stream);
 
 /*
+ * kvsel_select_compact -- kvsel_select followed by kvsel_compact with
+ * n_keep = budget + n_sink + W (Eq. 8, then Algorithm 2's GATHER), in one
+ * launch when a KV head's candidates fit one workgroup and n_keep <= 4096
+ * (every other shape runs the two steps in order).  The outputs are exactly
+ * those of the two calls: idx as kvsel_select writes it, and k_out, v_out as
+ * kvsel_compact writes them from that idx.
+ *
+ *   pooled       [Bt,Hkv,S] float32, device (kvsel_score)
+ *   idx          [Bt,Hkv,budget+n_sink+W] int32 out, device
+ *   k, v         [Bt,Hkv,S,D] dtype, device (v may be NULL with v_out)
+ *   k_out, v_out [Bt,Hkv,budget+n_sink+W,D] dtype out, device
+ *   ws           device scratch of >= kvsel_select_workspace(desc, budget)
+ * Errors: those of kvsel_select and kvsel_compact.
+ */
+kvsel_status kvsel_select_compact(const kvsel_desc* desc, const float* pooled, int32_t budget,
+                                  int32_t* idx, const void* k, const void* v, void* k_out,
+                                  void* v_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kara decode-window compression (Kara, "Kara: Efficient Reasoning LLM
  * Serving via Sliding-Window KV Cache Compression", Section 3).  A window of
  * `window` recent tokens per (sequence, KV head); its last `buffer` tokens

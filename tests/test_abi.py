@@ -173,6 +173,23 @@ def test_kara_checks(kv):
     assert need < 64 * 1024 * 1024
 
 
+def test_select_compact_checks(kv):
+    L = kv.lib()
+    call = lambda d, b=100, idx=FAKE, k=FAKE, v=FAKE, ko=FAKE, vo=FAKE, ws=FAKE, wsb=1 << 30: \
+        L.kvsel_select_compact(ctypes.byref(d), FAKE, b, idx, k, v, ko, vo, ws, wsb, None)  # noqa
+    d = _desc(kv)
+    assert call(d, b=-1) == kv.ERR_BUDGET
+    assert call(d, b=8192 - 32 + 1) == kv.ERR_BUDGET
+    assert call(d, idx=None) == kv.ERR_ARG
+    assert call(d, k=None) == kv.ERR_ARG
+    assert call(d, vo=None) == kv.ERR_ARG          # v without v_out
+    assert call(d, ko=FAKE + 4) == kv.ERR_ARG
+    long_d = _desc(kv, seq_len=131072, obs_window=64)
+    need = L.kvsel_select_workspace(ctypes.byref(long_d), 4096)
+    assert need > 0
+    assert call(long_d, b=4096, wsb=need - 1) == kv.ERR_WORKSPACE
+
+
 def test_compact_checks(kv):
     L = kv.lib()
     d = _desc(kv)

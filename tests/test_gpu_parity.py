@@ -90,6 +90,41 @@ def test_small_parity(name, spec, cid):
     _run_and_check(dataclasses.replace(spec, name=name), cid)
 
 
+@pytest.mark.parametrize("seed,Bt,Hq,Hkv,D,S,W,n_sink,budget,dtype,with_v", [
+    (0, 1, 32, 8, 128, 8192, 32, 0, 1024, "bf16", True),     # the 8K layer
+    (1, 2, 8, 2, 128, 3001, 20, 3, 200, "bf16", True),       # ragged, sinks
+    (2, 1, 4, 2, 64, 900, 16, 0, 0, "f32", True),            # budget 0
+    (3, 1, 4, 4, 128, 5000, 40, 2, 4000, "bf16", False),     # n_keep 4042, K only
+    (4, 1, 8, 2, 128, 20000, 64, 0, 4096, "bf16", True),     # long rows: two launches
+])
+def test_select_compact_equals_select_then_compact(seed, Bt, Hq, Hkv, D, S, W, n_sink, budget,
+                                                   dtype, with_v):
+    """kvsel_select_compact gives exactly the outputs of kvsel_select followed
+    by kvsel_compact."""
+    kvsel = _kvsel()
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    # pooled-like scores: non-negative with repeated values (plateaus)
+    pooled = torch.rand((Bt, Hkv, S), generator=g, device="cuda")
+    pooled = torch.floor(pooled * 4096) / 4096
+    k = torch.randn((Bt, Hkv, S, D), generator=g, device="cuda").to(tdt)
+    v = torch.randn((Bt, Hkv, S, D), generator=g, device="cuda").to(tdt) if with_v else None
+    print(f"case select_compact seed {seed} S={S} budget={budget}", flush=True)
+    idx1 = kvsel.select(pooled, budget, obs_window=W, n_q_heads=Hq, head_dim=D, n_sink=n_sink,
+                        dtype=tdt)
+    k1, v1 = kvsel.compact(k, v, idx1)
+    idx2, k2, v2 = kvsel.select_compact(pooled, k, v, budget, obs_window=W, n_q_heads=Hq,
+                                        n_sink=n_sink)
+    torch.cuda.synchronize()
+    bits = torch.int16 if tdt == torch.bfloat16 else torch.int32
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(k1.view(bits), k2.view(bits))
+    if with_v:
+        assert torch.equal(v1.view(bits), v2.view(bits))
+    else:
+        assert v2 is None
+
+
 def test_raw_only_scores_equal_pooled_call():
     """kvsel_score with pooled = NULL (raw scores only, no max filter) gives
     the same raw scores, bit for bit, as the full call."""
