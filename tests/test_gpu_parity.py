@@ -49,6 +49,7 @@ SMALL = [
     ("bf16-long-gw640-groups", L(1, 20, 2, 128, 4160, 64, 7, 256), 114),
     ("bf16-long-noncausal", L(1, 8, 2, 128, 5000, 40, 3, 100, causal=0, structure="heavy"), 115),
     ("bf16-long-gw320", L(1, 10, 2, 128, 4100, 64, 7, 128, n_sink=4), 116),
+    ("bf16-long-d64-gw384", L(1, 12, 2, 64, 4200, 64, 5, 100, structure="heavy"), 117),
 ]
 
 
