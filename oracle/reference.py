@@ -11,7 +11,7 @@ Sources (the pages' titles; section / equation / algorithm of each):
   Long-Context Decoding": §4.2 cumulative window scoring, §4.3 recoverable
   hierarchy, Appendix A routing.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 pooling weights w_q = 1; GQA aggregation is a sum over the group with query
 head h mapped to KV head floor(h / G); the 1-D max-pool over key positions runs
 over the candidate range only, stride 1, window clipped at its edges; ties in
