@@ -8,8 +8,13 @@ Sources (the pages' titles; section / equation / algorithm of each):
   Memory-Efficient Long-Context LLM Inference": §4.2 Eqs. (4)-(8),
   Algorithm 2 (LayerEndCompress), §4.3 memory model, §6.1 setup.
 * QEvict -- "Recoverable Quantized KV Eviction for Attention-Drift-Robust
-  Long-Context Decoding": §4.2 cumulative window scoring, §4.3 recoverable
-  hierarchy, Appendix A routing.
+  Long-Context Decoding": §4.1 protected regions and windows, §4.2
+  cumulative window scoring repeated every Omega tokens, §4.3 recoverable
+  hierarchy, Appendix A routing, §1 persistent backing store, §B.5 defaults
+  (INT2 tier, five sinks).
+* Kara -- "Kara: Efficient Reasoning LLM Serving via Sliding-Window KV Cache
+  Compression": §3.1 Eq. (4) bidirectional window scoring, §3.2 Eqs. (5)-(8)
+  Token2Chunk and its fill-up rule.
 
 Readings where the pages are silent:
 pooling weights w_q = 1; GQA aggregation is a sum over the group with query
