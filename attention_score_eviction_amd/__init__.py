@@ -14,9 +14,10 @@ There is no CPU fallback: without the built library every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
+from contextlib import nullcontext
 from dataclasses import dataclass
+from fractions import Fraction
 from typing import Optional
 
 import torch
@@ -130,6 +131,12 @@ def lib() -> ctypes.CDLL:
     L.kvsel_qevict_step_workspace.restype = SZ
     L.kvsel_qevict_step.argtypes = [QP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.kvsel_qevict_step.restype = ctypes.c_int
+    L.kvsel_kara_keep.argtypes = [I32, I32, I32, I32]
+    L.kvsel_kara_keep.restype = I32
+    L.kvsel_timing_start.argtypes = [ctypes.c_char_p]
+    L.kvsel_timing_start.restype = ctypes.c_int
+    L.kvsel_timing_read.argtypes = [P, I32, P, P, I32]
+    L.kvsel_timing_read.restype = I32
     _lib = L
     return L
 
@@ -157,6 +164,17 @@ def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _on(stream):
+    """Context in which the binding allocates outputs and workspaces: the
+    launch stream, so that torch's caching allocator orders any reuse of
+    those blocks after the kernels enqueued there."""
+    if stream is None:
+        return nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -197,22 +215,24 @@ def score(q_obs: torch.Tensor, k: torch.Tensor, *, pool_kernel: int, n_sink: int
           want_pooled: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
     """kvsel_score: returns (pooled [Bt,Hkv,S] fp32 or None, raw [Bt,Hkv,S] fp32 or
     None).  want_pooled=False skips the max filter (raw scores only)."""
-    d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
-    shape = (d.batch, d.n_kv_heads, d.seq_len)
-    if not want_pooled:
-        pooled = None
-        want_raw = True
-    elif pooled is None:
-        pooled = torch.empty(shape, dtype=torch.float32, device=k.device)
-    if raw is None and want_raw:
-        raw = torch.empty(shape, dtype=torch.float32, device=k.device)
-    nbytes = score_workspace_bytes(d)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
-    st = lib().kvsel_score(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(raw), _ptr(pooled),
-                           int(pool_kernel), _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "kvsel_score")
-    return pooled, raw
+    with _on(stream):
+        d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
+        shape = (d.batch, d.n_kv_heads, d.seq_len)
+        if not want_pooled:
+            pooled = None
+            want_raw = True
+        elif pooled is None:
+            pooled = torch.empty(shape, dtype=torch.float32, device=k.device)
+        if raw is None and want_raw:
+            raw = torch.empty(shape, dtype=torch.float32, device=k.device)
+        nbytes = score_workspace_bytes(d)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+        st = lib().kvsel_score(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(raw), _ptr(pooled),
+                               int(pool_kernel), _ptr(workspace), workspace.numel(),
+                               _stream(stream))
+        _check(st, "kvsel_score")
+        return pooled, raw
 
 
 def select(pooled: torch.Tensor, budget: int, *, obs_window: int, n_q_heads: int,
@@ -220,38 +240,40 @@ def select(pooled: torch.Tensor, budget: int, *, obs_window: int, n_q_heads: int
            idx: Optional[torch.Tensor] = None, dtype=torch.bfloat16,
            workspace: Optional[torch.Tensor] = None, stream=None):
     """kvsel_select: returns idx [Bt,Hkv,budget+n_sink+W] int32 (ascending)."""
-    Bt, Hkv, S = pooled.shape
-    d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
-                dtype=dtype)
-    n_keep = budget + n_sink + obs_window
-    if idx is None:
-        idx = torch.empty((Bt, Hkv, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
-    nbytes = select_workspace_bytes(d, budget)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=pooled.device)
-    ws_ptr = _ptr(workspace) if workspace is not None else None
-    ws_n = workspace.numel() if workspace is not None else 0
-    st = lib().kvsel_select(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx), ws_ptr, ws_n,
-                            _stream(stream))
-    _check(st, "kvsel_select")
-    return idx
+    with _on(stream):
+        Bt, Hkv, S = pooled.shape
+        d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
+                    dtype=dtype)
+        n_keep = budget + n_sink + obs_window
+        if idx is None:
+            idx = torch.empty((Bt, Hkv, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
+        nbytes = select_workspace_bytes(d, budget)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=pooled.device)
+        ws_ptr = _ptr(workspace) if workspace is not None else None
+        ws_n = workspace.numel() if workspace is not None else 0
+        st = lib().kvsel_select(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx), ws_ptr, ws_n,
+                                _stream(stream))
+        _check(st, "kvsel_select")
+        return idx
 
 
 def compact(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor, *,
             k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
             stream=None):
     """kvsel_compact: returns (k_hat, v_hat) [Bt,Hkv,n_keep,D]."""
-    Bt, Hkv, S, D = k.shape
-    n_keep = idx.shape[-1]
-    d = Desc(Bt, Hkv, Hkv, D, S, 1, 0, 1, _dtype_code(k), 0.0)
-    if k_out is None:
-        k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
-    if v is not None and v_out is None:
-        v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
-    st = lib().kvsel_compact(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(idx), int(n_keep),
-                             _ptr(k_out), _ptr(v_out), _stream(stream))
-    _check(st, "kvsel_compact")
-    return k_out, v_out
+    with _on(stream):
+        Bt, Hkv, S, D = k.shape
+        n_keep = idx.shape[-1]
+        d = Desc(Bt, Hkv, Hkv, D, S, 1, 0, 1, _dtype_code(k), 0.0)
+        if k_out is None:
+            k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
+        if v is not None and v_out is None:
+            v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
+        st = lib().kvsel_compact(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(idx), int(n_keep),
+                                 _ptr(k_out), _ptr(v_out), _stream(stream))
+        _check(st, "kvsel_compact")
+        return k_out, v_out
 
 
 def select_compact(pooled: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
@@ -261,23 +283,24 @@ def select_compact(pooled: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tens
                    workspace: Optional[torch.Tensor] = None, stream=None):
     """kvsel_select_compact: returns (idx, k_hat, v_hat), the outputs of
     select() followed by compact()."""
-    Bt, Hkv, S, D = k.shape
-    d = Desc(Bt, n_q_heads, Hkv, D, S, obs_window, n_sink, int(causal), _dtype_code(k), 0.0)
-    n_keep = budget + n_sink + obs_window
-    if idx is None:
-        idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=k.device)
-    if k_out is None:
-        k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
-    if v is not None and v_out is None:
-        v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
-    if workspace is None:
-        workspace = torch.empty(max(select_workspace_bytes(d, budget), 1), dtype=torch.uint8,
-                                device=k.device)
-    st = lib().kvsel_select_compact(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx),
-                                    _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
-                                    _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "kvsel_select_compact")
-    return idx, k_out, v_out
+    with _on(stream):
+        Bt, Hkv, S, D = k.shape
+        d = Desc(Bt, n_q_heads, Hkv, D, S, obs_window, n_sink, int(causal), _dtype_code(k), 0.0)
+        n_keep = budget + n_sink + obs_window
+        if idx is None:
+            idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=k.device)
+        if k_out is None:
+            k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=k.device)
+        if v is not None and v_out is None:
+            v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=v.device)
+        if workspace is None:
+            workspace = torch.empty(max(select_workspace_bytes(d, budget), 1), dtype=torch.uint8,
+                                    device=k.device)
+        st = lib().kvsel_select_compact(ctypes.byref(d), _ptr(pooled), int(budget), _ptr(idx),
+                                        _ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out),
+                                        _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(st, "kvsel_select_compact")
+        return idx, k_out, v_out
 
 
 def select_adaptive_workspace_bytes(desc: Desc, total_budget: int) -> int:
@@ -290,40 +313,43 @@ def select_adaptive(pooled: torch.Tensor, total_budget: int, *, obs_window: int,
                     dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None, stream=None):
     """kvsel_select_adaptive: returns (idx [Bt, Hkv*(n_sink+W)+total_budget] int32,
     head_off [Bt, Hkv+1] int32)."""
-    Bt, Hkv, S = pooled.shape
-    d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
-                dtype=dtype)
-    n_keep = Hkv * (n_sink + obs_window) + total_budget
-    if idx is None:
-        idx = torch.empty((Bt, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
-    if head_off is None:
-        head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=pooled.device)
-    nbytes = select_adaptive_workspace_bytes(d, total_budget)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=pooled.device)
-    ws_ptr = _ptr(workspace) if workspace is not None else None
-    ws_n = workspace.numel() if workspace is not None else 0
-    st = lib().kvsel_select_adaptive(ctypes.byref(d), _ptr(pooled), int(total_budget), _ptr(idx),
-                                     _ptr(head_off), ws_ptr, ws_n, _stream(stream))
-    _check(st, "kvsel_select_adaptive")
-    return idx, head_off
+    with _on(stream):
+        Bt, Hkv, S = pooled.shape
+        d = desc_of(Bt, n_q_heads, Hkv, head_dim, S, obs_window, n_sink=n_sink, causal=causal,
+                    dtype=dtype)
+        n_keep = Hkv * (n_sink + obs_window) + total_budget
+        if idx is None:
+            idx = torch.empty((Bt, max(n_keep, 0)), dtype=torch.int32, device=pooled.device)
+        if head_off is None:
+            head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=pooled.device)
+        nbytes = select_adaptive_workspace_bytes(d, total_budget)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=pooled.device)
+        ws_ptr = _ptr(workspace) if workspace is not None else None
+        ws_n = workspace.numel() if workspace is not None else 0
+        st = lib().kvsel_select_adaptive(ctypes.byref(d), _ptr(pooled), int(total_budget),
+                                         _ptr(idx), _ptr(head_off), ws_ptr, ws_n,
+                                         _stream(stream))
+        _check(st, "kvsel_select_adaptive")
+        return idx, head_off
 
 
 def compact_flat(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor,
                  head_off: torch.Tensor, *, k_out: Optional[torch.Tensor] = None,
                  v_out: Optional[torch.Tensor] = None, stream=None):
     """kvsel_compact_flat: returns (k_hat, v_hat) [Bt, n_keep, D]."""
-    Bt, Hkv, S, D = k.shape
-    n_keep = idx.shape[-1]
-    d = Desc(Bt, Hkv, Hkv, D, S, 1, 0, 1, _dtype_code(k), 0.0)
-    if k_out is None:
-        k_out = torch.empty((Bt, n_keep, D), dtype=k.dtype, device=k.device)
-    if v is not None and v_out is None:
-        v_out = torch.empty((Bt, n_keep, D), dtype=v.dtype, device=v.device)
-    st = lib().kvsel_compact_flat(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(idx), _ptr(head_off),
-                                  int(n_keep), _ptr(k_out), _ptr(v_out), _stream(stream))
-    _check(st, "kvsel_compact_flat")
-    return k_out, v_out
+    with _on(stream):
+        Bt, Hkv, S, D = k.shape
+        n_keep = idx.shape[-1]
+        d = Desc(Bt, Hkv, Hkv, D, S, 1, 0, 1, _dtype_code(k), 0.0)
+        if k_out is None:
+            k_out = torch.empty((Bt, n_keep, D), dtype=k.dtype, device=k.device)
+        if v is not None and v_out is None:
+            v_out = torch.empty((Bt, n_keep, D), dtype=v.dtype, device=v.device)
+        st = lib().kvsel_compact_flat(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(idx), _ptr(head_off),
+                                      int(n_keep), _ptr(k_out), _ptr(v_out), _stream(stream))
+        _check(st, "kvsel_compact_flat")
+        return k_out, v_out
 
 
 def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
@@ -361,9 +387,21 @@ def kara_desc(q_win: torch.Tensor, k_win: torch.Tensor, *, buffer: int, keep: in
                     int(alpha), _dtype_code(k_win), float(scale))
 
 
-def kara_keep(window: int, buffer: int, ratio: float) -> int:
-    """|I| = ceil(r * (|W| - |U|))   (Kara Eq. 5)."""
-    return int(math.ceil(ratio * (window - buffer) - 1e-9))
+def kara_keep(window: int, buffer: int, ratio) -> int:
+    """kvsel_kara_keep: |I| = ceil(r * (|W| - |U|)) of Kara Eq. (5), computed
+    exactly by the library.  `ratio` is a fraction (num, den), a
+    fractions.Fraction, or a number, which is read as the nearest fraction
+    with a denominator of at most 10**6 (0.4 -> 2/5)."""
+    if isinstance(ratio, tuple):
+        num, den = ratio
+    else:
+        f = Fraction(ratio).limit_denominator(10 ** 6)
+        num, den = f.numerator, f.denominator
+    n = lib().kvsel_kara_keep(int(window), int(buffer), int(num), int(den))
+    if n < 0:
+        raise ValueError(f"kvsel_kara_keep: invalid window {window}, buffer {buffer} or "
+                         f"ratio {num}/{den}")
+    return int(n)
 
 
 def kara_score_workspace_bytes(kd: KaraDesc) -> int:
@@ -374,30 +412,32 @@ def kara_score(q_win: torch.Tensor, k_win: torch.Tensor, kd: KaraDesc, *,
                scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     """kvsel_kara_score: importance [Bt,Hkv,window-buffer] float32."""
-    n = kd.window - kd.buffer
-    if scores is None:
-        scores = torch.empty((kd.batch, kd.n_kv_heads, n), dtype=torch.float32,
-                             device=k_win.device)
-    nbytes = kara_score_workspace_bytes(kd)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k_win.device)
-    st = lib().kvsel_kara_score(ctypes.byref(kd), _ptr(q_win), _ptr(k_win), _ptr(scores),
-                                _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "kvsel_kara_score")
-    return scores
+    with _on(stream):
+        n = kd.window - kd.buffer
+        if scores is None:
+            scores = torch.empty((kd.batch, kd.n_kv_heads, n), dtype=torch.float32,
+                                 device=k_win.device)
+        nbytes = kara_score_workspace_bytes(kd)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k_win.device)
+        st = lib().kvsel_kara_score(ctypes.byref(kd), _ptr(q_win), _ptr(k_win), _ptr(scores),
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(st, "kvsel_kara_score")
+        return scores
 
 
 def kara_select(scores: torch.Tensor, kd: KaraDesc, *, idx: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
     """kvsel_kara_select: window-relative kept positions [Bt,Hkv,n_out+buffer]."""
-    n = kd.window - kd.buffer
-    n_out = min(n, kd.keep + kd.alpha)
-    if idx is None:
-        idx = torch.empty((kd.batch, kd.n_kv_heads, n_out + kd.buffer), dtype=torch.int32,
-                          device=scores.device)
-    st = lib().kvsel_kara_select(ctypes.byref(kd), _ptr(scores), _ptr(idx), _stream(stream))
-    _check(st, "kvsel_kara_select")
-    return idx
+    with _on(stream):
+        n = kd.window - kd.buffer
+        n_out = min(n, kd.keep + kd.alpha)
+        if idx is None:
+            idx = torch.empty((kd.batch, kd.n_kv_heads, n_out + kd.buffer), dtype=torch.int32,
+                              device=scores.device)
+        st = lib().kvsel_kara_select(ctypes.byref(kd), _ptr(scores), _ptr(idx), _stream(stream))
+        _check(st, "kvsel_kara_select")
+        return idx
 
 
 def kara_compress(q_win: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor, *,
@@ -434,43 +474,68 @@ def route_tiers(scores: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, n_ful
                 out: Optional[TierOutputs] = None, workspace: Optional[torch.Tensor] = None,
                 stream=None) -> TierOutputs:
     """kvsel_route_tiers (QEvict window tiers with int4 and promotion)."""
-    Bt, Hkv, S, D = k.shape
-    td = TierDesc(Bt, Hkv, D, S, win, n_full, n_quant, _dtype_code(k))
-    nW = S // win
-    n_prom = 0 if promote is None else promote.shape[-1]
-    dev = k.device
-    if out is None:
-        e = lambda *s, dt: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
-        out = TierOutputs(
-            e(Bt, Hkv, nW, dt=torch.int8), e(Bt, Hkv, nW, dt=torch.int32),
-            e(Bt, Hkv, n_full * win, D, dt=k.dtype), e(Bt, Hkv, n_full * win, D, dt=k.dtype),
-            e(Bt, Hkv, n_quant, win, D // 2, dt=torch.uint8),
-            e(Bt, Hkv, n_quant, win, D // 2, dt=torch.uint8),
-            e(Bt, Hkv, n_quant, D, 2, dt=torch.float32), e(Bt, Hkv, n_quant, D, 2, dt=torch.float32),
-            e(Bt, Hkv, n_prom * win, D, dt=k.dtype), e(Bt, Hkv, n_prom * win, D, dt=k.dtype))
-    nbytes = route_tiers_workspace_bytes(td)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    nz = lambda t: _ptr(t) if t is not None and t.numel() > 0 else None  # noqa: E731
-    st = lib().kvsel_route_tiers(
-        ctypes.byref(td), _ptr(scores), _ptr(k), _ptr(v), _ptr(out.tier), _ptr(out.rank),
-        nz(out.k_full), nz(out.v_full), nz(out.k_codes), nz(out.v_codes), nz(out.k_meta),
-        nz(out.v_meta), nz(promote), int(n_prom), nz(out.k_prom), nz(out.v_prom),
-        _ptr(workspace), workspace.numel(), _stream(stream))
-    _check(st, "kvsel_route_tiers")
-    return out
-
-
+    with _on(stream):
+        Bt, Hkv, S, D = k.shape
+        td = TierDesc(Bt, Hkv, D, S, win, n_full, n_quant, _dtype_code(k))
+        nW = S // win
+        n_prom = 0 if promote is None else promote.shape[-1]
+        dev = k.device
+        if out is None:
+            e = lambda *s, dt: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+            out = TierOutputs(
+                e(Bt, Hkv, nW, dt=torch.int8), e(Bt, Hkv, nW, dt=torch.int32),
+                e(Bt, Hkv, n_full * win, D, dt=k.dtype), e(Bt, Hkv, n_full * win, D, dt=k.dtype),
+                e(Bt, Hkv, n_quant, win, D // 2, dt=torch.uint8),
+                e(Bt, Hkv, n_quant, win, D // 2, dt=torch.uint8),
+                e(Bt, Hkv, n_quant, D, 2, dt=torch.float32),
+                e(Bt, Hkv, n_quant, D, 2, dt=torch.float32),
+                e(Bt, Hkv, n_prom * win, D, dt=k.dtype), e(Bt, Hkv, n_prom * win, D, dt=k.dtype))
+        nbytes = route_tiers_workspace_bytes(td)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        nz = lambda t: _ptr(t) if t is not None and t.numel() > 0 else None  # noqa: E731
+        st = lib().kvsel_route_tiers(
+            ctypes.byref(td), _ptr(scores), _ptr(k), _ptr(v), _ptr(out.tier), _ptr(out.rank),
+            nz(out.k_full), nz(out.v_full), nz(out.k_codes), nz(out.v_codes), nz(out.k_meta),
+            nz(out.v_meta), nz(promote), int(n_prom), nz(out.k_prom), nz(out.v_prom),
+            _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(st, "kvsel_route_tiers")
+        return out
 EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_select_workspace",
            "kvsel_select", "kvsel_compact", "kvsel_route_tiers_workspace", "kvsel_route_tiers",
            "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat",
            "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select",
-           "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact")
+           "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact",
+           "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read")
+
+
+def timing_start(prefix: Optional[str] = "*") -> None:
+    """kvsel_timing_start: bracket every later launch of a kernel whose name
+    starts with `prefix` ("*" = all, None = stop) with HIP events."""
+    _check(lib().kvsel_timing_start(prefix.encode() if prefix else None), "kvsel_timing_start")
+
+
+def timing_read(max_kernels: int = 64) -> dict:
+    """kvsel_timing_read: {kernel name: (total ms, launches)} since the last
+    read; waits for the recorded events."""
+    nb = 96
+    names = ctypes.create_string_buffer(nb * max_kernels)
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int32 * max_kernels)()
+    n = lib().kvsel_timing_read(names, nb, ms, cnt, max_kernels)
+    if n < 0:
+        raise RuntimeError(f"kvsel_timing_read failed ({n})")
+    out = {}
+    for i in range(min(n, max_kernels)):
+        nm = names.raw[i * nb:(i + 1) * nb].split(b"\0", 1)[0].decode()
+        out[nm] = (float(ms[i]), int(cnt[i]))
+    return out
 
 
 # ---------------------------------------------------------------------------
 # Repeated recoverable routing (kvsel_qevict_step)
 # ---------------------------------------------------------------------------
+
 
 def qevict_desc(k: torch.Tensor, *, seq_len: int, max_windows: int, n_sink: int,
                 n_recent: int, n_full: int, n_quant: int, bits: int = 2) -> QevictDesc:
@@ -504,13 +569,14 @@ def qevict_step(qd: QevictDesc, token_scores: torch.Tensor, state: dict, k: torc
                 v: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
                 stream=None) -> dict:
     """kvsel_qevict_step: updates state (and promoted rows of k, v) in place."""
-    if workspace is None:
-        workspace = torch.empty(max(qevict_step_workspace_bytes(qd), 1), dtype=torch.uint8,
-                                device=k.device)
-    st = lib().kvsel_qevict_step(
-        ctypes.byref(qd), _ptr(token_scores), _ptr(state["w_acc"]), _ptr(state["tier"]),
-        _ptr(state["has_codes"]), _ptr(k), _ptr(v), _ptr(state["k_codes"]),
-        _ptr(state["v_codes"]), _ptr(state["k_meta"]), _ptr(state["v_meta"]), _ptr(workspace),
-        workspace.numel(), _stream(stream))
-    _check(st, "kvsel_qevict_step")
-    return state
+    with _on(stream):
+        if workspace is None:
+            workspace = torch.empty(max(qevict_step_workspace_bytes(qd), 1), dtype=torch.uint8,
+                                    device=k.device)
+        st = lib().kvsel_qevict_step(
+            ctypes.byref(qd), _ptr(token_scores), _ptr(state["w_acc"]), _ptr(state["tier"]),
+            _ptr(state["has_codes"]), _ptr(k), _ptr(v), _ptr(state["k_codes"]),
+            _ptr(state["v_codes"]), _ptr(state["k_meta"]), _ptr(state["v_meta"]), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+        _check(st, "kvsel_qevict_step")
+        return state

@@ -27,35 +27,65 @@ def hipcc() -> str:
     return found
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep the compiler from forming packed-fp32 instructions by itself
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs: the score passes read every
+    # logit with VALU instructions, so accumulator-register copies would
+    # cost one extra instruction per logit
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def includes() -> list[str]:
+    return ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+
+
 def command(out: str = LIB) -> list[str]:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # keep the compiler from forming packed-fp32 instructions by itself
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # matrix-core results straight into VGPRs: the score passes read every
-        # logit with VALU instructions, so accumulator-register copies would
-        # cost one extra instruction per logit
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-        "-Wall", "-Wno-unused-function",
-        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-        *srcs, "-o", out,
-    ]
+    """One hipcc command that compiles and links every source (reference form)."""
+    return [hipcc(), *FLAGS, "-shared", *includes(), *sources(), "-o", out]
+
+
+_NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd: list[str]) -> str:
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{err}")
+    return err
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source of the package into libkvsel.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+    """Compile every HIP source of the package (one hipcc per file, in
+    parallel) and link libkvsel.so in-tree; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    cmds = [[hipcc(), *FLAGS, *includes(), "-c", s, "-o", o] for s, o in zip(srcs, objs)]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        errs = list(ex.map(_run, cmds))
+    tmp = LIB + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    errs.append(_run(link))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e, file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -2,9 +2,14 @@
 //
 // Every precondition is checked on the host before anything is enqueued, and
 // no check calls the HIP runtime, so invalid calls fail the same way on a
-// machine without a GPU.  The library holds no global mutable state.
+// machine without a GPU.  Two environment switches help debugging:
+// KVSEL_VALIDATE_ONLY=1 returns after the checks without enqueuing anything,
+// KVSEL_SYNC=1 waits for the stream after each call and reports a device
+// error as KVSEL_ERR_DEVICE.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "common.h"
 
@@ -15,6 +20,24 @@ namespace {
 constexpr int64_t kMaxSeq = (int64_t)1 << 28;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// Runs the launch sequence of a call whose arguments passed every check,
+// honouring KVSEL_VALIDATE_ONLY and KVSEL_SYNC.
+template <typename F>
+kvsel_status enqueue(void* stream, F&& launch) {
+  if (env_flag("KVSEL_VALIDATE_ONLY")) return KVSEL_OK;
+  kvsel_status st = launch();
+  if (st == KVSEL_OK && env_flag("KVSEL_SYNC")) {
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess || hipGetLastError() != hipSuccess)
+      st = KVSEL_ERR_DEVICE;
+  }
+  return st;
+}
 
 kvsel_status check_desc(const kvsel_desc* d) {
   if (!d) return KVSEL_ERR_ARG;
@@ -142,8 +165,9 @@ kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* 
   plan_score(*desc, &p);
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
-  return launch_score(*desc, p, q_obs, k, raw_scores, pooled, pool_kernel, (char*)ws,
-                      (hipStream_t)stream, desc->seq_len);
+  return enqueue(stream, [&] {
+    return launch_score(*desc, p, q_obs, k, raw_scores, pooled, pool_kernel, (char*)ws,
+                        (hipStream_t)stream, desc->seq_len); });
 }
 
 size_t kvsel_select_workspace(const kvsel_desc* desc, int32_t budget) {
@@ -165,7 +189,8 @@ kvsel_status kvsel_select(const kvsel_desc* desc, const float* pooled, int32_t b
   plan_select(*desc, budget, 1, &p);
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
-  return launch_select(*desc, p, pooled, budget, idx, nullptr, (char*)ws, (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_select(*desc, p, pooled, budget, idx, nullptr, (char*)ws, (hipStream_t)stream); });
 }
 
 kvsel_status kvsel_select_compact(const kvsel_desc* desc, const float* pooled, int32_t budget,
@@ -184,8 +209,9 @@ kvsel_status kvsel_select_compact(const kvsel_desc* desc, const float* pooled, i
   plan_select(*desc, budget, 1, &p);
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
-  return launch_select_compact(*desc, p, pooled, budget, idx, k, v, k_out, v_out, (char*)ws,
-                               (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_select_compact(*desc, p, pooled, budget, idx, k, v, k_out, v_out, (char*)ws,
+                                 (hipStream_t)stream); });
 }
 
 size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget) {
@@ -205,8 +231,9 @@ kvsel_status kvsel_select_adaptive(const kvsel_desc* desc, const float* pooled,
   if (!plan_select(*desc, (int)total_budget, desc->n_kv_heads, &p)) return KVSEL_ERR_UNSUPPORTED;
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
-  return launch_select(*desc, p, pooled, (int)total_budget, idx, head_off, (char*)ws,
-                       (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_select(*desc, p, pooled, (int)total_budget, idx, head_off, (char*)ws,
+                         (hipStream_t)stream); });
 }
 
 kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
@@ -220,7 +247,8 @@ kvsel_status kvsel_compact(const kvsel_desc* desc, const void* k, const void* v,
   if (!aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(k_out) ||
       !aligned16(v_out))
     return KVSEL_ERR_ARG;
-  return launch_compact(*desc, k, v, idx, n_keep, k_out, v_out, (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_compact(*desc, k, v, idx, n_keep, k_out, v_out, (hipStream_t)stream); });
 }
 
 kvsel_status kvsel_compact_flat(const kvsel_desc* desc, const void* k, const void* v,
@@ -234,8 +262,9 @@ kvsel_status kvsel_compact_flat(const kvsel_desc* desc, const void* k, const voi
   if (!aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(k_out) ||
       !aligned16(v_out))
     return KVSEL_ERR_ARG;
-  return launch_compact_flat(*desc, k, v, idx, head_off, (int)n_keep, k_out, v_out,
-                             (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_compact_flat(*desc, k, v, idx, head_off, (int)n_keep, k_out, v_out,
+                               (hipStream_t)stream); });
 }
 
 size_t kvsel_kara_score_workspace(const kvsel_kara_desc* kdesc) {
@@ -257,8 +286,17 @@ kvsel_status kvsel_kara_score(const kvsel_kara_desc* kdesc, const void* q_win, c
   plan_score(d, &p);
   if (ws_bytes < p.total || (p.total > 0 && !ws)) return KVSEL_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVSEL_ERR_ARG;
-  return launch_score(d, p, q_win, k_win, scores, nullptr, 1, (char*)ws, (hipStream_t)stream,
-                      kdesc->window);
+  return enqueue(stream, [&] {
+    return launch_score(d, p, q_win, k_win, scores, nullptr, 1, (char*)ws, (hipStream_t)stream,
+                        kdesc->window); });
+}
+
+int32_t kvsel_kara_keep(int32_t window, int32_t buffer, int32_t ratio_num, int32_t ratio_den) {
+  if (window < 2 || buffer < 0 || buffer >= window) return -1;
+  if (ratio_den < 1 || ratio_num < 0 || ratio_num > ratio_den) return -1;
+  const int64_t n = (int64_t)window - buffer;
+  // ceil(n * num / den) in integers: exact for every rational ratio
+  return (int32_t)((n * ratio_num + ratio_den - 1) / ratio_den);
 }
 
 kvsel_status kvsel_kara_select(const kvsel_kara_desc* kdesc, const float* scores, int32_t* idx,
@@ -268,8 +306,9 @@ kvsel_status kvsel_kara_select(const kvsel_kara_desc* kdesc, const float* scores
   if (!scores || !idx) return KVSEL_ERR_ARG;
   const int n = kdesc->window - kdesc->buffer;
   if (!kara_supported(n)) return KVSEL_ERR_UNSUPPORTED;
-  return launch_kara_select(scores, idx, kdesc->batch * kdesc->n_kv_heads, n, kdesc->buffer,
-                            kdesc->keep, kdesc->gamma, kdesc->alpha, (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_kara_select(scores, idx, kdesc->batch * kdesc->n_kv_heads, n, kdesc->buffer,
+                              kdesc->keep, kdesc->gamma, kdesc->alpha, (hipStream_t)stream); });
 }
 
 size_t kvsel_route_tiers_workspace(const kvsel_tier_desc* desc) {
@@ -299,9 +338,10 @@ kvsel_status kvsel_route_tiers(const kvsel_tier_desc* desc, const float* token_s
   TierPlan p;
   plan_tiers(*desc, &p);
   if (ws_bytes < p.total || !ws) return KVSEL_ERR_WORKSPACE;
-  return launch_tiers(*desc, p, token_scores, k, v, tier, win_rank, k_full, v_full, k_codes,
-                      v_codes, k_meta, v_meta, promote, n_promote, k_prom, v_prom, (char*)ws,
-                      (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_tiers(*desc, p, token_scores, k, v, tier, win_rank, k_full, v_full, k_codes,
+                        v_codes, k_meta, v_meta, promote, n_promote, k_prom, v_prom, (char*)ws,
+                        (hipStream_t)stream); });
 }
 
 size_t kvsel_qevict_step_workspace(const kvsel_qevict_desc* desc) {
@@ -320,8 +360,9 @@ kvsel_status kvsel_qevict_step(const kvsel_qevict_desc* desc, const float* token
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return KVSEL_ERR_ARG;
   if (ws_bytes < qevict_workspace(*desc)) return KVSEL_ERR_WORKSPACE;
-  return launch_qevict(*desc, token_scores, w_acc, tier, has_codes, k, v, k_codes, v_codes,
-                       k_meta, v_meta, (char*)ws, (hipStream_t)stream);
+  return enqueue(stream, [&] {
+    return launch_qevict(*desc, token_scores, w_acc, tier, has_codes, k, v, k_codes, v_codes,
+                         k_meta, v_meta, (char*)ws, (hipStream_t)stream); });
 }
 
 }  // extern "C"

@@ -16,6 +16,23 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing (kvsel_timing_start / kvsel_timing_read).  Off by
+// default; while a name prefix is set, every launch of a kernel whose name
+// starts with it is bracketed by two HIP events recorded on its stream.
+// ---------------------------------------------------------------------------
+bool timing_wanted(const char* kernel_name);
+hipEvent_t timing_open(hipStream_t stream);
+void timing_close(const char* kernel_name, hipEvent_t start, hipStream_t stream);
+
+#define KVSEL_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                        \
+  do {                                                                                   \
+    const bool kvsel_timed_ = ::kvsel::timing_wanted(NAME);                              \
+    hipEvent_t kvsel_t0_ = kvsel_timed_ ? ::kvsel::timing_open(STREAM) : nullptr;        \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                 \
+    if (kvsel_timed_) ::kvsel::timing_close(NAME, kvsel_t0_, STREAM);                    \
+  } while (0)
+
 // Sort key for (value desc, index asc) as one ascending 64-bit integer: the
 // value's bits mapped to an order-preserving unsigned form, complemented for
 // descending order, above the index.  -0.0 is folded into +0.0 so equal

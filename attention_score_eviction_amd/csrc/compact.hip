@@ -97,7 +97,7 @@ kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
   const int vpr = d.head_dim * e / 16;
   const int nheads = d.batch * d.n_kv_heads;
   const int rpb = 256 / vpr;   // vpr <= 32 (D * e <= 512 bytes)
-  hipLaunchKernelGGL(compact_kernel, dim3((n_keep + rpb - 1) / rpb, nheads),
+  KVSEL_LAUNCH("compact_kernel", compact_kernel, dim3((n_keep + rpb - 1) / rpb, nheads),
                      dim3(256), 0, stream, (const u32x4_t*)k, (const u32x4_t*)v, idx,
                      (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, n_keep, vpr);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
@@ -109,7 +109,7 @@ kvsel_status launch_compact_flat(const kvsel_desc& d, const void* k, const void*
   if (n_keep == 0) return KVSEL_OK;
   const int e = d.dtype == KVSEL_F32 ? 4 : 2;
   const int vpr = d.head_dim * e / 16;
-  hipLaunchKernelGGL(compact_flat_kernel,
+  KVSEL_LAUNCH("compact_flat_kernel", compact_flat_kernel,
                      dim3((n_keep + kRowsPerBlock - 1) / kRowsPerBlock, d.batch), dim3(256), 0,
                      stream, (const u32x4_t*)k, (const u32x4_t*)v, idx, head_off,
                      (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, d.n_kv_heads, n_keep, vpr);

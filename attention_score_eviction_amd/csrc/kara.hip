@@ -194,8 +194,9 @@ bool kara_supported(int n) { return n >= 1 && n <= kKaraMax; }
 
 kvsel_status launch_kara_select(const float* scores, int32_t* idx, int rows, int n, int buffer,
                                 int keep, int gamma, int alpha, hipStream_t stream) {
-  const int n_out = keep + alpha < n ? keep + alpha : n;
-  hipLaunchKernelGGL(kara_select_kernel, dim3(rows), dim3(kKaraThreads), 0, stream, scores, idx,
+  // keep + alpha in 64 bits: alpha may be any non-negative int32
+  const int n_out = (int64_t)keep + alpha < (int64_t)n ? keep + alpha : n;
+  KVSEL_LAUNCH("kara_select_kernel", kara_select_kernel, dim3(rows), dim3(kKaraThreads), 0, stream, scores, idx,
                      n, buffer, keep, gamma, alpha, n_out);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }

@@ -219,11 +219,11 @@ void launch_qe_move(const kvsel_qevict_desc& d, dim3 g, void* k, void* v, const 
                     uint8_t* k_codes, uint8_t* v_codes, float* k_meta, float* v_meta,
                     hipStream_t stream) {
   if (d.bits == 2)
-    hipLaunchKernelGGL((qe_move_kernel<D, 2>), g, dim3(256), 0, stream, (uint16_t*)k,
+    KVSEL_LAUNCH("qe_move_kernel", (qe_move_kernel<D, 2>), g, dim3(256), 0, stream, (uint16_t*)k,
                        (uint16_t*)v, act, k_codes, v_codes, k_meta, v_meta, d.capacity,
                        d.n_sink, d.max_windows);
   else
-    hipLaunchKernelGGL((qe_move_kernel<D, 4>), g, dim3(256), 0, stream, (uint16_t*)k,
+    KVSEL_LAUNCH("qe_move_kernel", (qe_move_kernel<D, 4>), g, dim3(256), 0, stream, (uint16_t*)k,
                        (uint16_t*)v, act, k_codes, v_codes, k_meta, v_meta, d.capacity,
                        d.n_sink, d.max_windows);
 }
@@ -247,7 +247,7 @@ kvsel_status launch_qevict(const kvsel_qevict_desc& d, const float* scores, floa
   const int nwin = qevict_windows(d);
   if (nwin == 0) return KVSEL_OK;
   int8_t* act = (int8_t*)ws;
-  hipLaunchKernelGGL(qe_rank_kernel, dim3(nheads), dim3(kQeRankThreads), 0, stream, scores,
+  KVSEL_LAUNCH("qe_rank_kernel", qe_rank_kernel, dim3(nheads), dim3(kQeRankThreads), 0, stream, scores,
                      w_acc, tier, has_codes, act, d.seq_len, d.n_sink, nwin, d.max_windows,
                      d.n_full, d.n_quant);
   const dim3 g(nwin, nheads);

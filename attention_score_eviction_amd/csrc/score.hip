@@ -742,24 +742,24 @@ __global__ void __launch_bounds__(256) maxpool_kernel(const float* __restrict__ 
 
 template <typename T, int D, int NQT, int NW>
 void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
-  hipLaunchKernelGGL((score_pass1<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
+  KVSEL_LAUNCH("score_pass1", (score_pass1<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
   int tl = 0;
   while ((4 << tl) < p.nchunk && tl < 6) ++tl;
   const long lanes = ((long)p.nheads * p.GW) << tl;
-  hipLaunchKernelGGL(score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
+  KVSEL_LAUNCH("score_combine", score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
                      args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl);
-  hipLaunchKernelGGL((score_pass2<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
+  KVSEL_LAUNCH("score_pass2", (score_pass2<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 
 template <int D, int NQ, int NW>
 void launch_passes32(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
-  hipLaunchKernelGGL((score_pass1_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
+  KVSEL_LAUNCH("score_pass1_32", (score_pass1_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
   int tl = 0;
   while ((4 << tl) < p.nchunk && tl < 6) ++tl;
   const long lanes = ((long)p.nheads * p.GW) << tl;
-  hipLaunchKernelGGL(score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
+  KVSEL_LAUNCH("score_combine", score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
                      args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl);
-  hipLaunchKernelGGL((score_pass2_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
+  KVSEL_LAUNCH("score_pass2_32", (score_pass2_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 
 template <int D>
@@ -912,12 +912,12 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   if (!ok) return KVSEL_ERR_UNSUPPORTED;
   if (p.ngroups > 1) {
     const size_t n = (size_t)p.nheads * d.seq_len;
-    hipLaunchKernelGGL(score_group_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+    KVSEL_LAUNCH("score_group_sum", score_group_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                        a.s_out, s, n, p.ngroups);
   }
   if (!pooled) return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
-  hipLaunchKernelGGL(maxpool_kernel, dim3((d.seq_len + 255) / 256, p.nheads), dim3(256), 0, stream,
+  KVSEL_LAUNCH("maxpool_kernel", maxpool_kernel, dim3((d.seq_len + 255) / 256, p.nheads), dim3(256), 0, stream,
                      s, pooled, d.seq_len, lo, hi, (pool_kernel - 1) / 2);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }

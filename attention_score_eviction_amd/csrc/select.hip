@@ -872,7 +872,7 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
     const dim3 g(groups);
     const GatherArgs none = {nullptr, nullptr, nullptr, nullptr, 0, 1};
 #define KVSEL_SELECT_1WG(NT, NB)                                                              \
-  hipLaunchKernelGGL((select_kernel<NT, NB, false>), g, dim3(NT), 0, stream, pooled, idx,      \
+  KVSEL_LAUNCH("select_kernel", (select_kernel<NT, NB, false>), g, dim3(NT), 0, stream, pooled, idx,      \
                      head_off, d.seq_len, lo, hi, budget, d.n_sink, d.obs_window, n_keep, hg, \
                      p.nsl, none)
     if (tot <= 256) KVSEL_SELECT_1WG(256, 1);
@@ -904,12 +904,12 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   a.hg = hg;
   a.nst = p.ns * hg;
   const dim3 sg(a.nst, groups);
-  hipLaunchKernelGGL(sel_init, dim3(groups), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_hist2, sg, dim3(kSliceThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_resolve, dim3(groups), dim3(kSelThreads), 0, stream, a);
-  hipLaunchKernelGGL(sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_init", sel_init, dim3(groups), dim3(256), 0, stream, a);
+  KVSEL_LAUNCH("sel_hist", sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_hist2", sel_hist2, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_cand", sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_resolve", sel_resolve, dim3(groups), dim3(kSelThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_emit", sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 
@@ -939,7 +939,7 @@ kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, con
   const long tot = (long)p.nsl;
   const dim3 g(p.groups * reps);
 #define KVSEL_SELECT_GATHER(NT, NB)                                                          \
-  hipLaunchKernelGGL((select_kernel<NT, NB, true>), g, dim3(NT), 0, stream, pooled, idx,      \
+  KVSEL_LAUNCH("select_kernel", (select_kernel<NT, NB, true>), g, dim3(NT), 0, stream, pooled, idx,      \
                      (int32_t*)nullptr, d.seq_len, lo, hi, budget, d.n_sink, d.obs_window,    \
                      n_keep, 1, p.nsl, ga)
   if (tot <= 256) KVSEL_SELECT_GATHER(256, 1);

@@ -273,23 +273,23 @@ kvsel_status launch_tiers(const kvsel_tier_desc& d, const TierPlan& p, const flo
                           float* k_meta, float* v_meta, const int32_t* promote, int n_promote,
                           void* k_prom, void* v_prom, char* ws, hipStream_t stream) {
   int32_t* slot = (int32_t*)(ws + p.off_slot);
-  hipLaunchKernelGGL(tier_rank_kernel, dim3(p.nheads), dim3(kRankThreads), 0, stream, scores,
+  KVSEL_LAUNCH("tier_rank_kernel", tier_rank_kernel, dim3(p.nheads), dim3(kRankThreads), 0, stream, scores,
                      tier, rank, slot, d.seq_len, p.nwin, d.n_full, d.n_quant);
   const dim3 g(p.nwin, p.nheads);
   if (d.head_dim == 128) {
-    hipLaunchKernelGGL(tier_move_kernel<128>, g, dim3(256), 0, stream, (const uint16_t*)k,
+    KVSEL_LAUNCH("tier_move_kernel", tier_move_kernel<128>, g, dim3(256), 0, stream, (const uint16_t*)k,
                        (const uint16_t*)v, tier, slot, (uint16_t*)k_full, (uint16_t*)v_full,
                        k_codes, v_codes, k_meta, v_meta, d.seq_len, p.nwin, d.n_full, d.n_quant);
     if (n_promote > 0)
-      hipLaunchKernelGGL(tier_promote_kernel<128>, dim3(n_promote, p.nheads), dim3(256), 0,
+      KVSEL_LAUNCH("tier_promote_kernel", tier_promote_kernel<128>, dim3(n_promote, p.nheads), dim3(256), 0,
                          stream, k_codes, v_codes, k_meta, v_meta, promote, (uint16_t*)k_prom,
                          (uint16_t*)v_prom, d.n_quant, n_promote);
   } else {
-    hipLaunchKernelGGL(tier_move_kernel<64>, g, dim3(256), 0, stream, (const uint16_t*)k,
+    KVSEL_LAUNCH("tier_move_kernel", tier_move_kernel<64>, g, dim3(256), 0, stream, (const uint16_t*)k,
                        (const uint16_t*)v, tier, slot, (uint16_t*)k_full, (uint16_t*)v_full,
                        k_codes, v_codes, k_meta, v_meta, d.seq_len, p.nwin, d.n_full, d.n_quant);
     if (n_promote > 0)
-      hipLaunchKernelGGL(tier_promote_kernel<64>, dim3(n_promote, p.nheads), dim3(256), 0,
+      KVSEL_LAUNCH("tier_promote_kernel", tier_promote_kernel<64>, dim3(n_promote, p.nheads), dim3(256), 0,
                          stream, k_codes, v_codes, k_meta, v_meta, promote, (uint16_t*)k_prom,
                          (uint16_t*)v_prom, d.n_quant, n_promote);
   }

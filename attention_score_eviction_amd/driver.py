@@ -1,0 +1,140 @@
+"""Layer-major driver of the layer-end step (TideKV Algorithm 1, Section 4.1).
+
+TideKV runs prefill layer by layer: a layer's full-prompt K/V is built over
+all prompt chunks, then LayerEndCompress (Algorithm 2) keeps the retained
+rows, the compact cache is committed, and the full K/V is released before
+the next layer starts, so only one layer's full-prompt K/V is ever resident.
+
+This driver holds that single active buffer (Q_obs, K, V of one layer) and
+the scratch of the layer-end step, fills the buffer in place for each layer,
+runs kvsel_score and kvsel_select_compact on one stream, and commits each
+layer's compact K/V and absolute positions to a per-layer store.  The model
+forward that would produce the K/V is not part of it: the caller supplies
+each layer's tensors.  Host orchestration only; every step of the layer-end
+computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import Desc, _dtype_code, score, score_workspace_bytes, select_compact, \
+    select_workspace_bytes
+
+
+@dataclass
+class LayerCache:
+    """Committed compact cache of one layer."""
+    budget: int
+    idx: torch.Tensor        # [Bt, Hkv, budget + n_sink + W] int32, absolute positions
+    k_hat: torch.Tensor      # [Bt, Hkv, budget + n_sink + W, D]
+    v_hat: torch.Tensor
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.idx, self.k_hat, self.v_hat))
+
+
+@dataclass
+class LayerMajorDriver:
+    """One resident layer plus the layer-end scratch; see the module docstring."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seq_len: int
+    obs_window: int
+    pool_kernel: int
+    max_budget: int
+    n_sink: int = 0
+    dtype: torch.dtype = torch.bfloat16
+    device: str = "cuda"
+    store: list = field(default_factory=list)
+
+    def __post_init__(self):
+        Bt, Hq, Hkv, D, S, W = (self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                                self.seq_len, self.obs_window)
+        dev = torch.device(self.device)
+        e = lambda *s, dt=self.dtype: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        # the active layer: the only full-prompt K/V that is resident
+        self.q, self.k, self.v = e(Bt, Hq, W, D), e(Bt, Hkv, S, D), e(Bt, Hkv, S, D)
+        self.pooled = e(Bt, Hkv, S, dt=torch.float32)
+        self.raw = e(Bt, Hkv, S, dt=torch.float32)
+        self.desc = Desc(Bt, Hq, Hkv, D, S, W, self.n_sink, 1, _dtype_code(self.k), 0.0)
+        self.score_ws = e(max(score_workspace_bytes(self.desc), 1), dt=torch.uint8)
+        self.select_ws = e(max(select_workspace_bytes(self.desc, self.max_budget), 1),
+                           dt=torch.uint8)
+
+    @property
+    def active_bytes(self) -> int:
+        """Device bytes of the active layer (Q_obs, K, V)."""
+        return sum(t.numel() * t.element_size() for t in (self.q, self.k, self.v))
+
+    @property
+    def scratch_bytes(self) -> int:
+        """Score vectors and workspaces of the layer-end step."""
+        return sum(t.numel() * t.element_size()
+                   for t in (self.pooled, self.raw, self.score_ws, self.select_ws))
+
+    @property
+    def store_bytes(self) -> int:
+        return sum(c.nbytes for c in self.store)
+
+    def load(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Fill the active buffer with a layer's Q_obs, K, V (host or device
+        tensors of the active shapes), overwriting the previous layer."""
+        for dst, src in ((self.q, q), (self.k, k), (self.v, v)):
+            if tuple(src.shape) != tuple(dst.shape) or src.dtype != dst.dtype:
+                raise ValueError(f"layer tensor {tuple(src.shape)} {src.dtype} does not match "
+                                 f"the active buffer {tuple(dst.shape)} {dst.dtype}")
+            dst.copy_(src)
+
+    def new_cache(self, budget: int) -> LayerCache:
+        """Output buffers of a layer's compact cache at `budget`."""
+        if not 0 <= budget <= self.max_budget:
+            raise ValueError(f"budget {budget} outside [0, {self.max_budget}]")
+        n_keep = budget + self.n_sink + self.obs_window
+        shape = (self.batch, self.n_kv_heads, n_keep)
+        dev = self.k.device
+        return LayerCache(budget, torch.empty(shape, dtype=torch.int32, device=dev),
+                          torch.empty(shape + (self.head_dim,), dtype=self.dtype, device=dev),
+                          torch.empty(shape + (self.head_dim,), dtype=self.dtype, device=dev))
+
+    def layer_end(self, cache: LayerCache, stream=None) -> LayerCache:
+        """LayerEndCompress of the active layer into `cache` (score ->
+        max-pool -> top-budget + window -> gather), enqueued on `stream`."""
+        if select_workspace_bytes(self.desc, cache.budget) > self.select_ws.numel():
+            raise ValueError("select workspace sized for a smaller budget")
+        score(self.q, self.k, pool_kernel=self.pool_kernel, n_sink=self.n_sink,
+              pooled=self.pooled, raw=self.raw, workspace=self.score_ws, stream=stream)
+        select_compact(self.pooled, self.k, self.v, cache.budget, obs_window=self.obs_window,
+                       n_q_heads=self.n_q_heads, n_sink=self.n_sink, idx=cache.idx,
+                       k_out=cache.k_hat, v_out=cache.v_hat, workspace=self.select_ws,
+                       stream=stream)
+        return cache
+
+    def commit(self, budget: int, stream=None) -> LayerCache:
+        """Compress the active layer at `budget` and append its compact cache
+        to the store (the layer-end commit; the active buffer may then be
+        refilled with the next layer)."""
+        cache = self.layer_end(self.new_cache(budget), stream=stream)
+        self.store.append(cache)
+        return cache
+
+    def run(self, layers, budgets, stream=None) -> list:
+        """Algorithm 1's outer loop over an iterable of (q, k, v) per layer
+        with its budget schedule; returns the store."""
+        for (q, k, v), b in zip(layers, budgets):
+            self.load(q, k, v)
+            self.commit(b, stream=stream)
+        return self.store
+
+
+def linear_budgets(n_layers: int, first: int, last: int) -> list:
+    """A PyramidKV-style per-layer budget schedule falling linearly from
+    `first` (layer 0) to `last` (layer n_layers-1), rounded down:
+    B_l = first - floor((first - last) * l / (n_layers - 1))."""
+    if n_layers == 1:
+        return [first]
+    return [first - ((first - last) * l) // (n_layers - 1) for l in range(n_layers)]

@@ -1,18 +1,19 @@
 """Throughput of the layer-end KV selection path on one MI355X.
 
 A step is one pass of the whole path over one layer of synthetic input that
-is already resident in HBM: kvsel_score (two streaming passes over K, row
-statistics, max-pool) -> kvsel_select (exact top-B + window) -> kvsel_compact
-(K/V gather).  The metric is prompt-KV tokens scored + selected + compacted
-per second per layer.
+is already resident in HBM, as the layer-major driver runs it: kvsel_score
+(two streaming passes over K, row statistics, max-pool), then
+kvsel_select_compact (exact top-B + window, K/V gather).  The metric is
+prompt-KV tokens scored + selected + compacted per second per layer.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --copy-calibration     # plain device copy, for counter scaling
+  python bench.py --summarize-trace kernel_trace.csv --last N --title T --command C
 
 Workloads (one JSON line each):
-  llama8k      one Llama-3-8B-shaped layer, 8192-token prompt (default)
-  llama64k     the same shape at 65536 tokens, B = 4096
-  qwen128k     one Qwen3-14B-shaped layer (40 q / 8 kv heads), 131072 tokens
+  qwen128k     one Qwen3-14B-shaped layer (40 q / 8 kv heads), 131072 tokens (default)
+  llama8k      one Llama-3-8B-shaped layer, 8192-token prompt
+  llama64k     the Llama shape at 65536 tokens, B = 4096 (first layer of the sweep)
   sweep64k     32 layers at 65536 tokens, budget 4096 -> 512, one layer resident
   qevict32k    16 x 32768-token caches, 256 decode queries, window tiers
   qevict-steps QEvict decode-time routing every 8 tokens: 16 x 32768-token caches,
@@ -23,6 +24,9 @@ Workloads (one JSON line each):
   llama8k-adaptive / qwen128k-adaptive
                the same layers with a head-adaptive budget: Hkv*B picks per
                sequence over all KV heads, flattened output with head offsets
+
+The timed region is the run's last GPU work, so the last steps x
+dispatches_per_step dispatches of a kernel trace of the run are exactly it.
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,7 +46,8 @@ if ROOT not in sys.path:
 
 import synth  # noqa: E402
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 METRIC = "prompt-KV tokens scored+selected+compacted/sec per layer; % of HBM BW peak"
 WORKLOADS = {
     "llama8k": (2, "llama3-8b-layer-8k"),
@@ -56,7 +62,7 @@ WORKLOADS = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "qevict.hip",
-                  "common.h"]
+                  "common.h", "api.hip", "timing.hip"]
 
 
 def source_hash() -> str:
@@ -69,8 +75,8 @@ def source_hash() -> str:
 
 
 def algorithmic_bytes(spec: synth.LayerSpec) -> dict:
-    """Bytes each ABI call must move per layer (two K sweeps, score vectors,
-    gather); the sum is the path's algorithmic traffic."""
+    """Bytes the path must move per layer (two K sweeps, the score vectors,
+    the gather): per ABI call and the path's sum."""
     e = 2 if spec.dtype == "bf16" else 4
     H = spec.batch * spec.n_kv_heads
     S, W, D, n_keep = spec.seq_len, spec.obs_window, spec.head_dim, spec.n_keep
@@ -78,10 +84,9 @@ def algorithmic_bytes(spec: synth.LayerSpec) -> dict:
     d = {
         # two K sweeps + raw score write + max-pool read of raw, write of pooled
         "kvsel_score": 2 * k_sweep + H * S * 4 + H * S * 4 + H * (S - W) * 4,
-        # pooled read + index write
-        "kvsel_select": H * (S - W) * 4 + H * n_keep * 4,
-        # K and V rows read and written + index read
-        "kvsel_compact": 2 * 2 * H * n_keep * D * e + H * n_keep * 4,
+        # pooled read + index write; K and V rows read and written + index read
+        "kvsel_select_compact": H * (S - W) * 4 + H * n_keep * 4
+        + 2 * 2 * H * n_keep * D * e + H * n_keep * 4,
     }
     d["path"] = sum(d.values())
     return d
@@ -100,43 +105,49 @@ def tier_bytes(spec: synth.LayerSpec, n_full: int, n_quant: int, n_prom: int, wi
 
 def cpu_baseline(spec: synth.LayerSpec, x: dict, budget_s: float = 12.0,
                  adaptive: bool = False) -> dict:
-    """The oracle, as it stands, timed on this host on the same layer."""
+    """The oracle, as it stands, timed on this host on the same workload.
+    Layers whose dense fp64 scoring is large run on a sample of KV heads (the
+    oracle's work is the same for every head), scaled to the whole layer."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    q64 = synth.to_f64(x["q"], spec.dtype)
-    k64 = synth.to_f64(x["k"], spec.dtype)
+    S, W, G, Hkv = spec.seq_len, spec.obs_window, spec.group, spec.n_kv_heads
+    heads = Hkv if adaptive or spec.n_q_heads * W * S <= 64 * 1024 * 1024 else 1
+    q64 = synth.to_f64(x["q"][:, :heads * G], spec.dtype)
+    k64 = synth.to_f64(x["k"][:, :heads], spec.dtype)
+    ks, vs = x["k"][:, :heads], x["v"][:, :heads]
     reps, t0 = 0, time.perf_counter()
-    S, W = spec.seq_len, spec.obs_window
     while True:
         if adaptive:
             s = oracle.head_scores(q64, k64, causal=bool(spec.causal))
             p = oracle.max_pool(s, spec.pool_kernel, spec.n_sink, S - W)
-            idx, off = oracle.select_head_adaptive(p, spec.n_kv_heads * spec.budget,
-                                                   spec.n_sink, W)
-            oracle.compact_flat(x["k"], idx, off)
-            oracle.compact_flat(x["v"], idx, off)
+            idx, off = oracle.select_head_adaptive(p, heads * spec.budget, spec.n_sink, W)
+            oracle.compact_flat(ks, idx, off)
+            oracle.compact_flat(vs, idx, off)
         else:
-            oracle.layer_end_compress(q64, k64, x["v"], budget=spec.budget,
-                                      window=W, pool_kernel=spec.pool_kernel,
-                                      n_sink=spec.n_sink, causal=bool(spec.causal),
-                                      k_store=x["k"], v_store=x["v"])
+            oracle.layer_end_compress(q64, k64, vs, budget=spec.budget, window=W,
+                                      pool_kernel=spec.pool_kernel, n_sink=spec.n_sink,
+                                      causal=bool(spec.causal), k_store=ks, v_store=vs)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
             break
-    return {"value": round(spec.batch * spec.seq_len * reps / el, 1), "unit": "tokens/s",
+    per_layer_s = el / reps * (Hkv / heads)
+    what = (f"{reps} full layer(s)" if heads == Hkv else
+            f"KV head 0 of the layer ({G} query heads x {W} queries x {S} keys: score, pool, "
+            f"select, gather) {reps} time(s), scaled x{Hkv} to the layer's {Hkv} KV heads")
+    return {"value": round(spec.batch * S / per_layer_s, 1), "unit": "tokens/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full layer(s) of the same workload through the fp64 oracle "
+            "sample": f"{what} of the same workload through the fp64 oracle "
                       f"({el:.1f} s, {threads} BLAS threads)"}
 
 
-def traffic_for(workload: str, call: str):
-    """Measured HBM bytes per call from the committed counter summary, if it
-    was taken with the current kernel sources; else None."""
+def traffic_for(workload: str, kernel: str):
+    """Measured HBM bytes per launch of `kernel` from the committed counter
+    summary, if it was taken with the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -144,7 +155,7 @@ def traffic_for(workload: str, call: str):
         return None
     if t.get("source_hash") != source_hash():
         return None
-    return t.get("per_call_bytes", {}).get(workload, {}).get(call)
+    return t.get("per_kernel_bytes", {}).get(workload, {}).get(kernel)
 
 
 def event_time_us(torch, stream, fn, reps: int) -> float:
@@ -158,82 +169,141 @@ def event_time_us(torch, stream, fn, reps: int) -> float:
     return a.elapsed_time(b) / reps * 1e3
 
 
+def kernel_times(kvsel, torch, fn, steps: int, prefix: str = "*") -> dict:
+    """Per-kernel HIP-event timing inside the library (kvsel_timing_start):
+    {kernel: (average us per launch, launches per step)} over `steps` calls
+    of fn()."""
+    kvsel.timing_read()
+    kvsel.timing_start(prefix)
+    try:
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+    finally:
+        kvsel.timing_start(None)
+    return {name: (ms * 1e3 / n, n / steps) for name, (ms, n) in kvsel.timing_read().items()}
+
+
+def kernel_work(spec: synth.LayerSpec, kernel: str, n_keep: int) -> tuple:
+    """Algorithmic (bytes, flops) of one launch of a kernel of the prompt path:
+    what the kernel's own step of the method must move and compute (two K
+    sweeps for the two score passes; score vectors; the gather)."""
+    e = 2 if spec.dtype == "bf16" else 4
+    H = spec.batch * spec.n_kv_heads
+    S, W, D = spec.seq_len, spec.obs_window, spec.head_dim
+    GW = spec.group * W
+    sweep, flops = H * S * D * e, 2 * H * GW * D * S
+    if kernel.startswith("score_pass1"):
+        return sweep, flops
+    if kernel.startswith("score_pass2"):
+        return sweep + H * S * 4, flops
+    if kernel == "maxpool_kernel":
+        return 2 * H * S * 4, 0
+    if kernel in ("select_kernel", "sel_emit"):
+        return H * (S - W) * 4 + H * n_keep * 4, 0
+    if kernel.startswith("sel_hist") or kernel == "sel_cand":
+        return H * (S - W) * 4, 0
+    if kernel == "compact_kernel":
+        return 4 * H * n_keep * D * e + H * n_keep * 4, 0
+    return 0, 0
+
+
+def roofline_entry(kernel: str, us: float, nbytes: int, flops: int, traffic) -> dict:
+    """Roofline of one kernel launch: the binding bound is the larger of its
+    HBM time and its bf16 matrix-core time at MI355X's published peaks."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        ach = flops / (us * 1e-6) / 1e12
+        ent = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+               "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = nbytes / (us * 1e-6) / 1e9
+        ent = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+    ent["traffic"] = traffic
+    ent.update({"kernel": kernel, "us_per_launch": round(us, 2),
+                "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+                "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)})
+    return ent
+
+
+def copy_bandwidth_gbs(torch, stream, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """A plain device-to-device copy on the launch stream: the achievable
+    read + write bandwidth of this GPU (a STREAM-copy style reference)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    us = event_time_us(torch, stream, lambda: b.copy_(a), reps)
+    del a, b
+    return 2 * nbytes / (us * 1e-6) / 1e9
+
+
 class Layer:
-    """Device buffers of one resident layer and its preallocated outputs."""
+    """One resident layer on the layer-major driver, with its preallocated
+    compact cache; a step is the layer-end step as the driver runs it
+    (kvsel_score, then kvsel_select_compact).  The head-adaptive variant
+    runs kvsel_score, kvsel_select_adaptive and kvsel_compact_flat."""
 
-    def __init__(self, kvsel, torch, spec, x, dev, adaptive=False):
-        self.kvsel, self.torch, self.spec = kvsel, torch, spec
-        self.adaptive = adaptive
-        if spec.dtype == "bf16":
-            up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
-        else:
-            up = lambda a: torch.from_numpy(a).to(dev)  # noqa
-        self.q, self.k, self.v = up(x["q"]), up(x["k"]), up(x["v"])
-        Bt, Hkv, S, D = self.k.shape
-        self.pooled = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev)
-        self.raw = torch.empty_like(self.pooled)
-        self.desc = kvsel.make_desc(self.q, self.k, n_sink=spec.n_sink, causal=bool(spec.causal))
-        self.ws = torch.empty(max(kvsel.score_workspace_bytes(self.desc), 1), dtype=torch.uint8,
-                              device=dev)
+    def __init__(self, kvsel, torch, spec, x, adaptive=False):
+        from attention_score_eviction_amd.driver import LayerMajorDriver
+        self.kvsel, self.torch, self.spec, self.adaptive = kvsel, torch, spec, adaptive
+        dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+        self.drv = LayerMajorDriver(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
+                                    spec.seq_len, spec.obs_window, spec.pool_kernel,
+                                    max_budget=spec.budget, n_sink=spec.n_sink, dtype=dt)
+        self.load(x)
         self.set_budget(spec.budget)
-
-    def set_budget(self, budget):
-        torch, kvsel = self.torch, self.kvsel
-        Bt, Hkv, S, D = self.k.shape
-        dev = self.k.device
-        self.budget = budget
-        n_keep = budget + self.spec.n_sink + self.spec.obs_window
-        if self.adaptive:
-            # the same rows in total, chosen over all KV heads of a sequence
-            self.idx = torch.empty((Bt, Hkv * n_keep), dtype=torch.int32, device=dev)
-            self.head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=dev)
-            nb = kvsel.select_adaptive_workspace_bytes(self.desc, Hkv * budget)
-            self.k_hat = torch.empty((Bt, Hkv * n_keep, D), dtype=self.k.dtype, device=dev)
-        else:
-            self.idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
-            nb = kvsel.select_workspace_bytes(self.desc, budget)
-            self.k_hat = torch.empty((Bt, Hkv, n_keep, D), dtype=self.k.dtype, device=dev)
-        self.sel_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
-        self.v_hat = torch.empty_like(self.k_hat)
 
     def load(self, x):
         """Overwrite the resident layer in place (the single active buffer)."""
         torch = self.torch
-        for name, t in (("q", self.q), ("k", self.k), ("v", self.v)):
-            t.copy_(torch.from_numpy(x[name].view(np.int16)).view(torch.bfloat16))
+        if self.spec.dtype == "bf16":
+            t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+        else:
+            t = torch.from_numpy
+        self.drv.load(t(x["q"]), t(x["k"]), t(x["v"]))
+
+    def set_budget(self, budget):
+        self.budget = budget
+        self.cache = self.drv.new_cache(budget)
+        if self.adaptive:
+            torch, kvsel, d = self.torch, self.kvsel, self.drv
+            Bt, Hkv = self.spec.batch, self.spec.n_kv_heads
+            n_keep = Hkv * (budget + self.spec.n_sink + self.spec.obs_window)
+            dev = d.k.device
+            self.idx = torch.empty((Bt, n_keep), dtype=torch.int32, device=dev)
+            self.head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=dev)
+            self.k_hat = torch.empty((Bt, n_keep, self.spec.head_dim), dtype=d.k.dtype,
+                                     device=dev)
+            self.v_hat = torch.empty_like(self.k_hat)
+            nb = kvsel.select_adaptive_workspace_bytes(d.desc, Hkv * budget)
+            self.sel_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
 
     def score(self, stream):
-        s = self.spec
-        self.kvsel.score(self.q, self.k, pool_kernel=s.pool_kernel, n_sink=s.n_sink,
-                         causal=bool(s.causal), pooled=self.pooled, raw=self.raw,
-                         workspace=self.ws, stream=stream)
+        d = self.drv
+        self.kvsel.score(d.q, d.k, pool_kernel=d.pool_kernel, n_sink=d.n_sink, pooled=d.pooled,
+                         raw=d.raw, workspace=d.score_ws, stream=stream)
 
-    def select(self, stream):
-        s = self.spec
+    def select_compact(self, stream):
+        d, s = self.drv, self.spec
         if self.adaptive:
             self.kvsel.select_adaptive(
-                self.pooled, self.k.shape[1] * self.budget, obs_window=s.obs_window,
-                n_q_heads=s.n_q_heads, head_dim=self.k.shape[3], n_sink=s.n_sink,
-                causal=bool(s.causal), idx=self.idx, head_off=self.head_off, dtype=self.k.dtype,
-                workspace=self.sel_ws, stream=stream)
-            return
-        self.kvsel.select(self.pooled, self.budget, obs_window=s.obs_window,
-                          n_q_heads=s.n_q_heads, head_dim=self.k.shape[3], n_sink=s.n_sink,
-                          causal=bool(s.causal), idx=self.idx, dtype=self.k.dtype,
-                          workspace=self.sel_ws, stream=stream)
-
-    def compact(self, stream):
-        if self.adaptive:
-            self.kvsel.compact_flat(self.k, self.v, self.idx, self.head_off, k_out=self.k_hat,
+                d.pooled, s.n_kv_heads * self.budget, obs_window=s.obs_window,
+                n_q_heads=s.n_q_heads, head_dim=s.head_dim, n_sink=s.n_sink, idx=self.idx,
+                head_off=self.head_off, dtype=d.k.dtype, workspace=self.sel_ws, stream=stream)
+            self.kvsel.compact_flat(d.k, d.v, self.idx, self.head_off, k_out=self.k_hat,
                                     v_out=self.v_hat, stream=stream)
             return
-        self.kvsel.compact(self.k, self.v, self.idx, k_out=self.k_hat, v_out=self.v_hat,
-                           stream=stream)
+        c = self.cache
+        self.kvsel.select_compact(d.pooled, d.k, d.v, c.budget, obs_window=s.obs_window,
+                                  n_q_heads=s.n_q_heads, n_sink=s.n_sink, idx=c.idx,
+                                  k_out=c.k_hat, v_out=c.v_hat, workspace=d.select_ws,
+                                  stream=stream)
 
     def step(self, stream):
         self.score(stream)
-        self.select(stream)
-        self.compact(stream)
+        self.select_compact(stream)
 
 
 def copy_calibration(steps: int) -> int:
@@ -250,90 +320,145 @@ def copy_calibration(steps: int) -> int:
     return 0
 
 
-CALL_KERNELS = {
-    "kvsel_score": ("score_pass1", "score_combine", "score_pass2", "maxpool_kernel",
-                    "score_group_sum"),
-    "kvsel_select": ("select_kernel", "sel_init", "sel_hist", "sel_cand", "sel_resolve",
-                     "sel_emit"),
-    "kvsel_compact": ("compact_kernel",),
-    "kvsel_select_adaptive": ("sel_init", "sel_hist", "sel_cand", "sel_resolve", "sel_emit",
-                              "mandatory_only_kernel"),
-    "kvsel_compact_flat": ("compact_flat_kernel",),
-    "kvsel_route_tiers": ("tier_rank_kernel", "tier_move_kernel", "tier_promote_kernel"),
-}
+def short_kernel_name(n: str) -> str:
+    """A profiler's kernel name reduced to the library's base name:
+    'void ns::(anonymous namespace)::score_pass1_32<128, 10, 8>(args)' ->
+    'score_pass1_32'."""
+    n = re.sub(r"^void ", "", n.strip())
+    if n.endswith(")"):                      # drop the parameter list
+        depth = 0
+        for i in range(len(n) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(n[i], 0)
+            if depth == 0:
+                n = n[:i]
+                break
+    n = n.split("<")[0]                      # drop template arguments
+    return n.split("::")[-1].strip()
 
 
 def _counter_means(path: str, counter: str) -> dict:
-    """Mean per-dispatch value of `counter` for each kernel in a rocprofv3
-    counter_collection.csv."""
+    """Mean per-dispatch value of `counter` for each kernel (base name) in a
+    rocprofv3 counter_collection.csv."""
     import csv
     acc = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        acc.setdefault(r["Kernel_Name"], {})
-        acc[r["Kernel_Name"]].setdefault(r["Dispatch_Id"], 0.0)
-        acc[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        k = short_kernel_name(r["Kernel_Name"])
+        acc.setdefault(k, {})
+        acc[k].setdefault(r["Dispatch_Id"], 0.0)
+        acc[k][r["Dispatch_Id"]] += float(r["Counter_Value"])
     return {k: sum(v.values()) / len(v) for k, v in acc.items()}
 
 
 def ingest_counters(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: str,
                     cal_write_csv: str) -> int:
     """Turn FETCH_SIZE / WRITE_SIZE runs of this bench (and of the copy
-    calibration) into measured HBM bytes per ABI call, stored with the hash of
-    the kernel sources in profiles/traffic.json."""
+    calibration) into measured HBM bytes per kernel launch, stored with the
+    hash of the kernel sources in profiles/traffic.json."""
     cal_bytes = 256 * 1024 * 1024
     cf = max(_counter_means(cal_fetch_csv, "FETCH_SIZE").values())
     cw = max(_counter_means(cal_write_csv, "WRITE_SIZE").values())
     f_scale, w_scale = cal_bytes / cf, cal_bytes / cw
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
-    per_call = {}
-    adaptive = workload.endswith("-adaptive")
-    for call, kernels in CALL_KERNELS.items():
-        if (call in ("kvsel_select_adaptive", "kvsel_compact_flat")) != adaptive and \
-                call in ("kvsel_select", "kvsel_compact", "kvsel_select_adaptive",
-                         "kvsel_compact_flat"):
-            continue
-        tot, seen = 0.0, False
-        for name in set(fetch) | set(write):
-            if any(kn in name for kn in kernels):
-                tot += fetch.get(name, 0.0) * f_scale + write.get(name, 0.0) * w_scale
-                seen = True
-        if seen:
-            per_call[call] = int(round(tot))
+    per_kernel = {k: int(round(fetch.get(k, 0.0) * f_scale + write.get(k, 0.0) * w_scale))
+                  for k in set(fetch) | set(write)}
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except OSError:
         t = {}
     if t.get("source_hash") != source_hash():
-        t = {"per_call_bytes": {}}
+        t = {"per_kernel_bytes": {}}
+    t.setdefault("per_kernel_bytes", {})
     t["source_hash"] = source_hash()
     t["scale"] = {"fetch_bytes_per_unit": f_scale, "write_bytes_per_unit": w_scale,
                   "calibration": "bench.py --copy-calibration (256 MiB device copy)"}
-    t["per_call_bytes"][workload] = per_call
+    t["per_kernel_bytes"][workload] = per_kernel
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(t, f, indent=1, sort_keys=True)
-    print(json.dumps({"workload": workload, "per_call_bytes": per_call}))
+    print(json.dumps({"workload": workload, "per_kernel_bytes": per_kernel}))
+    return 0
+
+
+def _trace_rows(path: str) -> list:
+    """(start, end, kernel base name) of every dispatch in a rocprofv3 kernel
+    trace (kernel_trace.csv, or a results .db), in start order."""
+    rows = []
+    if path.endswith(".csv"):
+        import csv
+        for r in csv.DictReader(open(path)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                         short_kernel_name(r["Kernel_Name"])))
+    else:
+        import sqlite3
+        con = sqlite3.connect(path)
+        cols = [c[1] for c in con.execute("pragma table_info(kernels)")]
+        st = "start" if "start" in cols else "start_timestamp"
+        en = "end" if "end" in cols else "end_timestamp"
+        for a, b, n in con.execute(f"select {st}, {en}, name from kernels"):
+            rows.append((int(a), int(b), short_kernel_name(n)))
+    rows.sort()
+    return rows
+
+
+def summarize_trace(path: str, last: int, title: str, command: str) -> int:
+    """Markdown summary of the last `last` dispatches of a kernel trace (the
+    timed region of a bench run: it is the run's last GPU work), per kernel:
+    launches, mean / median / min duration and share, plus the sum of the
+    per-step medians."""
+    import statistics
+    rows = _trace_rows(path)
+    if last <= 0 or last > len(rows):
+        print(f"trace has {len(rows)} dispatches, asked for the last {last}", file=sys.stderr)
+        return 1
+    sel = rows[-last:]
+    per = {}
+    for a, b, n in sel:
+        per.setdefault(n, []).append((b - a) / 1e3)
+    tot = sum(sum(v) for v in per.values())
+    span_us = (sel[-1][1] - sel[0][0]) / 1e3
+    out = [f"# rocprofv3 kernel trace: {title}", "", "Command (from the repository root on "
+           "the GPU host):", "", "```", command, "```", "",
+           f"The last {last} dispatches of the run: the bench's timed region (its last GPU "
+           f"work), {span_us:.1f} us from the first start to the last end.  Microseconds.", "",
+           "| kernel | launches | mean us | median us | min us | share |",
+           "|---|---|---|---|---|---|"]
+    steps = None
+    for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {n} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} "
+                   f"| {min(v):.2f} | {100 * sum(v) / tot:.1f}% |")
+        steps = len(v) if steps is None else min(steps, len(v))
+    med_sum = sum(statistics.median(v) * len(v) / steps for v in per.values()) if steps else 0
+    out += ["", f"Sum of per-kernel medians per step ({steps} steps): {med_sum:.2f} us; "
+                f"mean time per step from first start to last end: {span_us / steps:.2f} us."]
+    print("\n".join(out))
     return 0
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama8k", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen128k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                     help="record measured traffic for --workload from rocprofv3 csv files")
+    ap.add_argument("--summarize-trace", metavar="TRACE",
+                    help="markdown summary of the last --last dispatches of a kernel trace")
+    ap.add_argument("--last", type=int, default=0)
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
     args = ap.parse_args()
     if args.ingest_counters:
         return ingest_counters(args.workload, *args.ingest_counters)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.last, args.title, args.command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the work shards by KV head with no exchange); run with --gpus 1", file=sys.stderr)
@@ -356,12 +481,26 @@ def main() -> int:
         return bench_tiers(args, kvsel, torch, spec, wname, dev, stream)
     x = synth.make_layer(spec, cid)
     adaptive = args.workload.endswith("-adaptive")
-    L = Layer(kvsel, torch, spec, x, dev, adaptive=adaptive)
+    L = Layer(kvsel, torch, spec, x, adaptive=adaptive)
     if args.workload == "sweep64k":
-        return bench_sweep(args, torch, spec, wname, L, stream)
+        return bench_sweep(args, kvsel, torch, spec, wname, L, stream)
 
+    copy_gbs = copy_bandwidth_gbs(torch, stream)
     for _ in range(args.warmup):
         L.step(stream)
+    torch.cuda.synchronize()
+    # per-call breakdown (HIP events around each ABI call), then per kernel
+    reps = max(args.steps // 2, 20)
+    sel_name = "kvsel_select_adaptive+compact_flat" if adaptive else "kvsel_select_compact"
+    us_call = {"kvsel_score": event_time_us(torch, stream, lambda: L.score(stream), reps),
+               sel_name: event_time_us(torch, stream, lambda: L.select_compact(stream), reps)}
+    kt = kernel_times(kvsel, torch, lambda: L.step(stream), reps)
+    dispatches = sum(n for _, n in kt.values())
+    dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
+    # timed region: the last GPU work of the run; the dominant kernel's
+    # launches are bracketed by HIP events on the launch stream
+    kvsel.timing_read()
+    kvsel.timing_start(dom)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -371,24 +510,20 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    kvsel.timing_start(None)
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    dom_ms, dom_n = kvsel.timing_read()[dom]
+    dom_us = dom_ms * 1e3 / dom_n
 
-    reps = max(args.steps, 50)
-    sel_name = "kvsel_select_adaptive" if adaptive else "kvsel_select"
-    cmp_name = "kvsel_compact_flat" if adaptive else "kvsel_compact"
-    us = {"kvsel_score": event_time_us(torch, stream, lambda: L.score(stream), reps),
-          sel_name: event_time_us(torch, stream, lambda: L.select(stream), reps),
-          cmp_name: event_time_us(torch, stream, lambda: L.compact(stream), reps)}
-    ab = algorithmic_bytes(spec)
-    if adaptive:
-        ab[sel_name] = ab.pop("kvsel_select") + spec.batch * (spec.n_kv_heads + 1) * 4
-        ab[cmp_name] = ab.pop("kvsel_compact") + spec.batch * (spec.n_kv_heads + 1) * 4
-        ab["path"] = ab["kvsel_score"] + ab[sel_name] + ab[cmp_name]
     Bt, S = spec.batch, spec.seq_len
+    n_keep = spec.n_keep
+    ab = algorithmic_bytes(spec)
     value = Bt * S / (ms_step * 1e-3)
     path_gbs = ab["path"] / (ms_step * 1e-3) / 1e9
-    dom = max(us, key=us.get)
-    dom_gbs = ab[dom] / (us[dom] * 1e-6) / 1e9
+    nbytes, flops = kernel_work(spec, dom, n_keep)
+    score_flops = 2 * 2 * Bt * spec.n_q_heads * spec.obs_window * spec.head_dim * S
+    t_score_us = sum(us * n for k, (us, n) in kt.items()
+                     if k.startswith("score_") or k == "maxpool_kernel")
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -400,13 +535,17 @@ def main() -> int:
                    "budget": (f"{spec.n_kv_heads * spec.budget} per sequence over all KV heads"
                               if adaptive else spec.budget), "parallelism": "none"},
         "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+        "path_copy_frac": round(path_gbs / copy_gbs, 4),
+        "copy_gbs": round(copy_gbs, 1),
         "path_algorithmic_bytes": ab["path"],
-        "us_per_call": {k: round(v, 2) for k, v in us.items()},
+        "score_mfma_util": round(score_flops / (t_score_us * 1e-6) / 1e12
+                                 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "us_per_call": {k: round(v, 2) for k, v in us_call.items()},
+        "us_per_kernel": {k: round(us, 2) for k, (us, n) in
+                          sorted(kt.items(), key=lambda kv: -kv[1][0] * kv[1][1])},
+        "dispatches_per_step": int(round(dispatches)),
         "wall_s": round(wall, 3),
-        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(args.workload, dom), "kernel": dom,
-                     "algorithmic_bytes_per_launch": ab[dom]},
+        "roofline": roofline_entry(dom, dom_us, nbytes, flops, traffic_for(args.workload, dom)),
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(spec, x, adaptive=adaptive)
@@ -414,25 +553,29 @@ def main() -> int:
     return 0
 
 
-def bench_sweep(args, torch, spec, wname, L, stream) -> int:
-    """32 layers, one resident full-prompt layer buffer overwritten per layer;
-    each layer's compact K/V goes to a per-layer store (the only state kept)."""
+def bench_sweep(args, kvsel, torch, spec, wname, L, stream) -> int:
+    """TideKV Algorithm 1 over 32 layers with the layer-major driver: one
+    resident full-prompt layer buffer refilled per layer, each layer's
+    compact K/V and positions committed to the driver's per-layer store."""
+    from attention_score_eviction_amd.driver import linear_budgets
     n_layers = 32
-    per_layer_us, store_bytes = [], 0
+    budgets = linear_budgets(n_layers, 4096, 512)
+    drv = L.drv
+    per_layer_us = []
     reps = max(1, args.steps // 10)
-    store = []
+    torch.cuda.reset_peak_memory_stats()
     for layer in range(n_layers):
-        b = synth.sweep_budget(layer, n_layers)
         if layer > 0:
             L.load(synth.make_layer(spec, 3, layer))
-        L.set_budget(b)
+        cache = drv.new_cache(budgets[layer])
         for _ in range(max(1, args.warmup // 10)):
-            L.step(stream)
+            drv.layer_end(cache, stream=stream)
         torch.cuda.synchronize()
-        per_layer_us.append(event_time_us(torch, stream, lambda: L.step(stream), reps))
-        store.append((L.k_hat.clone(), L.v_hat.clone(), L.idx.clone()))
-        store_bytes += sum(t.numel() * t.element_size() for t in store[-1])
-        print(f"layer {layer} budget {b}: {per_layer_us[-1]:.1f} us", file=sys.stderr, flush=True)
+        per_layer_us.append(event_time_us(torch, stream,
+                                          lambda: drv.layer_end(cache, stream=stream), reps))
+        drv.store.append(cache)     # the layer-end commit
+        print(f"layer {layer} budget {budgets[layer]}: {per_layer_us[-1]:.1f} us",
+              file=sys.stderr, flush=True)
     mean_us = sum(per_layer_us) / n_layers
     S = spec.seq_len
     out = {
@@ -443,10 +586,12 @@ def bench_sweep(args, torch, spec, wname, L, stream) -> int:
         "config": {"workload": wname, "layers": n_layers, "seq_len": S,
                    "n_q_heads": spec.n_q_heads, "n_kv_heads": spec.n_kv_heads,
                    "head_dim": spec.head_dim, "obs_window": spec.obs_window,
-                   "budget_first": synth.sweep_budget(0), "budget_last": synth.sweep_budget(31),
+                   "budget_first": budgets[0], "budget_last": budgets[-1],
                    "parallelism": "none"},
         "per_layer_us_mean": round(mean_us, 2), "per_layer_us_max": round(max(per_layer_us), 2),
-        "compact_store_bytes": store_bytes,
+        "active_layer_bytes": drv.active_bytes,
+        "compact_store_bytes": drv.store_bytes,
+        "scratch_bytes": drv.scratch_bytes,
         "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
     }
     print(json.dumps(out), flush=True)
@@ -489,8 +634,9 @@ def bench_tiers(args, kvsel, torch, spec, wname, dev, stream) -> int:
           "kvsel_route_tiers": event_time_us(torch, stream, tiers, reps)}
     step_us = us["kvsel_score"] + us["kvsel_route_tiers"]
     tb = tier_bytes(spec, n_full, n_quant, n_prom)
-    flops = 2 * 2 * Bt * spec.n_q_heads * spec.obs_window * D * S
-    tflops = flops / (us["kvsel_score"] * 1e-6) / 1e12
+    kt = kernel_times(kvsel, torch, lambda: (score(), tiers()), reps)
+    dom = max(kt, key=lambda kk: kt[kk][0] * kt[kk][1])
+    nbytes, flops = kernel_work(spec, dom, 0)
     out = {
         "metric": METRIC, "value": round(Bt * S / (step_us * 1e-6), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": reps, "warmup": args.warmup,
@@ -501,10 +647,9 @@ def bench_tiers(args, kvsel, torch, spec, wname, dev, stream) -> int:
                    "tiers": [n_full, n_quant, (S // 64) - n_full - n_quant], "promote": n_prom,
                    "parallelism": "none"},
         "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
-                     "traffic": traffic_for(args.workload, "kvsel_score"),
-                     "kernel": "kvsel_score", "algorithmic_flops_per_launch": flops},
+        "us_per_kernel": {kk: round(u, 2) for kk, (u, n) in kt.items()},
+        "roofline": roofline_entry(dom, kt[dom][0], nbytes, flops,
+                                   traffic_for(args.workload, dom)),
         "route_tiers_hbm_frac": round(tb / (us["kvsel_route_tiers"] * 1e-6) / 1e9
                                       / HBM_PEAK_GBS, 4),
     }
@@ -564,8 +709,10 @@ def bench_kara(args, kvsel, torch, wname) -> int:
     path = sum(ab.values())
     # The scoring contraction has G*|W| = 2048 query rows per key: it is bound
     # by the matrix cores (and the exponentials), not by HBM.
-    flops = 2 * 2 * Bt * Hq * Wn * n * D
-    tflops = flops / (us["kvsel_kara_score"] * 1e-6) / 1e12
+    kt = kernel_times(kvsel, torch, step, reps)
+    dom = max(kt, key=lambda kk: kt[kk][0] * kt[kk][1])
+    kspec = synth.LayerSpec(Bt, Hq, Hkv, D, n, Wn, 1, 0, causal=0)
+    nbytes, kflops = kernel_work(kspec, dom, n_keep)
     out = {
         "metric": METRIC, "value": round(Bt * Wn / (step_us * 1e-6), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -577,10 +724,9 @@ def bench_kara(args, kvsel, torch, wname) -> int:
         "path_hbm_frac": round(path / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "path_algorithmic_bytes": path,
         "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0,
-                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
-                     "traffic": traffic_for(args.workload, "kvsel_kara_score"),
-                     "kernel": "kvsel_kara_score", "algorithmic_flops_per_launch": flops},
+        "us_per_kernel": {kk: round(u, 2) for kk, (u, m) in kt.items()},
+        "roofline": roofline_entry(dom, kt[dom][0], nbytes, kflops,
+                                   traffic_for(args.workload, dom)),
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -634,10 +780,11 @@ def bench_qevict_steps(args, kvsel, torch, spec, wname) -> int:
     step_us = event_time_us(torch, stream, step, steps)
     us = {"kvsel_score": event_time_us(torch, stream, score, steps),
           "kvsel_qevict_step": event_time_us(torch, stream, route, steps)}
-    H = Bt * Hkv
     t = state["tier"].cpu().numpy()
-    score_bytes = 2 * H * S * D * 2 + H * S * 4   # two K sweeps + the raw scores
-    dom_gbs = score_bytes / (us["kvsel_score"] * 1e-6) / 1e9
+    kt = kernel_times(kvsel, torch, step, steps)
+    dom = max(kt, key=lambda kk: kt[kk][0] * kt[kk][1])
+    kspec = synth.LayerSpec(Bt, Hq, Hkv, D, S, omega, 1, 0, causal=0)
+    nbytes, kflops = kernel_work(kspec, dom, 0)
     out = {
         "metric": METRIC, "value": round(Bt * S / (step_us * 1e-6), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup,
@@ -650,10 +797,9 @@ def bench_qevict_steps(args, kvsel, torch, spec, wname) -> int:
         "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
         "final_tiers": {"full": int((t == 0).sum()), "quant": int((t == 1).sum()),
                         "evicted": int((t == 2).sum())},
-        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(args.workload, "kvsel_score"),
-                     "kernel": "kvsel_score", "algorithmic_bytes_per_launch": score_bytes},
+        "us_per_kernel": {kk: round(u, 2) for kk, (u, m) in kt.items()},
+        "roofline": roofline_entry(dom, kt[dom][0], nbytes, kflops,
+                                   traffic_for(args.workload, dom)),
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -45,6 +45,12 @@
  *  - Output buffers must not overlap inputs or each other.
  *  - Calls on one stream are ordered; concurrent calls on different streams
  *    must use different workspaces and outputs.
+ *  - Debugging switches, read from the environment at every call:
+ *    KVSEL_VALIDATE_ONLY=1 makes a call return after its checks without
+ *    enqueuing anything; KVSEL_SYNC=1 makes a call wait for its stream and
+ *    report a device error (a failed or faulting kernel) as KVSEL_ERR_DEVICE.
+ *  - The library keeps no state between calls, except the optional kernel
+ *    timing of kvsel_timing_start (off unless turned on).
  */
 #ifndef KVSEL_H
 #define KVSEL_H
@@ -259,7 +265,8 @@ typedef struct {
   int32_t buffer;      /* |U|, 0 <= buffer < window */
   int32_t keep;        /* size of I, ceil(r * (window - buffer)) for ratio r (Eq. 5) */
   int32_t gamma;       /* maximum chunk length, >= 1 (Eq. 7) */
-  int32_t alpha;       /* chunk budget: extra positions added, >= 0 (Eq. 7, fill-up) */
+  int32_t alpha;       /* chunk budget: extra positions added, >= 0, any int32 (Eq. 7,
+                          fill-up); when fewer free positions remain, all are added */
   int32_t dtype;       /* kvsel_dtype of q and k */
   float scale;         /* logit scale; 0 => 1/sqrt(head_dim) */
 } kvsel_kara_desc;
@@ -300,6 +307,16 @@ kvsel_status kvsel_kara_score(const kvsel_kara_desc* desc, const void* q_win, co
  */
 kvsel_status kvsel_kara_select(const kvsel_kara_desc* desc, const float* scores, int32_t* idx,
                                void* stream);
+
+/*
+ * kvsel_kara_keep -- |I| of Kara Eq. (5) for a retention ratio given as the
+ * fraction r = ratio_num / ratio_den: ceil(r * (window - buffer)), computed
+ * exactly in integer arithmetic (no rounding of r).  This is the `keep`
+ * field of kvsel_kara_desc.  Returns -1 when window < 2, buffer is outside
+ * [0, window), ratio_den < 1, or ratio_num is outside [0, ratio_den].
+ * Host-only; touches no device state.
+ */
+int32_t kvsel_kara_keep(int32_t window, int32_t buffer, int32_t ratio_num, int32_t ratio_den);
 
 /* Shape of a window-tier routing problem (QEvict Sections 4.1-4.3). */
 typedef struct {
@@ -418,6 +435,27 @@ kvsel_status kvsel_qevict_step(const kvsel_qevict_desc* desc, const float* token
                                float* w_acc, int8_t* tier, uint8_t* has_codes, void* k, void* v,
                                uint8_t* k_codes, uint8_t* v_codes, float* k_meta, float* v_meta,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing for benchmarks (not needed for normal use).
+ *
+ * kvsel_timing_start(prefix): from now on, every launch of a library kernel
+ *   whose name starts with `prefix` ("*" = every kernel) is bracketed by a
+ *   pair of HIP events recorded on the stream it is launched on.  NULL or ""
+ *   stops recording.  Kernel names are those a profiler shows without
+ *   template arguments (e.g. "score_pass1_32", "sel_hist", "compact_kernel").
+ * kvsel_timing_read: waits for every recorded pair, and writes per kernel
+ *   name (in first-launch order, at most max_kernels of them) the name into
+ *   names + i*name_bytes (NUL-terminated, truncated), the summed duration in
+ *   milliseconds into total_ms[i] and the launch count into launches[i];
+ *   the recorded pairs are then released.  Returns the number of distinct
+ *   kernel names, -1 on bad arguments, -2 when an event could not be read.
+ * Process-wide state behind a mutex; meant for one benchmarking thread.
+ * Timing adds two event records per matching launch to the stream.
+ */
+kvsel_status kvsel_timing_start(const char* kernel_prefix);
+int32_t kvsel_timing_read(char* names, int32_t name_bytes, double* total_ms, int32_t* launches,
+                          int32_t max_kernels);
 
 #ifdef __cplusplus
 }

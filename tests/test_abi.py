@@ -255,3 +255,83 @@ def test_workspace_is_linear_in_prompt_not_window_times_prompt(kv):
         dense = Hq * W * S * 4
         assert ws <= 8 * S * 4 + 4 * 1024 * 1024, (S, ws)
         assert ws * 20 < dense
+
+
+# Kara Eq. (5): |I| = ceil(r * (|W| - |U|)), worked by hand for each row.
+KARA_KEEP = [
+    # window, buffer, (num, den), |I|
+    (512, 64, (2, 5), 180),      # 0.4 * 448 = 179.2
+    (384, 32, (2, 5), 141),      # 0.4 * 352 = 140.8
+    (256, 32, (2, 5), 90),       # 0.4 * 224 = 89.6
+    (97, 13, (2, 5), 34),        # 0.4 * 84 = 33.6
+    (512, 64, (1, 4), 112),      # exact: 448 / 4
+    (40, 10, (1, 10), 3),        # exact: 30 / 10
+    (10, 0, (3, 10), 3),         # exact: 3
+    (10, 0, (7, 10), 7),         # exact: 7
+    (9, 2, (1, 3), 3),           # 7 / 3 = 2.33
+    (8, 2, (1, 3), 2),           # exact: 6 / 3
+    (512, 64, (0, 1), 0),
+    (512, 64, (1, 1), 448),
+    (2, 1, (1, 2), 1),           # 0.5 * 1
+]
+
+
+@pytest.mark.parametrize("window,buffer,ratio,want", KARA_KEEP)
+def test_kara_keep_table(kv, window, buffer, ratio, want):
+    """The library computes Kara's |I| exactly; a ratio given as a decimal
+    number is read as the fraction it names (0.4 -> 2/5, 0.1 -> 1/10)."""
+    assert kv.lib().kvsel_kara_keep(window, buffer, *ratio) == want
+    assert kv.kara_keep(window, buffer, ratio) == want
+    assert kv.kara_keep(window, buffer, ratio[0] / ratio[1]) == want
+
+
+def test_kara_keep_rejects(kv):
+    L = kv.lib()
+    for args in ((1, 0, 1, 2), (10, 10, 1, 2), (10, -1, 1, 2), (10, 0, 1, 0), (10, 0, -1, 2),
+                 (10, 0, 3, 2)):
+        assert L.kvsel_kara_keep(*args) == -1, args
+    with pytest.raises(ValueError):
+        kv.kara_keep(10, 0, 1.5)
+
+
+def test_validate_only_mode(kv, monkeypatch):
+    """KVSEL_VALIDATE_ONLY=1: a call whose arguments pass every check returns
+    OK without enqueuing anything (fake pointers are never touched), and a
+    bad call still fails.  Used here to show that a Kara chunk budget of
+    INT32_MAX passes validation (keep + alpha is formed in 64 bits)."""
+    L = kv.lib()
+    monkeypatch.setenv("KVSEL_VALIDATE_ONLY", "1")
+    d = _desc(kv)
+    need = L.kvsel_score_workspace(ctypes.byref(d))
+    assert L.kvsel_score(ctypes.byref(d), FAKE, FAKE, None, FAKE, 7, FAKE, need, None) == kv.OK
+    assert L.kvsel_score(ctypes.byref(d), FAKE, FAKE, None, FAKE, 6, FAKE, need, None) \
+        == kv.ERR_ARG
+    assert L.kvsel_compact(ctypes.byref(d), FAKE, FAKE, FAKE, 100, FAKE, FAKE, None) == kv.OK
+    kd = kv.KaraDesc(2, 32, 8, 128, 512, 64, 180, 8, 2 ** 31 - 1, kv.BF16, 0.0)
+    assert L.kvsel_kara_select(ctypes.byref(kd), FAKE, FAKE, None) == kv.OK
+    monkeypatch.setenv("KVSEL_VALIDATE_ONLY", "0")
+    assert L.kvsel_kara_select(ctypes.byref(kd), None, FAKE, None) == kv.ERR_ARG
+
+
+def test_timing_idle(kv):
+    """With nothing recorded the timing read returns no kernels; bad
+    arguments are refused."""
+    kv.timing_start(None)
+    assert kv.timing_read() == {}
+    L = kv.lib()
+    assert L.kvsel_timing_read(None, 64, None, None, 4) == -1
+    assert L.kvsel_timing_read(None, 0, None, None, 0) == 0
+
+
+def test_linear_budget_schedule():
+    """The layer-major driver's linear schedule from 4096 to 512 over 32
+    layers: B_l = 4096 - floor(3584 * l / 31), written out at a few layers."""
+    from attention_score_eviction_amd.driver import linear_budgets
+    b = linear_budgets(32, 4096, 512)
+    assert b[0] == 4096 and b[31] == 512
+    assert b[1] == 4096 - 115       # 3584 / 31 = 115.6
+    assert b[15] == 2362            # 3584 * 15 / 31 = 1734.2
+    assert b[16] == 4096 - 1849     # 3584 * 16 / 31 = 1849.8
+    assert all(x >= y for x, y in zip(b, b[1:]))
+    assert sum(b) == 73743
+    assert linear_budgets(1, 100, 50) == [100]

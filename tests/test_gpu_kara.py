@@ -93,6 +93,49 @@ def _margins_ok(a, keep, gamma, alpha, rel=1e-5):
     return gap_ok(rest, need)
 
 
+def test_kara_select_alpha_int32_max():
+    """A chunk budget of INT32_MAX (every free position is added by the
+    fill-up): exact with the oracle, n_out = n."""
+    kvsel = _kvsel()
+    rng = np.random.default_rng(310)
+    Bt, Hkv, n, U, keep, gamma, alpha = 2, 3, 200, 16, 50, 8, 2 ** 31 - 1
+    A = rng.random((Bt, Hkv, n)).astype(np.float32)
+    kd = kvsel.KaraDesc(Bt, Hkv, Hkv, 128, n + U, U, keep, gamma, alpha, kvsel.BF16, 0.0)
+    got = kvsel.kara_select(torch.from_numpy(A).cuda(), kd).cpu().numpy()
+    want = oracle.kara_select(A.astype(np.float64), keep, gamma, alpha, U)
+    assert got.shape == (Bt, Hkv, n + U)
+    np.testing.assert_array_equal(got, want)
+
+
+def _token2chunk_structure(row, A32, n, keep, gamma, alpha):
+    """Validity of a Token2Chunk output against the scores it was computed
+    from: the keep best positions are present, every other kept position is
+    either inside a qualifying chunk (strictly between consecutive members
+    of I, at most gamma apart) or a fill-up pick, and exactly min(alpha,
+    n - keep) positions were added."""
+    comp = row[row < n]
+    order = np.lexsort((np.arange(n), -A32.astype(np.float64)))
+    I = np.sort(order[:keep])
+    assert set(I.tolist()) <= set(comp.tolist())
+    added = sorted(set(comp.tolist()) - set(I.tolist()))
+    assert len(added) == min(alpha, n - keep)
+    in_chunk = set()
+    for k in range(len(I) - 1):
+        if I[k + 1] - I[k] <= gamma:
+            in_chunk.update(range(I[k] + 1, I[k + 1]))
+    fill = [j for j in added if j not in in_chunk]
+    # fill-up picks are the best of what remained: none of them is beaten by a
+    # position left out that is not inside a chunk interior
+    left = [j for j in range(n) if j not in set(comp.tolist()) and j not in in_chunk]
+    if fill and left:
+        key = lambda j: (-float(A32[j]), j)  # noqa: E731
+        assert max(key(j) for j in fill) < min(key(j) for j in left)
+
+
+# Kara Eq. (5) for r = 0.4, worked by hand: ceil(0.4 * (|W| - |U|)).
+KARA_KEEP_04 = {(512, 64): 180, (384, 32): 141, (256, 32): 90, (97, 13): 34}
+
+
 @pytest.mark.parametrize("shape,dtype,seed", [
     # (Bt, Hq, Hkv, window, buffer, D), as Qwen3-14B and R1-Llama-8B decode windows
     ((4, 40, 8, 512, 64, 128), "bf16", 1),
@@ -101,6 +144,10 @@ def _margins_ok(a, keep, gamma, alpha, rel=1e-5):
     ((1, 4, 2, 97, 13, 64), "f32", 4),
 ])
 def test_kara_window_end_to_end(shape, dtype, seed):
+    """Scores within 1e-3 of the oracle.  Every row is exactly Token2Chunk
+    of the GPU's own scores (the oracle replayed on them) and structurally
+    valid; rows whose oracle cuts are not near ties equal the oracle's
+    selection from its own scores."""
     kvsel = _kvsel()
     Bt, Hq, Hkv, Wn, U, D = shape
     x = synth.decode_window(seed, Bt, Hq, Hkv, Wn, D, dtype)
@@ -113,14 +160,18 @@ def test_kara_window_end_to_end(shape, dtype, seed):
     A_ref = oracle.kara_scores(synth.to_f64(x["q"], dtype), synth.to_f64(x["k"], dtype)[:, :, :n])
     assert_scores_close(out["A"].cpu().numpy(), A_ref, what="Kara importance")
     keep = out["desc"].keep
-    assert keep == int(np.ceil(ratio * n - 1e-9))
+    assert keep == KARA_KEEP_04[(Wn, U)]
     want = oracle.kara_select(A_ref, keep, gamma, alpha, U)
     got = out["idx"].cpu().numpy()
+    A_gpu = out["A"].cpu().numpy()
     assert got.shape == want.shape
+    np.testing.assert_array_equal(got, oracle.kara_select(A_gpu.astype(np.float64), keep, gamma,
+                                                          alpha, U))
     exact_rows = 0
     for b in range(Bt):
         for h in range(Hkv):
             row = got[b, h]
+            _token2chunk_structure(row, A_gpu[b, h], n, keep, gamma, alpha)
             assert (np.diff(row) > 0).all() and row[-U:].tolist() == list(range(n, Wn)) if U \
                 else (np.diff(row) > 0).all()
             top = np.sort(A_ref[b, h])[::-1]
@@ -148,8 +199,12 @@ def test_kara_bench_config_sampled_rows():
     torch.cuda.synchronize()
     n = Wn - U
     keep = out["desc"].keep
+    assert keep == KARA_KEEP_04[(Wn, U)]
     A = out["A"].cpu().numpy()
     got = out["idx"].cpu().numpy()
+    # every row is exactly Token2Chunk of the GPU's own scores
+    np.testing.assert_array_equal(got, oracle.kara_select(A.astype(np.float64), keep, gamma,
+                                                          alpha, U))
     exact = 0
     for b in (0, 31, 63):
         A_ref = oracle.kara_scores(synth.to_f64(x["q"][b:b + 1], "bf16"),

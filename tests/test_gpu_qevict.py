@@ -76,6 +76,57 @@ def test_qevict_steps_exact(case):
         assert np.any(st_o["tier"][..., :nW] == 2) and np.any(st_o["has_codes"])
 
 
+def test_qevict_growing_cache_exact():
+    """Routing every Omega = 8 decode tokens on a growing cache (QEvict §4.2):
+    seq_len grows by 8 per step at a fixed capacity, so the routed region
+    gains a window each time 64 more tokens have left the protected recent
+    region; the new window joins the ranking with the score of its own
+    tokens.  Tiers, flags, accumulated scores, codes, metadata and cache rows
+    stay bit-exact with the oracle at every step."""
+    Bt, H, D, n_sink, n_recent, bits, omega = 2, 3, 128, 5, 64, 2, 8
+    nW0, tail0, steps = 12, 40, 20
+    S0 = n_sink + 64 * nW0 + n_recent + tail0
+    S_end = S0 + omega * (steps - 1)
+    cap = S_end + 16
+    M = oracle.qevict_windows(S_end, n_sink, n_recent, 64) + 1
+    n_full, n_quant = 3, 5
+    cache = synth.qevict_cache(11, Bt, H, cap, D)
+    k_o, v_o = cache["k"].copy(), cache["v"].copy()
+    k_g, v_g = _bf16_dev(cache["k"]), _bf16_dev(cache["v"])
+    st_o = oracle.qevict_init(Bt, H, M, D, 64, bits)
+    st_g = None
+    grew = 0
+    print(f"qevict growing cache S {S0} -> {S_end}, capacity {cap}", flush=True)
+    for step in range(steps):
+        S = S0 + omega * step
+        nW = oracle.qevict_windows(S, n_sink, n_recent, 64)
+        if step and nW > oracle.qevict_windows(S - omega, n_sink, n_recent, 64):
+            grew += 1
+        qd = kvsel.qevict_desc(k_g, seq_len=S, max_windows=M, n_sink=n_sink, n_recent=n_recent,
+                               n_full=n_full, n_quant=n_quant, bits=bits)
+        if st_g is None:
+            st_g = kvsel.qevict_state(qd, k_g.device)
+        sc = synth.qevict_token_scores(12, step, Bt, H, S)
+        st_o = oracle.qevict_step(st_o, sc, k_o, v_o, seq_len=S, n_sink=n_sink,
+                                  n_recent=n_recent, win=64, n_full=n_full, n_quant=n_quant,
+                                  bits=bits)
+        kvsel.qevict_step(qd, _dev(sc), st_g, k_g, v_g)
+        torch.cuda.synchronize()
+        assert np.array_equal(st_g["tier"].cpu().numpy(), st_o["tier"]), f"step {step}: tiers"
+        assert np.array_equal(st_g["has_codes"].cpu().numpy(), st_o["has_codes"]), step
+        assert np.array_equal(st_g["w_acc"].cpu().numpy().astype(np.float64), st_o["w_acc"]), step
+        for name in ("k_codes", "v_codes"):
+            assert np.array_equal(st_g[name].cpu().numpy(), st_o[name]), (step, name)
+        for name in ("k_meta", "v_meta"):
+            assert np.array_equal(st_g[name].cpu().numpy().view(np.uint32),
+                                  st_o[name].view(np.uint32)), (step, name)
+        assert np.array_equal(_bits(k_g), k_o) and np.array_equal(_bits(v_g), v_o), step
+        # slots past the routed windows are untouched (zero state)
+        assert not st_o["w_acc"][..., nW:].any() and not st_o["tier"][..., nW:].any()
+    assert grew == 3
+    assert np.any(st_o["tier"] == 2) and np.any(st_o["has_codes"])
+
+
 def test_qevict_real_scores_band():
     """One step with real-valued scores: tiers equal except for windows whose
     oracle score lies within 1e-5 (relative) of a boundary window's score;
