@@ -137,6 +137,8 @@ def lib() -> ctypes.CDLL:
     L.kvsel_timing_start.restype = ctypes.c_int
     L.kvsel_timing_read.argtypes = [P, I32, P, P, I32]
     L.kvsel_timing_read.restype = I32
+    L.kvsel_score_static.argtypes = [DP, P, P, P, P, I32, P]
+    L.kvsel_score_static.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -506,7 +508,22 @@ EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_se
            "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat",
            "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select",
            "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact",
-           "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read")
+           "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read", "kvsel_score_static")
+
+STATIC_SCRATCH_BYTES = 32 << 20   # KVSEL_STATIC_SCRATCH_BYTES
+
+
+def score_static(q_obs: torch.Tensor, k: torch.Tensor, *, pooled: torch.Tensor,
+                 raw: Optional[torch.Tensor] = None, pool_kernel: int, n_sink: int = 0,
+                 causal: bool = True, scale: float = 0.0, stream=None):
+    """kvsel_score_static: kvsel_score into caller-provided outputs with the
+    library's static scratch; allocates nothing (usable under graph capture).
+    Calls that overlap on one GPU race on the shared scratch."""
+    d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
+    st = lib().kvsel_score_static(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(raw),
+                                  _ptr(pooled), int(pool_kernel), _stream(stream))
+    _check(st, "kvsel_score_static")
+    return pooled, raw
 
 
 def timing_start(prefix: Optional[str] = "*") -> None:

@@ -33,9 +33,9 @@
  *    Query head h reads KV head floor(h / G).
  *  - Every pointer argument is a DEVICE pointer (hipMalloc'd or equivalent)
  *    unless stated otherwise and must be 16-byte aligned.  The caller owns all
- *    buffers; the library never allocates, frees or keeps device memory.
- *    Scratch memory is passed in as `ws` with a size from the matching
- *    *_workspace() query.
+ *    buffers; the library never allocates or frees device memory.  Scratch
+ *    memory is passed in as `ws` with a size from the matching *_workspace()
+ *    query (kvsel_score_static alone uses a static array inside the library).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously; no call synchronises the host or reads device memory back.
  *  - Every precondition is checked before anything is enqueued.  A failed check
@@ -50,7 +50,8 @@
  *    enqueuing anything; KVSEL_SYNC=1 makes a call wait for its stream and
  *    report a device error (a failed or faulting kernel) as KVSEL_ERR_DEVICE.
  *  - The library keeps no state between calls, except the optional kernel
- *    timing of kvsel_timing_start (off unless turned on).
+ *    timing of kvsel_timing_start (off unless turned on) and the static
+ *    scratch array of kvsel_score_static.
  */
 #ifndef KVSEL_H
 #define KVSEL_H
@@ -435,6 +436,25 @@ kvsel_status kvsel_qevict_step(const kvsel_qevict_desc* desc, const float* token
                                float* w_acc, int8_t* tier, uint8_t* has_codes, void* k, void* v,
                                uint8_t* k_codes, uint8_t* v_codes, float* k_meta, float* v_meta,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_score_static -- kvsel_score for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation, outputs and errors, with the
+ * scratch taken from a static device array of KVSEL_STATIC_SCRATCH_BYTES
+ * inside the library instead of a caller workspace.  No allocation of any
+ * kind happens in the call.  Each GPU holds its own copy of the array from
+ * the first call on it until the process ends; every call on one GPU shares
+ * it, so calls that overlap on one GPU (different streams or threads) race,
+ * while calls on one stream are ordered.  A problem whose
+ * kvsel_score_workspace(desc) exceeds KVSEL_STATIC_SCRATCH_BYTES returns
+ * KVSEL_ERR_WORKSPACE before any device call; KVSEL_ERR_DEVICE if the
+ * array's device address cannot be obtained.
+ */
+#define KVSEL_STATIC_SCRATCH_BYTES (32u << 20)
+kvsel_status kvsel_score_static(const kvsel_desc* desc, const void* q_obs, const void* k,
+                                float* raw_scores, float* pooled, int32_t pool_kernel,
+                                void* stream);
 
 /*
  * Kernel timing for benchmarks (not needed for normal use).
