@@ -137,6 +137,10 @@ def lib() -> ctypes.CDLL:
     L.kvsel_timing_start.restype = ctypes.c_int
     L.kvsel_timing_read.argtypes = [P, I32, P, P, I32]
     L.kvsel_timing_read.restype = I32
+    L.kvsel_layer_end_workspace.argtypes = [DP, I32]
+    L.kvsel_layer_end_workspace.restype = SZ
+    L.kvsel_layer_end.argtypes = [DP, P, P, P, I32, I32, P, P, P, P, P, P, SZ, P]
+    L.kvsel_layer_end.restype = ctypes.c_int
     L.kvsel_score_static.argtypes = [DP, P, P, P, P, I32, P]
     L.kvsel_score_static.restype = ctypes.c_int
     _lib = L
@@ -354,17 +358,52 @@ def compact_flat(k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor,
         return k_out, v_out
 
 
+def layer_end_workspace_bytes(desc: Desc, budget: int) -> int:
+    return int(lib().kvsel_layer_end_workspace(ctypes.byref(desc), int(budget)))
+
+
+def layer_end(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *, budget: int,
+              pool_kernel: int, n_sink: int = 0, causal: bool = True, scale: float = 0.0,
+              raw: Optional[torch.Tensor] = None, pooled: Optional[torch.Tensor] = None,
+              idx: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+              v_out: Optional[torch.Tensor] = None, want_scores: bool = True,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_layer_end: TideKV's LayerEndCompress in one call.  Returns
+    (idx, k_hat, v_hat, raw, pooled); raw and pooled are None when
+    want_scores is False and none were given (then kept in the workspace)."""
+    with _on(stream):
+        d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
+        Bt, Hkv, S, D = k.shape
+        n_keep = budget + n_sink + q_obs.shape[2]
+        dev = k.device
+        if want_scores:
+            raw = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev) if raw is None \
+                else raw
+            pooled = torch.empty_like(raw) if pooled is None else pooled
+        if idx is None:
+            idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
+        if k_out is None:
+            k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=dev)
+        if v is not None and v_out is None:
+            v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(layer_end_workspace_bytes(d, budget), 1),
+                                    dtype=torch.uint8, device=dev)
+        st = lib().kvsel_layer_end(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(v), int(budget),
+                                   int(pool_kernel), _ptr(raw), _ptr(pooled), _ptr(idx),
+                                   _ptr(k_out), _ptr(v_out), _ptr(workspace), workspace.numel(),
+                                   _stream(stream))
+        _check(st, "kvsel_layer_end")
+        return idx, k_out, v_out, raw, pooled
+
+
 def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
                        pool_kernel: int, n_sink: int = 0, causal: bool = True,
                        scale: float = 0.0, stream=None) -> dict:
-    """score -> select + compact (kvsel_select_compact) on one stream: TideKV's
-    layer-end step."""
-    W = q_obs.shape[2]
-    pooled, raw = score(q_obs, k, pool_kernel=pool_kernel, n_sink=n_sink, causal=causal,
-                        scale=scale, stream=stream)
-    idx, k_hat, v_hat = select_compact(pooled, k, v, budget, obs_window=W,
-                                       n_q_heads=q_obs.shape[1], n_sink=n_sink, causal=causal,
-                                       stream=stream)
+    """TideKV's layer-end step (kvsel_layer_end) on one stream, as a dict."""
+    idx, k_hat, v_hat, raw, pooled = layer_end(q_obs, k, v, budget=budget,
+                                               pool_kernel=pool_kernel, n_sink=n_sink,
+                                               causal=causal, scale=scale, stream=stream)
     return {"s": raw, "p": pooled, "idx": idx, "k_hat": k_hat, "v_hat": v_hat}
 
 
@@ -508,7 +547,8 @@ EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_se
            "kvsel_select_adaptive_workspace", "kvsel_select_adaptive", "kvsel_compact_flat",
            "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select",
            "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact",
-           "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read", "kvsel_score_static")
+           "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read", "kvsel_score_static",
+           "kvsel_layer_end_workspace", "kvsel_layer_end")
 
 STATIC_SCRATCH_BYTES = 32 << 20   # KVSEL_STATIC_SCRATCH_BYTES
 

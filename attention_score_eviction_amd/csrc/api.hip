@@ -214,6 +214,72 @@ kvsel_status kvsel_select_compact(const kvsel_desc* desc, const float* pooled, i
                                  (hipStream_t)stream); });
 }
 
+// Workspace of kvsel_layer_end: the score scratch, then the select scratch,
+// then the pooled scores when the caller does not take them.
+struct LayerEndWs {
+  ScorePlan sp;
+  SelectPlan lp;
+  size_t off_sel, off_pooled, total;
+};
+
+LayerEndWs layer_end_ws(const kvsel_desc& d, int budget, bool own_pooled) {
+  LayerEndWs w;
+  plan_score(d, &w.sp);
+  plan_select(d, budget, 1, &w.lp);
+  w.off_sel = align256(w.sp.total);
+  w.off_pooled = align256(w.off_sel + w.lp.total);
+  w.total = w.off_pooled +
+            (own_pooled ? align256((size_t)d.batch * d.n_kv_heads * d.seq_len * sizeof(float)) : 0);
+  return w;
+}
+
+size_t kvsel_layer_end_workspace(const kvsel_desc* desc, int32_t budget) {
+  if (check_desc(desc) != KVSEL_OK) return 0;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink) return 0;
+  return layer_end_ws(*desc, budget, true).total;
+}
+
+kvsel_status kvsel_layer_end(const kvsel_desc* desc, const void* q_obs, const void* k,
+                             const void* v, int32_t budget, int32_t pool_kernel,
+                             float* raw_scores, float* pooled, int32_t* idx, void* k_out,
+                             void* v_out, void* ws, size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink)
+    return KVSEL_ERR_BUDGET;
+  if (!q_obs || !k || !idx || !k_out) return KVSEL_ERR_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVSEL_ERR_ARG;
+  const void* ptrs[] = {q_obs, k, v, raw_scores, pooled, idx, k_out, v_out, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return KVSEL_ERR_ARG;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 1 + 2 * (1 << 20))
+    return KVSEL_ERR_ARG;
+  const LayerEndWs w = layer_end_ws(*desc, budget, pooled == nullptr);
+  if (ws_bytes < w.total || !ws) return KVSEL_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  float* pool_buf = pooled ? pooled : (float*)(wsc + w.off_pooled);
+  return enqueue(stream, [&] {
+    const hipStream_t s = (hipStream_t)stream;
+    char* sel_ws = wsc + w.off_sel;
+    if (layer_end_fusable(*desc, w.lp, budget, pool_kernel)) {
+      // max filter, select and gather fused behind the two score passes
+      float* raw = raw_scores ? raw_scores : (float*)(wsc + w.sp.off_raw);
+      size_t words = 0;
+      uint32_t* h1 = select_hists(w.lp, sel_ws, &words);
+      kvsel_status r = launch_score(*desc, w.sp, q_obs, k, raw, nullptr, pool_kernel, wsc, s,
+                                    desc->seq_len, h1, words);
+      if (r != KVSEL_OK) return r;
+      return launch_layer_end_select(*desc, w.lp, raw, pool_buf, pool_kernel, budget, idx, k, v,
+                                     k_out, v_out, sel_ws, s);
+    }
+    kvsel_status r = launch_score(*desc, w.sp, q_obs, k, raw_scores, pool_buf, pool_kernel, wsc,
+                                  s, desc->seq_len);
+    if (r != KVSEL_OK) return r;
+    return launch_select_compact(*desc, w.lp, pool_buf, budget, idx, k, v, k_out, v_out, sel_ws,
+                                 s);
+  });
+}
+
 size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget) {
   if (check_adaptive(desc, total_budget) != KVSEL_OK) return 0;
   SelectPlan p;

@@ -1,6 +1,7 @@
 // Internal declarations shared by the kvsel HIP sources (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -19,18 +20,23 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing (kvsel_timing_start / kvsel_timing_read).  Off by
 // default; while a name prefix is set, every launch of a kernel whose name
-// starts with it is bracketed by two HIP events recorded on its stream.
+// starts with it goes through hipExtLaunchKernelGGL with a start and a stop
+// event, which the dispatch itself stamps with the kernel's begin and end.
 // ---------------------------------------------------------------------------
 bool timing_wanted(const char* kernel_name);
-hipEvent_t timing_open(hipStream_t stream);
-void timing_close(const char* kernel_name, hipEvent_t start, hipStream_t stream);
+bool timing_events(hipEvent_t* start, hipEvent_t* stop);
+void timing_record(const char* kernel_name, hipEvent_t start, hipEvent_t stop);
 
-#define KVSEL_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                        \
-  do {                                                                                   \
-    const bool kvsel_timed_ = ::kvsel::timing_wanted(NAME);                              \
-    hipEvent_t kvsel_t0_ = kvsel_timed_ ? ::kvsel::timing_open(STREAM) : nullptr;        \
-    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                 \
-    if (kvsel_timed_) ::kvsel::timing_close(NAME, kvsel_t0_, STREAM);                    \
+#define KVSEL_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                         \
+  do {                                                                                    \
+    hipEvent_t kvsel_e0_ = nullptr, kvsel_e1_ = nullptr;                                  \
+    if (::kvsel::timing_wanted(NAME) && ::kvsel::timing_events(&kvsel_e0_, &kvsel_e1_)) { \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, kvsel_e0_, kvsel_e1_, 0,  \
+                            __VA_ARGS__);                                                 \
+      ::kvsel::timing_record(NAME, kvsel_e0_, kvsel_e1_);                                 \
+    } else {                                                                              \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                \
+    }                                                                                     \
   } while (0)
 
 // Sort key for (value desc, index asc) as one ascending 64-bit integer: the
@@ -98,14 +104,19 @@ struct ScoreArgs {
   int Hq, Hkv, G, W, S, GW, GWr, qcap, chunk, nchunk, causal;
   int kstride;         // key rows between consecutive KV heads in k (>= S)
   float c;             // scale * log2(e)
+  uint32_t* zero;      // cleared by the combine kernel (may be null)
+  long zero_words;
 };
 
 // kstride: key rows per KV head in k (the head's first seq_len rows are
 // scored); pooled may be null (no max-pool launched) for callers that only
 // need the raw scores.
+// zero / zero_words: a buffer the score launch clears on the way (inside
+// the row-statistics combine), for a select that follows on the stream.
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
-                          hipStream_t stream, int kstride);
+                          hipStream_t stream, int kstride, uint32_t* zero = nullptr,
+                          size_t zero_words = 0);
 // Selection groups: hg consecutive KV heads of a sequence share one budget
 // (hg = 1: per-head budget; hg = n_kv_heads: head-adaptive budget).
 constexpr int kMaxGroupSlices = 2048;
@@ -126,6 +137,15 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
 kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
                                    int budget, int32_t* idx, const void* k, const void* v,
                                    void* k_out, void* v_out, char* ws, hipStream_t stream);
+// The fused select-and-gather of kvsel_layer_end (long per-head rows): from
+// the raw scores, with the digit histograms select_hists zeroed earlier on
+// the stream.
+bool layer_end_fusable(const kvsel_desc& d, const SelectPlan& p, int budget, int pool_kernel);
+uint32_t* select_hists(const SelectPlan& p, char* ws, size_t* words);
+kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, const float* raw,
+                                     float* pooled, int pool_kernel, int budget, int32_t* idx,
+                                     const void* k, const void* v, void* k_out, void* v_out,
+                                     char* ws, hipStream_t stream);
 kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
                             const int32_t* idx, int n_keep, void* k_out, void* v_out,
                             hipStream_t stream);

@@ -626,9 +626,12 @@ __global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) score_combine(const float2* __restrict__ part,
                                                      float* __restrict__ lse, int nheads,
-                                                     int nchunk, int GW, int GWr, int tpr_log2) {
+                                                     int nchunk, int GW, int GWr, int tpr_log2,
+                                                     uint32_t* __restrict__ zero,
+                                                     long zero_words) {
   const int tpr = 1 << tpr_log2;
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  for (long i = gid; i < zero_words; i += (long)gridDim.x * 256) zero[i] = 0u;
   const long row_id = gid >> tpr_log2;
   const int sub = (int)(gid & (tpr - 1));
   const bool valid = row_id < (long)nheads * GW;
@@ -747,7 +750,8 @@ void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const S
   while ((4 << tl) < p.nchunk && tl < 6) ++tl;
   const long lanes = ((long)p.nheads * p.GW) << tl;
   KVSEL_LAUNCH("score_combine", score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
-                     args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl);
+                     args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl, args.zero,
+               args.zero_words);
   KVSEL_LAUNCH("score_pass2", (score_pass2<T, D, NQT, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 
@@ -758,7 +762,8 @@ void launch_passes32(const ScoreArgs& args, dim3 grid, hipStream_t stream, const
   while ((4 << tl) < p.nchunk && tl < 6) ++tl;
   const long lanes = ((long)p.nheads * p.GW) << tl;
   KVSEL_LAUNCH("score_combine", score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
-                     args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl);
+                     args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl, args.zero,
+               args.zero_words);
   KVSEL_LAUNCH("score_pass2_32", (score_pass2_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
 }
 
@@ -875,8 +880,10 @@ static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes) {
 
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
-                          hipStream_t stream, int kstride) {
+                          hipStream_t stream, int kstride, uint32_t* zero, size_t zero_words) {
   ScoreArgs a;
+  a.zero = zero;
+  a.zero_words = (long)zero_words;
   a.q = q;
   a.k = k;
   a.part = (float2*)(ws + p.off_part);

@@ -811,6 +811,108 @@ __global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
   }
 }
 
+// First-digit histogram fused with the max filter: each slice stages its
+// raw scores with a halo of h positions on either side (clipped to the
+// candidate range [lo, hi)), writes the pooled scores of its positions, and
+// adds the first digits of its candidates to the group's global histogram
+// (zeroed earlier on the stream).  The first and last slices of a row also
+// write the zeros of the non-candidate positions [0, lo) and [hi, S).
+constexpr int kMaxPoolHalo = 64;
+
+// Histogram add of one element per lane, where lanes hold consecutive
+// positions: a run of equal bins over consecutive lanes costs one atomic by
+// its first lane (max-pooling repeats a local maximum over its neighbours).
+// bin = ~0u marks an element that is not counted.
+__device__ __forceinline__ void hist_add_lane_runs(uint32_t* hist, uint32_t bin) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(((lane + 63) & 63) << 2, (int)bin);
+  const bool start = lane == 0 || prev != bin;
+  const unsigned long long starts = __ballot(start);
+  if (!start || bin == ~0u) return;
+  const unsigned long long above = lane == 63 ? 0ull : starts & (~0ull << (lane + 1));
+  const int next = above ? __ffsll((long long)above) - 1 : 64;
+  atomicAdd(&hist[bin], (uint32_t)(next - lane));
+}
+
+constexpr int kPoolThreads = 1024;
+
+__global__ void __launch_bounds__(kPoolThreads) sel_pool_hist(SelArgs a, const float* raw,
+                                                              float* pooled, int ph) {
+  constexpr int NT = kPoolThreads, PER = kSlice / kPoolThreads;
+  __shared__ uint32_t hist[kD1Bins];
+  __shared__ float sv[kSlice + 2 * kMaxPoolHalo];
+  const int grp = blockIdx.y, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, blockIdx.x);
+  for (int i = tid; i < kD1Bins; i += NT) hist[i] = 0u;
+  const size_t rbase = (size_t)at.row * a.S;
+  const int base = slice_base(a, at.row) + at.sl * kSlice;
+  for (int i = tid; i < kSlice + 2 * ph; i += NT) {
+    const int pos = base - ph + i;
+    sv[i] = (pos >= a.lo && pos < a.hi) ? raw[rbase + pos] : -INFINITY;
+  }
+  __syncthreads();
+  // Position base + j*NT + tid per step j: consecutive lanes read
+  // consecutive LDS words and write consecutive pooled scores.
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int off = j * NT + tid;
+    const int pos = base + off;
+    const bool ok = pos >= a.lo && pos < a.hi;
+    uint32_t bin = ~0u;
+    if (ok) {
+      const float* w = sv + off;   // positions pos - ph .. pos + ph
+      float m = w[0];
+      if (ph <= 3) {
+#pragma unroll
+        for (int t = 1; t <= 6; ++t)
+          if (t <= 2 * ph) m = fmaxf(m, w[t]);
+      } else {
+        for (int t = 1; t <= 2 * ph; ++t) m = fmaxf(m, w[t]);
+      }
+      pooled[rbase + pos] = m;
+      bin = (__float_as_uint(m) >> kD1Shift) & (uint32_t)(kD1Bins - 1);
+    }
+    hist_add_lane_runs(hist, bin);
+  }
+  if (at.sl == 0)
+    for (int pos = tid; pos < a.lo; pos += NT) pooled[rbase + pos] = 0.f;
+  if (at.sl == a.ns - 1)
+    for (int pos = a.hi + tid; pos < a.S; pos += NT) pooled[rbase + pos] = 0.f;
+  __syncthreads();
+  uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
+  for (int i = tid; i < kD1Bins; i += NT)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+// Arguments of the sliced kernels for one launch sequence.
+SelArgs sel_args(const kvsel_desc& d, const SelectPlan& p, const float* pooled, int budget,
+                 int32_t* idx, int32_t* head_off, char* ws) {
+  const int seg = d.n_sink + d.obs_window;
+  SelArgs a;
+  a.pooled = pooled;
+  a.idx = idx;
+  a.head_off = head_off;
+  a.hist1 = (uint32_t*)(ws + p.off_hist);
+  a.hist2 = a.hist1 + (size_t)p.groups * kD1Bins;
+  a.gtc = (uint32_t*)(ws + p.off_gtc);
+  a.candc = (uint32_t*)(ws + p.off_candc);
+  a.offs = (uint32_t*)(ws + p.off_offs);
+  a.params = (uint32_t*)(ws + p.off_params);
+  a.cval = (uint32_t*)(ws + p.off_cval);
+  a.cidx = (int32_t*)(ws + p.off_cidx);
+  a.S = d.seq_len;
+  a.lo = d.n_sink;
+  a.hi = d.seq_len - d.obs_window;
+  a.budget = budget;
+  a.n_sink = d.n_sink;
+  a.W = d.obs_window;
+  a.ns = p.ns;
+  a.hg = p.hg;
+  a.nst = p.ns * p.hg;
+  a.n_keep = p.hg * seg + budget;
+  return a;
+}
+
 }  // namespace
 
 bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p) {
@@ -881,28 +983,7 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
 #undef KVSEL_SELECT_1WG
     return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   }
-  SelArgs a;
-  a.pooled = pooled;
-  a.idx = idx;
-  a.head_off = head_off;
-  a.hist1 = (uint32_t*)(ws + p.off_hist);
-  a.hist2 = a.hist1 + (size_t)groups * kD1Bins;
-  a.gtc = (uint32_t*)(ws + p.off_gtc);
-  a.candc = (uint32_t*)(ws + p.off_candc);
-  a.offs = (uint32_t*)(ws + p.off_offs);
-  a.params = (uint32_t*)(ws + p.off_params);
-  a.cval = (uint32_t*)(ws + p.off_cval);
-  a.cidx = (int32_t*)(ws + p.off_cidx);
-  a.S = d.seq_len;
-  a.lo = lo;
-  a.hi = hi;
-  a.budget = budget;
-  a.n_sink = d.n_sink;
-  a.W = d.obs_window;
-  a.n_keep = n_keep;
-  a.ns = p.ns;
-  a.hg = hg;
-  a.nst = p.ns * hg;
+  SelArgs a = sel_args(d, p, pooled, budget, idx, head_off, ws);
   const dim3 sg(a.nst, groups);
   KVSEL_LAUNCH("sel_init", sel_init, dim3(groups), dim3(256), 0, stream, a);
   KVSEL_LAUNCH("sel_hist", sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
@@ -912,6 +993,7 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   KVSEL_LAUNCH("sel_emit", sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
+
 
 kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
                                    int budget, int32_t* idx, const void* k, const void* v,
@@ -947,6 +1029,36 @@ kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, con
   else KVSEL_SELECT_GATHER(512, 2);
 #undef KVSEL_SELECT_GATHER
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+uint32_t* select_hists(const SelectPlan& p, char* ws, size_t* words) {
+  *words = (size_t)p.groups * (kD1Bins + kD2Bins);
+  return (uint32_t*)(ws + p.off_hist);
+}
+
+bool layer_end_fusable(const kvsel_desc& d, const SelectPlan& p, int budget, int pool_kernel) {
+  return p.multi && p.hg == 1 && budget > 0 && (pool_kernel - 1) / 2 <= kMaxPoolHalo &&
+         d.n_sink + d.obs_window + budget <= d.seq_len;
+}
+
+// The gather runs as its own evenly spread kernel after the emit: copying
+// each slice's picks inside the emit left the slices that hold many picks
+// (clustered scores) far behind the rest (15.8 us for emit + copy at 128K
+// against 4.6 + 7.0 us for the two kernels).
+kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, const float* raw,
+                                     float* pooled, int pool_kernel, int budget, int32_t* idx,
+                                     const void* k, const void* v, void* k_out, void* v_out,
+                                     char* ws, hipStream_t stream) {
+  SelArgs a = sel_args(d, p, pooled, budget, idx, nullptr, ws);
+  const dim3 sg(a.nst, p.groups);
+  KVSEL_LAUNCH("sel_pool_hist", sel_pool_hist, sg, dim3(kPoolThreads), 0, stream, a, raw, pooled,
+               (pool_kernel - 1) / 2);
+  KVSEL_LAUNCH("sel_hist2", sel_hist2, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_cand", sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_resolve", sel_resolve, dim3(p.groups), dim3(kSelThreads), 0, stream, a);
+  KVSEL_LAUNCH("sel_emit", sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return KVSEL_ERR_DEVICE;
+  return launch_compact(d, k, v, idx, a.n_keep, k_out, v_out, stream);
 }
 
 }  // namespace kvsel

@@ -1,8 +1,8 @@
 // Optional per-kernel timing for benchmarks (kvsel_timing_start /
 // kvsel_timing_read).  While a kernel-name prefix is set, every launch of a
-// matching kernel is bracketed by a pair of HIP events on the stream it is
-// launched on; reading waits for the pairs and sums their durations per
-// kernel name.  This is the only process-wide mutable state of the library
+// matching kernel carries a start and a stop event that its dispatch stamps
+// with the kernel's begin and end (hipExtLaunchKernelGGL); reading waits for
+// the pairs and sums their durations per kernel name.  This is the only process-wide mutable state of the library
 // and is off unless a caller turns it on.
 #include <string.h>
 
@@ -35,30 +35,20 @@ bool timing_wanted(const char* kernel_name) {
   return strncmp(kernel_name, g_prefix.c_str(), g_prefix.size()) == 0;
 }
 
-hipEvent_t timing_open(hipStream_t stream) {
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  if (hipEventRecord(e, stream) != hipSuccess) {
-    (void)hipEventDestroy(e);
-    return nullptr;
+bool timing_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (hipEventCreate(start) != hipSuccess) return false;
+  if (hipEventCreate(stop) != hipSuccess) {
+    (void)hipEventDestroy(*start);
+    *start = nullptr;
+    return false;
   }
-  return e;
+  return true;
 }
 
-void timing_close(const char* kernel_name, hipEvent_t start, hipStream_t stream) {
-  if (!start) return;
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) {
-    (void)hipEventDestroy(start);
-    return;
-  }
-  if (hipEventRecord(e, stream) != hipSuccess) {
-    (void)hipEventDestroy(start);
-    (void)hipEventDestroy(e);
-    return;
-  }
+void timing_record(const char* kernel_name, hipEvent_t start, hipEvent_t stop) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_pending.push_back({kernel_name, start, e});
+  g_pending.push_back({kernel_name, start, stop});
 }
 
 }  // namespace kvsel

@@ -7,7 +7,7 @@ the next layer starts, so only one layer's full-prompt K/V is ever resident.
 
 This driver holds that single active buffer (Q_obs, K, V of one layer) and
 the scratch of the layer-end step, fills the buffer in place for each layer,
-runs kvsel_score and kvsel_select_compact on one stream, and commits each
+runs the layer-end step (kvsel_layer_end) on one stream, and commits each
 layer's compact K/V and absolute positions to a per-layer store.  The model
 forward that would produce the K/V is not part of it: the caller supplies
 each layer's tensors.  Host orchestration only; every step of the layer-end
@@ -19,8 +19,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import Desc, _dtype_code, score, score_workspace_bytes, select_compact, \
-    select_workspace_bytes
+from . import Desc, _dtype_code, layer_end, layer_end_workspace_bytes
 
 
 @dataclass
@@ -62,9 +61,8 @@ class LayerMajorDriver:
         self.pooled = e(Bt, Hkv, S, dt=torch.float32)
         self.raw = e(Bt, Hkv, S, dt=torch.float32)
         self.desc = Desc(Bt, Hq, Hkv, D, S, W, self.n_sink, 1, _dtype_code(self.k), 0.0)
-        self.score_ws = e(max(score_workspace_bytes(self.desc), 1), dt=torch.uint8)
-        self.select_ws = e(max(select_workspace_bytes(self.desc, self.max_budget), 1),
-                           dt=torch.uint8)
+        self.ws = e(max(layer_end_workspace_bytes(self.desc, self.max_budget), 1),
+                    dt=torch.uint8)
 
     @property
     def active_bytes(self) -> int:
@@ -74,8 +72,7 @@ class LayerMajorDriver:
     @property
     def scratch_bytes(self) -> int:
         """Score vectors and workspaces of the layer-end step."""
-        return sum(t.numel() * t.element_size()
-                   for t in (self.pooled, self.raw, self.score_ws, self.select_ws))
+        return sum(t.numel() * t.element_size() for t in (self.pooled, self.raw, self.ws))
 
     @property
     def store_bytes(self) -> int:
@@ -104,14 +101,9 @@ class LayerMajorDriver:
     def layer_end(self, cache: LayerCache, stream=None) -> LayerCache:
         """LayerEndCompress of the active layer into `cache` (score ->
         max-pool -> top-budget + window -> gather), enqueued on `stream`."""
-        if select_workspace_bytes(self.desc, cache.budget) > self.select_ws.numel():
-            raise ValueError("select workspace sized for a smaller budget")
-        score(self.q, self.k, pool_kernel=self.pool_kernel, n_sink=self.n_sink,
-              pooled=self.pooled, raw=self.raw, workspace=self.score_ws, stream=stream)
-        select_compact(self.pooled, self.k, self.v, cache.budget, obs_window=self.obs_window,
-                       n_q_heads=self.n_q_heads, n_sink=self.n_sink, idx=cache.idx,
-                       k_out=cache.k_hat, v_out=cache.v_hat, workspace=self.select_ws,
-                       stream=stream)
+        layer_end(self.q, self.k, self.v, budget=cache.budget, pool_kernel=self.pool_kernel,
+                  n_sink=self.n_sink, raw=self.raw, pooled=self.pooled, idx=cache.idx,
+                  k_out=cache.k_hat, v_out=cache.v_hat, workspace=self.ws, stream=stream)
         return cache
 
     def commit(self, budget: int, stream=None) -> LayerCache:

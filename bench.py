@@ -1,9 +1,9 @@
 """Throughput of the layer-end KV selection path on one MI355X.
 
 A step is one pass of the whole path over one layer of synthetic input that
-is already resident in HBM, as the layer-major driver runs it: kvsel_score
-(two streaming passes over K, row statistics, max-pool), then
-kvsel_select_compact (exact top-B + window, K/V gather).  The metric is
+is already resident in HBM, as the layer-major driver runs it: one
+kvsel_layer_end call (two streaming passes over K, row statistics, max-pool,
+exact top-B + window, K/V gather).  The metric is
 prompt-KV tokens scored + selected + compacted per second per layer.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
@@ -62,7 +62,7 @@ WORKLOADS = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "qevict.hip",
-                  "common.h", "api.hip", "timing.hip"]
+                  "common.h"]
 
 
 def source_hash() -> str:
@@ -197,7 +197,7 @@ def kernel_work(spec: synth.LayerSpec, kernel: str, n_keep: int) -> tuple:
         return sweep, flops
     if kernel.startswith("score_pass2"):
         return sweep + H * S * 4, flops
-    if kernel == "maxpool_kernel":
+    if kernel in ("maxpool_kernel", "sel_pool_hist"):
         return 2 * H * S * 4, 0
     if kernel in ("select_kernel", "sel_emit"):
         return H * (S - W) * 4 + H * n_keep * 4, 0
@@ -265,10 +265,16 @@ class Layer:
         self.drv.load(t(x["q"]), t(x["k"]), t(x["v"]))
 
     def set_budget(self, budget):
+        torch, kvsel, d = self.torch, self.kvsel, self.drv
         self.budget = budget
         self.cache = self.drv.new_cache(budget)
+        # separate scratch for the composed calls (kvsel_score, then the
+        # select), timed alone for the per-call breakdown
+        self.score_ws = torch.empty(max(kvsel.score_workspace_bytes(d.desc), 1),
+                                    dtype=torch.uint8, device=d.k.device)
+        self.select_ws = torch.empty(max(kvsel.select_workspace_bytes(d.desc, budget), 1),
+                                     dtype=torch.uint8, device=d.k.device)
         if self.adaptive:
-            torch, kvsel, d = self.torch, self.kvsel, self.drv
             Bt, Hkv = self.spec.batch, self.spec.n_kv_heads
             n_keep = Hkv * (budget + self.spec.n_sink + self.spec.obs_window)
             dev = d.k.device
@@ -283,7 +289,7 @@ class Layer:
     def score(self, stream):
         d = self.drv
         self.kvsel.score(d.q, d.k, pool_kernel=d.pool_kernel, n_sink=d.n_sink, pooled=d.pooled,
-                         raw=d.raw, workspace=d.score_ws, stream=stream)
+                         raw=d.raw, workspace=self.score_ws, stream=stream)
 
     def select_compact(self, stream):
         d, s = self.drv, self.spec
@@ -298,12 +304,15 @@ class Layer:
         c = self.cache
         self.kvsel.select_compact(d.pooled, d.k, d.v, c.budget, obs_window=s.obs_window,
                                   n_q_heads=s.n_q_heads, n_sink=s.n_sink, idx=c.idx,
-                                  k_out=c.k_hat, v_out=c.v_hat, workspace=d.select_ws,
+                                  k_out=c.k_hat, v_out=c.v_hat, workspace=self.select_ws,
                                   stream=stream)
 
     def step(self, stream):
-        self.score(stream)
-        self.select_compact(stream)
+        if self.adaptive:
+            self.score(stream)
+            self.select_compact(stream)
+        else:
+            self.drv.layer_end(self.cache, stream=stream)
 
 
 def copy_calibration(steps: int) -> int:
@@ -494,6 +503,8 @@ def main() -> int:
     sel_name = "kvsel_select_adaptive+compact_flat" if adaptive else "kvsel_select_compact"
     us_call = {"kvsel_score": event_time_us(torch, stream, lambda: L.score(stream), reps),
                sel_name: event_time_us(torch, stream, lambda: L.select_compact(stream), reps)}
+    if not adaptive:
+        us_call["kvsel_layer_end"] = event_time_us(torch, stream, lambda: L.step(stream), reps)
     kt = kernel_times(kvsel, torch, lambda: L.step(stream), reps)
     dispatches = sum(n for _, n in kt.values())
     dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])

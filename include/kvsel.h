@@ -251,6 +251,32 @@ kvsel_status kvsel_select_compact(const kvsel_desc* desc, const float* pooled, i
                                   void* v_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_layer_end -- TideKV Algorithm 2 (LayerEndCompress) in one call:
+ * kvsel_score, then kvsel_select_compact, with exactly their results
+ * (raw and pooled scores, idx, k_out, v_out as those calls define them).
+ * For long rows the max filter, the selection and the gather run fused
+ * behind the two score passes (fewer kernel launches, the same bits).
+ *
+ *   q_obs        [Bt,Hq,W,D] dtype, device
+ *   k, v         [Bt,Hkv,S,D] dtype, device (v may be NULL together with v_out)
+ *   budget       0 <= budget <= S - W - n_sink, else KVSEL_ERR_BUDGET
+ *   pool_kernel  odd, >= 1
+ *   raw_scores   [Bt,Hkv,S] float32 out, device, may be NULL (kept in ws)
+ *   pooled       [Bt,Hkv,S] float32 out, device, may be NULL (kept in ws)
+ *   idx          [Bt,Hkv,budget+n_sink+W] int32 out, device, ascending
+ *   k_out, v_out [Bt,Hkv,budget+n_sink+W,D] dtype out, device
+ *   ws           device scratch of >= kvsel_layer_end_workspace(desc, budget)
+ *                bytes (computed for pooled == NULL, the larger case)
+ * Errors: those of kvsel_score and kvsel_select_compact.
+ */
+size_t kvsel_layer_end_workspace(const kvsel_desc* desc, int32_t budget);
+kvsel_status kvsel_layer_end(const kvsel_desc* desc, const void* q_obs, const void* k,
+                             const void* v, int32_t budget, int32_t pool_kernel,
+                             float* raw_scores, float* pooled, int32_t* idx, void* k_out,
+                             void* v_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kara decode-window compression/*
  * Kara decode-window compression (Kara, "Kara: Efficient Reasoning LLM
  * Serving via Sliding-Window KV Cache Compression", Section 3).  A window of
  * `window` recent tokens per (sequence, KV head); its last `buffer` tokens
@@ -460,9 +486,9 @@ kvsel_status kvsel_score_static(const kvsel_desc* desc, const void* q_obs, const
  * Kernel timing for benchmarks (not needed for normal use).
  *
  * kvsel_timing_start(prefix): from now on, every launch of a library kernel
- *   whose name starts with `prefix` ("*" = every kernel) is bracketed by a
- *   pair of HIP events recorded on the stream it is launched on.  NULL or ""
- *   stops recording.  Kernel names are those a profiler shows without
+ *   whose name starts with `prefix` ("*" = every kernel) carries a start and
+ *   a stop HIP event that its dispatch stamps with the kernel's begin and end
+ *   (hipExtLaunchKernel).  NULL or "" stops recording.  Kernel names are those a profiler shows without
  *   template arguments (e.g. "score_pass1_32", "sel_hist", "compact_kernel").
  * kvsel_timing_read: waits for every recorded pair, and writes per kernel
  *   name (in first-launch order, at most max_kernels of them) the name into
@@ -471,7 +497,6 @@ kvsel_status kvsel_score_static(const kvsel_desc* desc, const void* q_obs, const
  *   the recorded pairs are then released.  Returns the number of distinct
  *   kernel names, -1 on bad arguments, -2 when an event could not be read.
  * Process-wide state behind a mutex; meant for one benchmarking thread.
- * Timing adds two event records per matching launch to the stream.
  */
 kvsel_status kvsel_timing_start(const char* kernel_prefix);
 int32_t kvsel_timing_read(char* names, int32_t name_bytes, double* total_ms, int32_t* launches,
