@@ -141,6 +141,10 @@ def lib() -> ctypes.CDLL:
     L.kvsel_layer_end_workspace.restype = SZ
     L.kvsel_layer_end.argtypes = [DP, P, P, P, I32, I32, P, P, P, P, P, P, SZ, P]
     L.kvsel_layer_end.restype = ctypes.c_int
+    L.kvsel_layer_end_stream_workspace.argtypes = [DP, I32, I32]
+    L.kvsel_layer_end_stream_workspace.restype = SZ
+    L.kvsel_layer_end_stream.argtypes = [DP, P, P, P, I32, I32, P, P, P, P, SZ, P]
+    L.kvsel_layer_end_stream.restype = ctypes.c_int
     L.kvsel_score_static.argtypes = [DP, P, P, P, P, I32, P]
     L.kvsel_score_static.restype = ctypes.c_int
     _lib = L
@@ -397,6 +401,40 @@ def layer_end(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *
         return idx, k_out, v_out, raw, pooled
 
 
+def layer_end_stream_workspace_bytes(desc: Desc, budget: int, pool_kernel: int) -> int:
+    return int(lib().kvsel_layer_end_stream_workspace(ctypes.byref(desc), int(budget),
+                                                      int(pool_kernel)))
+
+
+def layer_end_stream(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *,
+                     budget: int, pool_kernel: int, n_sink: int = 0, causal: bool = True,
+                     scale: float = 0.0, idx: Optional[torch.Tensor] = None,
+                     k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvsel_layer_end_stream: the layer-end step with the streaming top-k of
+    pass 2 (no per-key score vector).  Returns (idx, k_hat, v_hat)."""
+    with _on(stream):
+        d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
+        Bt, Hkv, S, D = k.shape
+        n_keep = budget + n_sink + q_obs.shape[2]
+        dev = k.device
+        if idx is None:
+            idx = torch.empty((Bt, Hkv, n_keep), dtype=torch.int32, device=dev)
+        if k_out is None:
+            k_out = torch.empty((Bt, Hkv, n_keep, D), dtype=k.dtype, device=dev)
+        if v is not None and v_out is None:
+            v_out = torch.empty((Bt, Hkv, n_keep, D), dtype=v.dtype, device=dev)
+        if workspace is None:
+            nbytes = layer_end_stream_workspace_bytes(d, budget, pool_kernel)
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        st = lib().kvsel_layer_end_stream(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(v),
+                                          int(budget), int(pool_kernel), _ptr(idx), _ptr(k_out),
+                                          _ptr(v_out), _ptr(workspace), workspace.numel(),
+                                          _stream(stream))
+        _check(st, "kvsel_layer_end_stream")
+        return idx, k_out, v_out
+
+
 def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
                        pool_kernel: int, n_sink: int = 0, causal: bool = True,
                        scale: float = 0.0, stream=None) -> dict:
@@ -548,7 +586,8 @@ EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_se
            "kvsel_kara_score_workspace", "kvsel_kara_score", "kvsel_kara_select",
            "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact",
            "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read", "kvsel_score_static",
-           "kvsel_layer_end_workspace", "kvsel_layer_end")
+           "kvsel_layer_end_workspace", "kvsel_layer_end", "kvsel_layer_end_stream_workspace",
+           "kvsel_layer_end_stream")
 
 STATIC_SCRATCH_BYTES = 32 << 20   # KVSEL_STATIC_SCRATCH_BYTES
 

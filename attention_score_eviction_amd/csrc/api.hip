@@ -280,6 +280,96 @@ kvsel_status kvsel_layer_end(const kvsel_desc* desc, const void* q_obs, const vo
   });
 }
 
+// Streaming path (TideKV Algorithm 2's top-k kept during pass 2): scratch
+// is the row statistics, the per-row candidate lists, the merge selection
+// and its workspace -- no per-key score vector.
+struct StreamWs {
+  ScorePlan sp;
+  kvsel_desc ld;     // the merge: a selection over the rows' candidate lists
+  SelectPlan lp;
+  int M;
+  size_t off_cval, off_cpos, off_sel, off_lws, total;
+};
+
+bool stream_ws(const kvsel_desc& d, int budget, int pool_kernel, StreamWs* w) {
+  if (!plan_score_stream(d, &w->sp) || (pool_kernel - 1) / 2 > 64) return false;
+  const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
+  w->M = stream_list_len(w->sp, lo, hi, budget);
+  w->ld = d;
+  w->ld.n_q_heads = d.n_kv_heads;
+  w->ld.seq_len = w->M > 0 ? w->M : 1;
+  w->ld.obs_window = 0;
+  w->ld.n_sink = 0;
+  plan_select(w->ld, budget, 1, &w->lp);
+  const size_t rows = (size_t)d.batch * d.n_kv_heads;
+  size_t off = align256(w->sp.off_raw);   // partials and row statistics only
+  w->off_cval = off;
+  off = align256(off + rows * w->M * sizeof(float));
+  w->off_cpos = off;
+  off = align256(off + rows * w->M * sizeof(int32_t));
+  w->off_sel = off;
+  off = align256(off + rows * budget * sizeof(int32_t));
+  w->off_lws = off;
+  w->total = off + w->lp.total;
+  return true;
+}
+
+size_t kvsel_layer_end_stream_workspace(const kvsel_desc* desc, int32_t budget,
+                                        int32_t pool_kernel) {
+  if (check_desc(desc) != KVSEL_OK) return 0;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink) return 0;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0) return 0;
+  StreamWs w;
+  if (!stream_ws(*desc, budget, pool_kernel, &w)) return 0;
+  return w.total;
+}
+
+kvsel_status kvsel_layer_end_stream(const kvsel_desc* desc, const void* q_obs, const void* k,
+                                    const void* v, int32_t budget, int32_t pool_kernel,
+                                    int32_t* idx, void* k_out, void* v_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_desc(desc);
+  if (st != KVSEL_OK) return st;
+  if (budget < 0 || budget > desc->seq_len - desc->obs_window - desc->n_sink)
+    return KVSEL_ERR_BUDGET;
+  if (!q_obs || !k || !idx || !k_out) return KVSEL_ERR_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVSEL_ERR_ARG;
+  const void* ptrs[] = {q_obs, k, v, idx, k_out, v_out, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return KVSEL_ERR_ARG;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 1 + 2 * (1 << 20))
+    return KVSEL_ERR_ARG;
+  StreamWs w;
+  if (!stream_ws(*desc, budget, pool_kernel, &w)) return KVSEL_ERR_UNSUPPORTED;
+  if (ws_bytes < w.total || !ws) return KVSEL_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  return enqueue(stream, [&] {
+    const hipStream_t s = (hipStream_t)stream;
+    const int rows = desc->batch * desc->n_kv_heads;
+    const int32_t* cpos = (const int32_t*)(wsc + w.off_cpos);
+    int32_t* sel = (int32_t*)(wsc + w.off_sel);
+    if (budget > 0) {
+      StreamArgs sa;
+      sa.cval = (float*)(wsc + w.off_cval);
+      sa.cpos = (int32_t*)(wsc + w.off_cpos);
+      sa.lo = desc->n_sink;
+      sa.hi = desc->seq_len - desc->obs_window;
+      sa.budget = budget;
+      sa.ph = (pool_kernel - 1) / 2;
+      sa.M = w.M;
+      kvsel_status r = launch_score_stream(*desc, w.sp, q_obs, k, sa, wsc, s);
+      if (r != KVSEL_OK) return r;
+      r = launch_select(w.ld, w.lp, sa.cval, budget, sel, nullptr, wsc + w.off_lws, s);
+      if (r != KVSEL_OK) return r;
+    }
+    kvsel_status r = launch_stream_finish(sel, cpos, idx, rows, w.M, budget, desc->n_sink,
+                                          desc->obs_window, desc->seq_len, s);
+    if (r != KVSEL_OK) return r;
+    return launch_compact(*desc, k, v, idx, desc->n_sink + budget + desc->obs_window, k_out,
+                          v_out, s);
+  });
+}
+
 size_t kvsel_select_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget) {
   if (check_adaptive(desc, total_budget) != KVSEL_OK) return 0;
   SelectPlan p;

@@ -117,7 +117,27 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
                           float* raw, float* pooled, int pool_kernel, char* ws,
                           hipStream_t stream, int kstride, uint32_t* zero = nullptr,
                           size_t zero_words = 0);
-// Selection groups: hg consecutive KV heads of a sequence share one budget
+// Streaming top-k (TideKV Algorithm 2's heap in pass 2): per (sequence, KV
+// head) row, a list of M candidates (each chunk's top-`budget` pooled scores
+// in ascending position order, chunk after chunk) instead of a score vector.
+struct StreamArgs {
+  float* cval;     // [nheads][M] candidate scores
+  int32_t* cpos;   // [nheads][M] their positions
+  int lo, hi;      // candidate range [n_sink, S - W)
+  int budget, ph, M;
+};
+// False when the problem does not fit the streaming pass (bf16 prompts of
+// 4096 keys or more with one query group per KV head, chunks <= 16384 keys).
+bool plan_score_stream(const kvsel_desc& d, ScorePlan* p);
+int stream_list_len(const ScorePlan& p, int lo, int hi, int budget);
+kvsel_status launch_score_stream(const kvsel_desc& d, const ScorePlan& p, const void* q,
+                                 const void* k, const StreamArgs& sa, char* ws,
+                                 hipStream_t stream);
+kvsel_status launch_stream_finish(const int32_t* sel, const int32_t* cpos, int32_t* idx,
+                                  int rows, int M, int budget, int n_sink, int W, int S,
+                                  hipStream_t stream);
+
+// Selection groups: hg consecutive KV heads of a sequence share one budget// Selection groups: hg consecutive KV heads of a sequence share one budget
 // (hg = 1: per-head budget; hg = n_kv_heads: head-adaptive budget).
 constexpr int kMaxGroupSlices = 2048;
 struct SelectPlan {

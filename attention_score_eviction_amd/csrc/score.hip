@@ -28,7 +28,10 @@
 //  * Exponentials are exp2 with scale*log2(e) folded into one FMA per logit.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
+#include "select_util.h"
 
 namespace kvsel {
 namespace {
@@ -618,6 +621,155 @@ __global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Pass 2 with the streaming top-k of TideKV Algorithm 2 (the heap of pass 2):
+// no per-key score vector leaves the workgroup.  A workgroup computes the
+// raw scores of its key chunk plus one 64-key block on either side (the
+// halo the max filter needs) into LDS, pools them there, and keeps the
+// top-`budget` pooled candidates of the chunk (all of them when the chunk
+// has fewer), which it writes in ascending position order to its slot of a
+// per-row candidate list.  The global top-budget is a subset of the union of
+// the chunk lists, so a selection over the lists (ties to the lower list
+// index, which is the lower position) finishes the job.  Scratch is
+// O(chunks x budget) per row, independent of S while the chunk count is
+// fixed by the machine.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxChunk = 16384;
+
+// Candidates of chunk c: [max(lo, c*chunk), min(hi, (c+1)*chunk)).
+__device__ __forceinline__ int chunk_candidates(int c, int chunk, int lo, int hi) {
+  return max(0, min(hi, (c + 1) * chunk) - max(lo, c * chunk));
+}
+
+template <int D, int NQ, int NW>
+__global__ void __launch_bounds__(NW * 64) score_pass2_stream(ScoreArgs a, StreamArgs sa) {
+  constexpr int NV = D / 16;
+  constexpr int NT = NW * 64;
+  constexpr int PER = kStreamMaxChunk / NT;
+  __shared__ u32x4_t qs[NQ * NV * 64];
+  __shared__ float ls[NQ * 32];
+  __shared__ int lims[NQ * 32];
+  extern __shared__ float sc[];   // a.chunk + 128 scores (dynamic)
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+  __shared__ uint32_t wsum[NT / 64];
+  __shared__ uint32_t pick[3];
+  __shared__ int off_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, head = blockIdx.y;
+  const int b = head / a.Hkv, hk = head - b * a.Hkv;
+  const int nrows = min(a.qcap, a.GW);
+  const int S = a.S;
+  const float c = a.c;
+  const char* kh = (const char*)((const uint16_t*)a.k + (size_t)head * a.kstride * D);
+  const int k0 = chunk * a.chunk;
+  const int kend = min(S, k0 + a.chunk);
+  const int x0 = k0 >= 64 ? k0 - 64 : 0;        // chunk with a one-block halo
+  const int x1 = min(S, kend + 64);
+  const int mask_from = a.causal ? (S - a.W + 1) : S;
+
+  int kb = x0 + wave * 64;
+  Frag<NV> kf[2];
+  if (kb < x1) load_key_block32<D>(kf, kh, kb, S, lane);
+  const uint16_t* qg = (const uint16_t*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W) * D;
+  stage_queries32<D, NT>(qs, qg, nrows, NQ);
+  for (int r = tid; r < NQ * 32; r += NT) {
+    ls[r] = (r < nrows) ? a.lse[(size_t)head * a.GWr + r] : INFINITY;
+    lims[r] = key_limit(a, r);
+  }
+  if (tid == 0) {
+    int off = 0;
+    for (int cc = 0; cc < chunk; ++cc) off += min(sa.budget, chunk_candidates(cc, a.chunk, sa.lo, sa.hi));
+    off_s = off;
+  }
+  __syncthreads();
+  for (; kb < x1; kb += NT) {
+    float as[2] = {0.f, 0.f};
+    if (kb + 64 > mask_from) pass2_block32<NV, NQ, true>(lims, kf, qs, ls, as, kb, lane, c);
+    else pass2_block32<NV, NQ, false>(lims, kf, qs, ls, as, kb, lane, c);
+    if (kb + NT < x1) load_key_block32<D>(kf, kh, kb + NT, S, lane);
+    as[0] += __shfl_xor(as[0], 32);
+    as[1] += __shfl_xor(as[1], 32);
+    const float mine = (lane >> 5) ? as[1] : as[0];
+    if (kb + lane < x1) sc[kb - x0 + lane] = mine;
+  }
+  __syncthreads();
+  // Max filter over the candidate range, into registers, then in place.
+  const int c0 = max(sa.lo, k0), c1 = min(sa.hi, kend);
+  const int nc = max(0, c1 - c0);
+  float pv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = c0 + j * NT + tid;
+    float m = 0.f;
+    if (i < c1) {
+      const int j0 = max(sa.lo, i - sa.ph), j1 = min(sa.hi - 1, i + sa.ph);
+      m = sc[j0 - x0];
+      for (int t = j0 + 1; t <= j1; ++t) m = fmaxf(m, sc[t - x0]);
+    }
+    pv[j] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (j * NT + tid < nc) sc[j * NT + tid] = pv[j];
+  __syncthreads();
+  const int keep = min(sa.budget, nc);
+  if (keep == 0) return;
+  float* dv = sa.cval + (size_t)head * sa.M + off_s;
+  int32_t* dp = sa.cpos + (size_t)head * sa.M + off_s;
+  if (nc <= sa.budget) {
+    for (int i = tid; i < nc; i += NT) {
+      dv[i] = sc[i];
+      dp[i] = c0 + i;
+    }
+    return;
+  }
+  // Exact top-keep of the chunk: radix select on the bit patterns (scores
+  // are >= 0, so bit order is value order), ties to the lower position.
+  const uint32_t* sb = (const uint32_t*)sc;
+  uint32_t prefix = 0u, pmask = 0u, rem = (uint32_t)keep;
+  for (int r = 0; r < 3; ++r) {
+    const int shift = r == 0 ? 20 : (r == 1 ? 10 : 0);
+    const int nb = r == 0 ? 2048 : 1024;
+    for (int i = tid; i < nb; i += NT) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t x = sb[i];
+      hist_add(hist, (x >> shift) & (uint32_t)(nb - 1), (x & pmask) == prefix);
+    }
+    __syncthreads();
+    if (r == 0) block_find_digit<2048>(hist, rem, pick);
+    else block_find_digit<1024>(hist, rem, pick);
+    rem -= pick[1];
+    prefix |= pick[0] << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    const bool whole = rem == pick[2];
+    __syncthreads();
+    if (whole) break;
+  }
+  // Ordered write: kept = above the prefix, or equal to it among the first
+  // `rem` equal ones in position order.
+  uint32_t out_base = 0u, eq_base = 0u;
+  for (int i0 = 0; i0 < nc; i0 += NT) {
+    const int i = i0 + tid;
+    const uint32_t x = i < nc ? sb[i] : 0u;
+    const uint32_t km = x & pmask;
+    const bool gt = i < nc && km > prefix;
+    const bool eq = i < nc && km == prefix;
+    uint32_t eq_tot;
+    const uint32_t eq_before = eq_base + block_exclusive_scan<NT>(eq ? 1u : 0u, &eq_tot, wsum);
+    const bool kp = gt || (eq && eq_before < rem);
+    uint32_t kp_tot;
+    const uint32_t slot = out_base + block_exclusive_scan<NT>(kp ? 1u : 0u, &kp_tot, wsum);
+    if (kp && slot < (uint32_t)keep) {
+      dv[slot] = __uint_as_float(x);
+      dp[slot] = c0 + i;
+    }
+    out_base += kp_tot;
+    eq_base += eq_tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Combine the per-chunk partials of each query row: lse = max + log2(sum).
 // 2^tpr_log2 consecutive lanes share a row (just enough for about four
 // partials each, so short chunk lists do not leave a wave per row mostly
@@ -926,6 +1078,88 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
   KVSEL_LAUNCH("maxpool_kernel", maxpool_kernel, dim3((d.seq_len + 255) / 256, p.nheads), dim3(256), 0, stream,
                      s, pooled, d.seq_len, lo, hi, (pool_kernel - 1) / 2);
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+}
+
+bool plan_score_stream(const kvsel_desc& d, ScorePlan* p) {
+  if (!plan_score(d, p) || !p->mfma32 || p->ngroups != 1 || p->maxqt > 10) return false;
+  // A chunk is held in LDS next to the query tiles.
+  return p->chunk <= kStreamMaxChunk;
+}
+
+int stream_list_len(const ScorePlan& p, int lo, int hi, int budget) {
+  int m = 0;
+  for (int c = 0; c < p.nchunk; ++c) {
+    const int n = std::max(0, std::min(hi, (c + 1) * p.chunk) - std::max(lo, c * p.chunk));
+    m += std::min(budget, n);
+  }
+  return m;
+}
+
+template <int D, int NQ, int NW>
+static void launch_stream_passes(const ScoreArgs& args, const StreamArgs& sa, dim3 grid,
+                                 hipStream_t stream, const ScorePlan& p) {
+  KVSEL_LAUNCH("score_pass1_32", (score_pass1_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream,
+               args);
+  int tl = 0;
+  while ((4 << tl) < p.nchunk && tl < 6) ++tl;
+  const long lanes = ((long)p.nheads * p.GW) << tl;
+  KVSEL_LAUNCH("score_combine", score_combine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0,
+               stream, args.part, args.lse, p.nheads, p.nchunk, p.GW, p.GWr, tl, args.zero,
+               args.zero_words);
+  const size_t lds = (size_t)(p.chunk + 128) * sizeof(float);
+  KVSEL_LAUNCH("score_pass2_stream", (score_pass2_stream<D, NQ, NW>), grid, dim3(NW * 64), lds,
+               stream, args, sa);
+}
+
+kvsel_status launch_score_stream(const kvsel_desc& d, const ScorePlan& p, const void* q,
+                                 const void* k, const StreamArgs& sa, char* ws,
+                                 hipStream_t stream) {
+  ScoreArgs a;
+  a.q = q;
+  a.k = k;
+  a.part = (float2*)(ws + p.off_part);
+  a.lse = (float*)(ws + p.off_lse);
+  a.s_out = nullptr;
+  a.Hq = d.n_q_heads;
+  a.Hkv = d.n_kv_heads;
+  a.G = p.G;
+  a.W = d.obs_window;
+  a.S = d.seq_len;
+  a.kstride = d.seq_len;
+  a.GW = p.GW;
+  a.GWr = p.GWr;
+  a.qcap = p.qcap;
+  a.chunk = p.chunk;
+  a.nchunk = p.nchunk;
+  a.causal = d.causal;
+  a.zero = nullptr;
+  a.zero_words = 0;
+  const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
+  a.c = scale * kLog2e;
+  const dim3 grid(p.nchunk, p.nheads, 1);
+  const int nq = p.maxqt;
+#define KVSEL_STREAM(DD, NQQ, NWW) launch_stream_passes<DD, NQQ, NWW>(a, sa, grid, stream, p)
+  if (d.head_dim == 128) {
+    switch (nq) {
+      case 1: KVSEL_STREAM(128, 1, 4); break;
+      case 2: KVSEL_STREAM(128, 2, 4); break;
+      case 4: KVSEL_STREAM(128, 4, 4); break;
+      case 8: KVSEL_STREAM(128, 8, 4); break;
+      case 10: KVSEL_STREAM(128, 10, 8); break;
+      default: return KVSEL_ERR_UNSUPPORTED;
+    }
+  } else {
+    switch (nq) {
+      case 1: KVSEL_STREAM(64, 1, 4); break;
+      case 2: KVSEL_STREAM(64, 2, 4); break;
+      case 4: KVSEL_STREAM(64, 4, 4); break;
+      case 8: KVSEL_STREAM(64, 8, 4); break;
+      case 10: KVSEL_STREAM(64, 10, 8); break;
+      default: return KVSEL_ERR_UNSUPPORTED;
+    }
+  }
+#undef KVSEL_STREAM
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 

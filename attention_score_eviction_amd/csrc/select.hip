@@ -16,124 +16,12 @@
 // Short rows: one workgroup per (batch, KV head), the row held in registers,
 // histograms in LDS.  Long rows and head groups: the sliced kernels below.
 #include "common.h"
+#include "select_util.h"
 
 namespace kvsel {
 namespace {
 
 constexpr int kSelThreads = 1024;
-
-// Inclusive prefix sum across the 64 lanes of a wave: DPP row shifts build
-// the sums inside each row of 16 lanes, two row broadcasts carry them across
-// rows (no LDS round trips).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
-// Exclusive prefix sum over a workgroup of NT threads; *total receives the
-// sum of all.  wsum must hold NT/64 entries.  Two barriers.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total,
-                                                         uint32_t* wsum) {
-  constexpr int NWV = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0u, tot = 0u;
-#pragma unroll
-  for (int w = 0; w < NWV; ++w) {
-    const uint32_t sw = wsum[w];
-    before += w < wave ? sw : 0u;
-    tot += sw;
-  }
-  *total = tot;
-  __syncthreads();   // wsum may be reused after this
-  return before + incl - v;
-}
-
-// Histogram update: one LDS atomic per counted score.  (Aggregating equal
-// bins across a wave first costs more in cross-lane latency than the atomic
-// conflicts it saves, at every row length measured.)
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
-  if (active) atomicAdd(&hist[bin], 1u);
-}
-
-// Histogram update for a thread's kPerThread consecutive scores: runs of
-// equal bins (common, since max-pooling repeats a local maximum over its
-// neighbours) are counted in registers and added with one atomic per run,
-// which cuts same-address conflicts on the crowded bins.
-template <int N>
-__device__ __forceinline__ void hist_add_runs(uint32_t* hist, const uint32_t (&bin)[N],
-                                              uint32_t active) {
-  uint32_t cur = bin[0], cnt = active & 1u;
-#pragma unroll
-  for (int e = 1; e < N; ++e) {
-    const bool a = (active >> e) & 1u;
-    if (a && bin[e] == cur) {
-      ++cnt;
-    } else {
-      if (cnt) atomicAdd(&hist[cur], cnt);
-      cur = bin[e];
-      cnt = a ? 1u : 0u;
-    }
-  }
-  if (cnt) atomicAdd(&hist[cur], cnt);
-}
-
-// Among the NB bins of `hist` (16-byte aligned), read in descending value
-// order, find the bin holding the rem-th largest counted element (rem >= 1
-// and at most the total count).  pick[0] = that bin, pick[1] = count strictly
-// above it, pick[2] = its own count.  One wave, two levels: each lane sums
-// NB/64 consecutive bins and a wave scan finds the lane whose range holds
-// the rank; then the wave reads that lane's bins, one per lane, highest
-// first, and a second scan finds the bin.  (Keeping a lane's bins in
-// registers and walking them serially costs ~100 VGPRs in the kernels that
-// inline this.)
-template <int NB>
-__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t rem,
-                                                uint32_t* pick) {
-  constexpr int PER = NB / 64;
-  static_assert(PER <= 64 && PER % 4 == 0, "bins per lane");
-  const int lane = threadIdx.x & 63;
-  uint32_t local = 0u;
-  {
-    const int b0 = NB - (lane + 1) * PER;
-#pragma unroll
-    for (int j = 0; j < PER; j += 4) {
-      const u32x4_t w = *(const u32x4_t*)(hist + b0 + j);
-      local += (w[0] + w[1]) + (w[2] + w[3]);
-    }
-  }
-  const uint32_t incl = wave_incl_scan(local);
-  const uint32_t excl = incl - local;
-  const unsigned long long hit = __ballot(excl < rem && rem <= incl);
-  if (hit == 0ull) return;
-  const int L = __ffsll((long long)hit) - 1;
-  const uint32_t run = __builtin_amdgcn_readlane(excl, L);
-  const int bin = NB - L * PER - 1 - lane;   // lane 0: lane L's highest bin
-  const uint32_t c = lane < PER ? hist[bin] : 0u;
-  const uint32_t i2 = wave_incl_scan(c);
-  if (lane < PER && run + (i2 - c) < rem && rem <= run + i2) {
-    pick[0] = (uint32_t)bin;
-    pick[1] = run + (i2 - c);
-    pick[2] = c;
-  }
-}
-
-// wave_find_digit by the first wave, then a barrier so every thread can
-// read pick.  Every thread of the block must call.
-template <int NB>
-__device__ __forceinline__ void block_find_digit(const uint32_t* hist, uint32_t rem,
-                                                 uint32_t* pick) {
-  if (threadIdx.x < 64) wave_find_digit<NB>(hist, rem, pick);
-  __syncthreads();
-}
 
 // Each thread takes 16 consecutive scores per batch as four 16-byte loads
 // (scalar loads only at the unaligned ends), so a sweep keeps many bytes in
@@ -1059,6 +947,39 @@ kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, c
   KVSEL_LAUNCH("sel_emit", sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return KVSEL_ERR_DEVICE;
   return launch_compact(d, k, v, idx, a.n_keep, k_out, v_out, stream);
+}
+
+// Final index rows of the streaming path: sinks, then the positions of the
+// selected list entries (selected in ascending list order, which is
+// ascending position order), then the observation window.
+__global__ void __launch_bounds__(256) stream_finish_kernel(const int32_t* __restrict__ sel,
+                                                            const int32_t* __restrict__ cpos,
+                                                            int32_t* __restrict__ idx, int M,
+                                                            int budget, int n_sink, int W, int S) {
+  const int row = blockIdx.y;
+  const int n_keep = n_sink + budget + W;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= n_keep) return;
+  int32_t pos;
+  if (r < n_sink) {
+    pos = r;
+  } else if (r < n_sink + budget) {
+    const int32_t li = sel[(size_t)row * budget + (r - n_sink)];
+    pos = (li >= 0 && li < M) ? cpos[(size_t)row * M + li] : -1;
+  } else {
+    pos = S - W + (r - n_sink - budget);
+  }
+  idx[(size_t)row * n_keep + r] = pos;
+}
+
+kvsel_status launch_stream_finish(const int32_t* sel, const int32_t* cpos, int32_t* idx,
+                                  int rows, int M, int budget, int n_sink, int W, int S,
+                                  hipStream_t stream) {
+  const int n_keep = n_sink + budget + W;
+  if (n_keep == 0) return KVSEL_OK;
+  KVSEL_LAUNCH("stream_finish_kernel", stream_finish_kernel, dim3((n_keep + 255) / 256, rows),
+               dim3(256), 0, stream, sel, cpos, idx, M, budget, n_sink, W, S);
+  return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 
 }  // namespace kvsel

@@ -24,6 +24,9 @@ Workloads (one JSON line each):
   llama8k-adaptive / qwen128k-adaptive
                the same layers with a head-adaptive budget: Hkv*B picks per
                sequence over all KV heads, flattened output with head offsets
+  qwen128k-stream / llama64k-stream
+               the same layers through kvsel_layer_end_stream (the top-k kept
+               during pass 2, no per-key score vector)
 
 The timed region is the run's last GPU work, so the last steps x
 dispatches_per_step dispatches of a kernel trace of the run are exactly it.
@@ -59,6 +62,8 @@ WORKLOADS = {
     "qwen128k-adaptive": (4, "qwen3-14b-layer-128k-head-adaptive"),
     "kara512": (0, "kara-decode-window-64x512"),
     "qevict-steps": (5, "qevict-routing-steps-16x32k-int2"),
+    "qwen128k-stream": (4, "qwen3-14b-layer-128k-streaming-topk"),
+    "llama64k-stream": (3, "llama3-8b-layer0-64k-streaming-topk"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "qevict.hip",
@@ -245,9 +250,10 @@ class Layer:
     (kvsel_score, then kvsel_select_compact).  The head-adaptive variant
     runs kvsel_score, kvsel_select_adaptive and kvsel_compact_flat."""
 
-    def __init__(self, kvsel, torch, spec, x, adaptive=False):
+    def __init__(self, kvsel, torch, spec, x, adaptive=False, streaming=False):
         from attention_score_eviction_amd.driver import LayerMajorDriver
         self.kvsel, self.torch, self.spec, self.adaptive = kvsel, torch, spec, adaptive
+        self.streaming = streaming
         dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
         self.drv = LayerMajorDriver(spec.batch, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
                                     spec.seq_len, spec.obs_window, spec.pool_kernel,
@@ -274,6 +280,9 @@ class Layer:
                                     dtype=torch.uint8, device=d.k.device)
         self.select_ws = torch.empty(max(kvsel.select_workspace_bytes(d.desc, budget), 1),
                                      dtype=torch.uint8, device=d.k.device)
+        if self.streaming:
+            nb = kvsel.layer_end_stream_workspace_bytes(d.desc, budget, d.pool_kernel)
+            self.stream_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=d.k.device)
         if self.adaptive:
             Bt, Hkv = self.spec.batch, self.spec.n_kv_heads
             n_keep = Hkv * (budget + self.spec.n_sink + self.spec.obs_window)
@@ -311,6 +320,11 @@ class Layer:
         if self.adaptive:
             self.score(stream)
             self.select_compact(stream)
+        elif self.streaming:
+            d, c = self.drv, self.cache
+            self.kvsel.layer_end_stream(d.q, d.k, d.v, budget=c.budget, pool_kernel=d.pool_kernel,
+                                        n_sink=d.n_sink, idx=c.idx, k_out=c.k_hat,
+                                        v_out=c.v_hat, workspace=self.stream_ws, stream=stream)
         else:
             self.drv.layer_end(self.cache, stream=stream)
 
@@ -490,7 +504,8 @@ def main() -> int:
         return bench_tiers(args, kvsel, torch, spec, wname, dev, stream)
     x = synth.make_layer(spec, cid)
     adaptive = args.workload.endswith("-adaptive")
-    L = Layer(kvsel, torch, spec, x, adaptive=adaptive)
+    streaming = args.workload.endswith("-stream")
+    L = Layer(kvsel, torch, spec, x, adaptive=adaptive, streaming=streaming)
     if args.workload == "sweep64k":
         return bench_sweep(args, kvsel, torch, spec, wname, L, stream)
 
@@ -503,7 +518,12 @@ def main() -> int:
     sel_name = "kvsel_select_adaptive+compact_flat" if adaptive else "kvsel_select_compact"
     us_call = {"kvsel_score": event_time_us(torch, stream, lambda: L.score(stream), reps),
                sel_name: event_time_us(torch, stream, lambda: L.select_compact(stream), reps)}
-    if not adaptive:
+    if streaming:
+        us_call["kvsel_layer_end_stream"] = event_time_us(torch, stream, lambda: L.step(stream),
+                                                          reps)
+        us_call["workspace_bytes"] = {"kvsel_layer_end_stream": L.stream_ws.numel(),
+                                      "kvsel_layer_end": L.drv.ws.numel()}
+    elif not adaptive:
         us_call["kvsel_layer_end"] = event_time_us(torch, stream, lambda: L.step(stream), reps)
     kt = kernel_times(kvsel, torch, lambda: L.step(stream), reps)
     dispatches = sum(n for _, n in kt.values())
@@ -551,7 +571,8 @@ def main() -> int:
         "path_algorithmic_bytes": ab["path"],
         "score_mfma_util": round(score_flops / (t_score_us * 1e-6) / 1e12
                                  / MFMA_BF16_PEAK_TFLOPS, 4),
-        "us_per_call": {k: round(v, 2) for k, v in us_call.items()},
+        "us_per_call": {k: (round(v, 2) if isinstance(v, float) else v)
+                        for k, v in us_call.items()},
         "us_per_kernel": {k: round(us, 2) for k, (us, n) in
                           sorted(kt.items(), key=lambda kv: -kv[1][0] * kv[1][1])},
         "dispatches_per_step": int(round(dispatches)),

@@ -276,6 +276,33 @@ kvsel_status kvsel_layer_end(const kvsel_desc* desc, const void* q_obs, const vo
                              void* v_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_layer_end_stream -- TideKV Algorithm 2 with its streaming top-k: the
+ * top candidates are kept while pass 2 streams over the keys (Section 4.2,
+ * the heap of pass 2, and its temporary-memory bound), so no per-key score
+ * vector is formed.  Each workgroup of pass 2 pools its key chunk in LDS and
+ * keeps the chunk's top-`budget` candidates; a selection over the per-row
+ * candidate lists picks the final top-`budget`.  idx, k_out and v_out are
+ * exactly those of kvsel_layer_end (the same scores, the same order of
+ * ties); raw and pooled scores are not returned.
+ *
+ *   arguments as kvsel_layer_end without raw_scores / pooled
+ *   ws  device scratch of >= kvsel_layer_end_stream_workspace(desc, budget,
+ *       pool_kernel) bytes: O(rows x chunks x budget) for the candidate
+ *       lists, independent of S while the chunk count (set by the size of
+ *       the GPU) is fixed
+ * Supported: bf16 prompts of 4096 keys or more with G*W <= 320 query rows
+ * per KV head, key chunks of at most 16384 keys, pool_kernel <= 129;
+ * otherwise KVSEL_ERR_UNSUPPORTED (the workspace query returns 0).
+ */
+size_t kvsel_layer_end_stream_workspace(const kvsel_desc* desc, int32_t budget,
+                                        int32_t pool_kernel);
+kvsel_status kvsel_layer_end_stream(const kvsel_desc* desc, const void* q_obs, const void* k,
+                                    const void* v, int32_t budget, int32_t pool_kernel,
+                                    int32_t* idx, void* k_out, void* v_out, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/*
+ * Kara decode-window compression/*
  * Kara decode-window compression/*
  * Kara decode-window compression (Kara, "Kara: Efficient Reasoning LLM
  * Serving via Sliding-Window KV Cache Compression", Section 3).  A window of
