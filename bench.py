@@ -461,6 +461,85 @@ def summarize_trace(path: str, last: int, title: str, command: str) -> int:
     return 0
 
 
+N_XCD, N_SIMD = 8, 1024     # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_counters(paths: list, kernels: str, title: str, command: str) -> int:
+    """Markdown table of SQ/GRBM counters per kernel from rocprofv3 --pmc
+    runs (one counter_collection.csv per pass), mean per dispatch, with the
+    derived issue shares:
+
+    - cycles: GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs);
+    - MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles);
+    - VALU busy: 4 x SQ_ACTIVE_INST_VALU / (1024 x cycles) (the counter is in
+      quad-cycles, summed over waves; one wave issues VALU on a SIMD at a time);
+    - co-issue: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES;
+    - idle: the share of SIMD cycles with neither unit busy."""
+    want = [k for k in kernels.split(",") if k]
+    means = {}
+    names = []
+    for p in paths:
+        import csv
+        acc = {}
+        for r in csv.DictReader(open(p)):
+            k = short_kernel_name(r["Kernel_Name"])
+            if want and k not in want:
+                continue
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            acc.setdefault((k, c), {}).setdefault(r["Dispatch_Id"], 0.0)
+            acc[(k, c)][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for key, v in acc.items():
+            means[key] = (sum(v.values()) / len(v), len(v))
+    ks = want or sorted({k for k, _ in means})
+    out = [f"# rocprofv3 counters: {title}", "", "Commands (from the repository root on the "
+           "GPU host; one --pmc pass each):", "", "```", command, "```", "",
+           "Mean per dispatch over every dispatch of the kernel in the run.", "",
+           "| counter | " + " | ".join(ks) + " |", "|---" * (len(ks) + 1) + "|"]
+    for c in names:
+        cells = []
+        for k in ks:
+            m = means.get((k, c))
+            cells.append("—" if m is None else f"{m[0]:,.0f}")
+        out.append(f"| {c} | " + " | ".join(cells) + " |")
+    out += ["", "Derived (MI355X: 8 XCDs, 1024 SIMDs):", "",
+            "| | " + " | ".join(ks) + " |", "|---" * (len(ks) + 1) + "|"]
+
+    def val(k, c):
+        m = means.get((k, c))
+        return None if m is None else m[0]
+    rows = {"cycles per XCD": [], "MFMA busy": [], "VALU busy": [],
+            "VALU co-issued during MFMA": [], "neither busy": [],
+            "VALU instructions per MFMA": [], "transcendentals per MFMA": [],
+            "LDS instructions per MFMA": []}
+    for k in ks:
+        cyc = val(k, "GRBM_GUI_ACTIVE")
+        cyc = cyc / N_XCD if cyc else None
+        mf, va, co = (val(k, "SQ_VALU_MFMA_BUSY_CYCLES"), val(k, "SQ_ACTIVE_INST_VALU"),
+                      val(k, "SQ_VALU_MFMA_COEXEC_CYCLES"))
+        nm, nv, nt, nl = (val(k, "SQ_INSTS_MFMA"), val(k, "SQ_INSTS_VALU"),
+                          val(k, "SQ_INSTS_VALU_TRANS_F32"), val(k, "SQ_INSTS_LDS"))
+        f = lambda x: "—" if x is None else f"{100 * x:.0f}%"     # noqa: E731
+        r = lambda a, b: "—" if a is None or not b else f"{a / b:.2f}"   # noqa: E731
+        mfb = mf / (N_SIMD * cyc) if mf is not None and cyc else None
+        vab = 4 * va / (N_SIMD * cyc) if va is not None and cyc else None
+        cob = co / mf if co is not None and mf else None
+        idle = (1 - mfb - vab + cob * mfb) if None not in (mfb, vab, cob) else None
+        rows["cycles per XCD"].append("—" if cyc is None else f"{cyc:,.0f}")
+        rows["MFMA busy"].append(f(mfb))
+        rows["VALU busy"].append(f(vab))
+        rows["VALU co-issued during MFMA"].append(f(cob))
+        rows["neither busy"].append(f(idle))
+        rows["VALU instructions per MFMA"].append(r(nv, nm))
+        rows["transcendentals per MFMA"].append(r(nt, nm))
+        rows["LDS instructions per MFMA"].append(r(nl, nm))
+    for n, cells in rows.items():
+        out.append(f"| {n} | " + " | ".join(cells) + " |")
+    print("\n".join(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,6 +553,9 @@ def main() -> int:
                     help="record measured traffic for --workload from rocprofv3 csv files")
     ap.add_argument("--summarize-trace", metavar="TRACE",
                     help="markdown summary of the last --last dispatches of a kernel trace")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="markdown counter table from rocprofv3 --pmc csv files")
+    ap.add_argument("--kernels", default="", help="comma-separated kernel base names")
     ap.add_argument("--last", type=int, default=0)
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
@@ -482,6 +564,8 @@ def main() -> int:
         return ingest_counters(args.workload, *args.ingest_counters)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args.last, args.title, args.command)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.kernels, args.title, args.command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the work shards by KV head with no exchange); run with --gpus 1", file=sys.stderr)
