@@ -791,10 +791,17 @@ __global__ void __launch_bounds__(256) score_combine(const float2* __restrict__ 
   const int r = valid ? (int)(row_id - (long)head * GW) : 0;
   float m = -INFINITY, z = 0.f;
   if (valid) {
+    // A lane's partials, in chunk order, read CB at a time with all CB loads
+    // in flight before the first merge.
+    constexpr int CB = 4;
     const float2* p = part + ((size_t)head * GWr + r) * nchunk;
-    for (int ch = sub; ch < nchunk; ch += tpr) {
-      const float2 pz = p[ch];
-      lse_merge(m, z, pz.x, pz.y);
+    for (int ch0 = sub; ch0 < nchunk; ch0 += CB * tpr) {
+      float2 pz[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) pz[j] = p[min(ch0 + j * tpr, nchunk - 1)];
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        if (ch0 + j * tpr < nchunk) lse_merge(m, z, pz[j].x, pz[j].y);
     }
   }
   for (int off = tpr >> 1; off >= 1; off >>= 1) {

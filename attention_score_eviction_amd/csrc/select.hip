@@ -23,33 +23,55 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 
-// Each thread takes 16 consecutive scores per batch as four 16-byte loads
-// (scalar loads only at the unaligned ends), so a sweep keeps many bytes in
-// flight per CU.  Elements outside [lo, hi) come back invalid.
+// Each thread takes 16 consecutive scores per batch as four 16-byte loads,
+// so a sweep keeps many bytes in flight per CU.  Elements outside [lo, hi)
+// come back invalid.  The four loads are unconditional and independent: a
+// vector that is not wholly inside [lo, hi) loads from the nearest one that
+// is (same alignment), and only its valid elements, if any, are reloaded one
+// by one.  (With a vector/scalar choice per load the compiler waits for each
+// vector load before issuing the next: four memory latencies in a row.)
 constexpr int kPerThread = 16;
 
 __device__ __forceinline__ uint32_t load16(const uint32_t* row, int p0, int lo, int hi,
                                            uint32_t (&x)[kPerThread]) {
-  uint32_t valid = 0u;
+  // Starts of the vectors wholly inside [lo, hi) congruent to p0 mod 4.
+  const int f_lo = lo + ((p0 - lo) & 3);
+  const int f_hi = (hi - 4) - ((hi - 4 - p0) & 3);
+  uint32_t valid = 0u, fix = 0u;
+  if (f_lo <= f_hi) {
+    u32x4_t w[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int p = p0 + 4 * v;
-    if (p >= lo && p + 3 < hi) {
-      const u32x4_t w = *(const u32x4_t*)(row + p);
-      x[4 * v] = w[0];
-      x[4 * v + 1] = w[1];
-      x[4 * v + 2] = w[2];
-      x[4 * v + 3] = w[3];
-      valid |= 0xfu << (4 * v);
-    } else {
+    for (int v = 0; v < 4; ++v) {
+      const int pc = min(max(p0 + 4 * v, f_lo), f_hi);
+      w[v] = *(const u32x4_t*)(row + pc);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = p0 + 4 * v;
+      const bool same = p >= f_lo && p <= f_hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = p + e;
         const bool ok = i >= lo && i < hi;
-        x[4 * v + e] = ok ? row[i] : 0u;
         valid |= (uint32_t)ok << (4 * v + e);
+        fix |= (uint32_t)(ok && !same) << (4 * v + e);
+        x[4 * v + e] = (ok && same) ? w[v][e] : 0u;
       }
     }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = p0 + e;
+      const bool ok = i >= lo && i < hi;
+      valid |= (uint32_t)ok << e;
+      fix |= (uint32_t)ok << e;
+      x[e] = 0u;
+    }
+  }
+  if (fix) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if ((fix >> e) & 1u) x[e] = row[p0 + e];
   }
   return valid;
 }
@@ -699,10 +721,42 @@ __global__ void __launch_bounds__(kSliceThreads) sel_emit(SelArgs a) {
   }
 }
 
-// First-digit histogram fused with the max filter: each slice stages its
-// raw scores with a halo of h positions on either side (clipped to the
-// candidate range [lo, hi)), writes the pooled scores of its positions, and
-// adds the first digits of its candidates to the group's global histogram
+// ---------------------------------------------------------------------------
+// Layer-end selection of one KV-head row (hg = 1) straight from the raw
+// scores, in three launches (plus the gather):
+//
+//   sel_pool_hist  the max filter, fused with the histogram of a 12-bit
+//                  first digit (bits 30..19): each slice stages its raw
+//                  scores with a halo, writes the pooled scores and adds its
+//                  digits to the row's global histogram;
+//   le_cand        every slice settles the first digit from that histogram,
+//                  counts its scores above the digit's bin and compacts the
+//                  ones inside it (about 1-2% of a row) in position order;
+//   le_emit        every slice reads its row's compacted scores (into
+//                  registers, or LDS when a slice holds more than its threads
+//                  take) and settles the other 19 bits there (10 + 9, or a
+//                  direct ranking when at most 64 candidates share the first
+//                  22) and the tie cut -- the same result in every workgroup
+//                  of the row, with no grid-wide step -- then takes its output
+//                  offset from the per-slice counts and writes its picks;
+//                  slice 0 also writes the sinks and the window.
+//
+// The kept set and its order are those of the generic sliced select above:
+// the budget largest scores by (score desc, position asc), ascending.
+// ---------------------------------------------------------------------------
+constexpr int kLeD1Bits = 12, kLeD1Bins = 1 << kLeD1Bits, kLeD1Shift = 31 - kLeD1Bits;
+constexpr int kLeD2Bits = 10, kLeD2Bins = 1 << kLeD2Bits, kLeD2Shift = kLeD1Shift - kLeD2Bits;
+constexpr int kLeD3Bins = 1 << kLeD2Shift;
+constexpr uint32_t kLeFullMask = 0x7fffffffu;
+// Compacted scores a row may hold in le_emit's LDS (more are read from
+// global memory on every pass instead: correct, slower), and the slices of
+// a row whose counters le_emit keeps in LDS.
+constexpr int kLeCandCap = 8192;
+constexpr int kLeMaxSlices = 1024;
+
+// Each slice stages its raw scores with a halo of h positions on either side
+// (clipped to the candidate range [lo, hi)), writes the pooled scores of its
+// positions, and adds their first digits to the row's global histogram
 // (zeroed earlier on the stream).  The first and last slices of a row also
 // write the zeros of the non-candidate positions [0, lo) and [hi, S).
 constexpr int kMaxPoolHalo = 64;
@@ -727,16 +781,30 @@ constexpr int kPoolThreads = 1024;
 __global__ void __launch_bounds__(kPoolThreads) sel_pool_hist(SelArgs a, const float* raw,
                                                               float* pooled, int ph) {
   constexpr int NT = kPoolThreads, PER = kSlice / kPoolThreads;
-  __shared__ uint32_t hist[kD1Bins];
+  __shared__ uint32_t hist[kLeD1Bins];
   __shared__ float sv[kSlice + 2 * kMaxPoolHalo];
   const int grp = blockIdx.y, tid = threadIdx.x;
   const SliceAt at = slice_at(a, grp, blockIdx.x);
-  for (int i = tid; i < kD1Bins; i += NT) hist[i] = 0u;
+  for (int i = tid; i < kLeD1Bins; i += NT) hist[i] = 0u;
   const size_t rbase = (size_t)at.row * a.S;
   const int base = slice_base(a, at.row) + at.sl * kSlice;
-  for (int i = tid; i < kSlice + 2 * ph; i += NT) {
-    const int pos = base - ph + i;
-    sv[i] = (pos >= a.lo && pos < a.hi) ? raw[rbase + pos] : -INFINITY;
+  {
+    // Every load issued before the first is used: positions clamped into
+    // the candidate range (always a valid address), out-of-range ones
+    // replaced after the load.
+    constexpr int NS = (kSlice + 2 * kMaxPoolHalo + NT - 1) / NT;
+    float r[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int pos = base - ph + j * NT + tid;
+      r[j] = raw[rbase + min(max(pos, a.lo), a.hi - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int i = j * NT + tid;
+      const int pos = base - ph + i;
+      if (i < kSlice + 2 * ph) sv[i] = (pos >= a.lo && pos < a.hi) ? r[j] : -INFINITY;
+    }
   }
   __syncthreads();
   // Position base + j*NT + tid per step j: consecutive lanes read
@@ -758,7 +826,7 @@ __global__ void __launch_bounds__(kPoolThreads) sel_pool_hist(SelArgs a, const f
         for (int t = 1; t <= 2 * ph; ++t) m = fmaxf(m, w[t]);
       }
       pooled[rbase + pos] = m;
-      bin = (__float_as_uint(m) >> kD1Shift) & (uint32_t)(kD1Bins - 1);
+      bin = (__float_as_uint(m) >> kLeD1Shift) & (uint32_t)(kLeD1Bins - 1);
     }
     hist_add_lane_runs(hist, bin);
   }
@@ -767,9 +835,386 @@ __global__ void __launch_bounds__(kPoolThreads) sel_pool_hist(SelArgs a, const f
   if (at.sl == a.ns - 1)
     for (int pos = a.hi + tid; pos < a.S; pos += NT) pooled[rbase + pos] = 0.f;
   __syncthreads();
-  uint32_t* g = a.hist1 + (size_t)grp * kD1Bins;
-  for (int i = tid; i < kD1Bins; i += NT)
+  uint32_t* g = a.hist1 + (size_t)grp * kLeD1Bins;
+  for (int i = tid; i < kLeD1Bins; i += NT)
     if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__global__ void __launch_bounds__(kSliceThreads) le_cand(SelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kLeD1Bins];
+  __shared__ uint32_t wsum[kSliceThreads / 64];
+  __shared__ uint32_t pick[3];
+  const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)grp * a.S;
+  const int i0 = slice_base(a, grp) + sg * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  {
+    constexpr int NV = kLeD1Bins / (4 * kSliceThreads);
+    const u32x4_t* g1 = (const u32x4_t*)(a.hist1 + (size_t)grp * kLeD1Bins);
+    u32x4_t hv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) hv[j] = g1[j * kSliceThreads + tid];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ((u32x4_t*)h1)[j * kSliceThreads + tid] = hv[j];
+  }
+  __syncthreads();
+  block_find_digit<kLeD1Bins>(h1, (uint32_t)a.budget, pick);
+  const uint32_t d1 = pick[0], rem = (uint32_t)a.budget - pick[1];
+  const bool whole = rem == pick[2];
+  uint32_t gt = 0u, in = 0u;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool ok = (valid >> e) & 1u;
+    const uint32_t b = (x[e] >> kLeD1Shift) & (uint32_t)(kLeD1Bins - 1);
+    gt += ok && (b > d1 || (whole && b == d1));
+    in |= (uint32_t)(ok && !whole && b == d1) << e;
+  }
+  uint32_t tot;
+  uint32_t pos = block_exclusive_scan<kSliceThreads>((gt << 16) | __popc(in), &tot, wsum) & 0xffffu;
+  const size_t cbase = ((size_t)grp * a.nst + sg) * kSlice;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if ((in >> e) & 1u) {
+      a.cval[cbase + pos] = x[e];
+      a.cidx[cbase + pos] = i0 + e;
+      ++pos;
+    }
+  }
+  if (tid == 0) {
+    a.gtc[(size_t)grp * a.nst + sg] = tot >> 16;
+    a.candc[(size_t)grp * a.nst + sg] = tot & 0xffffu;
+    if (sg == 0) {
+      uint32_t* pr = a.params + (size_t)grp * 4;
+      pr[0] = d1;
+      pr[1] = rem;
+      pr[2] = whole ? 1u : 0u;
+    }
+  }
+}
+
+// le_emit runs 1024 threads per slice: thread t takes candidates
+// [c*kLeR, (c+1)*kLeR) of slice t / TPS (c = t mod TPS, TPS threads per
+// slice, a power of two), so the row's candidates come straight from their
+// slices' regions into registers, with the counts and this slice's scores in
+// the same round trip.  Thread order is slice order, and slice order with
+// chunk order is position order, so one scan over threads orders the ties.
+// A row with more candidates in one slice than its threads hold takes the
+// general path: the candidates gathered into LDS (or read from global
+// memory on every pass when there are too many), numbered in position order.
+constexpr int kLeEmitThreads = 1024;
+constexpr int kLeR = 8;
+
+__global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log2) {
+  constexpr int NT = kLeEmitThreads, PT = kSlice / NT;
+  static_assert(PT == 4, "four scores of the slice per thread");
+  __shared__ uint32_t lval[kLeCandCap];
+  __shared__ int32_t lidx[kLeCandCap];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kLeD2Bins];
+  __shared__ uint32_t cstart[kLeMaxSlices];
+  __shared__ uint32_t kept[kLeMaxSlices];
+  __shared__ uint32_t wsum[2 * NT / 64];
+  __shared__ uint32_t pick[3];
+  __shared__ uint32_t tval[64];
+  __shared__ int32_t tkey[64];
+  __shared__ uint32_t cut_s, val_s, over_s, tcnt;
+  const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
+  const int ns = a.nst;
+  const int tps = 1 << tps_log2;
+  const int s_t = tid >> tps_log2, c_t = tid & (tps - 1);
+  const bool has_slice = s_t < ns;
+  // One round trip: the row's digit, this thread's slice counts and
+  // candidates, this slice's four scores of this thread.
+  const uint32_t* pr = a.params + (size_t)grp * 4;
+  const uint32_t d1 = pr[0];
+  uint32_t rem = pr[1];
+  const bool whole1 = pr[2] != 0u;
+  const size_t srow = (size_t)grp * ns;
+  const uint32_t cnt_t = has_slice ? a.candc[srow + s_t] : 0u;
+  const uint32_t gt_t = (has_slice && c_t == 0) ? a.gtc[srow + s_t] : 0u;
+  uint32_t cv[kLeR];
+  int32_t ci[kLeR];
+  {
+    const int j0 = min(c_t * kLeR, kSlice - kLeR);
+    const size_t rb = (srow + (has_slice ? s_t : 0)) * kSlice + j0;
+    const u32x4_t* pv = (const u32x4_t*)(a.cval + rb);
+    const u32x4_t* pi = (const u32x4_t*)(a.cidx + rb);
+#pragma unroll
+    for (int h = 0; h < kLeR / 4; ++h) {
+      const u32x4_t w = pv[h], z = pi[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cv[4 * h + e] = w[e];
+        ci[4 * h + e] = (int32_t)z[e];
+      }
+    }
+  }
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)grp * a.S;
+  const int base = slice_base(a, grp);
+  const int i0 = base + sg * kSlice + tid * PT;
+  uint32_t x[PT];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    const int i = i0 + e;
+    valid |= (uint32_t)(i >= a.lo && i < a.hi) << e;
+  }
+  if (valid == 0xfu) {
+    const u32x4_t w = *(const u32x4_t*)(u + i0);
+#pragma unroll
+    for (int e = 0; e < PT; ++e) x[e] = w[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < PT; ++e) x[e] = ((valid >> e) & 1u) ? u[i0 + e] : 0u;
+  }
+  uint32_t prefix = d1 << kLeD1Shift, pmask = (uint32_t)(kLeD1Bins - 1) << kLeD1Shift;
+  // Candidates this thread holds (its chunk of its slice), and whether any
+  // slice has more than its threads hold.
+  const uint32_t j0 = (uint32_t)c_t * kLeR;
+  const uint32_t nmine = cnt_t > j0 ? min(cnt_t - j0, (uint32_t)kLeR) : 0u;
+  if (tid == 0) {
+    cut_s = 0xffffffffu;
+    over_s = 0u;
+    tcnt = 0u;
+  }
+  __syncthreads();
+  if (has_slice && c_t == 0 && cnt_t > (uint32_t)tps * kLeR) over_s = 1u;
+  __syncthreads();
+  // This thread's share of the picks of the slices before this one (the
+  // output offset of this slice is their sum).
+  uint32_t off_part = 0u;
+  if (!whole1 && !over_s) {
+    // Register path.  Second digit (bits 18..9): runs of equal bins among a
+    // thread's consecutive candidates cost one atomic.
+    uint32_t act = (1u << nmine) - 1u;
+    uint32_t bin[kLeR];
+    for (int i = tid; i < kLeD2Bins; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kLeR; ++r) bin[r] = (cv[r] >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1);
+    hist_add_runs(hist, bin, act);
+    __syncthreads();
+    block_find_digit<kLeD2Bins>(hist, rem, pick);
+    rem -= pick[1];
+    prefix |= pick[0] << kLeD2Shift;
+    pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
+    const uint32_t nshare = pick[2];
+    bool whole = rem == nshare;
+    __syncthreads();
+    if (!whole && nshare <= 64u) {
+      // Few candidates share the 22-bit prefix (typically one max-pooled
+      // plateau): rank them directly by (score desc, position asc); the
+      // rem-th gives the exact score and the tie cut.
+#pragma unroll
+      for (int r = 0; r < kLeR; ++r) {
+        if (((act >> r) & 1u) && (cv[r] & pmask) == prefix) {
+          const uint32_t slot = atomicAdd(&tcnt, 1u);
+          tval[slot] = cv[r] & kLeFullMask;
+          tkey[slot] = ci[r];
+        }
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t v = tid < (int)nshare ? tval[tid] : 0u;
+        const int32_t kk = tid < (int)nshare ? tkey[tid] : 0;
+        uint32_t rank = 0u;
+#pragma unroll 8
+        for (uint32_t j = 0; j < nshare; ++j) {
+          const uint32_t vj = tval[j];
+          rank += vj > v || (vj == v && tkey[j] < kk);
+        }
+        if (tid < (int)nshare && rank == rem - 1u) {
+          val_s = v;
+          cut_s = (uint32_t)kk;
+        }
+      }
+      __syncthreads();
+      prefix = val_s;
+      pmask = kLeFullMask;
+    } else if (!whole) {
+      // Last digit (bits 8..0) over the candidates sharing the 22-bit prefix.
+      for (int i = tid; i < kLeD3Bins; i += NT) hist[i] = 0u;
+      __syncthreads();
+      uint32_t act3 = 0u;
+#pragma unroll
+      for (int r = 0; r < kLeR; ++r) {
+        bin[r] = cv[r] & (uint32_t)(kLeD3Bins - 1);
+        act3 |= (uint32_t)(((act >> r) & 1u) && (cv[r] & pmask) == prefix) << r;
+      }
+      hist_add_runs(hist, bin, act3);
+      __syncthreads();
+      block_find_digit<kLeD3Bins>(hist, rem, pick);
+      rem -= pick[1];
+      prefix |= pick[0];
+      pmask = kLeFullMask;
+      whole = rem == pick[2];
+      __syncthreads();
+      if (!whole) {
+        // Tie cut: the position of the rem-th candidate equal to the prefix,
+        // counting in thread order (= position order).
+        uint32_t neq = 0u;
+#pragma unroll
+        for (int r = 0; r < kLeR; ++r)
+          neq += ((act >> r) & 1u) && (cv[r] & kLeFullMask) == prefix;
+        uint32_t tot;
+        uint32_t seen = block_exclusive_scan<NT>(neq, &tot, wsum);
+        if (seen < rem && rem <= seen + neq) {
+#pragma unroll
+          for (int r = 0; r < kLeR; ++r) {
+            if (((act >> r) & 1u) && (cv[r] & kLeFullMask) == prefix && ++seen == rem)
+              cut_s = (uint32_t)ci[r];
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const uint32_t cut = cut_s;
+    if (s_t < sg) {
+      uint32_t nk = gt_t;
+#pragma unroll
+      for (int r = 0; r < kLeR; ++r) {
+        const uint32_t m = cv[r] & pmask;
+        nk += ((act >> r) & 1u) && (m > prefix || (m == prefix && (uint32_t)ci[r] <= cut));
+      }
+      off_part = nk;
+    }
+  } else if (whole1) {
+    off_part = s_t < sg ? gt_t : 0u;
+  } else {
+    // General path: flat numbering of the candidates in position order.
+    static_assert(kLeMaxSlices <= NT, "one slice count per thread");
+    const uint32_t c1 = tid < ns ? a.candc[srow + tid] : 0u;
+    kept[tid] = tid < ns ? a.gtc[srow + tid] : 0u;
+    uint32_t ncand;
+    const uint32_t ex = block_exclusive_scan<NT>(c1, &ncand, wsum);
+    if (tid < ns) cstart[tid] = ex;
+    __syncthreads();
+    const uint32_t* cvg = a.cval + srow * kSlice;
+    const int32_t* cig = a.cidx + srow * kSlice;
+    const bool in_lds = ncand <= (uint32_t)kLeCandCap;
+    if (in_lds) {
+      for (uint32_t k = tid; k < ncand; k += NT) {
+        const int sl = slice_of(cstart, ns, k);
+        const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
+        lval[k] = cvg[at];
+        lidx[k] = cig[at];
+      }
+    }
+    for (int i = tid; i < kLeD2Bins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    auto cand = [&](uint32_t k, uint32_t& v, int32_t& i) {
+      if (in_lds) {
+        v = lval[k];
+        i = lidx[k];
+      } else {
+        const int sl = slice_of(cstart, ns, k);
+        const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
+        v = cvg[at];
+        i = cig[at];
+      }
+    };
+    for (uint32_t k0 = 0; k0 < ncand; k0 += NT) {
+      const uint32_t k = k0 + tid;
+      uint32_t v = 0u;
+      int32_t key;
+      if (k < ncand) cand(k, v, key);
+      hist_add(hist, (v >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1), k < ncand);
+    }
+    __syncthreads();
+    block_find_digit<kLeD2Bins>(hist, rem, pick);
+    rem -= pick[1];
+    prefix |= pick[0] << kLeD2Shift;
+    pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
+    bool whole = rem == pick[2];
+    __syncthreads();
+    if (!whole) {
+      for (int i = tid; i < kLeD3Bins; i += NT) hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t k0 = 0; k0 < ncand; k0 += NT) {
+        const uint32_t k = k0 + tid;
+        uint32_t v = 0u;
+        int32_t key;
+        if (k < ncand) cand(k, v, key);
+        hist_add(hist, v & (uint32_t)(kLeD3Bins - 1), k < ncand && (v & pmask) == prefix);
+      }
+      __syncthreads();
+      block_find_digit<kLeD3Bins>(hist, rem, pick);
+      rem -= pick[1];
+      prefix |= pick[0];
+      pmask = kLeFullMask;
+      whole = rem == pick[2];
+      __syncthreads();
+      if (!whole) {
+        const uint32_t per = (ncand + NT - 1) / NT;
+        const uint32_t k0 = tid * per, k1 = min(ncand, k0 + per);
+        uint32_t neq = 0u;
+        for (uint32_t k = k0; k < k1; ++k) {
+          uint32_t v;
+          int32_t key;
+          cand(k, v, key);
+          neq += (v & kLeFullMask) == prefix;
+        }
+        uint32_t tot;
+        uint32_t seen = block_exclusive_scan<NT>(neq, &tot, wsum);
+        if (seen < rem && rem <= seen + neq) {
+          for (uint32_t k = k0; k < k1; ++k) {
+            uint32_t v;
+            int32_t key;
+            cand(k, v, key);
+            if ((v & kLeFullMask) == prefix && ++seen == rem) {
+              cut_s = (uint32_t)key;
+              break;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const uint32_t cut = cut_s;
+    for (uint32_t k0 = 0; k0 < ncand; k0 += NT) {
+      const uint32_t k = k0 + tid;
+      bool keep = false;
+      int sl = 0;
+      if (k < ncand) {
+        uint32_t v;
+        int32_t key;
+        cand(k, v, key);
+        const uint32_t m = v & pmask;
+        keep = m > prefix || (m == prefix && (uint32_t)key <= cut);
+        sl = (key - base) / kSlice;
+      }
+      hist_add(kept, (uint32_t)sl, keep);
+    }
+    __syncthreads();
+    off_part = tid < sg ? kept[tid] : 0u;
+  }
+  const uint32_t cut = cut_s;
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    const uint32_t m = x[e] & pmask;
+    const bool k = ((valid >> e) & 1u) &&
+                   (m > prefix || (m == prefix && (uint32_t)(i0 + e) <= cut));
+    keep |= (uint32_t)k << e;
+  }
+  uint32_t off, npick;
+  const uint32_t pos0 = block_scan_pair<NT>(off_part, __popc(keep), &off, &npick, wsum);
+  uint32_t pos = pos0 + off;
+  int32_t* row = a.idx + (size_t)grp * a.n_keep;
+  int32_t* out = row + a.n_sink;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    if ((keep >> e) & 1u) {
+      if (pos < (uint32_t)a.budget) out[pos] = i0 + e;
+      ++pos;
+    }
+  }
+  if (sg == 0) {
+    for (int t = tid; t < a.n_sink + a.W; t += NT) {
+      if (t < a.n_sink) row[t] = t;
+      else row[a.n_sink + a.budget + (t - a.n_sink)] = a.S - a.W + (t - a.n_sink);
+    }
+  }
 }
 
 // Arguments of the sliced kernels for one launch sequence.
@@ -836,7 +1281,9 @@ bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p) {
     return o;
   };
   if (p->multi) {
-    p->off_hist = take((size_t)groups * (kD1Bins + kD2Bins) * 4);
+    // both digit histograms of the generic select, or the layer-end
+    // chain's 12-bit first-digit histogram
+    p->off_hist = take((size_t)groups * max(kD1Bins + kD2Bins, kLeD1Bins) * 4);
     p->off_gtc = take((size_t)groups * nst * 4);
     p->off_candc = take((size_t)groups * nst * 4);
     p->off_offs = take((size_t)groups * nst * 4);
@@ -920,13 +1367,13 @@ kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, con
 }
 
 uint32_t* select_hists(const SelectPlan& p, char* ws, size_t* words) {
-  *words = (size_t)p.groups * (kD1Bins + kD2Bins);
+  *words = (size_t)p.groups * kLeD1Bins;
   return (uint32_t*)(ws + p.off_hist);
 }
 
 bool layer_end_fusable(const kvsel_desc& d, const SelectPlan& p, int budget, int pool_kernel) {
   return p.multi && p.hg == 1 && budget > 0 && (pool_kernel - 1) / 2 <= kMaxPoolHalo &&
-         d.n_sink + d.obs_window + budget <= d.seq_len;
+         p.ns <= kLeMaxSlices && d.n_sink + d.obs_window + budget <= d.seq_len;
 }
 
 // The gather runs as its own evenly spread kernel after the emit: copying
@@ -941,10 +1388,10 @@ kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, c
   const dim3 sg(a.nst, p.groups);
   KVSEL_LAUNCH("sel_pool_hist", sel_pool_hist, sg, dim3(kPoolThreads), 0, stream, a, raw, pooled,
                (pool_kernel - 1) / 2);
-  KVSEL_LAUNCH("sel_hist2", sel_hist2, sg, dim3(kSliceThreads), 0, stream, a);
-  KVSEL_LAUNCH("sel_cand", sel_cand, sg, dim3(kSliceThreads), 0, stream, a);
-  KVSEL_LAUNCH("sel_resolve", sel_resolve, dim3(p.groups), dim3(kSelThreads), 0, stream, a);
-  KVSEL_LAUNCH("sel_emit", sel_emit, sg, dim3(kSliceThreads), 0, stream, a);
+  KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  int tps_log2 = 0;
+  while ((2 << tps_log2) * a.nst <= kLeEmitThreads && (2 << tps_log2) * kLeR <= kSlice) ++tps_log2;
+  KVSEL_LAUNCH("le_emit", le_emit, sg, dim3(kLeEmitThreads), 0, stream, a, tps_log2);
   if (hipGetLastError() != hipSuccess) return KVSEL_ERR_DEVICE;
   return launch_compact(d, k, v, idx, a.n_keep, k_out, v_out, stream);
 }

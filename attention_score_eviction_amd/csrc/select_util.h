@@ -42,6 +42,33 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   return before + incl - v;
 }
 
+// Exclusive prefix sum of b over a workgroup of NT threads, and the totals
+// of a and of b over all threads, in one pass: two scans per wave, one exchange through
+// wsum2 (2*NT/64 entries), two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_pair(uint32_t a, uint32_t b, uint32_t* a_total,
+                                                   uint32_t* b_total, uint32_t* wsum2) {
+  constexpr int NWV = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == 63) {
+    wsum2[wave] = ia;
+    wsum2[NWV + wave] = ib;
+  }
+  __syncthreads();
+  uint32_t ta = 0u, tb = 0u, before = 0u;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    ta += wsum2[w];
+    tb += wsum2[NWV + w];
+    before += w < wave ? wsum2[NWV + w] : 0u;
+  }
+  *a_total = ta;
+  *b_total = tb;
+  __syncthreads();
+  return before + ib - b;
+}
+
 // Histogram update: one LDS atomic per counted score.  (Aggregating equal
 // bins across a wave first costs more in cross-lane latency than the atomic
 // conflicts it saves, at every row length measured.)

@@ -302,8 +302,6 @@ kvsel_status kvsel_layer_end_stream(const kvsel_desc* desc, const void* q_obs, c
                                     size_t ws_bytes, void* stream);
 
 /*
- * Kara decode-window compression/*
- * Kara decode-window compression/*
  * Kara decode-window compression (Kara, "Kara: Efficient Reasoning LLM
  * Serving via Sliding-Window KV Cache Compression", Section 3).  A window of
  * `window` recent tokens per (sequence, KV head); its last `buffer` tokens

@@ -4,6 +4,8 @@ exactly the outputs of kvsel_score followed by kvsel_select_compact: raw and
 pooled scores, indices and gathered rows, bit for bit."""
 import dataclasses
 
+import numpy as np
+
 import pytest
 
 import synth
@@ -70,3 +72,86 @@ def test_layer_end_without_score_outputs():
     assert torch.equal(a[0], b[0])
     assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
     assert torch.equal(a[2].view(torch.int16), b[2].view(torch.int16))
+
+
+DEGENERATE = [
+    # every key zero: uniform attention, every candidate has the same score,
+    # so the whole row sits in one bin and the cut is a pure position tie
+    ("zero-keys", L(1, 8, 2, 128, 40000, 32, 7, 3000), 0.0, 51),
+    # keys scaled down: a few distinct values crowded into a handful of bins
+    ("crowded", L(1, 8, 2, 128, 40000, 32, 3, 5000), 1e-3, 52),
+    ("crowded-b1", L(1, 8, 2, 128, 30000, 32, 1, 1), 1e-3, 53),
+    # more slices per row than the 128K workload, ragged tail
+    ("long-ragged", L(1, 8, 2, 64, 200003, 64, 7, 4096, structure="heavy"), 1.0, 54),
+]
+
+
+@pytest.mark.parametrize("name,spec,kscale,seed", DEGENERATE, ids=[c[0] for c in DEGENERATE])
+def test_layer_end_degenerate_scores(name, spec, kscale, seed):
+    """Rows whose scores crowd into few bins (the compacted boundary bin larger
+    than the fused selection keeps in LDS) and all-equal rows: the fused path
+    still equals the composed calls bit for bit."""
+    import attention_score_eviction_amd as kvsel
+    x = synth.make_layer(spec, seed)
+    if kscale != 1.0:
+        k32 = synth.bf16_bits_to_f32(x["k"]) * np.float32(kscale)
+        x["k"] = synth.f32_to_bf16_bits(k32)
+    q, k, v = (dev_tensor(x[n], spec.dtype) for n in ("q", "k", "v"))
+    print(f"case layer_end degenerate {name} S={spec.seq_len} B={spec.budget}", flush=True)
+    pooled, raw = kvsel.score(q, k, pool_kernel=spec.pool_kernel)
+    idx, kh, vh = kvsel.select_compact(pooled, k, v, spec.budget, obs_window=spec.obs_window,
+                                       n_q_heads=spec.n_q_heads)
+    idx2, kh2, vh2, raw2, pooled2 = kvsel.layer_end(q, k, v, budget=spec.budget,
+                                                    pool_kernel=spec.pool_kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(raw2, raw)
+    assert torch.equal(pooled2, pooled)
+    assert torch.equal(idx2, idx)
+    assert torch.equal(kh2.view(torch.int16), kh.view(torch.int16))
+    assert torch.equal(vh2.view(torch.int16), vh.view(torch.int16))
+    # a head whose candidates all tie keeps the first `budget` positions
+    S, W = spec.seq_len, spec.obs_window
+    pc = pooled2.cpu().numpy()[0, :, :S - W]
+    got = idx2.cpu().numpy()[0, :, :spec.budget]
+    ties = [h for h in range(spec.n_kv_heads) if (pc[h] == pc[h, 0]).all()]
+    for h in ties:
+        assert (got[h] == np.arange(spec.budget)).all()
+    print(f"heads with all candidates tied: {ties}", flush=True)
+
+
+@pytest.mark.parametrize("ndup,budget", [(300, 150), (40, 20), (40, 40)])
+def test_layer_end_duplicate_keys_tie_across_slices(ndup, budget):
+    """Every key zero except ndup identical keys at scattered positions, which
+    take the top scores, all exactly equal (no pooling): the budget cuts
+    inside that tie, so the picks are its first `budget` positions.  More than
+    64 tied candidates settle the last digit and the cut by scan, up to 64 by
+    direct ranking, and a budget equal to the tie keeps its bin whole."""
+    import attention_score_eviction_amd as kvsel
+    spec = L(1, 8, 2, 128, 40000, 32, 1, budget)
+    x = synth.make_layer(spec, 61)
+    rng = np.random.default_rng(62)
+    S, W, G = spec.seq_len, spec.obs_window, spec.group
+    pos = np.sort(rng.choice(S - W, size=ndup, replace=False))
+    q32 = synth.bf16_bits_to_f32(x["q"])
+    k32 = np.zeros_like(synth.bf16_bits_to_f32(x["k"]))
+    for hk in range(spec.n_kv_heads):
+        d = q32[0, hk * G:(hk + 1) * G].reshape(-1, spec.head_dim).mean(axis=0)
+        k32[0, hk, pos] = (d / np.linalg.norm(d) * 40.0).astype(np.float32)
+    x["k"] = synth.f32_to_bf16_bits(k32)
+    q, k, v = (dev_tensor(x[n], spec.dtype) for n in ("q", "k", "v"))
+    print(f"case layer_end duplicate keys ndup={ndup} B={budget}", flush=True)
+    pooled, raw = kvsel.score(q, k, pool_kernel=1)
+    idx, kh, vh = kvsel.select_compact(pooled, k, v, budget, obs_window=W,
+                                       n_q_heads=spec.n_q_heads)
+    idx2, kh2, vh2, raw2, pooled2 = kvsel.layer_end(q, k, v, budget=budget, pool_kernel=1)
+    torch.cuda.synchronize()
+    assert torch.equal(pooled2, pooled)
+    assert torch.equal(idx2, idx)
+    assert torch.equal(kh2.view(torch.int16), kh.view(torch.int16))
+    assert torch.equal(vh2.view(torch.int16), vh.view(torch.int16))
+    p = pooled2.cpu().numpy()[0]
+    got = idx2.cpu().numpy()[0, :, :budget]
+    for hk in range(spec.n_kv_heads):
+        vals = p[hk, pos]
+        assert (vals == vals[0]).all() and vals[0] > np.delete(p[hk, :S - W], pos).max()
+        assert (got[hk] == pos[:budget]).all()
