@@ -182,6 +182,9 @@ def _on(stream):
     those blocks after the kernels enqueued there."""
     if stream is None:
         return nullcontext()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if handle == torch.cuda.current_stream().cuda_stream:
+        return nullcontext()          # already the current stream
     if not isinstance(stream, torch.cuda.Stream):
         stream = torch.cuda.ExternalStream(int(stream))
     return torch.cuda.stream(stream)
@@ -375,7 +378,11 @@ def layer_end(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *
     """kvsel_layer_end: TideKV's LayerEndCompress in one call.  Returns
     (idx, k_hat, v_hat, raw, pooled); raw and pooled are None when
     want_scores is False and none were given (then kept in the workspace)."""
-    with _on(stream):
+    # the stream context only when something is allocated here (a caller
+    # that passes every buffer, like the layer-major driver, pays nothing)
+    alloc = (want_scores and (raw is None or pooled is None)) or idx is None or k_out is None \
+        or (v is not None and v_out is None) or workspace is None
+    with (_on(stream) if alloc else nullcontext()):
         d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
         Bt, Hkv, S, D = k.shape
         n_keep = budget + n_sink + q_obs.shape[2]
@@ -413,7 +420,8 @@ def layer_end_stream(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Ten
                      workspace: Optional[torch.Tensor] = None, stream=None):
     """kvsel_layer_end_stream: the layer-end step with the streaming top-k of
     pass 2 (no per-key score vector).  Returns (idx, k_hat, v_hat)."""
-    with _on(stream):
+    alloc = idx is None or k_out is None or (v is not None and v_out is None) or workspace is None
+    with (_on(stream) if alloc else nullcontext()):
         d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
         Bt, Hkv, S, D = k.shape
         n_keep = budget + n_sink + q_obs.shape[2]
