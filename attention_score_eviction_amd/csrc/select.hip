@@ -840,6 +840,33 @@ __global__ void __launch_bounds__(kPoolThreads) sel_pool_hist(SelArgs a, const f
     if (hist[i]) atomicAdd(&g[i], hist[i]);
 }
 
+// For kvsel_select over long rows (scores already pooled): the first-digit
+// histogram zeroed, then built from the pooled scores; le_cand and le_emit
+// follow as in the layer-end path.
+__global__ void __launch_bounds__(256) le_init(SelArgs a) {
+  uint32_t* h1 = a.hist1 + (size_t)blockIdx.x * kLeD1Bins;
+  for (int i = threadIdx.x; i < kLeD1Bins; i += 256) h1[i] = 0u;
+}
+
+__global__ void __launch_bounds__(kSliceThreads) le_hist(SelArgs a) {
+  __shared__ uint32_t hist[kLeD1Bins];
+  const int grp = blockIdx.y, tid = threadIdx.x;
+  for (int i = tid; i < kLeD1Bins; i += kSliceThreads) hist[i] = 0u;
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)grp * a.S;
+  const int i0 = slice_base(a, grp) + blockIdx.x * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  uint32_t bin[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) bin[e] = (x[e] >> kLeD1Shift) & (uint32_t)(kLeD1Bins - 1);
+  __syncthreads();
+  hist_add_runs(hist, bin, valid);
+  __syncthreads();
+  uint32_t* g = a.hist1 + (size_t)grp * kLeD1Bins;
+  for (int i = tid; i < kLeD1Bins; i += kSliceThreads)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
 __global__ void __launch_bounds__(kSliceThreads) le_cand(SelArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t h1[kLeD1Bins];
   __shared__ uint32_t wsum[kSliceThreads / 64];
@@ -1217,6 +1244,14 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
   }
 }
 
+// Threads per slice in le_emit: the largest power of two with every slice
+// of a row covered by the workgroup and a slice's region not overrun.
+int le_tps_log2(int nst) {
+  int t = 0;
+  while ((2 << t) * nst <= kLeEmitThreads && (2 << t) * kLeR <= kSlice) ++t;
+  return t;
+}
+
 // Arguments of the sliced kernels for one launch sequence.
 SelArgs sel_args(const kvsel_desc& d, const SelectPlan& p, const float* pooled, int budget,
                  int32_t* idx, int32_t* head_off, char* ws) {
@@ -1320,6 +1355,14 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   }
   SelArgs a = sel_args(d, p, pooled, budget, idx, head_off, ws);
   const dim3 sg(a.nst, groups);
+  if (hg == 1 && a.nst <= kLeMaxSlices) {
+    // one KV-head row per group: the three-step select of the layer-end path
+    KVSEL_LAUNCH("le_init", le_init, dim3(groups), dim3(256), 0, stream, a);
+    KVSEL_LAUNCH("le_hist", le_hist, sg, dim3(kSliceThreads), 0, stream, a);
+    KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
+    KVSEL_LAUNCH("le_emit", le_emit, sg, dim3(kLeEmitThreads), 0, stream, a, le_tps_log2(a.nst));
+    return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
+  }
   KVSEL_LAUNCH("sel_init", sel_init, dim3(groups), dim3(256), 0, stream, a);
   KVSEL_LAUNCH("sel_hist", sel_hist, sg, dim3(kSliceThreads), 0, stream, a);
   KVSEL_LAUNCH("sel_hist2", sel_hist2, sg, dim3(kSliceThreads), 0, stream, a);
@@ -1389,9 +1432,7 @@ kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, c
   KVSEL_LAUNCH("sel_pool_hist", sel_pool_hist, sg, dim3(kPoolThreads), 0, stream, a, raw, pooled,
                (pool_kernel - 1) / 2);
   KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
-  int tps_log2 = 0;
-  while ((2 << tps_log2) * a.nst <= kLeEmitThreads && (2 << tps_log2) * kLeR <= kSlice) ++tps_log2;
-  KVSEL_LAUNCH("le_emit", le_emit, sg, dim3(kLeEmitThreads), 0, stream, a, tps_log2);
+  KVSEL_LAUNCH("le_emit", le_emit, sg, dim3(kLeEmitThreads), 0, stream, a, le_tps_log2(a.nst));
   if (hipGetLastError() != hipSuccess) return KVSEL_ERR_DEVICE;
   return launch_compact(d, k, v, idx, a.n_keep, k_out, v_out, stream);
 }

@@ -5,9 +5,9 @@ pooled scores, indices and gathered rows, bit for bit."""
 import dataclasses
 
 import numpy as np
-
 import pytest
 
+import oracle
 import synth
 from helpers import dev_tensor
 
@@ -109,8 +109,11 @@ def test_layer_end_degenerate_scores(name, spec, kscale, seed):
     assert torch.equal(idx2, idx)
     assert torch.equal(kh2.view(torch.int16), kh.view(torch.int16))
     assert torch.equal(vh2.view(torch.int16), vh.view(torch.int16))
-    # a head whose candidates all tie keeps the first `budget` positions
+    # the exact (score desc, position asc) selection on these fp32 scores
     S, W = spec.seq_len, spec.obs_window
+    ref = oracle.select(pooled2.cpu().numpy().astype(np.float64), spec.budget, 0, W)
+    assert (idx2.cpu().numpy() == ref).all()
+    # a head whose candidates all tie keeps the first `budget` positions
     pc = pooled2.cpu().numpy()[0, :, :S - W]
     got = idx2.cpu().numpy()[0, :, :spec.budget]
     ties = [h for h in range(spec.n_kv_heads) if (pc[h] == pc[h, 0]).all()]
@@ -149,6 +152,8 @@ def test_layer_end_duplicate_keys_tie_across_slices(ndup, budget):
     assert torch.equal(idx2, idx)
     assert torch.equal(kh2.view(torch.int16), kh.view(torch.int16))
     assert torch.equal(vh2.view(torch.int16), vh.view(torch.int16))
+    ref = oracle.select(pooled2.cpu().numpy().astype(np.float64), budget, 0, W)
+    assert (idx2.cpu().numpy() == ref).all()
     p = pooled2.cpu().numpy()[0]
     got = idx2.cpu().numpy()[0, :, :budget]
     for hk in range(spec.n_kv_heads):
