@@ -19,7 +19,9 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import Desc, _dtype_code, layer_end, layer_end_workspace_bytes
+import ctypes
+
+from . import Desc, _check, _dtype_code, _ptr, _stream, layer_end, layer_end_workspace_bytes, lib
 
 
 @dataclass
@@ -100,10 +102,24 @@ class LayerMajorDriver:
 
     def layer_end(self, cache: LayerCache, stream=None) -> LayerCache:
         """LayerEndCompress of the active layer into `cache` (score ->
-        max-pool -> top-budget + window -> gather), enqueued on `stream`."""
-        layer_end(self.q, self.k, self.v, budget=cache.budget, pool_kernel=self.pool_kernel,
-                  n_sink=self.n_sink, raw=self.raw, pooled=self.pooled, idx=cache.idx,
-                  k_out=cache.k_hat, v_out=cache.v_hat, workspace=self.ws, stream=stream)
+        max-pool -> top-budget + window -> gather), enqueued on `stream`.
+        The call's arguments are marshalled once per cache and reused (every
+        buffer is the driver's or the cache's), so a call costs one ctypes
+        call on the host."""
+        call = getattr(cache, "_call", None)
+        if call is None:
+            # checks of the generic binding, once: shapes and dtypes
+            layer_end(self.q, self.k, self.v, budget=cache.budget, pool_kernel=self.pool_kernel,
+                      n_sink=self.n_sink, raw=self.raw, pooled=self.pooled, idx=cache.idx,
+                      k_out=cache.k_hat, v_out=cache.v_hat, workspace=self.ws, stream=stream)
+            args = (ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                    int(cache.budget), int(self.pool_kernel), _ptr(self.raw), _ptr(self.pooled),
+                    _ptr(cache.idx), _ptr(cache.k_hat), _ptr(cache.v_hat), _ptr(self.ws),
+                    self.ws.numel())
+            fn = lib().kvsel_layer_end
+            cache._call = lambda s: _check(fn(*args, s), "kvsel_layer_end")
+            return cache
+        call(_stream(stream))
         return cache
 
     def commit(self, budget: int, stream=None) -> LayerCache:

@@ -547,6 +547,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen128k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ingest-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
@@ -609,6 +611,21 @@ def main() -> int:
                                       "kvsel_layer_end": L.drv.ws.numel()}
     elif not adaptive:
         us_call["kvsel_layer_end"] = event_time_us(torch, stream, lambda: L.step(stream), reps)
+    if args.graph and not adaptive:
+        # the step captured once in a HIP graph and replayed (host launch cost
+        # removed; the same kernels on the same buffers)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            L.step(None)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            L.step(None)
+        torch.cuda.synchronize()
+        us_call["step_graph_replay"] = event_time_us(torch, stream, g.replay, reps)
     kt = kernel_times(kvsel, torch, lambda: L.step(stream), reps)
     dispatches = sum(n for _, n in kt.values())
     dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
