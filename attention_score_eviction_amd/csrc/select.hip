@@ -845,15 +845,18 @@ __global__ void __launch_bounds__(kPoolThreads) sel_pool_hist(SelArgs a, const f
 // follow as in the layer-end path.
 __global__ void __launch_bounds__(256) le_init(SelArgs a) {
   uint32_t* h1 = a.hist1 + (size_t)blockIdx.x * kLeD1Bins;
+  uint32_t* h2 = a.hist1 + (size_t)gridDim.x * kLeD1Bins + (size_t)blockIdx.x * kLeD2Bins;
   for (int i = threadIdx.x; i < kLeD1Bins; i += 256) h1[i] = 0u;
+  for (int i = threadIdx.x; i < kLeD2Bins; i += 256) h2[i] = 0u;
 }
 
 __global__ void __launch_bounds__(kSliceThreads) le_hist(SelArgs a) {
   __shared__ uint32_t hist[kLeD1Bins];
   const int grp = blockIdx.y, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, blockIdx.x);
   for (int i = tid; i < kLeD1Bins; i += kSliceThreads) hist[i] = 0u;
-  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)grp * a.S;
-  const int i0 = slice_base(a, grp) + blockIdx.x * kSlice + tid * kPerThread;
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
   uint32_t x[kPerThread];
   const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
   uint32_t bin[kPerThread];
@@ -913,9 +916,134 @@ __global__ void __launch_bounds__(kSliceThreads) le_cand(SelArgs a) {
     a.candc[(size_t)grp * a.nst + sg] = tot & 0xffffu;
     if (sg == 0) {
       uint32_t* pr = a.params + (size_t)grp * 4;
-      pr[0] = d1;
+      pr[0] = d1 << kLeD1Shift;
       pr[1] = rem;
       pr[2] = whole ? 1u : 0u;
+      pr[3] = kLeD1Bits;
+    }
+  }
+}
+
+// Head groups (a selection over all KV heads of a sequence: a group holds
+// hg times the candidates, too many in one 12-bit bin): the second digit is
+// settled from global histograms before the compaction, so le_emit starts
+// from a 22-bit prefix.  lg_hist2: every slice settles the first digit and
+// adds the bits 18..9 of its scores in that bin to the group's second-digit
+// histogram.  lg_cand: every slice settles both digits, counts its scores
+// above the 22-bit prefix and compacts the ones sharing it with their keys
+// h*S + position, in position order.
+__device__ __forceinline__ uint32_t* le_hist2_of(const SelArgs& a, int grp) {
+  return a.hist1 + (size_t)gridDim.y * kLeD1Bins + (size_t)grp * kLeD2Bins;
+}
+
+__global__ void __launch_bounds__(kSliceThreads) lg_hist2(SelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kLeD1Bins];
+  __shared__ uint32_t hist[kLeD2Bins];
+  __shared__ uint32_t pick[3];
+  const int grp = blockIdx.y, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, blockIdx.x);
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  {
+    constexpr int NV = kLeD1Bins / (4 * kSliceThreads);
+    const u32x4_t* g1 = (const u32x4_t*)(a.hist1 + (size_t)grp * kLeD1Bins);
+    u32x4_t hv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) hv[j] = g1[j * kSliceThreads + tid];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ((u32x4_t*)h1)[j * kSliceThreads + tid] = hv[j];
+  }
+  for (int i = tid; i < kLeD2Bins; i += kSliceThreads) hist[i] = 0u;
+  __syncthreads();
+  block_find_digit<kLeD1Bins>(h1, (uint32_t)a.budget, pick);
+  const uint32_t d1 = pick[0];
+  if ((uint32_t)a.budget - pick[1] == pick[2]) return;   // d1's bin kept whole
+  uint32_t bin[kPerThread];
+  uint32_t act = 0u;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    bin[e] = (x[e] >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1);
+    act |= (uint32_t)(((valid >> e) & 1u) &&
+                      ((x[e] >> kLeD1Shift) & (uint32_t)(kLeD1Bins - 1)) == d1) << e;
+  }
+  hist_add_runs(hist, bin, act);
+  __syncthreads();
+  uint32_t* g2 = le_hist2_of(a, grp);
+  for (int i = tid; i < kLeD2Bins; i += kSliceThreads)
+    if (hist[i]) atomicAdd(&g2[i], hist[i]);
+}
+
+__global__ void __launch_bounds__(kSliceThreads) lg_cand(SelArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t h1[kLeD1Bins];
+  __shared__ __attribute__((aligned(16))) uint32_t h2[kLeD2Bins];
+  __shared__ uint32_t wsum[kSliceThreads / 64];
+  __shared__ uint32_t pick[3];
+  const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
+  const SliceAt at = slice_at(a, grp, sg);
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * kPerThread;
+  uint32_t x[kPerThread];
+  const uint32_t valid = load16(u, i0, a.lo, a.hi, x);
+  {
+    constexpr int NV = kLeD1Bins / (4 * kSliceThreads);
+    const u32x4_t* g1 = (const u32x4_t*)(a.hist1 + (size_t)grp * kLeD1Bins);
+    const u32x4_t* g2 = (const u32x4_t*)le_hist2_of(a, grp);
+    u32x4_t hv[NV], hw;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) hv[j] = g1[j * kSliceThreads + tid];
+    hw = g2[tid];   // kLeD2Bins = 4 * kSliceThreads
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ((u32x4_t*)h1)[j * kSliceThreads + tid] = hv[j];
+    ((u32x4_t*)h2)[tid] = hw;
+  }
+  __syncthreads();
+  block_find_digit<kLeD1Bins>(h1, (uint32_t)a.budget, pick);
+  uint32_t rem = (uint32_t)a.budget - pick[1];
+  uint32_t prefix = pick[0] << kLeD1Shift;
+  uint32_t pmask = (uint32_t)(kLeD1Bins - 1) << kLeD1Shift;
+  bool whole = rem == pick[2];
+  int bits = kLeD1Bits;
+  __syncthreads();
+  if (!whole) {
+    block_find_digit<kLeD2Bins>(h2, rem, pick);
+    rem -= pick[1];
+    prefix |= pick[0] << kLeD2Shift;
+    pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
+    whole = rem == pick[2];
+    bits = kLeD1Bits + kLeD2Bits;
+    __syncthreads();
+  }
+  const uint32_t key0 = (uint32_t)(at.h * a.S + i0);
+  uint32_t gt = 0u, in = 0u;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool ok = (valid >> e) & 1u;
+    const uint32_t m = x[e] & pmask;
+    gt += ok && (m > prefix || (whole && m == prefix));
+    in |= (uint32_t)(ok && !whole && m == prefix) << e;
+  }
+  uint32_t tot;
+  uint32_t pos = block_exclusive_scan<kSliceThreads>((gt << 16) | __popc(in), &tot, wsum) & 0xffffu;
+  const size_t cbase = ((size_t)grp * a.nst + sg) * kSlice;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    if ((in >> e) & 1u) {
+      a.cval[cbase + pos] = x[e];
+      a.cidx[cbase + pos] = (int32_t)(key0 + e);
+      ++pos;
+    }
+  }
+  if (tid == 0) {
+    a.gtc[(size_t)grp * a.nst + sg] = tot >> 16;
+    a.candc[(size_t)grp * a.nst + sg] = tot & 0xffffu;
+    if (sg == 0) {
+      uint32_t* pr = a.params + (size_t)grp * 4;
+      pr[0] = prefix;
+      pr[1] = rem;
+      pr[2] = whole ? 1u : 0u;
+      pr[3] = (uint32_t)bits;
     }
   }
 }
@@ -945,6 +1073,7 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
   __shared__ uint32_t tval[64];
   __shared__ int32_t tkey[64];
   __shared__ uint32_t cut_s, val_s, over_s, tcnt;
+  __shared__ uint32_t pb[kMaxWgHeads + 1];
   const int grp = blockIdx.y, sg = blockIdx.x, tid = threadIdx.x;
   const int ns = a.nst;
   const int tps = 1 << tps_log2;
@@ -953,9 +1082,12 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
   // One round trip: the row's digit, this thread's slice counts and
   // candidates, this slice's four scores of this thread.
   const uint32_t* pr = a.params + (size_t)grp * 4;
-  const uint32_t d1 = pr[0];
+  uint32_t prefix = pr[0];
   uint32_t rem = pr[1];
-  const bool whole1 = pr[2] != 0u;
+  const bool whole1 = pr[2] != 0u;       // the settled prefix's bin is kept whole
+  const bool two = pr[3] != (uint32_t)kLeD1Bits;   // 22 bits settled (head groups)
+  uint32_t pmask = two ? ((1u << (kLeD1Bits + kLeD2Bits)) - 1u) << kLeD2Shift
+                       : (uint32_t)(kLeD1Bins - 1) << kLeD1Shift;
   const size_t srow = (size_t)grp * ns;
   const uint32_t cnt_t = has_slice ? a.candc[srow + s_t] : 0u;
   const uint32_t gt_t = (has_slice && c_t == 0) ? a.gtc[srow + s_t] : 0u;
@@ -976,9 +1108,10 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
       }
     }
   }
-  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)grp * a.S;
-  const int base = slice_base(a, grp);
-  const int i0 = base + sg * kSlice + tid * PT;
+  const SliceAt at = slice_at(a, grp, sg);
+  const uint32_t* u = (const uint32_t*)a.pooled + (size_t)at.row * a.S;
+  const int i0 = slice_base(a, at.row) + at.sl * kSlice + tid * PT;
+  const uint32_t key0 = (uint32_t)(at.h * a.S + i0);
   uint32_t x[PT];
   uint32_t valid = 0u;
 #pragma unroll
@@ -994,7 +1127,6 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
 #pragma unroll
     for (int e = 0; e < PT; ++e) x[e] = ((valid >> e) & 1u) ? u[i0 + e] : 0u;
   }
-  uint32_t prefix = d1 << kLeD1Shift, pmask = (uint32_t)(kLeD1Bins - 1) << kLeD1Shift;
   // Candidates this thread holds (its chunk of its slice), and whether any
   // slice has more than its threads hold.
   const uint32_t j0 = (uint32_t)c_t * kLeR;
@@ -1011,23 +1143,33 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
   // output offset of this slice is their sum).
   uint32_t off_part = 0u;
   if (!whole1 && !over_s) {
-    // Register path.  Second digit (bits 18..9): runs of equal bins among a
-    // thread's consecutive candidates cost one atomic.
+    // Register path.  Second digit (bits 18..9) unless already settled:
+    // runs of equal bins among a thread's consecutive candidates cost one
+    // atomic.
     uint32_t act = (1u << nmine) - 1u;
     uint32_t bin[kLeR];
-    for (int i = tid; i < kLeD2Bins; i += NT) hist[i] = 0u;
-    __syncthreads();
+    uint32_t nshare;
+    bool whole;
+    if (!two) {
+      for (int i = tid; i < kLeD2Bins; i += NT) hist[i] = 0u;
+      __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kLeR; ++r) bin[r] = (cv[r] >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1);
-    hist_add_runs(hist, bin, act);
-    __syncthreads();
-    block_find_digit<kLeD2Bins>(hist, rem, pick);
-    rem -= pick[1];
-    prefix |= pick[0] << kLeD2Shift;
-    pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
-    const uint32_t nshare = pick[2];
-    bool whole = rem == nshare;
-    __syncthreads();
+      for (int r = 0; r < kLeR; ++r) bin[r] = (cv[r] >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1);
+      hist_add_runs(hist, bin, act);
+      __syncthreads();
+      block_find_digit<kLeD2Bins>(hist, rem, pick);
+      rem -= pick[1];
+      prefix |= pick[0] << kLeD2Shift;
+      pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
+      nshare = pick[2];
+      whole = rem == nshare;
+      __syncthreads();
+    } else {
+      uint32_t tot;
+      block_exclusive_scan<NT>(nmine, &tot, wsum);
+      nshare = tot;
+      whole = rem == nshare;
+    }
     if (!whole && nshare <= 64u) {
       // Few candidates share the 22-bit prefix (typically one max-pooled
       // plateau): rank them directly by (score desc, position asc); the
@@ -1122,9 +1264,9 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
     if (in_lds) {
       for (uint32_t k = tid; k < ncand; k += NT) {
         const int sl = slice_of(cstart, ns, k);
-        const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
-        lval[k] = cvg[at];
-        lidx[k] = cig[at];
+        const size_t o = (size_t)sl * kSlice + (k - cstart[sl]);
+        lval[k] = cvg[o];
+        lidx[k] = cig[o];
       }
     }
     for (int i = tid; i < kLeD2Bins; i += NT) hist[i] = 0u;
@@ -1135,25 +1277,28 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
         i = lidx[k];
       } else {
         const int sl = slice_of(cstart, ns, k);
-        const size_t at = (size_t)sl * kSlice + (k - cstart[sl]);
-        v = cvg[at];
-        i = cig[at];
+        const size_t o = (size_t)sl * kSlice + (k - cstart[sl]);
+        v = cvg[o];
+        i = cig[o];
       }
     };
-    for (uint32_t k0 = 0; k0 < ncand; k0 += NT) {
-      const uint32_t k = k0 + tid;
-      uint32_t v = 0u;
-      int32_t key;
-      if (k < ncand) cand(k, v, key);
-      hist_add(hist, (v >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1), k < ncand);
+    bool whole = false;
+    if (!two) {
+      for (uint32_t k0 = 0; k0 < ncand; k0 += NT) {
+        const uint32_t k = k0 + tid;
+        uint32_t v = 0u;
+        int32_t key;
+        if (k < ncand) cand(k, v, key);
+        hist_add(hist, (v >> kLeD2Shift) & (uint32_t)(kLeD2Bins - 1), k < ncand);
+      }
+      __syncthreads();
+      block_find_digit<kLeD2Bins>(hist, rem, pick);
+      rem -= pick[1];
+      prefix |= pick[0] << kLeD2Shift;
+      pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
+      whole = rem == pick[2];
+      __syncthreads();
     }
-    __syncthreads();
-    block_find_digit<kLeD2Bins>(hist, rem, pick);
-    rem -= pick[1];
-    prefix |= pick[0] << kLeD2Shift;
-    pmask |= (uint32_t)(kLeD2Bins - 1) << kLeD2Shift;
-    bool whole = rem == pick[2];
-    __syncthreads();
     if (!whole) {
       for (int i = tid; i < kLeD3Bins; i += NT) hist[i] = 0u;
       __syncthreads();
@@ -1208,7 +1353,8 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
         cand(k, v, key);
         const uint32_t m = v & pmask;
         keep = m > prefix || (m == prefix && (uint32_t)key <= cut);
-        sl = (key - base) / kSlice;
+        const int kh = key / a.S, kp = key - kh * a.S;
+        sl = kh * a.ns + (kp - slice_base(a, grp * a.hg + kh)) / kSlice;
       }
       hist_add(kept, (uint32_t)sl, keep);
     }
@@ -1221,14 +1367,14 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
   for (int e = 0; e < PT; ++e) {
     const uint32_t m = x[e] & pmask;
     const bool k = ((valid >> e) & 1u) &&
-                   (m > prefix || (m == prefix && (uint32_t)(i0 + e) <= cut));
+                   (m > prefix || (m == prefix && key0 + e <= cut));
     keep |= (uint32_t)k << e;
   }
   uint32_t off, npick;
   const uint32_t pos0 = block_scan_pair<NT>(off_part, __popc(keep), &off, &npick, wsum);
   uint32_t pos = pos0 + off;
   int32_t* row = a.idx + (size_t)grp * a.n_keep;
-  int32_t* out = row + a.n_sink;
+  int32_t* out = row + at.h * (a.n_sink + a.W) + a.n_sink;
 #pragma unroll
   for (int e = 0; e < PT; ++e) {
     if ((keep >> e) & 1u) {
@@ -1236,11 +1382,45 @@ __global__ void __launch_bounds__(kLeEmitThreads) le_emit(SelArgs a, int tps_log
       ++pos;
     }
   }
-  if (sg == 0) {
-    for (int t = tid; t < a.n_sink + a.W; t += NT) {
-      if (t < a.n_sink) row[t] = t;
-      else row[a.n_sink + a.budget + (t - a.n_sink)] = a.S - a.W + (t - a.n_sink);
+  if (sg != 0) return;
+  // Slice 0 of the group also writes every head's sinks and window and the
+  // head offsets: head h's rows start at h*(n_sink+W) + (picks of the heads
+  // before it), which needs the picks of every slice.
+  if (!whole1 && !over_s) {
+    kept[tid] = 0u;
+    __syncthreads();
+    if (has_slice) {
+      uint32_t nk = gt_t;
+#pragma unroll
+      for (int r = 0; r < kLeR; ++r) {
+        const uint32_t m = cv[r] & pmask;
+        nk += (r < (int)nmine) && (m > prefix || (m == prefix && (uint32_t)ci[r] <= cut));
+      }
+      if (nk) atomicAdd(&kept[s_t], nk);
     }
+    __syncthreads();
+  } else if (whole1) {
+    kept[tid] = tid < ns ? a.gtc[srow + tid] : 0u;
+    __syncthreads();
+  }
+  {
+    const uint32_t kt = tid < ns ? kept[tid] : 0u;
+    uint32_t tot;
+    const uint32_t exs = block_exclusive_scan<NT>(kt, &tot, wsum);
+    const int h = tid / a.ns;
+    if (tid < ns && tid == h * a.ns) pb[h] = min(exs, (uint32_t)a.budget);
+    if (tid == 0) pb[a.hg] = (uint32_t)a.budget;
+    __syncthreads();
+  }
+  const int seg = a.n_sink + a.W;
+  if (a.head_off)
+    for (int h = tid; h <= a.hg; h += NT)
+      a.head_off[(size_t)grp * (a.hg + 1) + h] = (int32_t)(h * seg + pb[h]);
+  for (int t = tid; t < a.hg * seg; t += NT) {
+    const int h = t / seg, j = t - h * seg;
+    const uint32_t start = h * seg + pb[h];
+    if (j < a.n_sink) row[start + j] = j;
+    else row[start + a.n_sink + (pb[h + 1] - pb[h]) + (j - a.n_sink)] = a.S - a.W + (j - a.n_sink);
   }
 }
 
@@ -1318,7 +1498,7 @@ bool plan_select(const kvsel_desc& d, int budget, int hg, SelectPlan* p) {
   if (p->multi) {
     // both digit histograms of the generic select, or the layer-end
     // chain's 12-bit first-digit histogram
-    p->off_hist = take((size_t)groups * max(kD1Bins + kD2Bins, kLeD1Bins) * 4);
+    p->off_hist = take((size_t)groups * max(kD1Bins + kD2Bins, kLeD1Bins + kLeD2Bins) * 4);
     p->off_gtc = take((size_t)groups * nst * 4);
     p->off_candc = take((size_t)groups * nst * 4);
     p->off_offs = take((size_t)groups * nst * 4);
@@ -1355,11 +1535,18 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
   }
   SelArgs a = sel_args(d, p, pooled, budget, idx, head_off, ws);
   const dim3 sg(a.nst, groups);
-  if (hg == 1 && a.nst <= kLeMaxSlices) {
-    // one KV-head row per group: the three-step select of the layer-end path
+  if (a.nst <= kLeMaxSlices) {
+    // the select of the layer-end path: one KV-head row per group settles a
+    // 12-bit digit before the compaction, a head group 22 bits (its group
+    // holds hg rows of candidates)
     KVSEL_LAUNCH("le_init", le_init, dim3(groups), dim3(256), 0, stream, a);
     KVSEL_LAUNCH("le_hist", le_hist, sg, dim3(kSliceThreads), 0, stream, a);
-    KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
+    if (hg == 1) {
+      KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
+    } else {
+      KVSEL_LAUNCH("lg_hist2", lg_hist2, sg, dim3(kSliceThreads), 0, stream, a);
+      KVSEL_LAUNCH("lg_cand", lg_cand, sg, dim3(kSliceThreads), 0, stream, a);
+    }
     KVSEL_LAUNCH("le_emit", le_emit, sg, dim3(kLeEmitThreads), 0, stream, a, le_tps_log2(a.nst));
     return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
   }
