@@ -294,6 +294,8 @@ def _tie_heavy_scores(rng, kind, shape):
     (3, 1, 8, 20000, 64, 0, "band"),
     (4, 3, 2, 5, 2, 1, "uniform"),
     (5, 1, 8, 131072, 64, 4, "uniform"),
+    # more than 1024 slices in the group: the generic sliced select
+    (6, 1, 8, 540000, 64, 0, "band"),
 ])
 def test_select_adaptive_exact_on_identical_inputs(seed, Bt, Hkv, S, W, n_sink, kind):
     """Given the same fp32 scores, the head-adaptive picks and per-head
