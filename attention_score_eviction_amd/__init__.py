@@ -141,6 +141,10 @@ def lib() -> ctypes.CDLL:
     L.kvsel_layer_end_workspace.restype = SZ
     L.kvsel_layer_end.argtypes = [DP, P, P, P, I32, I32, P, P, P, P, P, P, SZ, P]
     L.kvsel_layer_end.restype = ctypes.c_int
+    L.kvsel_layer_end_adaptive_workspace.argtypes = [DP, I32]
+    L.kvsel_layer_end_adaptive_workspace.restype = SZ
+    L.kvsel_layer_end_adaptive.argtypes = [DP, P, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P]
+    L.kvsel_layer_end_adaptive.restype = ctypes.c_int
     L.kvsel_layer_end_stream_workspace.argtypes = [DP, I32, I32]
     L.kvsel_layer_end_stream_workspace.restype = SZ
     L.kvsel_layer_end_stream.argtypes = [DP, P, P, P, I32, I32, P, P, P, P, SZ, P]
@@ -443,6 +447,55 @@ def layer_end_stream(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Ten
         return idx, k_out, v_out
 
 
+def layer_end_adaptive_workspace_bytes(desc: Desc, total_budget: int) -> int:
+    return int(lib().kvsel_layer_end_adaptive_workspace(ctypes.byref(desc), int(total_budget)))
+
+
+def layer_end_adaptive(q_obs: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], *,
+                       total_budget: int, pool_kernel: int, n_sink: int = 0, causal: bool = True,
+                       scale: float = 0.0, raw: Optional[torch.Tensor] = None,
+                       pooled: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                       head_off: Optional[torch.Tensor] = None,
+                       k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                       want_scores: bool = True, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """kvsel_layer_end_adaptive: the layer-end step with one head-adaptive
+    budget per sequence, into the flattened cache.  Returns (idx [Bt, n_keep],
+    head_off [Bt, Hkv+1], k_hat, v_hat [Bt, n_keep, D], raw, pooled) with
+    n_keep = Hkv*(n_sink+W) + total_budget; raw and pooled are None when
+    want_scores is False and none were given."""
+    alloc = (want_scores and (raw is None or pooled is None)) or idx is None or \
+        head_off is None or k_out is None or (v is not None and v_out is None) or \
+        workspace is None
+    with (_on(stream) if alloc else nullcontext()):
+        d = make_desc(q_obs, k, n_sink=n_sink, causal=causal, scale=scale)
+        Bt, Hkv, S, D = k.shape
+        n_keep = Hkv * (n_sink + q_obs.shape[2]) + total_budget
+        dev = k.device
+        if want_scores:
+            raw = torch.empty((Bt, Hkv, S), dtype=torch.float32, device=dev) if raw is None \
+                else raw
+            pooled = torch.empty_like(raw) if pooled is None else pooled
+        if idx is None:
+            idx = torch.empty((Bt, max(n_keep, 0)), dtype=torch.int32, device=dev)
+        if head_off is None:
+            head_off = torch.empty((Bt, Hkv + 1), dtype=torch.int32, device=dev)
+        if k_out is None:
+            k_out = torch.empty((Bt, max(n_keep, 0), D), dtype=k.dtype, device=dev)
+        if v is not None and v_out is None:
+            v_out = torch.empty((Bt, max(n_keep, 0), D), dtype=v.dtype, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(layer_end_adaptive_workspace_bytes(d, total_budget), 1),
+                                    dtype=torch.uint8, device=dev)
+        st = lib().kvsel_layer_end_adaptive(ctypes.byref(d), _ptr(q_obs), _ptr(k), _ptr(v),
+                                            int(total_budget), int(pool_kernel), _ptr(raw),
+                                            _ptr(pooled), _ptr(idx), _ptr(head_off), _ptr(k_out),
+                                            _ptr(v_out), _ptr(workspace), workspace.numel(),
+                                            _stream(stream))
+        _check(st, "kvsel_layer_end_adaptive")
+        return idx, head_off, k_out, v_out, raw, pooled
+
+
 def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, budget: int,
                        pool_kernel: int, n_sink: int = 0, causal: bool = True,
                        scale: float = 0.0, stream=None) -> dict:
@@ -456,14 +509,11 @@ def layer_end_compress(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
 def layer_end_compress_adaptive(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                                 total_budget: int, pool_kernel: int, n_sink: int = 0,
                                 causal: bool = True, scale: float = 0.0, stream=None) -> dict:
-    """score -> head-adaptive select -> flattened compact on one stream."""
-    W = q_obs.shape[2]
-    pooled, raw = score(q_obs, k, pool_kernel=pool_kernel, n_sink=n_sink, causal=causal,
-                        scale=scale, stream=stream)
-    idx, off = select_adaptive(pooled, total_budget, obs_window=W, n_q_heads=q_obs.shape[1],
-                               head_dim=k.shape[3], n_sink=n_sink, causal=causal, dtype=k.dtype,
-                               stream=stream)
-    k_hat, v_hat = compact_flat(k, v, idx, off, stream=stream)
+    """The head-adaptive layer-end step (kvsel_layer_end_adaptive) on one
+    stream, as a dict."""
+    idx, off, k_hat, v_hat, raw, pooled = layer_end_adaptive(
+        q_obs, k, v, total_budget=total_budget, pool_kernel=pool_kernel, n_sink=n_sink,
+        causal=causal, scale=scale, stream=stream)
     return {"s": raw, "p": pooled, "idx": idx, "head_off": off, "k_hat": k_hat, "v_hat": v_hat}
 
 
@@ -595,7 +645,8 @@ EXPORTS = ("kvsel_status_str", "kvsel_score_workspace", "kvsel_score", "kvsel_se
            "kvsel_qevict_step_workspace", "kvsel_qevict_step", "kvsel_select_compact",
            "kvsel_kara_keep", "kvsel_timing_start", "kvsel_timing_read", "kvsel_score_static",
            "kvsel_layer_end_workspace", "kvsel_layer_end", "kvsel_layer_end_stream_workspace",
-           "kvsel_layer_end_stream")
+           "kvsel_layer_end_stream", "kvsel_layer_end_adaptive_workspace",
+           "kvsel_layer_end_adaptive")
 
 STATIC_SCRATCH_BYTES = 32 << 20   # KVSEL_STATIC_SCRATCH_BYTES
 

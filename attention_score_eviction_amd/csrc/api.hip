@@ -222,7 +222,7 @@ struct LayerEndWs {
   size_t off_sel, off_pooled, total;
 };
 
-LayerEndWs layer_end_ws(const kvsel_desc& d, int budget, bool own_pooled) {
+static LayerEndWs layer_end_ws(const kvsel_desc& d, int budget, bool own_pooled) {
   LayerEndWs w;
   plan_score(d, &w.sp);
   plan_select(d, budget, 1, &w.lp);
@@ -269,14 +269,83 @@ kvsel_status kvsel_layer_end(const kvsel_desc* desc, const void* q_obs, const vo
       kvsel_status r = launch_score(*desc, w.sp, q_obs, k, raw, nullptr, pool_kernel, wsc, s,
                                     desc->seq_len, h1, words);
       if (r != KVSEL_OK) return r;
-      return launch_layer_end_select(*desc, w.lp, raw, pool_buf, pool_kernel, budget, idx, k, v,
-                                     k_out, v_out, sel_ws, s);
+      return launch_layer_end_select(*desc, w.lp, raw, pool_buf, pool_kernel, budget, idx,
+                                     nullptr, k, v, k_out, v_out, sel_ws, s);
     }
     kvsel_status r = launch_score(*desc, w.sp, q_obs, k, raw_scores, pool_buf, pool_kernel, wsc,
                                   s, desc->seq_len);
     if (r != KVSEL_OK) return r;
     return launch_select_compact(*desc, w.lp, pool_buf, budget, idx, k, v, k_out, v_out, sel_ws,
                                  s);
+  });
+}
+
+// Head-adaptive layer end: the score scratch, the head-group select scratch,
+// then the pooled scores when the caller does not take them.
+struct AdaptiveWs {
+  ScorePlan sp;
+  SelectPlan lp;
+  bool ok;
+  size_t off_sel, off_pooled, total;
+};
+
+static AdaptiveWs adaptive_ws(const kvsel_desc& d, int total_budget, bool own_pooled) {
+  AdaptiveWs w;
+  plan_score(d, &w.sp);
+  w.ok = plan_select(d, total_budget, d.n_kv_heads, &w.lp);
+  w.off_sel = align256(w.sp.total);
+  w.off_pooled = align256(w.off_sel + (w.ok ? w.lp.total : 0));
+  w.total = w.off_pooled +
+            (own_pooled ? align256((size_t)d.batch * d.n_kv_heads * d.seq_len * sizeof(float)) : 0);
+  return w;
+}
+
+size_t kvsel_layer_end_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget) {
+  if (check_adaptive(desc, total_budget) != KVSEL_OK) return 0;
+  const AdaptiveWs w = adaptive_ws(*desc, (int)total_budget, true);
+  return w.ok ? w.total : 0;
+}
+
+kvsel_status kvsel_layer_end_adaptive(const kvsel_desc* desc, const void* q_obs, const void* k,
+                                      const void* v, int32_t total_budget, int32_t pool_kernel,
+                                      float* raw_scores, float* pooled, int32_t* idx,
+                                      int32_t* head_off, void* k_out, void* v_out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  const kvsel_status st = check_adaptive(desc, total_budget);
+  if (st != KVSEL_OK) return st;
+  if (!q_obs || !k || !idx || !head_off || !k_out) return KVSEL_ERR_ARG;
+  if ((v == nullptr) != (v_out == nullptr)) return KVSEL_ERR_ARG;
+  const void* ptrs[] = {q_obs, k, v, raw_scores, pooled, idx, k_out, v_out, ws};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return KVSEL_ERR_ARG;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 1 + 2 * (1 << 20))
+    return KVSEL_ERR_ARG;
+  const AdaptiveWs w = adaptive_ws(*desc, (int)total_budget, pooled == nullptr);
+  if (!w.ok) return KVSEL_ERR_UNSUPPORTED;
+  if (ws_bytes < w.total || !ws) return KVSEL_ERR_WORKSPACE;
+  char* wsc = (char*)ws;
+  float* pool_buf = pooled ? pooled : (float*)(wsc + w.off_pooled);
+  const int n_keep = desc->n_kv_heads * (desc->n_sink + desc->obs_window) + total_budget;
+  return enqueue(stream, [&] {
+    const hipStream_t s = (hipStream_t)stream;
+    char* sel_ws = wsc + w.off_sel;
+    if (layer_end_fusable(*desc, w.lp, total_budget, pool_kernel)) {
+      // max filter with the first histogram, select and gather behind the passes
+      float* raw = raw_scores ? raw_scores : (float*)(wsc + w.sp.off_raw);
+      size_t words = 0;
+      uint32_t* h = select_hists(w.lp, sel_ws, &words);
+      kvsel_status r = launch_score(*desc, w.sp, q_obs, k, raw, nullptr, pool_kernel, wsc, s,
+                                    desc->seq_len, h, words);
+      if (r != KVSEL_OK) return r;
+      return launch_layer_end_select(*desc, w.lp, raw, pool_buf, pool_kernel, total_budget, idx,
+                                     head_off, k, v, k_out, v_out, sel_ws, s);
+    }
+    kvsel_status r = launch_score(*desc, w.sp, q_obs, k, raw_scores, pool_buf, pool_kernel, wsc,
+                                  s, desc->seq_len);
+    if (r != KVSEL_OK) return r;
+    r = launch_select(*desc, w.lp, pool_buf, total_budget, idx, head_off, sel_ws, s);
+    if (r != KVSEL_OK) return r;
+    return launch_compact_flat(*desc, k, v, idx, head_off, n_keep, k_out, v_out, s);
   });
 }
 
@@ -291,7 +360,7 @@ struct StreamWs {
   size_t off_cval, off_cpos, off_sel, off_lws, total;
 };
 
-bool stream_ws(const kvsel_desc& d, int budget, int pool_kernel, StreamWs* w) {
+static bool stream_ws(const kvsel_desc& d, int budget, int pool_kernel, StreamWs* w) {
   if (!plan_score_stream(d, &w->sp) || (pool_kernel - 1) / 2 > 64) return false;
   const int lo = d.n_sink, hi = d.seq_len - d.obs_window;
   w->M = stream_list_len(w->sp, lo, hi, budget);

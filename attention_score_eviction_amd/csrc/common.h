@@ -137,7 +137,7 @@ kvsel_status launch_stream_finish(const int32_t* sel, const int32_t* cpos, int32
                                   int rows, int M, int budget, int n_sink, int W, int S,
                                   hipStream_t stream);
 
-// Selection groups: hg consecutive KV heads of a sequence share one budget// Selection groups: hg consecutive KV heads of a sequence share one budget
+// Selection groups: hg consecutive KV heads of a sequence share one budget
 // (hg = 1: per-head budget; hg = n_kv_heads: head-adaptive budget).
 constexpr int kMaxGroupSlices = 2048;
 struct SelectPlan {
@@ -157,15 +157,16 @@ kvsel_status launch_select(const kvsel_desc& d, const SelectPlan& p, const float
 kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, const float* pooled,
                                    int budget, int32_t* idx, const void* k, const void* v,
                                    void* k_out, void* v_out, char* ws, hipStream_t stream);
-// The fused select-and-gather of kvsel_layer_end (long per-head rows): from
-// the raw scores, with the digit histograms select_hists zeroed earlier on
-// the stream.
+// The fused max filter, select and gather of the layer-end calls (long
+// rows; one KV head per group, or a head group with the flattened gather
+// and head_off): from the raw scores, with the digit histograms
+// select_hists names zeroed earlier on the stream.
 bool layer_end_fusable(const kvsel_desc& d, const SelectPlan& p, int budget, int pool_kernel);
 uint32_t* select_hists(const SelectPlan& p, char* ws, size_t* words);
 kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, const float* raw,
                                      float* pooled, int pool_kernel, int budget, int32_t* idx,
-                                     const void* k, const void* v, void* k_out, void* v_out,
-                                     char* ws, hipStream_t stream);
+                                     int32_t* head_off, const void* k, const void* v,
+                                     void* k_out, void* v_out, char* ws, hipStream_t stream);
 kvsel_status launch_compact(const kvsel_desc& d, const void* k, const void* v,
                             const int32_t* idx, int n_keep, void* k_out, void* v_out,
                             hipStream_t stream);

@@ -10,8 +10,6 @@
 namespace kvsel {
 namespace {
 
-constexpr int kRowsPerBlock = 64;   // flattened gather
-
 // One 16-byte vector of K and one of V per thread: a workgroup moves
 // 256 / vpr whole rows, so every thread has a single index -> row load chain
 // and all of a workgroup's loads are in flight together.
@@ -42,9 +40,24 @@ __global__ void __launch_bounds__(256) compact_kernel(const u32x4_t* __restrict_
 }
 
 // Flattened head-adaptive cache (TideKV Section 4.1): one row list per
-// sequence, head h owning rows [head_off[h], head_off[h+1]).  The first 64
-// threads resolve each row's head (binary search over the offsets) and
-// source row into LDS; then all threads move the rows as 16-byte vectors.
+// sequence, head h owning rows [head_off[h], head_off[h+1]).  Rows are moved
+// as in compact_kernel (one 16-byte vector of K and one of V per thread); a
+// thread's index load is issued before the sequence's offsets are staged in
+// LDS, and its head is found there by binary search (in global memory for
+// more than kFlatLdsHeads heads), so each thread waits on two loads in a row
+// as in the per-head gather.
+constexpr int kFlatLdsHeads = 1023;
+
+__device__ __forceinline__ int last_head_at_or_before(const int32_t* off, int hkv, int r) {
+  int lo = 0, hi = hkv - 1;   // last head whose first row is <= r (clamped)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 __global__ void __launch_bounds__(256) compact_flat_kernel(const u32x4_t* __restrict__ k,
                                                            const u32x4_t* __restrict__ v,
                                                            const int32_t* __restrict__ idx,
@@ -52,38 +65,31 @@ __global__ void __launch_bounds__(256) compact_flat_kernel(const u32x4_t* __rest
                                                            u32x4_t* __restrict__ ko,
                                                            u32x4_t* __restrict__ vo, int S,
                                                            int hkv, int n_keep, int vpr) {
-  __shared__ long long src_row[kRowsPerBlock];
+  __shared__ int32_t off_s[kFlatLdsHeads + 1];
   const int b = blockIdx.y;
-  const int r0 = blockIdx.x * kRowsPerBlock;
-  if (threadIdx.x < kRowsPerBlock) {
-    const int r = r0 + threadIdx.x;
-    long long sr = -1;
-    if (r < n_keep) {
-      const int32_t* off = head_off + (size_t)b * (hkv + 1);
-      int lo = 0, hi = hkv - 1;   // last head whose first row is <= r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= r) lo = mid;
-        else hi = mid - 1;
-      }
-      const int src = idx[(size_t)b * n_keep + r];
-      if (src >= 0 && src < S) sr = ((long long)b * hkv + lo) * S + src;
-    }
-    src_row[threadIdx.x] = sr;
-  }
+  const int rpb = 256 / vpr;
+  const int r = blockIdx.x * rpb + threadIdx.x / vpr;
+  const int c = threadIdx.x - (threadIdx.x / vpr) * vpr;
+  const bool live = r < n_keep && threadIdx.x < rpb * vpr;
+  const int src = live ? idx[(size_t)b * n_keep + r] : -1;
+  const int32_t* off = head_off + (size_t)b * (hkv + 1);
+  const bool in_lds = hkv <= kFlatLdsHeads;
+  if (in_lds)
+    for (int i = threadIdx.x; i <= hkv; i += 256) off_s[i] = off[i];
   __syncthreads();
-  const size_t dst_base = (size_t)b * n_keep;
-  for (int t = threadIdx.x; t < kRowsPerBlock * vpr; t += 256) {
-    const int rr = t / vpr;
-    const int c = t - rr * vpr;
-    if (r0 + rr >= n_keep) break;
-    const long long sr = src_row[rr];
-    const bool ok = sr >= 0;
-    const size_t so = (size_t)(ok ? sr : 0) * vpr + c;
-    const size_t dsto = (dst_base + r0 + rr) * vpr + c;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    ko[dsto] = ok ? k[so] : zero;
-    if (v) vo[dsto] = ok ? v[so] : zero;
+  if (!live) return;
+  const int h = last_head_at_or_before(in_lds ? off_s : off, hkv, r);
+  const bool ok = src >= 0 && src < S;
+  const size_t so = (((size_t)b * hkv + h) * S + (ok ? src : 0)) * vpr + c;
+  const size_t dsto = ((size_t)b * n_keep + r) * vpr + c;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const u32x4_t kx = ok ? k[so] : zero;
+  if (v) {
+    const u32x4_t vx = ok ? v[so] : zero;
+    ko[dsto] = kx;
+    vo[dsto] = vx;
+  } else {
+    ko[dsto] = kx;
   }
 }
 
@@ -109,10 +115,11 @@ kvsel_status launch_compact_flat(const kvsel_desc& d, const void* k, const void*
   if (n_keep == 0) return KVSEL_OK;
   const int e = d.dtype == KVSEL_F32 ? 4 : 2;
   const int vpr = d.head_dim * e / 16;
+  const int rpb = 256 / vpr;   // vpr <= 32 (D * e <= 512 bytes)
   KVSEL_LAUNCH("compact_flat_kernel", compact_flat_kernel,
-                     dim3((n_keep + kRowsPerBlock - 1) / kRowsPerBlock, d.batch), dim3(256), 0,
-                     stream, (const u32x4_t*)k, (const u32x4_t*)v, idx, head_off,
-                     (u32x4_t*)k_out, (u32x4_t*)v_out, d.seq_len, d.n_kv_heads, n_keep, vpr);
+               dim3((n_keep + rpb - 1) / rpb, d.batch), dim3(256), 0, stream,
+               (const u32x4_t*)k, (const u32x4_t*)v, idx, head_off, (u32x4_t*)k_out,
+               (u32x4_t*)v_out, d.seq_len, d.n_kv_heads, n_keep, vpr);
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 

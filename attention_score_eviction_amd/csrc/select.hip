@@ -1596,14 +1596,17 @@ kvsel_status launch_select_compact(const kvsel_desc& d, const SelectPlan& p, con
   return hipGetLastError() == hipSuccess ? KVSEL_OK : KVSEL_ERR_DEVICE;
 }
 
+// The first-digit histograms of every group, then (head groups) the
+// second-digit ones: one contiguous run of words to clear.
 uint32_t* select_hists(const SelectPlan& p, char* ws, size_t* words) {
-  *words = (size_t)p.groups * kLeD1Bins;
+  *words = (size_t)p.groups * (p.hg > 1 ? kLeD1Bins + kLeD2Bins : kLeD1Bins);
   return (uint32_t*)(ws + p.off_hist);
 }
 
 bool layer_end_fusable(const kvsel_desc& d, const SelectPlan& p, int budget, int pool_kernel) {
-  return p.multi && p.hg == 1 && budget > 0 && (pool_kernel - 1) / 2 <= kMaxPoolHalo &&
-         p.ns <= kLeMaxSlices && d.n_sink + d.obs_window + budget <= d.seq_len;
+  const long ncand = (long)d.seq_len - d.obs_window - d.n_sink;
+  return p.multi && budget > 0 && (pool_kernel - 1) / 2 <= kMaxPoolHalo &&
+         (long)p.ns * p.hg <= kLeMaxSlices && (long)budget <= (long)p.hg * ncand;
 }
 
 // The gather runs as its own evenly spread kernel after the emit: copying
@@ -1612,16 +1615,22 @@ bool layer_end_fusable(const kvsel_desc& d, const SelectPlan& p, int budget, int
 // against 4.6 + 7.0 us for the two kernels).
 kvsel_status launch_layer_end_select(const kvsel_desc& d, const SelectPlan& p, const float* raw,
                                      float* pooled, int pool_kernel, int budget, int32_t* idx,
-                                     const void* k, const void* v, void* k_out, void* v_out,
-                                     char* ws, hipStream_t stream) {
-  SelArgs a = sel_args(d, p, pooled, budget, idx, nullptr, ws);
+                                     int32_t* head_off, const void* k, const void* v,
+                                     void* k_out, void* v_out, char* ws, hipStream_t stream) {
+  SelArgs a = sel_args(d, p, pooled, budget, idx, head_off, ws);
   const dim3 sg(a.nst, p.groups);
   KVSEL_LAUNCH("sel_pool_hist", sel_pool_hist, sg, dim3(kPoolThreads), 0, stream, a, raw, pooled,
                (pool_kernel - 1) / 2);
-  KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  if (p.hg == 1) {
+    KVSEL_LAUNCH("le_cand", le_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  } else {
+    KVSEL_LAUNCH("lg_hist2", lg_hist2, sg, dim3(kSliceThreads), 0, stream, a);
+    KVSEL_LAUNCH("lg_cand", lg_cand, sg, dim3(kSliceThreads), 0, stream, a);
+  }
   KVSEL_LAUNCH("le_emit", le_emit, sg, dim3(kLeEmitThreads), 0, stream, a, le_tps_log2(a.nst));
   if (hipGetLastError() != hipSuccess) return KVSEL_ERR_DEVICE;
-  return launch_compact(d, k, v, idx, a.n_keep, k_out, v_out, stream);
+  if (p.hg == 1) return launch_compact(d, k, v, idx, a.n_keep, k_out, v_out, stream);
+  return launch_compact_flat(d, k, v, idx, head_off, a.n_keep, k_out, v_out, stream);
 }
 
 // Final index rows of the streaming path: sinks, then the positions of the

@@ -21,7 +21,8 @@ import torch
 
 import ctypes
 
-from . import Desc, _check, _dtype_code, _ptr, _stream, layer_end, layer_end_workspace_bytes, lib
+from . import (Desc, _check, _dtype_code, _ptr, _stream, layer_end, layer_end_adaptive,
+               layer_end_adaptive_workspace_bytes, layer_end_workspace_bytes, lib)
 
 
 @dataclass
@@ -35,6 +36,23 @@ class LayerCache:
     @property
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.idx, self.k_hat, self.v_hat))
+
+
+@dataclass
+class FlatLayerCache:
+    """Committed compact cache of one layer under a head-adaptive budget
+    (TideKV Section 4.1): every KV head's rows of a sequence in one flattened
+    list, head h owning rows [head_off[b,h], head_off[b,h+1])."""
+    total_budget: int
+    idx: torch.Tensor        # [Bt, n_keep] int32, absolute positions
+    head_off: torch.Tensor   # [Bt, Hkv + 1] int32
+    k_hat: torch.Tensor      # [Bt, n_keep, D]
+    v_hat: torch.Tensor
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.idx, self.head_off, self.k_hat, self.v_hat))
 
 
 @dataclass
@@ -118,6 +136,49 @@ class LayerMajorDriver:
                     self.ws.numel())
             fn = lib().kvsel_layer_end
             cache._call = lambda s: _check(fn(*args, s), "kvsel_layer_end")
+            return cache
+        call(_stream(stream))
+        return cache
+
+    def new_flat_cache(self, total_budget: int) -> FlatLayerCache:
+        """Output buffers of a layer's flattened cache at a head-adaptive
+        budget of `total_budget` picks per sequence (at most Hkv times the
+        per-head maximum the scratch was sized for)."""
+        if not 0 <= total_budget <= self.n_kv_heads * self.max_budget:
+            raise ValueError(f"total budget {total_budget} outside "
+                             f"[0, {self.n_kv_heads * self.max_budget}]")
+        n_keep = self.n_kv_heads * (self.n_sink + self.obs_window) + total_budget
+        dev = self.k.device
+        Bt, D = self.batch, self.head_dim
+        return FlatLayerCache(total_budget,
+                              torch.empty((Bt, n_keep), dtype=torch.int32, device=dev),
+                              torch.empty((Bt, self.n_kv_heads + 1), dtype=torch.int32,
+                                          device=dev),
+                              torch.empty((Bt, n_keep, D), dtype=self.dtype, device=dev),
+                              torch.empty((Bt, n_keep, D), dtype=self.dtype, device=dev))
+
+    def layer_end_adaptive(self, cache: FlatLayerCache, stream=None) -> FlatLayerCache:
+        """LayerEndCompress of the active layer with one head-adaptive budget
+        per sequence (kvsel_layer_end_adaptive) into `cache`, enqueued on
+        `stream`; marshalled once per cache like layer_end."""
+        call = getattr(cache, "_call", None)
+        if call is None:
+            ws = getattr(self, "_ws_adaptive", None)
+            need = max(layer_end_adaptive_workspace_bytes(self.desc, cache.total_budget), 1)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(need, dtype=torch.uint8, device=self.k.device)
+                self._ws_adaptive = ws
+            cache._ws = ws      # the prepared call below holds its address
+            layer_end_adaptive(self.q, self.k, self.v, total_budget=cache.total_budget,
+                               pool_kernel=self.pool_kernel, n_sink=self.n_sink, raw=self.raw,
+                               pooled=self.pooled, idx=cache.idx, head_off=cache.head_off,
+                               k_out=cache.k_hat, v_out=cache.v_hat, workspace=ws, stream=stream)
+            args = (ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                    int(cache.total_budget), int(self.pool_kernel), _ptr(self.raw),
+                    _ptr(self.pooled), _ptr(cache.idx), _ptr(cache.head_off), _ptr(cache.k_hat),
+                    _ptr(cache.v_hat), _ptr(ws), ws.numel())
+            fn = lib().kvsel_layer_end_adaptive
+            cache._call = lambda s: _check(fn(*args, s), "kvsel_layer_end_adaptive")
             return cache
         call(_stream(stream))
         return cache

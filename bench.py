@@ -247,8 +247,10 @@ def copy_bandwidth_gbs(torch, stream, nbytes: int = 1 << 30, reps: int = 20) -> 
 class Layer:
     """One resident layer on the layer-major driver, with its preallocated
     compact cache; a step is the layer-end step as the driver runs it
-    (kvsel_score, then kvsel_select_compact).  The head-adaptive variant
-    runs kvsel_score, kvsel_select_adaptive and kvsel_compact_flat."""
+    (kvsel_layer_end; kvsel_layer_end_adaptive into a flattened cache for the
+    head-adaptive variant).  The per-call breakdown times the composed calls
+    (kvsel_score, then kvsel_select_compact, or kvsel_select_adaptive and
+    kvsel_compact_flat)."""
 
     def __init__(self, kvsel, torch, spec, x, adaptive=False, streaming=False):
         from attention_score_eviction_amd.driver import LayerMajorDriver
@@ -294,6 +296,7 @@ class Layer:
             self.v_hat = torch.empty_like(self.k_hat)
             nb = kvsel.select_adaptive_workspace_bytes(d.desc, Hkv * budget)
             self.sel_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+            self.flat = self.drv.new_flat_cache(Hkv * budget)
 
     def score(self, stream):
         d = self.drv
@@ -318,8 +321,7 @@ class Layer:
 
     def step(self, stream):
         if self.adaptive:
-            self.score(stream)
-            self.select_compact(stream)
+            self.drv.layer_end_adaptive(self.flat, stream=stream)
         elif self.streaming:
             d, c = self.drv, self.cache
             self.kvsel.layer_end_stream(d.q, d.k, d.v, budget=c.budget, pool_kernel=d.pool_kernel,
@@ -609,9 +611,10 @@ def main() -> int:
                                                           reps)
         us_call["workspace_bytes"] = {"kvsel_layer_end_stream": L.stream_ws.numel(),
                                       "kvsel_layer_end": L.drv.ws.numel()}
-    elif not adaptive:
-        us_call["kvsel_layer_end"] = event_time_us(torch, stream, lambda: L.step(stream), reps)
-    if args.graph and not adaptive:
+    else:
+        name = "kvsel_layer_end_adaptive" if adaptive else "kvsel_layer_end"
+        us_call[name] = event_time_us(torch, stream, lambda: L.step(stream), reps)
+    if args.graph:
         # the step captured once in a HIP graph and replayed (host launch cost
         # removed; the same kernels on the same buffers)
         torch.cuda.synchronize()

@@ -276,6 +276,34 @@ kvsel_status kvsel_layer_end(const kvsel_desc* desc, const void* q_obs, const vo
                              void* v_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_layer_end_adaptive -- TideKV Algorithm 2 with the head-adaptive
+ * budget of Section 4.1 in one call: kvsel_score, then kvsel_select_adaptive,
+ * then kvsel_compact_flat with n_keep = Hkv*(n_sink+W) + total_budget, with
+ * exactly their results (raw and pooled scores, idx, head_off, k_out, v_out
+ * as those calls define them).  When a sequence's candidates span at most
+ * 1024 slices of 4096, the max filter runs fused with the selection's first
+ * histogram behind the two score passes (fewer launches, the same bits).
+ *
+ *   q_obs         [Bt,Hq,W,D] dtype, device
+ *   k, v          [Bt,Hkv,S,D] dtype, device (v may be NULL with v_out)
+ *   total_budget  0 <= total_budget <= Hkv*(S-W-n_sink), else KVSEL_ERR_BUDGET
+ *   pool_kernel   odd, >= 1
+ *   raw_scores    [Bt,Hkv,S] float32 out, device, may be NULL (kept in ws)
+ *   pooled        [Bt,Hkv,S] float32 out, device, may be NULL (kept in ws)
+ *   idx           [Bt,n_keep] int32 out; head_off [Bt,Hkv+1] int32 out
+ *   k_out, v_out  [Bt,n_keep,D] dtype out, device
+ *   ws            device scratch of >= kvsel_layer_end_adaptive_workspace(desc,
+ *                 total_budget) bytes (computed for pooled == NULL)
+ * Errors: those of kvsel_score, kvsel_select_adaptive and kvsel_compact_flat.
+ */
+size_t kvsel_layer_end_adaptive_workspace(const kvsel_desc* desc, int32_t total_budget);
+kvsel_status kvsel_layer_end_adaptive(const kvsel_desc* desc, const void* q_obs, const void* k,
+                                      const void* v, int32_t total_budget, int32_t pool_kernel,
+                                      float* raw_scores, float* pooled, int32_t* idx,
+                                      int32_t* head_off, void* k_out, void* v_out, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/*
  * kvsel_layer_end_stream -- TideKV Algorithm 2 with its streaming top-k: the
  * top candidates are kept while pass 2 streams over the keys (Section 4.2,
  * the heap of pass 2, and its temporary-memory bound), so no per-key score

@@ -139,6 +139,33 @@ def test_select_adaptive_checks(kv):
                                        None) == kv.ERR_UNSUPPORTED
 
 
+def test_layer_end_adaptive_checks(kv):
+    L = kv.lib()
+    d = _desc(kv, seq_len=1000, obs_window=40, n_sink=4)
+    need = L.kvsel_layer_end_adaptive_workspace(ctypes.byref(d), 100)
+    assert need > 0
+    call = lambda T, dd=d, pk=7, idx=FAKE, off=FAKE, v=FAKE, vo=FAKE, wsb=need: \
+        L.kvsel_layer_end_adaptive(ctypes.byref(dd), FAKE, FAKE, v, T, pk, None, None, idx, off,  # noqa
+                                   FAKE, vo, FAKE, wsb, None)
+    ncand = 1000 - 40 - 4
+    assert call(-1) == kv.ERR_BUDGET
+    assert call(8 * ncand + 1) == kv.ERR_BUDGET
+    assert call(100, off=None) == kv.ERR_ARG
+    assert call(100, idx=None) == kv.ERR_ARG
+    assert call(100, idx=FAKE + 4) == kv.ERR_ARG
+    assert call(100, vo=None) == kv.ERR_ARG          # v without v_out
+    assert call(100, pk=6) == kv.ERR_ARG
+    assert call(100, wsb=need - 1) == kv.ERR_WORKSPACE
+    assert L.kvsel_layer_end_adaptive_workspace(ctypes.byref(d), -1) == 0
+    # the head-adaptive scratch holds the per-head select's and more
+    long_d = _desc(kv, seq_len=131072, obs_window=64)
+    assert L.kvsel_layer_end_adaptive_workspace(ctypes.byref(long_d), 8 * 4096) >= \
+        L.kvsel_select_adaptive_workspace(ctypes.byref(long_d), 8 * 4096) + 8 * 131072 * 4
+    many = _desc(kv, n_q_heads=65, n_kv_heads=65, seq_len=1000)
+    assert L.kvsel_layer_end_adaptive_workspace(ctypes.byref(many), 10) == 0
+    assert call(10, dd=many, wsb=1 << 40) == kv.ERR_UNSUPPORTED
+
+
 def test_compact_flat_checks(kv):
     L = kv.lib()
     d = _desc(kv, seq_len=100)
