@@ -160,3 +160,34 @@ def test_layer_end_duplicate_keys_tie_across_slices(ndup, budget):
         vals = p[hk, pos]
         assert (vals == vals[0]).all() and vals[0] > np.delete(p[hk, :S - W], pos).max()
         assert (got[hk] == pos[:budget]).all()
+
+
+@pytest.mark.parametrize("S", [4194317, 4194318])
+def test_layer_end_at_slice_limit(S):
+    """The longest rows of the fused path: 1024 slices of 4096 candidates
+    (S = 4194317 with W = 16), and one slice more, where the composed calls
+    run instead.  Both equal the composed calls bit for bit and the oracle's
+    selection on the same pooled scores; the raw scores sum to G*W."""
+    import attention_score_eviction_amd as kvsel
+    Hq, Hkv, D, W, B = 2, 1, 64, 16, 100000
+    g = torch.Generator(device="cuda").manual_seed(S)
+    q = torch.randn((1, Hq, W, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, Hkv, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, Hkv, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    print(f"case layer_end slice limit S={S}", flush=True)
+    pooled, raw = kvsel.score(q, k, pool_kernel=7)
+    idx, kh, vh = kvsel.select_compact(pooled, k, v, B, obs_window=W, n_q_heads=Hq)
+    idx2, kh2, vh2, raw2, pooled2 = kvsel.layer_end(q, k, v, budget=B, pool_kernel=7)
+    torch.cuda.synchronize()
+    assert torch.equal(raw2, raw)
+    assert torch.equal(pooled2, pooled)
+    assert torch.equal(idx2, idx)
+    assert torch.equal(kh2.view(torch.int16), kh.view(torch.int16))
+    assert torch.equal(vh2.view(torch.int16), vh.view(torch.int16))
+    p = pooled2.cpu().numpy().astype(np.float64)
+    ref = oracle.select(p, B, 0, W)
+    assert (idx2.cpu().numpy() == ref).all()
+    total = raw2.cpu().numpy().astype(np.float64).sum()
+    assert abs(total - (Hq // Hkv) * W) <= 1e-4 * (Hq // Hkv) * W
+    rows = idx2[0, 0].long()
+    assert torch.equal(kh2[0, 0].view(torch.int16), k[0, 0, rows].view(torch.int16))

@@ -182,6 +182,25 @@ def test_select_exact_on_identical_inputs(seed, S):
         np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("S,kind", [(4194365, "band"), (4194366, "plateau")])
+def test_select_exact_at_slice_limits(S, kind):
+    """One row of 1024 slices of 4096 candidates (S = 4194365 with W = 64),
+    the most the layer-end select chain takes, and one slice more (the
+    generic sliced select): bit-exact with the oracle from one pick to all."""
+    kvsel = _kvsel()
+    rng = np.random.default_rng(S)
+    W = 64
+    p = _tie_heavy_scores(rng, kind, (1, 1, S))
+    p[..., S - W:] = 0
+    ncand = S - W
+    print(f"case select slice limit S={S} kind={kind}", flush=True)
+    pt = torch.from_numpy(p).cuda()
+    p64 = p.astype(np.float64)
+    for budget in [1, 4096, 123457, ncand]:
+        got = kvsel.select(pt, budget, obs_window=W, n_q_heads=1, head_dim=128).cpu().numpy()
+        np.testing.assert_array_equal(got, oracle.select(p64, budget, 0, W))
+
+
 def test_compact_exact_with_oracle_indices():
     kvsel = _kvsel()
     rng = np.random.default_rng(5)
