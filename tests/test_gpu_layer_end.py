@@ -26,8 +26,17 @@ CASES = [
     ("pool-129", L(1, 8, 2, 128, 20000, 32, 129, 3000, structure="heavy"), 46),
     ("f32-long", L(1, 4, 2, 64, 20000, 16, 5, 1000, dtype="f32"), 47),
     ("noncausal", L(1, 8, 2, 128, 24000, 40, 7, 2500, causal=0, structure="heavy"), 48),
-    # short rows and budget 0: the composed path
+    # short rows (one workgroup per row): the gather fused into the select
+    # while the kept rows fit its LDS list, else a separate gather
     ("short-8k", synth.config(2), 2),
+    ("short-pool-129", L(1, 8, 2, 128, 9000, 32, 129, 1000, structure="heavy"), 63),
+    ("short-sinks-ragged", L(2, 8, 2, 64, 7001, 16, 5, 700, n_sink=3), 64),
+    ("short-no-fused-gather", L(1, 8, 2, 128, 16000, 32, 7, 4500, structure="heavy"), 65),
+    ("short-no-candidates", L(1, 4, 2, 64, 64, 60, 3, 0, n_sink=4), 66),
+    ("short-f32", L(1, 4, 2, 64, 3000, 16, 7, 200, dtype="f32"), 67),
+    ("short-budget-all", L(1, 8, 2, 128, 4000, 32, 3, 4000 - 32 - 1, n_sink=1), 68),
+    # more candidates than one workgroup's register batches, budget 0: the
+    # composed path
     ("budget-0", L(1, 8, 2, 128, 20000, 32, 7, 0), 49),
 ]
 
