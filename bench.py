@@ -40,6 +40,7 @@ import os
 import re
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -51,6 +52,12 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
+# Vector-ALU ceilings of the score passes from the chip's 1024 SIMDs at the
+# 2.4 GHz peak clock and the issue cost of one wave64 instruction measured
+# in a standalone probe: v_exp_f32 11 cycles, v_fma_f32 / v_add_f32 4.8.
+N_SIMD, PEAK_CLOCK_HZ = 1024, 2.4e9
+EXP_CYCLES, FMA_CYCLES = 11.0, 4.8
+EXP_RATE = N_SIMD * 64 / EXP_CYCLES * PEAK_CLOCK_HZ          # exponentials per second
 METRIC = "prompt-KV tokens scored+selected+compacted/sec per layer; % of HBM BW peak"
 WORKLOADS = {
     "llama8k": (2, "llama3-8b-layer-8k"),
@@ -109,10 +116,15 @@ def tier_bytes(spec: synth.LayerSpec, n_full: int, n_quant: int, n_prom: int, wi
 
 
 def cpu_baseline(spec: synth.LayerSpec, x: dict, budget_s: float = 12.0,
-                 adaptive: bool = False) -> dict:
-    """The oracle, as it stands, timed on this host on the same workload.
-    Layers whose dense fp64 scoring is large run on a sample of KV heads (the
-    oracle's work is the same for every head), scaled to the whole layer."""
+                 adaptive: bool = False, threads: Optional[int] = None) -> dict:
+    """The oracle, as it stands, timed on this host on the same workload
+    (on `threads` BLAS threads when given, else all of them).  Layers whose
+    dense fp64 scoring is large run on a sample of KV heads (the oracle's work
+    is the same for every head), scaled to the whole layer."""
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads):
+            return cpu_baseline(spec, x, budget_s, adaptive)
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -211,6 +223,26 @@ def kernel_work(spec: synth.LayerSpec, kernel: str, n_keep: int) -> tuple:
     if kernel == "compact_kernel":
         return 4 * H * n_keep * D * e + H * n_keep * 4, 0
     return 0, 0
+
+
+def binding_roofline(spec: synth.LayerSpec, path_bytes: int, step_us: float) -> dict:
+    """The step against each ceiling: HBM (algorithmic bytes), the matrix
+    cores (both passes' flops), the exponentials alone (2 per logit), and the
+    vector ALU issue of the passes' per-logit arithmetic (pass 1: FMA, exp,
+    add and half a max3; pass 2: FMA, exp, add); the binding one is the
+    largest, and frac is it over the measured step."""
+    logits = spec.batch * spec.n_q_heads * spec.obs_window * spec.seq_len
+    t = {
+        "hbm": path_bytes / (HBM_PEAK_GBS * 1e9),
+        "mfma": 2 * 2 * logits * spec.head_dim / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "exp": 2 * logits / EXP_RATE,
+        "valu": logits * (2 * (2 * FMA_CYCLES + EXP_CYCLES) + FMA_CYCLES / 2) / 64
+        / N_SIMD / PEAK_CLOCK_HZ,
+    }
+    bound = max(t, key=t.get)
+    out = {f"t_{k}_us": round(v * 1e6, 2) for k, v in t.items()}
+    out.update({"bound": bound, "frac": round(t[bound] / (step_us * 1e-6), 4)})
+    return out
 
 
 def roofline_entry(kernel: str, us: float, nbytes: int, flops: int, traffic) -> dict:
@@ -675,6 +707,7 @@ def main() -> int:
         "path_algorithmic_bytes": ab["path"],
         "score_mfma_util": round(score_flops / (t_score_us * 1e-6) / 1e12
                                  / MFMA_BF16_PEAK_TFLOPS, 4),
+        "binding_roofline": binding_roofline(spec, ab["path"], ms_step * 1e3),
         "us_per_call": {k: (round(v, 2) if isinstance(v, float) else v)
                         for k, v in us_call.items()},
         "us_per_kernel": {k: round(us, 2) for k, (us, n) in
@@ -685,6 +718,9 @@ def main() -> int:
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(spec, x, adaptive=adaptive)
+        if S <= 8192:
+            # short layers: the oracle on one host thread as well
+            out["cpu_baseline_1thread"] = cpu_baseline(spec, x, adaptive=adaptive, threads=1)
     print(json.dumps(out), flush=True)
     return 0
 
