@@ -603,7 +603,7 @@ def main() -> int:
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.kernels, args.title, args.command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the work shards by KV head with no exchange); run with --gpus 1", file=sys.stderr)
         return 2
     if args.copy_calibration:
