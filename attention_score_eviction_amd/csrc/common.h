@@ -71,6 +71,76 @@ __device__ __forceinline__ void block_bitonic_sort(uint64_t* key, int n2) {
   }
 }
 
+// Up to kWaveSortN keys are sorted by one wave in registers, 8 keys per lane
+// (element lane*8 + r in x[r]), with no workgroup barrier: the same ascending
+// bitonic network, its exchanges at distance j < 8 inside a lane and at
+// j >= 8 between lanes lane and lane ^ (j / 8).
+constexpr int kWaveSortN = 512;
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void wave_bitonic_sort512(uint64_t (&x)[8], int lane) {
+#pragma unroll
+  for (int k = 2; k <= kWaveSortN; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 8) {
+        const bool lower = (lane & (j >> 3)) == 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const bool asc = ((lane * 8 + r) & k) == 0;
+          const uint64_t y = shfl_xor_u64(x[r], j >> 3);
+          // the lower index of the pair keeps the minimum when ascending
+          x[r] = (asc == lower) ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if ((r ^ j) > r) {
+            const bool asc = ((lane * 8 + r) & k) == 0;
+            const uint64_t a = x[r], b = x[r ^ j];
+            const bool sw = (a > b) == asc;
+            x[r] = sw ? b : a;
+            x[r ^ j] = sw ? a : b;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Ascending sort of key[0, n2) in LDS (n2 a power of two; entries past the
+// data hold ~0): by the first wave in registers when n2 <= kWaveSortN, else
+// by the whole workgroup of NT threads.  Every thread of the block must
+// call; the sorted keys are visible to all threads on return.
+template <int NT>
+__device__ __forceinline__ void sort_keys(uint64_t* key, int n2) {
+  if (n2 <= kWaveSortN) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+      uint64_t x[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int e = lane * 8 + r;
+        x[r] = e < n2 ? key[e] : ~0ull;
+      }
+      wave_bitonic_sort512(x, lane);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int e = lane * 8 + r;
+        if (e < n2) key[e] = x[r];
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  block_bitonic_sort<NT>(key, n2);
+}
+
 // ---------------------------------------------------------------------------
 // Score launch plan.  Keys of one (batch, KV head) are split into chunks of
 // `chunk` keys (a multiple of the per-step key count); query rows of the head

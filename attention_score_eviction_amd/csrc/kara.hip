@@ -59,74 +59,6 @@ __device__ __forceinline__ uint32_t kara_block_scan(uint32_t v, uint32_t* total,
 // Position states.
 constexpr uint8_t kNone = 0, kTop = 1, kChunk = 2, kFill = 3;
 
-// Rows of up to kWaveSortN keys are sorted by one wave in registers, 8 keys
-// per lane (element lane*8 + r in x[r]), with no workgroup barrier: the same
-// ascending bitonic network as block_bitonic_sort, its exchanges at distance
-// j < 8 inside a lane and at j >= 8 between lanes lane and lane ^ (j / 8).
-constexpr int kWaveSortN = 512;
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ void wave_bitonic_sort512(uint64_t (&x)[8], int lane) {
-#pragma unroll
-  for (int k = 2; k <= kWaveSortN; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 8) {
-        const bool lower = (lane & (j >> 3)) == 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const bool asc = ((lane * 8 + r) & k) == 0;
-          const uint64_t y = shfl_xor_u64(x[r], j >> 3);
-          // the lower index of the pair keeps the minimum when ascending
-          x[r] = (asc == lower) ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          if ((r ^ j) > r) {
-            const bool asc = ((lane * 8 + r) & k) == 0;
-            const uint64_t a = x[r], b = x[r ^ j];
-            const bool sw = (a > b) == asc;
-            x[r] = sw ? b : a;
-            x[r ^ j] = sw ? a : b;
-          }
-        }
-      }
-    }
-  }
-}
-
-// Ascending sort of key[0, n2) (n2 a power of two; entries past the data hold
-// ~0): by one wave when n2 <= kWaveSortN (the array padded with ~0 up to
-// it), else by the whole workgroup.  Every thread of the block must call.
-__device__ __forceinline__ void kara_sort(uint64_t* key, int n2) {
-  if (n2 <= kWaveSortN) {
-    const int lane = threadIdx.x & 63;
-    if (threadIdx.x < 64) {
-      uint64_t x[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int e = lane * 8 + r;
-        x[r] = e < n2 ? key[e] : ~0ull;
-      }
-      wave_bitonic_sort512(x, lane);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int e = lane * 8 + r;
-        if (e < n2) key[e] = x[r];
-      }
-    }
-    __syncthreads();
-    return;
-  }
-  block_bitonic_sort<kKaraThreads>(key, n2);
-}
-
 __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
     const float* __restrict__ scores, int32_t* __restrict__ idx, int n, int buffer, int keep,
     int gamma, int alpha, int n_out) {
@@ -154,7 +86,7 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   __syncthreads();
 
   // Eq. 5: the first `keep` positions in (score desc, position asc) order form I.
-  kara_sort(key, n2);
+  sort_keys<kKaraThreads>(key, n2);
   for (int r = tid; r < keep; r += kKaraThreads) state[(uint32_t)key[r]] = kTop;
   __syncthreads();
 
@@ -204,7 +136,7 @@ __global__ void __launch_bounds__(kKaraThreads) kara_select_kernel(
   // chunk (-inf) sorts after every qualifying one.
   const int want_chunks = alpha / gamma;
   if (nchunk > 0) {
-    kara_sort(key, nc2);
+    sort_keys<kKaraThreads>(key, nc2);
     for (int r = tid; r < want_chunks && r < nchunk; r += kKaraThreads) {
       const int k = (int)(uint32_t)key[r];
       if (rk[k] > -INFINITY)

@@ -50,21 +50,37 @@ __global__ void __launch_bounds__(kQeRankThreads) qe_rank_kernel(
   int n2 = 1;
   while (n2 < nwin) n2 <<= 1;
   // Window sums: one wave per window, lane l adds token l, a fixed butterfly.
-  for (int j = wave; j < nwin; j += kQeRankThreads / 64) {
-    float x = s[(size_t)j * kQeWin + lane];
+  // A wave takes its windows j, j + NWV, ... kSumBatch at a time, with the
+  // scores, accumulated sums and tiers of the batch all loaded before the
+  // first sum (one memory latency per batch, not per window).
+  constexpr int NWV = kQeRankThreads / 64, kSumBatch = 8;
+  for (int j0 = wave; j0 < nwin; j0 += NWV * kSumBatch) {
+    float x[kSumBatch], old[kSumBatch];
+    int8_t t[kSumBatch];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) {
-      const float acc = w_acc[so + j] + x;
-      w_acc[so + j] = acc;
-      // an evicted window sorts after every live one (its key's top bits are
-      // all ones, above -inf's)
-      key[j] = tier[so + j] == 2 ? (0xffffffff00000000ull | (uint32_t)j) : desc_key(acc, j);
+    for (int b = 0; b < kSumBatch; ++b) {
+      const int j = min(j0 + b * NWV, nwin - 1);
+      x[b] = s[(size_t)j * kQeWin + lane];
+      old[b] = w_acc[so + j];
+      t[b] = tier[so + j];
+    }
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b) {
+      const int j = j0 + b * NWV;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) x[b] += __shfl_xor(x[b], off);
+      if (lane == 0 && j < nwin) {
+        const float acc = old[b] + x[b];
+        w_acc[so + j] = acc;
+        // an evicted window sorts after every live one (its key's top bits
+        // are all ones, above -inf's)
+        key[j] = t[b] == 2 ? (0xffffffff00000000ull | (uint32_t)j) : desc_key(acc, j);
+      }
     }
   }
   for (int j = nwin + tid; j < n2; j += kQeRankThreads) key[j] = ~0ull;
   __syncthreads();
-  block_bitonic_sort<kQeRankThreads>(key, n2);
+  sort_keys<kQeRankThreads>(key, n2);
   for (int r = tid; r < nwin; r += kQeRankThreads) rk[(uint32_t)key[r]] = r;
   __syncthreads();
   // Live windows occupy the first sorted positions, so a live window's sorted

@@ -66,16 +66,25 @@ __global__ void __launch_bounds__(kRankThreads) tier_rank_kernel(
   const float* s = scores + (size_t)head * S;
   int n2 = 1;
   while (n2 < nwin) n2 <<= 1;
-  // Window sums: one wave per window, lane l adds tokens l; tree in fixed order.
-  for (int j = wave; j < nwin; j += kRankThreads / 64) {
-    float x = s[(size_t)j * kWin + lane];
+  // Window sums: one wave per window, lane l adds tokens l; tree in fixed
+  // order.  A wave takes its windows j, j + NWV, ... kSumBatch at a time, all
+  // of a batch's loads issued before the first sum.
+  constexpr int NWV = kRankThreads / 64, kSumBatch = 8;
+  for (int j0 = wave; j0 < nwin; j0 += NWV * kSumBatch) {
+    float x[kSumBatch];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) key[j] = desc_key(x, j);
+    for (int b = 0; b < kSumBatch; ++b)
+      x[b] = s[(size_t)min(j0 + b * NWV, nwin - 1) * kWin + lane];
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) x[b] += __shfl_xor(x[b], off);
+      if (lane == 0 && j0 + b * NWV < nwin) key[j0 + b * NWV] = desc_key(x[b], j0 + b * NWV);
+    }
   }
   for (int j = nwin + tid; j < n2; j += kRankThreads) key[j] = ~0ull;
   __syncthreads();
-  block_bitonic_sort<kRankThreads>(key, n2);
+  sort_keys<kRankThreads>(key, n2);
   for (int r = tid; r < nwin; r += kRankThreads) rk[(uint32_t)key[r]] = r;
   __syncthreads();
   uint32_t cf = 0u, cq = 0u;
