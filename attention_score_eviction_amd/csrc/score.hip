@@ -636,12 +636,14 @@ __global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
       pass2_block32<NV, NQ, true>(lims, kf, qsv, lsv, as, kb, lane, c);
     else
       pass2_block32<NV, NQ, false>(lims, kf, qsv, lsv, as, kb, lane, c);
-    if (kb + NW * 64 < kend) load_key_block32<D>(kf, kh, kb + NW * 64, S, lane);
     as[0] += __shfl_xor(as[0], 32);
     as[1] += __shfl_xor(as[1], 32);
-    // lane l writes key kb + l: key tile l / 32, column l % 32
+    // lane l writes key kb + l: key tile l / 32, column l % 32.  The store
+    // goes out before the next block's key loads, so waiting for those keys
+    // (the vector-memory counter counts stores too) never waits for it.
     const float mine = (lane >> 5) ? as[1] : as[0];
     if (kb + lane < kend) out[kb + lane] = mine;
+    if (kb + NW * 64 < kend) load_key_block32<D>(kf, kh, kb + NW * 64, S, lane);
     pace_partner<NW>(prog, wave, lane, nblk);
   }
   __builtin_amdgcn_s_setprio(0);
