@@ -26,6 +26,9 @@ CASES = [
     ("pool-129", L(1, 8, 2, 128, 20000, 32, 129, 3000, structure="heavy"), 46),
     ("f32-long", L(1, 4, 2, 64, 20000, 16, 5, 1000, dtype="f32"), 47),
     ("noncausal", L(1, 8, 2, 128, 24000, 40, 7, 2500, causal=0, structure="heavy"), 48),
+    # two sequences on the 10-tile (G*W = 320) 8-wave passes, with sinks
+    ("batch2-gw320", L(2, 10, 2, 128, 20000, 64, 7, 1500, n_sink=4, structure="spans",
+                       n_spans=8), 50),
     # short rows (one workgroup per row): the gather fused into the select
     # while the kept rows fit its LDS list, else a separate gather
     ("short-8k", synth.config(2), 2),

@@ -50,6 +50,8 @@ SMALL = [
     ("bf16-long-noncausal", L(1, 8, 2, 128, 5000, 40, 3, 100, causal=0, structure="heavy"), 115),
     ("bf16-long-gw320", L(1, 10, 2, 128, 4100, 64, 7, 128, n_sink=4), 116),
     ("bf16-long-d64-gw384", L(1, 12, 2, 64, 4200, 64, 5, 100, structure="heavy"), 117),
+    ("bf16-long-batch2-gw320", L(2, 10, 2, 128, 4300, 64, 7, 200, n_sink=2, structure="heavy"),
+     118),
 ]
 
 
