@@ -74,7 +74,7 @@ WORKLOADS = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.hip", "qevict.hip",
-                  "common.h"]
+                  "common.h", "select_util.h"]
 
 
 def source_hash() -> str:

@@ -2,23 +2,42 @@
  * kvsel.h -- C ABI of the attention-score KV selection and compaction library
  * (libkvsel.so, HIP kernels for gfx950 / MI355X).
  *
- * One layer-end step of an observation-window KV eviction method, split into
- * the three calls of the path and an optional tier router:
+ * One layer-end step of an observation-window KV eviction method, as the
+ * three calls of the path:
  *
  *   kvsel_score    observation-window attention scores, reduced over the
  *                  window queries and the GQA group, then max-pooled
  *   kvsel_select   top-`budget` candidate positions per KV head, plus the
  *                  always-kept sinks and observation window
  *   kvsel_compact  gather of the kept K/V rows into a compact cache
- *   kvsel_route_tiers  contiguous-window routing into full / int4 / evicted
- *                  tiers with int4 quantisation and promotion by dequantisation
+ *
+ * and around them:
+ *   kvsel_layer_end, kvsel_layer_end_stream, kvsel_layer_end_adaptive
+ *                  the whole step in one call (radix select over the score
+ *                  vector; streaming top-k inside pass 2; one head-adaptive
+ *                  budget per sequence into a flattened cache)
+ *   kvsel_select_compact, kvsel_select_adaptive, kvsel_compact_flat
+ *                  select and gather in one call; the head-adaptive select
+ *                  and its flattened gather
+ *   kvsel_route_tiers, kvsel_qevict_step
+ *                  contiguous-window routing into full / low-bit / evicted
+ *                  tiers (one shot; repeated over decode steps with a
+ *                  backing store)
+ *   kvsel_kara_score, kvsel_kara_select, kvsel_kara_keep
+ *                  decode-window compression by bidirectional scores and
+ *                  chunked selection
+ *   kvsel_score_static  kvsel_score without a workspace argument
+ *   kvsel_timing_start, kvsel_timing_read  per-kernel device timing
  *
  * Sources (web pages this library implements; title, then section/equation):
  *   [TideKV] "TideKV: Delayed KV Eviction via Layer-Wise Chunked Prefill for
  *            Memory-Efficient Long-Context LLM Inference", Section 4.2
- *            (Eqs. 4-8), Algorithm 2 (LayerEndCompress), Algorithm 1.
+ *            (Eqs. 4-8), Algorithm 2 (LayerEndCompress), Algorithm 1,
+ *            Section 4.1 (head-adaptive budgets).
  *   [QEvict] "QEvict: Recoverable Quantized KV Eviction for Attention-Drift-
- *            Robust Long-Context Decoding", Sections 4.1-4.3.
+ *            Robust Long-Context Decoding", Sections 4.1-4.3, Appendix A.
+ *   [Kara]   "Kara: Efficient Reasoning LLM Serving via Sliding-Window KV
+ *            Cache Compression", Section 3 (Eqs. 4-8).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -68,7 +87,8 @@ typedef enum {
   KVSEL_ERR_ARG = 1,          /* bad shape, null or misaligned pointer, bad enum */
   KVSEL_ERR_BUDGET = 2,       /* budget outside [0, S - W - n_sink] */
   KVSEL_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the workspace query */
-  KVSEL_ERR_UNSUPPORTED = 4,  /* valid but not built (head_dim other than 64/128) */
+  KVSEL_ERR_UNSUPPORTED = 4,  /* valid but not built for these sizes (head_dim other
+                                 than 64/128, and the limits each call states) */
   KVSEL_ERR_DEVICE = 5        /* a HIP launch reported an error */
 } kvsel_status;
 
