@@ -52,6 +52,9 @@ SMALL = [
     ("bf16-long-d64-gw384", L(1, 12, 2, 64, 4200, 64, 5, 100, structure="heavy"), 117),
     ("bf16-long-batch2-gw320", L(2, 10, 2, 128, 4300, 64, 7, 200, n_sink=2, structure="heavy"),
      118),
+    # fp32 prompts past 4096 keys (16-row tiles), and the widest max filter
+    ("f32-long-d128", L(1, 4, 2, 128, 9000, 32, 5, 500, n_sink=1, dtype="f32"), 119),
+    ("bf16-long-pool129", L(1, 8, 2, 128, 5000, 32, 129, 300, structure="heavy"), 120),
 ]
 
 
