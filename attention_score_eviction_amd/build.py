@@ -35,6 +35,10 @@ FLAGS = [
     # logit with VALU instructions, so accumulator-register copies would
     # cost one extra instruction per logit
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the instruction-level-parallelism scheduling strategy: measured on the
+    # layer-end step at 128K, pass 1 91.4 -> 89.2 us with the other kernels
+    # within +-0.4 us and bit-identical results
+    "-mllvm", "-amdgpu-sched-strategy=max-ilp",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -78,11 +78,14 @@ KERNEL_SOURCES = ["score.hip", "select.hip", "compact.hip", "tiers.hip", "kara.h
 
 
 def source_hash() -> str:
-    """Hash of the kernel sources; counter figures are only valid for it."""
+    """Hash of the kernel sources and the compiler flags they are built
+    with; counter figures are only valid for it."""
+    from attention_score_eviction_amd.build import FLAGS
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "attention_score_eviction_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(FLAGS).encode())
     return h.hexdigest()[:16]
 
 
