@@ -693,10 +693,13 @@ def timing_read(max_kernels: int = 64) -> dict:
 
 
 def qevict_desc(k: torch.Tensor, *, seq_len: int, max_windows: int, n_sink: int,
-                n_recent: int, n_full: int, n_quant: int, bits: int = 2) -> QevictDesc:
-    """Descriptor for a cache k [Bt, Hkv, capacity, D] (bf16)."""
+                n_recent: int, n_full: int, n_quant: int, bits: int = 2,
+                win: int = 64) -> QevictDesc:
+    """Descriptor for a cache k [Bt, Hkv, capacity, D] (bf16).  `win` is
+    passed through as given; the library decides which window lengths it
+    supports (KVSEL_ERR_UNSUPPORTED otherwise)."""
     Bt, Hkv, cap, D = k.shape
-    return QevictDesc(Bt, Hkv, D, int(seq_len), cap, int(max_windows), 64, int(n_sink),
+    return QevictDesc(Bt, Hkv, D, int(seq_len), cap, int(max_windows), int(win), int(n_sink),
                       int(n_recent), int(n_full), int(n_quant), int(bits), _dtype_code(k))
 
 

@@ -269,6 +269,12 @@ def test_qevict_checks(kv):
     assert call(good, first=None) == kv.ERR_ARG
     assert call(good, first=FAKE + 4) == kv.ERR_ARG
     assert call(good, ws_bytes=need - 1) == kv.ERR_WORKSPACE
+    # the binding passes the window length through; the library rejects it
+    import torch
+    kd = kv.qevict_desc(torch.zeros((1, 2, 256, 64), dtype=torch.bfloat16), seq_len=256,
+                        max_windows=8, n_sink=0, n_recent=0, n_full=1, n_quant=1, win=32)
+    assert kd.win == 32 and L.kvsel_qevict_step_workspace(ctypes.byref(kd)) == 0
+    assert call(kd, ws_bytes=1 << 30) == kv.ERR_UNSUPPORTED
 
 
 def test_workspace_is_linear_in_prompt_not_window_times_prompt(kv):
