@@ -712,8 +712,8 @@ def qevict_state(qd: QevictDesc, device) -> dict:
         "w_acc": z((Bt, H, M), torch.float32),
         "tier": z((Bt, H, M), torch.int8),
         "has_codes": z((Bt, H, M), torch.uint8),
-        "k_codes": z((Bt, H, M, 64, D * qd.bits // 8), torch.uint8),
-        "v_codes": z((Bt, H, M, 64, D * qd.bits // 8), torch.uint8),
+        "k_codes": z((Bt, H, M, qd.win, D * qd.bits // 8), torch.uint8),
+        "v_codes": z((Bt, H, M, qd.win, D * qd.bits // 8), torch.uint8),
         "k_meta": z((Bt, H, M, D, 2), torch.float32),
         "v_meta": z((Bt, H, M, D, 2), torch.float32),
     }
