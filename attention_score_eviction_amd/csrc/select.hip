@@ -202,7 +202,15 @@ __global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ po
           bin[e] = (x[e] >> shift) & (uint32_t)(nb - 1);
           act |= (uint32_t)(((valid >> e) & 1u) && (x[e] & pmask) == prefix) << e;
         }
-        hist_add_runs(hh, bin, act);
+        if (r == 0) {
+          hist_add_runs(hh, bin, act);
+        } else {
+          // later digits count only the scores that share the prefix, a
+          // few per thread: one masked atomic each
+#pragma unroll
+          for (int e = 0; e < kPerThread; ++e)
+            if ((act >> e) & 1u) atomicAdd(&hh[bin[e]], 1u);
+        }
       });
       __syncthreads();
       if (r == 0) block_find_digit<2048>(hh, rem, pick);
@@ -234,35 +242,43 @@ __global__ void __launch_bounds__(NT) select_kernel(const float* __restrict__ po
       const uint32_t ngt = __popc(gt), neq = __popc(eq);
       uint32_t tot;
       const uint32_t ex = block_exclusive_scan<NT>((ngt << 16) | neq, &tot, wsum);
-      uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
+      const uint32_t gtb = cgt + (ex >> 16), eqb = ceq + (ex & 0xffffu);
+      // Every score above the prefix is kept, and the first need_eq equal
+      // ones of the group: eq_before of them lie in earlier threads, this
+      // thread keeps its first `take`.  Both come from min() so that no
+      // unsigned difference can wrap (the guarded form
+      // `eqb < need_eq ? need_eq - eqb : 0` was compiled without its guard
+      // by this toolchain, which misplaced every pick after a tie run).
+      const uint32_t eq_before = min(eqb, need_eq);
+      const uint32_t take = min(neq, need_eq - eq_before);
+      uint32_t keep = gt;
+      for (uint32_t i = 0, m = eq; i < take; ++i) {
+        keep |= m & (0u - m);
+        m &= m - 1u;
+      }
+      // The kept scores of this thread take consecutive slots from `slot`,
+      // in position order.
+      uint32_t slot = gtb + eq_before;
       int32_t* oh = out + h * seg + n_sink;
       uint32_t nw = 0u;
-#pragma unroll
-      for (int e = 0; e < kPerThread; ++e) {
+      while (keep) {
+        const int e = __builtin_ctz(keep);
+        keep &= keep - 1u;
         // slot < budget always holds for finite non-negative scores; the
         // guard keeps malformed input from writing outside this group.
-        if ((gt >> e) & 1u) {
-          const uint32_t slot = gtb + min(eqb, need_eq);
-          if (slot < (uint32_t)budget) {
-            if (writer) oh[slot] = p0 + e;
-            if constexpr (GATHER) sidx[h * seg + n_sink + slot] = p0 + e;
-            ++nw;
-          }
-          ++gtb;
-        } else if ((eq >> e) & 1u) {
-          const uint32_t slot = gtb + eqb;
-          if (eqb < need_eq && slot < (uint32_t)budget) {
-            if (writer) oh[slot] = p0 + e;
-            if constexpr (GATHER) sidx[h * seg + n_sink + slot] = p0 + e;
-            ++nw;
-          }
-          ++eqb;
+        if (slot < (uint32_t)budget) {
+          if (writer) oh[slot] = p0 + e;
+          if constexpr (GATHER) sidx[h * seg + n_sink + slot] = p0 + e;
+          ++nw;
         }
+        ++slot;
       }
-      if (nw) atomicAdd(&kept[h], nw);
+      if (hg > 1 && nw) atomicAdd(&kept[h], nw);
       cgt += tot >> 16;
       ceq += tot & 0xffffu;
     });
+    // One head: its pick count is the number of slots filled.
+    if (hg == 1 && tid == 0) kept[0] = min((uint32_t)budget, cgt + min(ceq, need_eq));
   }
   __syncthreads();
   // Mandatory rows and head offsets from the per-head pick counts.

@@ -158,7 +158,7 @@ def test_score_is_deterministic():
 
 
 @pytest.mark.parametrize("seed,S", [(0, 9000), (1, 9777), (2, 10554), (3, 70001), (4, 131072),
-                                    (5, 50000)])
+                                    (5, 50000), (6, 8000), (7, 4000), (8, 2000)])
 def test_select_exact_on_identical_inputs(seed, S):
     """Given the same fp32 scores, the GPU selection is bit-exact with the
     oracle's (ties -> lowest positions), including heavy tie plateaus."""
@@ -171,7 +171,7 @@ def test_select_exact_on_identical_inputs(seed, S):
         # a dense band of near-equal values around the threshold
         p = (np.float32(1.0) + rng.integers(0, 3000, size=(Bt, Hkv, S)).astype(np.float32)
              * np.float32(2.0 ** -20)).astype(np.float32)
-    elif seed in (1, 3):
+    elif seed in (1, 3, 6, 8):
         p = rng.integers(0, 5, size=(Bt, Hkv, S)).astype(np.float32) * np.float32(0.25)
     else:
         p = np.full((Bt, Hkv, S), 0.125, np.float32)
@@ -180,11 +180,40 @@ def test_select_exact_on_identical_inputs(seed, S):
     p[..., :n_sink] = 0
     p[..., S - W:] = 0
     pt = torch.from_numpy(p).cuda()
-    for budget in [1, 7, 1000, 4096, S - W - n_sink]:
+    for budget in [b for b in (1, 7, 1000, 4096, S - W - n_sink) if b <= S - W - n_sink]:
         got = kvsel.select(pt, budget, obs_window=W, n_q_heads=Hkv, head_dim=128,
                            n_sink=n_sink).cpu().numpy()
         want = oracle.select(p.astype(np.float64), budget, n_sink, W)
         np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("S,kind,budget", [(8192, "quarters", 1024), (8192, "plateau", 1024),
+                                           (8192, "quarters", 3), (4000, "band", 700),
+                                           (2000, "quarters", 1500)])
+def test_select_compact_short_rows_with_ties(S, kind, budget):
+    """The one-launch select + gather of short rows against the oracle when
+    many scores tie at the cut: the ties before a thread that are not kept
+    must not shift that thread's picks."""
+    kvsel = _kvsel()
+    rng = np.random.default_rng(S + budget)
+    Bt, Hkv, Hq, D, W, n_sink = 1, 4, 16, 128, 32, 2
+    p = _tie_heavy_scores(rng, kind, (Bt, Hkv, S))
+    p[..., :n_sink] = 0
+    p[..., S - W:] = 0
+    k = torch.from_numpy(rng.standard_normal((Bt, Hkv, S, D)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((Bt, Hkv, S, D)).astype(np.float32)).to(torch.bfloat16)
+    print(f"case select_compact ties S={S} kind={kind} budget={budget}", flush=True)
+    idx, k_out, v_out = kvsel.select_compact(torch.from_numpy(p).cuda(), k.cuda(), v.cuda(),
+                                             budget, obs_window=W, n_q_heads=Hq, n_sink=n_sink)
+    torch.cuda.synchronize()
+    want = oracle.select(p.astype(np.float64), budget, n_sink, W)
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+    kb = k.view(torch.int16).numpy()
+    vb = v.view(torch.int16).numpy()
+    np.testing.assert_array_equal(k_out.view(torch.int16).cpu().numpy(),
+                                  np.take_along_axis(kb, want[..., None], axis=2))
+    np.testing.assert_array_equal(v_out.view(torch.int16).cpu().numpy(),
+                                  np.take_along_axis(vb, want[..., None], axis=2))
 
 
 @pytest.mark.parametrize("S,kind", [(4194365, "band"), (4194366, "plateau")])
