@@ -160,6 +160,8 @@ struct ScorePlan {
   int ngroups;    // ceil(GW / qcap)
   int chunk;      // keys per workgroup
   int nchunk;     // ceil(S / chunk)
+  int fold_tl;    // >= 0: no combine kernel; pass 2 merges the statistics
+                  // with 2^fold_tl partial merges per row (few rows and chunks)
   size_t off_part, off_lse, off_raw, off_grp, total;   // workspace layout (bytes)
 };
 
@@ -168,21 +170,25 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p);
 struct ScoreArgs {
   const void* q;       // [Bt,Hq,W,D]
   const void* k;       // [Bt,Hkv,S,D]
-  float2* part;        // [nheads][nchunk][GWr] (max, sum) in log2 units
+  float2* part;        // [nheads][GWr][nchunk] (max, sum) in log2 units
   float* lse;          // [nheads][GWr] row log2-sum-exp
   float* s_out;        // [ngroups][nheads][S] (ngroups == 1: the raw scores)
   int Hq, Hkv, G, W, S, GW, GWr, qcap, chunk, nchunk, causal;
   int kstride;         // key rows between consecutive KV heads in k (>= S)
   float c;             // scale * log2(e)
-  uint32_t* zero;      // cleared by the combine kernel (may be null)
-  long zero_words;
+  uint32_t* zero;      // cleared by the combine kernel, or by pass 1 when
+  long zero_words;     // pass 2 merges the statistics itself (may be null)
+  int fold_tl;         // >= 0: pass 2 merges each row's chunk statistics
+                       // itself, in the combine kernel's order with
+                       // 2^fold_tl partial merges per row; -1: it reads lse
 };
 
 // kstride: key rows per KV head in k (the head's first seq_len rows are
 // scored); pooled may be null (no max-pool launched) for callers that only
 // need the raw scores.
-// zero / zero_words: a buffer the score launch clears on the way (inside
-// the row-statistics combine), for a select that follows on the stream.
+// zero / zero_words: a buffer the score launch clears on the way (in the
+// row-statistics combine, or in pass 1 when there is none), for a select
+// that follows on the stream.
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
                           hipStream_t stream, int kstride, uint32_t* zero = nullptr,

@@ -105,9 +105,65 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ void lse_merge(float& m, float& z, float mo, float zo) {
   const float mn = fmaxf(m, mo);
   const float mu = (mn == -INFINITY) ? 0.f : mn;
-  z = z * __builtin_amdgcn_exp2f(m - mu) + zo * __builtin_amdgcn_exp2f(mo - mu);
+  // one explicit fma, so every caller rounds alike
+  z = fmaf(z, __builtin_amdgcn_exp2f(m - mu), zo * __builtin_amdgcn_exp2f(mo - mu));
   m = mn;
 }
+
+// The combine kernel's row statistics, computed inside pass 2 for plans
+// with few rows and chunks (no combine launch): the workgroup's threads take
+// the combine's lanes in its order, tpr = 2^tl adjacent lanes per row, lane
+// sub merging chunks sub, sub + tpr, sub + 2 tpr, sub + 3 tpr (the one block
+// of four each combine lane takes when nchunk <= 4 tpr, which the plan
+// keeps) and the same xor-shuffle tree, so the result is the combine's bit
+// for bit, with the loads of adjacent lanes coalesced.  Chunks past the end
+// merge (-inf, 0), which leaves (m, z) unchanged (fma(z, 2^0, 0)), so no
+// merge needs a branch; their z is the loaded sum times 0 (sums are finite
+// and >= 0), so every load is used and stays unconditional.  ls[r] receives
+// row r's log2-sum-exp for r < nrows.
+constexpr int kFoldMaxTpr = 8;
+
+template <int NT, int ROWS>
+struct FoldRows {
+  static constexpr int IT = (ROWS * kFoldMaxTpr + NT - 1) / NT;
+  float2 pz[IT][4];
+
+  // The loads, issued early (nothing waits for them until merge()).
+  __device__ __forceinline__ void load(const float2* __restrict__ part, int nchunk, int tl,
+                                       int nrows) {
+    const int tpr = 1 << tl, tasks = ROWS << tl, tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int it = min(i * NT + tid, tasks - 1);
+      const int row = min(it >> tl, nrows - 1), sub = it & (tpr - 1);
+      const float2* p = part + (size_t)row * nchunk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pz[i][j] = p[min(sub + j * tpr, nchunk - 1)];
+    }
+  }
+
+  __device__ __forceinline__ void merge(int nchunk, int tl, int nrows, float* ls) const {
+    const int tpr = 1 << tl, tasks = ROWS << tl, tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      if (i * NT >= tasks) break;   // uniform over the workgroup
+      const int it = i * NT + tid;
+      const int row = it >> tl, sub = it & (tpr - 1);
+      float m = -INFINITY, z = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = it < tasks && row < nrows && sub + j * tpr < nchunk;
+        lse_merge(m, z, in ? pz[i][j].x : -INFINITY, pz[i][j].y * (in ? 1.f : 0.f));
+      }
+      for (int off = tpr >> 1; off >= 1; off >>= 1) {
+        const float mo = __shfl_xor(m, off);
+        const float zo = __shfl_xor(z, off);
+        lse_merge(m, z, mo, zo);
+      }
+      if (it < tasks && row < nrows && sub == 0) ls[row] = m + log2f(z);
+    }
+  }
+};
 
 // Causal limit of a query row: the last key it may see.
 __device__ __forceinline__ int key_limit(const ScoreArgs& a, int qrow) {
@@ -547,6 +603,12 @@ __global__ void __launch_bounds__(NW * 64) score_pass1_32(ScoreArgs a) {
   const uint16_t* qg = (const uint16_t*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
   stage_queries32<D, NT>(qs, qg, nrows, NQ);
   for (int r = tid; r < NQ * 32; r += NT) lims[r] = key_limit(a, row0 + r);
+  if (a.fold_tl >= 0 && a.zero) {
+    // no combine launch follows: the select's buffer is cleared here
+    const long nthr = (long)gridDim.x * gridDim.y * gridDim.z * NT;
+    const long gt = ((long)(blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * NT + tid;
+    for (long i = gt; i < a.zero_words; i += nthr) a.zero[i] = 0u;
+  }
   __shared__ int prog[NW];
   if (tid < NW) prog[tid] = 0;
   int nblk = 0;
@@ -613,12 +675,21 @@ __global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
   int kb = k0 + wave * 64;
   Frag<NV> kf[2];
   if (kb < kend) load_key_block32<D>(kf, kh, kb, S, lane);
+  // No combine launch: this workgroup merges its rows' chunk statistics,
+  // their loads in flight with the keys and queries.
+  const bool fold = a.fold_tl >= 0;
+  FoldRows<NT, NQ * 32> fr;
+  if (fold) fr.load(a.part + ((size_t)head * a.GWr + row0) * a.nchunk, a.nchunk, a.fold_tl, nrows);
   const uint16_t* qg = (const uint16_t*)a.q + ((size_t)(b * a.Hq + hk * a.G) * a.W + row0) * D;
   stage_queries32<D, NT>(qs, qg, nrows, NQ);
   for (int r = tid; r < NQ * 32; r += NT) {
     // rows past the group's end get an infinite normaliser (weight 0)
-    ls[r] = (r < nrows) ? a.lse[(size_t)head * a.GWr + row0 + r] : INFINITY;
+    ls[r] = (r < nrows && !fold) ? a.lse[(size_t)head * a.GWr + row0 + r] : INFINITY;
     lims[r] = key_limit(a, row0 + r);
+  }
+  if (fold) {
+    __syncthreads();
+    fr.merge(a.nchunk, a.fold_tl, nrows, ls);
   }
   __shared__ int prog[NW];
   if (tid < NW) prog[tid] = 0;
@@ -946,6 +1017,11 @@ void launch_passes(const ScoreArgs& args, dim3 grid, hipStream_t stream, const S
 template <int D, int NQ, int NW>
 void launch_passes32(const ScoreArgs& args, dim3 grid, hipStream_t stream, const ScorePlan& p) {
   KVSEL_LAUNCH("score_pass1_32", (score_pass1_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream, args);
+  if (args.fold_tl >= 0) {
+    KVSEL_LAUNCH("score_pass2_32", (score_pass2_32<D, NQ, NW>), grid, dim3(NW * 64), 0, stream,
+                 args);
+    return;
+  }
   int tl = 0;
   while ((4 << tl) < p.nchunk && tl < 6) ++tl;
   const long lanes = ((long)p.nheads * p.GW) << tl;
@@ -1035,6 +1111,10 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   return plan_chunks(d, p, maxqt * tile_bytes + maxqt * 16 * 8);
 }
 
+// Chunk statistics (rows x chunks) up to which pass 2 merges them itself:
+// the 8K layer's 128 rows x 32 chunks, 32 KiB of L2 reads per workgroup.
+constexpr long kFoldMaxPartials = 4096;
+
 // Key chunks and the workspace layout for a plan whose tiles are chosen.
 static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes) {
   // Key chunk: a multiple of one workgroup step, sized so the grid is about
@@ -1053,6 +1133,16 @@ static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes) {
   if (steps < 1) steps = 1;
   p->chunk = (int)(steps * step);
   p->nchunk = (d.seq_len + p->chunk - 1) / p->chunk;
+  // Few rows and chunks: every pass-2 workgroup merges its rows' chunk
+  // statistics (at most kFoldMaxPartials reads from the L2) rather than
+  // waiting for a combine launch.
+  p->fold_tl = -1;
+  if (p->mfma32 && p->ngroups == 1 && (long)p->GW * p->nchunk <= kFoldMaxPartials) {
+    // the combine's lanes per row: the fewest with 4 << tl >= nchunk
+    int tl = 0;
+    while ((4 << tl) < p->nchunk && tl < 6) ++tl;
+    if (tl <= 3) p->fold_tl = tl;
+  }
   size_t off = 0;
   p->off_part = off;
   off = align256(off + (size_t)p->nheads * p->nchunk * p->GWr * sizeof(float2));
@@ -1090,6 +1180,7 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   a.chunk = p.chunk;
   a.nchunk = p.nchunk;
   a.causal = d.causal;
+  a.fold_tl = p.mfma32 ? p.fold_tl : -1;
   const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
   a.c = scale * kLog2e;
   const dim3 grid(p.nchunk, p.nheads, p.ngroups);
@@ -1171,6 +1262,7 @@ kvsel_status launch_score_stream(const kvsel_desc& d, const ScorePlan& p, const 
   a.causal = d.causal;
   a.zero = nullptr;
   a.zero_words = 0;
+  a.fold_tl = -1;   // the streaming pass 2 reads lse from the combine
   const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
   a.c = scale * kLog2e;
   const dim3 grid(p.nchunk, p.nheads, 1);
