@@ -2,10 +2,11 @@
 //
 // Every precondition is checked on the host before anything is enqueued, and
 // no check calls the HIP runtime, so invalid calls fail the same way on a
-// machine without a GPU.  Two environment switches help debugging:
+// machine without a GPU.  Environment switches help debugging:
 // KVSEL_VALIDATE_ONLY=1 returns after the checks without enqueuing anything,
 // KVSEL_SYNC=1 waits for the stream after each call and reports a device
-// error as KVSEL_ERR_DEVICE.
+// error as KVSEL_ERR_DEVICE, KVSEL_SCORE_COMBINE=1 keeps the separate
+// statistics combine launch for every score plan (read in launch_score).
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>

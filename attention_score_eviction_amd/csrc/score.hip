@@ -27,6 +27,8 @@
 //    rows on the MFMA rows (each lane keeps the running column sum for one key).
 //  * Exponentials are exp2 with scale*log2(e) folded into one FMA per logit.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -1180,7 +1182,10 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   a.chunk = p.chunk;
   a.nchunk = p.nchunk;
   a.causal = d.causal;
-  a.fold_tl = p.mfma32 ? p.fold_tl : -1;
+  // KVSEL_SCORE_COMBINE=1 (debugging): the combine launch for every plan
+  const char* force = getenv("KVSEL_SCORE_COMBINE");
+  const bool combine = force && force[0] && strcmp(force, "0") != 0;
+  a.fold_tl = (p.mfma32 && !combine) ? p.fold_tl : -1;
   const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)d.head_dim);
   a.c = scale * kLog2e;
   const dim3 grid(p.nchunk, p.nheads, p.ngroups);

@@ -67,7 +67,10 @@
  *  - Debugging switches, read from the environment at every call:
  *    KVSEL_VALIDATE_ONLY=1 makes a call return after its checks without
  *    enqueuing anything; KVSEL_SYNC=1 makes a call wait for its stream and
- *    report a device error (a failed or faulting kernel) as KVSEL_ERR_DEVICE.
+ *    report a device error (a failed or faulting kernel) as KVSEL_ERR_DEVICE;
+ *    KVSEL_SCORE_COMBINE=1 makes the score passes always merge the row
+ *    statistics in a separate launch (small problems otherwise merge them
+ *    inside the second pass; both give the same bits).
  *  - The library keeps no state between calls, except the optional kernel
  *    timing of kvsel_timing_start (off unless turned on) and the static
  *    scratch array of kvsel_score_static.

@@ -58,3 +58,45 @@ def test_validate_only_mode_enqueues_nothing(monkeypatch):
     torch.cuda.synchronize()
     assert (idx == -7).all() and (raw == 5.0).all() and (pooled == 6.0).all()
     assert not k_out.view(torch.int16).any() and not v_out.view(torch.int16).any()
+
+
+def _kernels_of(call):
+    """Names of the kernels one call launches (the library's launch timing)."""
+    import attention_score_eviction_amd as kvsel
+    torch.cuda.synchronize()
+    kvsel.timing_read()
+    kvsel.timing_start("*")
+    try:
+        out = call()
+        torch.cuda.synchronize()
+    finally:
+        kvsel.timing_start(None)
+    return out, set(kvsel.timing_read())
+
+
+def test_score_combine_mode_gives_the_same_bits(monkeypatch):
+    """Small score problems (the 8K layer, the decode-time routing step) merge
+    the per-chunk row statistics inside the second pass, in the combine
+    kernel's order; KVSEL_SCORE_COMBINE=1 runs the separate combine launch
+    instead.  Raw scores, selection and compacted cache are the same bits."""
+    import attention_score_eviction_amd as kvsel
+    spec, (q, k, v) = _layer()
+    kw = dict(budget=spec.budget, pool_kernel=spec.pool_kernel)
+    a, names_a = _kernels_of(lambda: kvsel.layer_end(q, k, v, **kw))
+    monkeypatch.setenv("KVSEL_SCORE_COMBINE", "1")
+    b, names_b = _kernels_of(lambda: kvsel.layer_end(q, k, v, **kw))
+    monkeypatch.setenv("KVSEL_SCORE_COMBINE", "0")
+    assert "score_combine" not in names_a and "score_combine" in names_b
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+    # eight decode queries per KV head over 32K keys, two sequences
+    g = torch.Generator(device="cuda").manual_seed(5)
+    qd = torch.randn((2, 32, 8, 128), generator=g, device="cuda").to(torch.bfloat16)
+    kd = torch.randn((2, 8, 32768, 128), generator=g, device="cuda").to(torch.bfloat16)
+    (p1, s1), names_1 = _kernels_of(lambda: kvsel.score(qd, kd, pool_kernel=1, causal=False))
+    monkeypatch.setenv("KVSEL_SCORE_COMBINE", "1")
+    (p2, s2), names_2 = _kernels_of(lambda: kvsel.score(qd, kd, pool_kernel=1, causal=False))
+    monkeypatch.setenv("KVSEL_SCORE_COMBINE", "0")
+    assert "score_combine" not in names_1 and "score_combine" in names_2
+    assert torch.equal(s1, s2) and torch.equal(p1, p2)
