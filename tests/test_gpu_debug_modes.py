@@ -100,3 +100,22 @@ def test_score_combine_mode_gives_the_same_bits(monkeypatch):
     monkeypatch.setenv("KVSEL_SCORE_COMBINE", "0")
     assert "score_combine" not in names_1 and "score_combine" in names_2
     assert torch.equal(s1, s2) and torch.equal(p1, p2)
+
+
+def test_score_combine_mode_ragged_query_group(monkeypatch):
+    """A query group that does not fill its 32-row tiles (G·W = 5 x 8 = 40
+    rows in two tiles) over 8K keys: the rows past the group's end take no
+    part in the merged statistics, with or without the combine launch."""
+    import attention_score_eviction_amd as kvsel
+    g = torch.Generator(device="cuda").manual_seed(6)
+    q = torch.randn((1, 40, 8, 128), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, 8, 8192, 128), generator=g, device="cuda").to(torch.bfloat16)
+    (p1, s1), names_1 = _kernels_of(lambda: kvsel.score(q, k, pool_kernel=5))
+    monkeypatch.setenv("KVSEL_SCORE_COMBINE", "1")
+    (p2, s2), names_2 = _kernels_of(lambda: kvsel.score(q, k, pool_kernel=5))
+    monkeypatch.setenv("KVSEL_SCORE_COMBINE", "0")
+    assert "score_combine" not in names_1 and "score_combine" in names_2
+    assert torch.equal(s1, s2) and torch.equal(p1, p2)
+    # every query row's weights sum to one: each key column sums to the
+    # group's 40 rows in total
+    assert abs(float(s1.double().sum()) - 8 * 40) < 1e-2
