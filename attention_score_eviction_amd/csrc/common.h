@@ -162,6 +162,8 @@ struct ScorePlan {
   int nchunk;     // ceil(S / chunk)
   int fold_tl;    // >= 0: no combine kernel; pass 2 merges the statistics
                   // with 2^fold_tl partial merges per row (few rows and chunks)
+  bool keys_lds;  // one launch with the head's keys in LDS (no causal mask,
+                  // at most 512 keys, many query rows)
   size_t off_part, off_lse, off_raw, off_grp, total;   // workspace layout (bytes)
 };
 

@@ -723,6 +723,151 @@ __global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Keys in LDS, query rows streamed: for scoring without a causal mask over a
+// few keys by many query rows (Kara's decode window: G*|W| = 2048 rows per
+// KV head against its 448 compressible keys).  One workgroup per KV head
+// holds the head's S keys (a multiple of 32, at most 512) in LDS in fragment
+// order.  Each wave takes
+// 32-row query tiles straight from memory into registers and, with the same
+// fragments, first finds each row's max and log2-sum-exp over all keys
+// (keys on the matrix rows: one row per lane), then adds the row's
+// normalised weights into per-key column sums kept in registers (rows on the
+// matrix rows: one key per lane).  The waves' column sums are added in wave
+// order at the end.  Every key row and every query row is read once; there
+// are no per-chunk statistics and no combine launch.
+constexpr int kKsMaxKeyTiles = 16;   // up to 512 keys
+constexpr int kKsWaves = 8;
+
+template <int D, int NKT>
+__global__ void __launch_bounds__(kKsWaves * 64) score_keys_lds32(ScoreArgs a) {
+  constexpr int NV = D / 16, NW = kKsWaves, NT = NW * 64;
+  static_assert(NKT >= 1 && NKT <= kKsMaxKeyTiles, "key tiles");
+  __shared__ u32x4_t kl[NKT * NV * 64];   // key tile kt, fragment v, lane
+  __shared__ float csum[NW][NKT * 32];    // each wave's column sums
+  __shared__ __attribute__((aligned(16))) float lsw[NW][32];   // a tile's row normalisers
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int head = blockIdx.x, b = head / a.Hkv, hk = head - b * a.Hkv;
+  const int S = a.S, GW = a.GW;   // S == 32 * NKT: no key is masked
+  const float c = a.c;
+  if (a.zero) {
+    // the select that follows finds its histograms cleared
+    for (long i = (long)head * NT + tid; i < a.zero_words; i += (long)gridDim.x * NT)
+      a.zero[i] = 0u;
+  }
+  const char* kh = (const char*)((const uint16_t*)a.k + (size_t)head * a.kstride * D);
+  for (int tv = wave; tv < NKT * NV; tv += NW) {
+    const int kt = tv / NV, v = tv - kt * NV;
+    const int row = kt * 32 + r;
+    const char* src = kh + (size_t)row * (D * 2) + h * D + 16 * v;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)(kl + tv * 64),
+                                     16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const uint16_t* qg = (const uint16_t*)a.q + (size_t)(b * a.Hq + hk * a.G) * a.W * D;
+  // Key fragments are read from LDS at every use: each pass reads them
+  // through its own opaque copy of the base, or the compiler would keep the
+  // first pass's fragments of every tile in registers for the second.
+  auto kfrag = [&](const u32x4_t* base, int kt) {
+    Frag<NV> f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) f.v[i] = base[(kt * NV + i) * 64 + lane];
+    return f;
+  };
+  float cs[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) cs[kt] = 0.f;
+  const int ntq = (GW + 31) / 32;
+  for (int t = wave; t < ntq; t += NW) {
+    Frag<NV> qf;
+    {
+      const int row = min(t * 32 + r, GW - 1);
+      const char* src = (const char*)(qg + (size_t)row * D) + h * D;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) qf.v[i] = *(const u32x4_t*)(src + 16 * i);
+    }
+    // First pass: cur[i] is key kt*32 + 8*(i/4) + 4h + i%4 of query row r.
+    float m = -INFINITY, z = 0.f;
+    {
+      int off = 0;
+      asm volatile("" : "+v"(off));
+      const u32x4_t* k1 = kl + off;
+      f32x16_t acc[2];
+      acc[0] = mma32<NV>(kfrag(k1, 0), qf, zero16());
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        f32x16_t& cur = acc[kt & 1];
+        if (kt + 1 < NKT) acc[(kt + 1) & 1] = mma32<NV>(kfrag(k1, kt + 1), qf, zero16());
+        const float mnew = fmaxf(m, max16(cur) * c);
+        const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+        float e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(cur[i], c, -mu));
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int i = 0; i < w; ++i) e[i] += e[i + w];
+        z = fmaf(z, __builtin_amdgcn_exp2f(m - mu), e[0]);
+        m = mnew;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Lanes r and r + 32 hold the two key halves of row r.
+    lse_merge(m, z, __shfl_xor(m, 32), __shfl_xor(z, 32));
+    // rows past the group's end get an infinite normaliser (weight 0)
+    if (h == 0) lsw[wave][r] = (t * 32 + r < GW) ? m + log2f(z) : INFINITY;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4_t lq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lq[j] = *(const f32x4_t*)&lsw[wave][8 * j + 4 * h];
+    // Second pass: cur[i] is query row 8*(i/4) + 4h + i%4 of key kt*32 + r.
+    {
+      int off = 0;
+      asm volatile("" : "+v"(off));
+      const u32x4_t* k2 = kl + off;
+      f32x16_t acc[2];
+      acc[0] = mma32<NV>(qf, kfrag(k2, 0), zero16());
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        f32x16_t& cur = acc[kt & 1];
+        if (kt + 1 < NKT) acc[(kt + 1) & 1] = mma32<NV>(qf, kfrag(k2, kt + 1), zero16());
+        float e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          e[i] = __builtin_amdgcn_exp2f(fmaf(cur[i], c, -lq[i >> 2][i & 3]));
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int i = 0; i < w; ++i) e[i] += e[i + w];
+        cs[kt] += e[0];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // lsw is rewritten by the next tile only after every lane read it
+    __builtin_amdgcn_wave_barrier();
+  }
+  // Lanes r and r + 32 hold the two row halves of key kt*32 + r.
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    const float v = cs[kt] + __shfl_xor(cs[kt], 32);
+    if (h == 0) csum[wave][kt * 32 + r] = v;
+  }
+  __syncthreads();
+  float* out = a.s_out + (size_t)head * S;
+  for (int j = tid; j < S; j += NT) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += csum[w][j];
+    out[j] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pass 2 with the streaming top-k of TideKV Algorithm 2 (the heap of pass 2):
 // no per-key score vector leaves the workgroup.  A workgroup computes the
 // raw scores of its key chunk plus one 64-key block on either side (the
@@ -1084,6 +1229,10 @@ bool plan_score(const kvsel_desc& d, ScorePlan* p) {
   // re-reading its key chunk.
   // 32x32 tiles for bf16 prompts of 4096 keys or more; the 16x16 form is
   // faster on short key ranges (the 448-key decode window: 304 vs 353 us).
+  // No causal mask, few keys, many query rows (a decode window scoring its
+  // own keys): one workgroup per KV head with the keys in LDS.
+  p->keys_lds = d.dtype == KVSEL_BF16 && !d.causal && d.seq_len <= kKsMaxKeyTiles * 32 &&
+                d.seq_len % 32 == 0 && p->GW >= 256 && (d.head_dim == 64 || d.head_dim == 128);
   p->mfma32 = d.dtype == KVSEL_BF16 && d.seq_len >= 4096;
   if (p->mfma32) {
     // 32-row tiles: the whole group when it fits 10 tiles (8 waves), else
@@ -1158,6 +1307,38 @@ static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes) {
   return true;
 }
 
+template <int D, int NKT>
+static void launch_keys_lds(const ScoreArgs& a, int nheads, hipStream_t stream) {
+  KVSEL_LAUNCH("score_keys_lds32", (score_keys_lds32<D, NKT>), dim3(nheads), dim3(kKsWaves * 64),
+               0, stream, a);
+}
+
+// The keys-in-LDS scoring for S keys (a multiple of 32): the kernel built for
+// S / 32 tiles.
+template <int D>
+static bool dispatch_keys_lds(int S, const ScoreArgs& a, int nheads, hipStream_t stream) {
+  if (S % 32 != 0) return false;
+  switch (S / 32) {
+    case 1: launch_keys_lds<D, 1>(a, nheads, stream); return true;
+    case 2: launch_keys_lds<D, 2>(a, nheads, stream); return true;
+    case 3: launch_keys_lds<D, 3>(a, nheads, stream); return true;
+    case 4: launch_keys_lds<D, 4>(a, nheads, stream); return true;
+    case 5: launch_keys_lds<D, 5>(a, nheads, stream); return true;
+    case 6: launch_keys_lds<D, 6>(a, nheads, stream); return true;
+    case 7: launch_keys_lds<D, 7>(a, nheads, stream); return true;
+    case 8: launch_keys_lds<D, 8>(a, nheads, stream); return true;
+    case 9: launch_keys_lds<D, 9>(a, nheads, stream); return true;
+    case 10: launch_keys_lds<D, 10>(a, nheads, stream); return true;
+    case 11: launch_keys_lds<D, 11>(a, nheads, stream); return true;
+    case 12: launch_keys_lds<D, 12>(a, nheads, stream); return true;
+    case 13: launch_keys_lds<D, 13>(a, nheads, stream); return true;
+    case 14: launch_keys_lds<D, 14>(a, nheads, stream); return true;
+    case 15: launch_keys_lds<D, 15>(a, nheads, stream); return true;
+    case 16: launch_keys_lds<D, 16>(a, nheads, stream); return true;
+    default: return false;
+  }
+}
+
 kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q, const void* k,
                           float* raw, float* pooled, int pool_kernel, char* ws,
                           hipStream_t stream, int kstride, uint32_t* zero, size_t zero_words) {
@@ -1190,7 +1371,11 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
   a.c = scale * kLog2e;
   const dim3 grid(p.nchunk, p.nheads, p.ngroups);
   bool ok = false;
-  if (p.mfma32) {
+  if (p.keys_lds) {
+    a.s_out = s;
+    ok = d.head_dim == 128 ? dispatch_keys_lds<128>(d.seq_len, a, p.nheads, stream)
+                           : dispatch_keys_lds<64>(d.seq_len, a, p.nheads, stream);
+  } else if (p.mfma32) {
     ok = d.head_dim == 128 ? dispatch_qt32<128>(p.maxqt, a, grid, stream, p)
                            : dispatch_qt32<64>(p.maxqt, a, grid, stream, p);
   } else if (d.dtype == KVSEL_BF16) {
@@ -1201,7 +1386,7 @@ kvsel_status launch_score(const kvsel_desc& d, const ScorePlan& p, const void* q
                            : dispatch_qt<float, 64>(p.maxqt, a, grid, stream, p);
   }
   if (!ok) return KVSEL_ERR_UNSUPPORTED;
-  if (p.ngroups > 1) {
+  if (p.ngroups > 1 && !p.keys_lds) {
     const size_t n = (size_t)p.nheads * d.seq_len;
     KVSEL_LAUNCH("score_group_sum", score_group_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                        a.s_out, s, n, p.ngroups);
