@@ -151,6 +151,9 @@ size_t kvsel_score_workspace(const kvsel_desc* desc);
  *         KVSEL_ERR_DEVICE.
  * Numerics: bf16 or fp32 inputs, fp32 products and sums; the result does
  * not depend on how the keys are blocked; repeated calls are bitwise equal.
+ * Kernels: unmasked bf16 problems of at most 512 keys in whole 32-key tiles
+ * with at least 256 query rows per KV head run both passes in one launch per
+ * KV head, its keys held on chip; others run the two passes over key chunks.
  */
 kvsel_status kvsel_score(const kvsel_desc* desc, const void* q_obs, const void* k,
                          float* raw_scores, float* pooled, int32_t pool_kernel,
@@ -387,7 +390,9 @@ size_t kvsel_kara_score_workspace(const kvsel_kara_desc* desc);
  *   k_win   [Bt,Hkv,window,D] dtype, device: the window's keys (rows >= n,
  *           the buffer, are not read)
  *   scores  [Bt,Hkv,n] float32 out, device
- * Same kernels and numerics as kvsel_score (fp32 products and sums).
+ * Same kernels and numerics as kvsel_score on the same shape (fp32 products
+ * and sums); a window of n = window - buffer keys in whole 32-key tiles, up
+ * to 512, with G*window >= 256 query rows is scored in one launch per KV head.
  */
 kvsel_status kvsel_kara_score(const kvsel_kara_desc* desc, const void* q_win, const void* k_win,
                               float* scores, void* ws, size_t ws_bytes, void* stream);
