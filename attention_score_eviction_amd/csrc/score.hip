@@ -11,20 +11,26 @@
 // Kernel design (CDNA4, wave64):
 //  * One workgroup = one chunk of keys x one KV head x one group of up to
 //    qcap query rows.  The group's query rows are staged once in LDS in MFMA
-//    fragment order (each 16-row tile is 64 lanes x D*e/64 16-byte vectors,
-//    so every ds_read_b128 is a contiguous, conflict-free 1 KiB).
-//  * The query rows reach LDS by direct global->LDS copies (no registers).
+//    fragment order by direct global->LDS copies (every ds_read_b128 is a
+//    contiguous, conflict-free 1 KiB).
 //  * Every wave streams its own 64-key blocks straight from HBM into
-//    registers (4 tiles of 16 keys; each lane reads D*e/4 contiguous bytes of
-//    one key row, which is exactly its MFMA operand fragment), prefetching the
-//    next block, then loops over the query tiles in LDS.  Waves never
-//    synchronise inside the key loop.
-//  * The contraction uses v_mfma_f32_16x16x32_bf16 (bf16 inputs) or
-//    v_mfma_f32_16x16x4_f32 (fp32 inputs), fp32 accumulation.  The operand
-//    roles are swapped between the passes so that the dimension each pass
-//    reduces over stays inside a lane: pass 1 puts keys on the MFMA rows
+//    registers (each lane reads the contiguous bytes of one key row that
+//    form its MFMA operand fragment), then loops over the query tiles in
+//    LDS.  Waves never synchronise inside the key loop.
+//  * bf16 prompts of 4096 keys or more use v_mfma_f32_32x32x16_bf16 on
+//    32-row query tiles (score_pass1_32 / score_pass2_32); shorter ones and
+//    fp32 inputs use the 16x16 forms (score_pass1 / score_pass2).  The
+//    operand roles are swapped between the passes so that the dimension each
+//    pass reduces over stays inside a lane: pass 1 puts keys on the MFMA rows
 //    (each lane keeps running max/sum for one query row), pass 2 puts query
-//    rows on the MFMA rows (each lane keeps the running column sum for one key).
+//    rows on the MFMA rows (each lane keeps the running column sum for one
+//    key).
+//  * Pass 1 leaves per-chunk (max, sum) partials; score_combine merges them
+//    per row before pass 2, or, for plans with few rows and chunks, every
+//    pass-2 workgroup merges them itself in the same order (no launch).
+//  * Unmasked scoring of many query rows over at most 512 keys (a decode
+//    window scoring its own keys) runs both passes in one launch per KV head
+//    with the head's keys in LDS (score_keys_lds32).
 //  * Exponentials are exp2 with scale*log2(e) folded into one FMA per logit.
 #include <math.h>
 #include <stdlib.h>
@@ -727,13 +733,12 @@ __global__ void __launch_bounds__(NW * 64) score_pass2_32(ScoreArgs a) {
 // few keys by many query rows (Kara's decode window: G*|W| = 2048 rows per
 // KV head against its 448 compressible keys).  One workgroup per KV head
 // holds the head's S keys (a multiple of 32, at most 512) in LDS in fragment
-// order.  Each wave takes
-// 32-row query tiles straight from memory into registers and, with the same
-// fragments, first finds each row's max and log2-sum-exp over all keys
-// (keys on the matrix rows: one row per lane), then adds the row's
-// normalised weights into per-key column sums kept in registers (rows on the
-// matrix rows: one key per lane).  The waves' column sums are added in wave
-// order at the end.  Every key row and every query row is read once; there
+// order.  Each wave takes 32-row query tiles straight from memory into
+// registers and, with the same fragments, first finds each row's max and
+// log2-sum-exp over all keys (keys on the matrix rows: one row per lane),
+// then adds the row's normalised weights into per-key column sums kept in
+// registers (rows on the matrix rows: one key per lane).  The waves' column
+// sums are added in wave order at the end.  Every key row and every query row is read once; there
 // are no per-chunk statistics and no combine launch.
 constexpr int kKsMaxKeyTiles = 16;   // up to 512 keys
 constexpr int kKsWaves = 8;
