@@ -1309,6 +1309,11 @@ static bool plan_chunks(const kvsel_desc& d, ScorePlan* p, int lds_bytes) {
   p->off_grp = off;
   if (p->ngroups > 1) off = align256(off + (size_t)p->ngroups * p->nheads * d.seq_len * sizeof(float));
   p->total = off;
+  if (p->keys_lds) {
+    // one launch with no per-chunk statistics: only the raw score vector
+    p->off_part = p->off_lse = p->off_grp = p->off_raw = 0;
+    p->total = align256((size_t)p->nheads * d.seq_len * sizeof(float));
+  }
   return true;
 }
 

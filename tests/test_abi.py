@@ -198,6 +198,11 @@ def test_kara_checks(kv):
     assert L.kvsel_kara_select(ctypes.byref(good), None, FAKE, None) == kv.ERR_ARG
     # the window queries need no more scratch than O(Hkv * n + rows * chunks)
     assert need < 64 * 1024 * 1024
+    # 448 keys in whole 32-key tiles, 2560 query rows per KV head: one launch
+    # with the keys on chip, whose only scratch is the score vector
+    assert need == 2 * 8 * 448 * 4
+    # 452 keys (a partial last tile): the two-pass scoring and its statistics
+    assert L.kvsel_kara_score_workspace(ctypes.byref(K(buffer=60))) > 2 * 8 * 452 * 4
 
 
 def test_select_compact_checks(kv):
