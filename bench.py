@@ -213,6 +213,10 @@ def kernel_work(spec: synth.LayerSpec, kernel: str, n_keep: int) -> tuple:
     S, W, D = spec.seq_len, spec.obs_window, spec.head_dim
     GW = spec.group * W
     sweep, flops = H * S * D * e, 2 * H * GW * D * S
+    if kernel == "score_keys_lds32":
+        # both passes in one launch: keys and queries read once, the score
+        # vector written, the products of both passes
+        return sweep + H * GW * D * e + H * S * 4, 2 * flops
     if kernel.startswith("score_pass1"):
         return sweep, flops
     if kernel.startswith("score_pass2"):
@@ -900,6 +904,7 @@ def bench_kara(args, kvsel, torch, wname) -> int:
         "path_algorithmic_bytes": path,
         "us_per_call": {kk: round(vv, 2) for kk, vv in us.items()},
         "us_per_kernel": {kk: round(u, 2) for kk, (u, m) in kt.items()},
+        "binding_roofline": binding_roofline(kspec, path, step_us),
         "roofline": roofline_entry(dom, kt[dom][0], nbytes, kflops,
                                    traffic_for(args.workload, dom)),
     }

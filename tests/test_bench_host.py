@@ -38,6 +38,19 @@ def test_kernel_work_of_the_score_passes():
         4 * 8 * 4160 * 128 * 2 + 8 * 4160 * 4
 
 
+def test_kernel_work_of_the_keys_in_lds_scoring():
+    """Kara's 64 x 512 window batch (32 query / 8 KV heads, D = 128, 448
+    compressible keys): the one-launch scoring reads every key and every
+    query once, writes the score vector and does both passes' products."""
+    spec = synth.LayerSpec(64, 32, 8, 128, 448, 512, 1, 0, causal=0)
+    H, GW = 64 * 8, 4 * 512
+    keys, queries, scores = H * 448 * 128 * 2, H * GW * 128 * 2, H * 448 * 4
+    assert queries == 64 * 32 * 512 * 128 * 2
+    b, f = bench.kernel_work(spec, "score_keys_lds32", 0)
+    assert b == keys + queries + scores
+    assert f == 2 * (2 * H * GW * 128 * 448)
+
+
 def test_binding_roofline_of_the_128k_layer():
     spec = synth.config(4)
     r = bench.binding_roofline(spec, 587988992, 210.0)
