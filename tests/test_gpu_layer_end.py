@@ -38,6 +38,8 @@ CASES = [
     ("short-no-candidates", L(1, 4, 2, 64, 64, 60, 3, 0, n_sink=4), 66),
     ("short-f32", L(1, 4, 2, 64, 3000, 16, 7, 200, dtype="f32"), 67),
     ("short-budget-all", L(1, 8, 2, 128, 4000, 32, 3, 4000 - 32 - 1, n_sink=1), 68),
+    # unmasked, 512 keys, 256 query rows per KV head: keys-in-LDS scoring
+    ("short-noncausal-keys-on-chip", L(1, 32, 8, 128, 512, 64, 7, 300, causal=0), 69),
     # more candidates than one workgroup's register batches, budget 0: the
     # composed path
     ("budget-0", L(1, 8, 2, 128, 20000, 32, 7, 0), 49),

@@ -43,6 +43,11 @@ SMALL = [
     ("bf16-window-is-all", L(1, 2, 1, 128, 64, 64, 5, 0), 110),
     ("bf16-single-key", L(1, 2, 2, 64, 1, 1, 1, 0), 111),
     ("bf16-spans", L(1, 5, 1, 128, 4096, 64, 7, 512, structure="spans", n_spans=8), 112),
+    # unmasked, at most 512 keys in whole tiles, >= 256 query rows per KV
+    # head: one scoring launch per KV head with its keys in LDS
+    ("bf16-noncausal-keys-on-chip", L(1, 32, 8, 128, 512, 64, 7, 200, n_sink=2, causal=0,
+                                      structure="heavy"), 113),
+    ("bf16-noncausal-keys-on-chip-d64", L(2, 16, 2, 64, 320, 40, 5, 100, causal=0), 114),
     # prompts of 4096 keys or more run the 32x32 tiling: D = 64, a ragged
     # tail, sinks, no mask, and two query groups (640 rows: 512 + 128)
     ("bf16-long-d64-ragged", L(1, 4, 2, 64, 4500, 24, 5, 300, n_sink=2, structure="heavy"), 113),
